@@ -1,0 +1,217 @@
+/*
+ * eagle_mi355.h - C ABI of the EAGLE / EAGLE-2 tree-verification library for
+ * AMD MI355X (gfx950).
+ *
+ * One verification step of speculative decoding with a draft-token tree:
+ *   eagle2_rerank          build the EAGLE-2 dynamic draft tree from draft logits
+ *   eagle_tree_verify_attn tree attention of the target over prefix + tree
+ *   eagle_lm_head_argmax   frozen LM head fused with per-row max/argmax/softmax stats
+ *   eagle_accept_greedy    greedy acceptance (longest matching root path)
+ *   eagle_accept_spec      multi-round speculative sampling acceptance
+ *
+ * Sources (web pages on the method), cited per call below:
+ *   [P1] "大模型推理效率突破：EAGLE推测解码算法在摩尔线程GPU的实践与优化" (adg.csdn.net)
+ *   [P2] "大模型推理效率无损提升3倍，滑铁卢大学、北京大学等机构发布EAGLE" (www.0359xy.cn)
+ *   [P3] "EAGLE-2：動態草稿樹讓 LLM 推論加速 4 倍而不失精度" (friday-blog-bgf.pages.dev)
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Tree.  A draft tree of N nodes (N <= 64) per sequence is a parent array
+ *   parents[b][i]: parents[b][0] == -1 (node 0 is the root: the last token already
+ *   emitted) and 0 <= parents[b][i] < i for i > 0.  depth(root) = 0.
+ * Memory.  Every pointer is DEVICE memory owned by the caller, except where a
+ *   parameter name ends in _host.  The library allocates nothing, frees nothing
+ *   and keeps no state between calls; scratch memory is the caller's `workspace`
+ *   of at least the size the matching *_workspace() query returns (a query is a
+ *   pure function of the sizes and never touches the GPU).  All arrays are dense
+ *   row-major (C order) with the shapes given.
+ * Types.  bf16 tensors are IEEE bfloat16 bit patterns (uint16 storage); fp32 is
+ *   IEEE binary32; indices and tokens are int32.
+ * Streams.  Work is enqueued on `stream` (0 = the null stream) and the call
+ *   returns without waiting; outputs are valid when the stream reaches that point.
+ *   Calls are reentrant; two calls may share a workspace only if they are ordered
+ *   on one stream.
+ * Errors.  Arguments are checked on the host before anything is launched; a bad
+ *   argument returns a status and launches nothing.  EAGLE_ERR_HIP reports a HIP
+ *   launch error; eagle_last_error() gives the text (thread-local).  Kernels never
+ *   read or write outside the buffers described here whatever the CONTENT of
+ *   parents / tokens / draft_row; for contents that break the tree rules the
+ *   results are unspecified (eagle_check_tree() validates a tree on the host).
+ */
+#ifndef EAGLE_MI355_H
+#define EAGLE_MI355_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EAGLE_ABI_VERSION 1
+#define EAGLE_MAX_TREE 64   /* nodes per sequence, root included */
+#define EAGLE_MAX_TOPK 64
+
+typedef enum {
+  EAGLE_OK = 0,
+  EAGLE_ERR_NULL = 1,          /* a required pointer is NULL */
+  EAGLE_ERR_INVALID_ARG = 2,   /* a size is out of range or inconsistent */
+  EAGLE_ERR_UNSUPPORTED = 3,   /* valid but not implemented (e.g. N > 64, D not 64/128) */
+  EAGLE_ERR_WORKSPACE = 4,     /* workspace missing or smaller than the query's size */
+  EAGLE_ERR_TREE = 5,          /* eagle_check_tree: parent array breaks the tree rules */
+  EAGLE_ERR_HIP = 6            /* a HIP runtime call failed; see eagle_last_error() */
+} eagle_status_t;
+
+/* Version of this ABI (EAGLE_ABI_VERSION of the built library). */
+int eagle_abi_version(void);
+
+/* Static text for a status value (never NULL). */
+const char* eagle_status_string(int status);
+
+/* Detail text of the calling thread's last error (empty string if none). */
+const char* eagle_last_error(void);
+
+/*
+ * Host-side validation of B parent arrays of N nodes (parents_host[B][N], HOST
+ * memory): EAGLE_OK if every array has parents[0] == -1 and 0 <= parents[i] < i,
+ * EAGLE_ERR_TREE otherwise, EAGLE_ERR_INVALID_ARG if B < 1 or N < 1.
+ */
+eagle_status_t eagle_check_tree(const int32_t* parents_host, int32_t B, int32_t N);
+
+/*
+ * Tree-verify attention.  [P1] innovations list item 2 and [P2] workflow
+ * paragraph: every path of the draft tree is verified in ONE target pass by
+ * turning the tree into an attention mask.  For sequence b, tree node i and query
+ * head h (KV head g = h / (Hq / Hkv)), with keys
+ *     J(i) = {0 .. P-1}  U  {P + a : a is an ancestor of i or a == i}
+ * and scores s_j = scale * <q[b][i][h], k[b][g][j]>:
+ *     out[b][i][h] = sum_j softmax(s)_j * v[b][g][j]
+ *     lse[b][i][h] = log(sum_j exp(s_j))          (natural log)
+ * q, k are taken as already position-encoded.
+ *
+ *   q    bf16 [B][N][Hq][D]
+ *   k, v bf16 [B][Hkv][kv_cap][D]: rows 0..P-1 hold the prefix, rows P..P+N-1 the
+ *        tree nodes in node order; rows >= P+N are never read.  kv_cap >= P + N.
+ *   parents int32 [B][N]
+ *   out  bf16 [B][N][Hq][D] (written)
+ *   lse  fp32 [B][N][Hq] (written; may be NULL)
+ *   scale > 0 (usually 1/sqrt(D)); D in {64, 128}; Hq % Hkv == 0; N <= 64; P >= 0.
+ * Workspace: eagle_tree_verify_attn_workspace(B, N, Hq, Hkv, D, P) bytes (it holds
+ * split-KV partial results; 0 means none is needed and workspace may be NULL).
+ */
+size_t eagle_tree_verify_attn_workspace(int32_t B, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                                        int32_t P);
+eagle_status_t eagle_tree_verify_attn(const void* q, const void* k, const void* v,
+                                      const int32_t* parents, int32_t B, int32_t N, int32_t Hq,
+                                      int32_t Hkv, int32_t D, int32_t P, int32_t kv_cap,
+                                      float scale, void* out, float* lse, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Frozen LM head with fused row statistics.  [P2] paragraphs on the
+ * auto-regression head and the workflow: the target's frozen classification head
+ * turns a feature into the next-token distribution; [P1] greedy decoding takes its
+ * top-1.  logits = hidden @ weight^T, then per row m:
+ *     out_max[m]    = max_x logits[m][x]
+ *     out_argmax[m] = smallest x attaining that max
+ *     out_second[m] = max over x != out_argmax[m]   (judges near-ties; may be NULL)
+ *     out_lse[m]    = log(sum_x exp(logits[m][x]))   (natural log)
+ *     out_logits    = the fp32 logits [M][V] (may be NULL; needed by eagle_accept_spec)
+ *
+ *   hidden bf16 [M][H], weight bf16 [V][H] (nn.Linear layout).  H % 64 == 0, V >= 2.
+ * Workspace: eagle_lm_head_workspace(M, H, V) bytes (never 0).
+ */
+size_t eagle_lm_head_workspace(int32_t M, int32_t H, int32_t V);
+eagle_status_t eagle_lm_head_argmax(const void* hidden, const void* weight, int32_t M, int32_t H,
+                                    int32_t V, float* out_max, int32_t* out_argmax,
+                                    float* out_lse, float* out_second, float* out_logits,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Greedy acceptance.  [P1] greedy decoding paragraph and the figure paragraph
+ * after it; [P2] speculative sampling paragraph.  Node i (i > 0) survives when it
+ * and every node above it matches: tokens[i] == target_argmax[parents[i]] and its
+ * parent survives (the root always survives).  The winner v* is the deepest
+ * surviving node of depth <= max_depth (lowest index among equally deep ones);
+ * alpha = depth(v*) drafts are accepted and alpha + 1 tokens are emitted.
+ *
+ *   tokens, parents, target_argmax int32 [B][N] (target_argmax[b][i] = the target's
+ *     top-1 next token after node i; tokens[b][0] is the root token, not checked)
+ *   max_depth >= 0: capacity of the path outputs is max_depth + 1
+ *   accept_len  int32 [B]                 alpha
+ *   accept_path int32 [B][max_depth + 1]  root .. v* node indices, then -1
+ *   out_tokens  int32 [B][max_depth + 1]  tokens of path[1..], then target_argmax[v*], then -1
+ */
+eagle_status_t eagle_accept_greedy(const int32_t* tokens, const int32_t* parents,
+                                   const int32_t* target_argmax, int32_t B, int32_t N,
+                                   int32_t max_depth, int32_t* accept_len, int32_t* accept_path,
+                                   int32_t* out_tokens, hipStream_t stream);
+
+/*
+ * Multi-round speculative sampling.  [P1] stochastic verification paragraph (q is
+ * the target, p the draft; accept a draft token t when a uniform is below
+ * min(1, q(t)/p(t)), otherwise correct the target and retry), [P2] multi-round
+ * speculative sampling section (recursive form over the token tree, keeping the
+ * target distribution), [P3] section 2, speculative decoding basics.  At the
+ * current node v (starting at the root): q = softmax(target_logits[b][v]),
+ * p = softmax(draft_logits[b][draft_row[b][v]]); the children of v are tried in
+ * ascending node index with u_accept[b][child]: accept when
+ * u < min(1, q'(t)/p(t)) where q' is the corrected target (q' = q for the first
+ * child); a rejection replaces q' by the normalised positive part of (q' - p).  An
+ * accepted child becomes the current node.  When every child is rejected, one
+ * token is drawn from q' with u_sample[b][v]; at a node with no children, with
+ * draft_row < 0, or at depth max_depth, one token is drawn from q.  Draws are
+ * inverse-CDF: the smallest x whose cumulative mass exceeds u times the total.
+ *
+ *   tokens, parents, draft_row int32 [B][N] (draft_row[b][i] in [-1, draft_rows))
+ *   target_logits fp32 [B][N][V]; draft_logits fp32 [B][draft_rows][V]
+ *   u_accept, u_sample fp32 [B][N] in [0, 1)
+ *   outputs as eagle_accept_greedy.
+ * Workspace: eagle_accept_spec_workspace(B, N, V) bytes.
+ */
+size_t eagle_accept_spec_workspace(int32_t B, int32_t N, int32_t V);
+eagle_status_t eagle_accept_spec(const int32_t* tokens, const int32_t* parents,
+                                 const int32_t* draft_row, const float* target_logits,
+                                 const float* draft_logits, int32_t draft_rows,
+                                 const float* u_accept, const float* u_sample, int32_t B,
+                                 int32_t N, int32_t V, int32_t max_depth, int32_t* accept_len,
+                                 int32_t* accept_path, int32_t* out_tokens, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * EAGLE-2 dynamic draft tree.  [P3] section 2 (dynamic draft tree: confidence
+ * scoring, deep-where-confident / wide-where-not expansion, greedy maximisation of
+ * the expected acceptance length under a draft-token budget); [P1] innovations
+ * list items 1 and 3 (top tokens per draft step, pruning to high-probability
+ * paths).  Per sequence, draft_logits holds R = 1 + (depth-1)*top_k rows: row 0
+ * is the root's draft distribution, row 1 + (d-1)*top_k + j the one of frontier
+ * slot j at depth d.  Each expanded node proposes its row's top_k tokens (ties to
+ * the lower token id) with score = parent score + log_softmax(row)[token]; the
+ * frontier of depth d is the top_k depth-d candidates (score descending, then
+ * candidate id ascending; ids count depth by depth, slot by slot, rank by rank);
+ * the tree is the root plus the n_nodes - 1 best candidates overall, output
+ * breadth first (ascending candidate id).
+ *
+ *   draft_logits fp32 [B][R][V]; root_token int32 [B]
+ *   1 <= top_k <= 64, top_k <= V; depth >= 1; 1 <= n_nodes <= 64;
+ *   n_nodes - 1 <= top_k + (depth-1)*top_k*top_k
+ *   tokens, parents, depths int32 [B][n_nodes]; scores fp32 [B][n_nodes] (root 0)
+ *   draft_row int32 [B][n_nodes]: the row holding the node's own expansion (root 0,
+ *     -1 for nodes that were not expanded); draft_lse fp32 [B][R]: log-sum-exp of
+ *     every row.
+ * Workspace: eagle2_rerank_workspace(B, V, top_k, depth) bytes.
+ */
+size_t eagle2_rerank_workspace(int32_t B, int32_t V, int32_t top_k, int32_t depth);
+eagle_status_t eagle2_rerank(const float* draft_logits, const int32_t* root_token, int32_t B,
+                             int32_t V, int32_t top_k, int32_t depth, int32_t n_nodes,
+                             int32_t* tokens, int32_t* parents, int32_t* depths, float* scores,
+                             int32_t* draft_row, float* draft_lse, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EAGLE_MI355_H */

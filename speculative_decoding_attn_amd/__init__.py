@@ -1,0 +1,257 @@
+"""Python binding of the EAGLE / EAGLE-2 tree-verification library for MI355X.
+
+Thin ctypes wrappers with the C-ABI names (include/eagle_mi355.h).  They check
+tensor device, dtype and contiguity, allocate outputs and workspace through
+PyTorch (device memory only) and pass raw pointers plus the current HIP stream.
+Every step of the computation runs in the HIP kernels of ``libeagle_mi355.so``;
+there is no fallback: if the library is missing or a call fails, an exception is
+raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libeagle_mi355.so")
+
+_lib = None
+
+EAGLE_OK = 0
+STATUS_NAMES = {0: "EAGLE_OK", 1: "EAGLE_ERR_NULL", 2: "EAGLE_ERR_INVALID_ARG",
+                3: "EAGLE_ERR_UNSUPPORTED", 4: "EAGLE_ERR_WORKSPACE", 5: "EAGLE_ERR_TREE",
+                6: "EAGLE_ERR_HIP"}
+
+
+class EagleError(RuntimeError):
+    def __init__(self, status: int, func: str, detail: str):
+        super().__init__(f"{func}: {STATUS_NAMES.get(status, status)}: {detail}")
+        self.status = status
+
+
+_vp, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+
+_SIGNATURES = {
+    "eagle_abi_version": ([], ctypes.c_int),
+    "eagle_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "eagle_last_error": ([], ctypes.c_char_p),
+    "eagle_check_tree": ([_vp, _i32, _i32], ctypes.c_int),
+    "eagle_tree_verify_attn_workspace": ([_i32] * 6, _sz),
+    "eagle_tree_verify_attn": ([_vp, _vp, _vp, _vp] + [_i32] * 7 + [_f32, _vp, _vp, _vp, _sz, _vp],
+                               ctypes.c_int),
+    "eagle_lm_head_workspace": ([_i32] * 3, _sz),
+    "eagle_lm_head_argmax": ([_vp, _vp, _i32, _i32, _i32] + [_vp] * 6 + [_sz, _vp], ctypes.c_int),
+    "eagle_accept_greedy": ([_vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "eagle_accept_spec_workspace": ([_i32] * 3, _sz),
+    "eagle_accept_spec": ([_vp] * 5 + [_i32, _vp, _vp, _i32, _i32, _i32, _i32] + [_vp] * 4
+                          + [_sz, _vp], ctypes.c_int),
+    "eagle2_rerank_workspace": ([_i32] * 4, _sz),
+    "eagle2_rerank": ([_vp, _vp] + [_i32] * 5 + [_vp] * 7 + [_sz, _vp], ctypes.c_int),
+}
+
+
+def load(path: Optional[str] = None):
+    """Load the shared library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m speculative_decoding_attn_amd.build`")
+    lib = ctypes.CDLL(p)
+    for name, (args, res) in _SIGNATURES.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    _lib = lib
+    return lib
+
+
+def _check(status: int, func: str) -> None:
+    if status != EAGLE_OK:
+        raise EagleError(status, func, _lib.eagle_last_error().decode())
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtype, device) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def eagle_check_tree(parents) -> bool:
+    """Host-side validation of a [B][N] parent array (any array-like of ints)."""
+    lib = load()
+    t = torch.as_tensor(parents, dtype=torch.int32).contiguous().cpu()
+    if t.dim() == 1:
+        t = t[None]
+    st = lib.eagle_check_tree(t.data_ptr(), t.shape[0], t.shape[1])
+    if st not in (EAGLE_OK, 5):
+        _check(st, "eagle_check_tree")
+    return st == EAGLE_OK
+
+
+def eagle_tree_verify_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, parents: torch.Tensor,
+                           P: int, scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                           lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+                           workspace: Optional[torch.Tensor] = None):
+    """q [B][N][Hq][D] bf16; k, v [B][Hkv][kv_cap][D] bf16; parents [B][N] int32.
+
+    Returns (out [B][N][Hq][D] bf16, lse [B][N][Hq] fp32 or None)."""
+    lib = load()
+    dev = q.device
+    _need(q, "q", torch.bfloat16, dev)
+    _need(k, "k", torch.bfloat16, dev)
+    _need(v, "v", torch.bfloat16, dev)
+    _need(parents, "parents", torch.int32, dev)
+    B, N, Hq, D = q.shape
+    Hkv, kv_cap = k.shape[1], k.shape[2]
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != D or tuple(parents.shape) != (B, N):
+        raise ValueError("inconsistent shapes")
+    if scale is None:
+        scale = D ** -0.5
+    if out is None:
+        out = torch.empty((B, N, Hq, D), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, N, Hq), dtype=torch.float32, device=dev)
+    ws_bytes = lib.eagle_tree_verify_attn_workspace(B, N, Hq, Hkv, D, P)
+    if workspace is None and ws_bytes:
+        workspace = _workspace(ws_bytes, dev)
+    st = lib.eagle_tree_verify_attn(q.data_ptr(), k.data_ptr(), v.data_ptr(), parents.data_ptr(),
+                                    B, N, Hq, Hkv, D, P, kv_cap, float(scale), out.data_ptr(),
+                                    _ptr(lse), _ptr(workspace),
+                                    0 if workspace is None else workspace.numel(), _stream())
+    _check(st, "eagle_tree_verify_attn")
+    return out, lse
+
+
+def eagle_lm_head_argmax(hidden: torch.Tensor, weight: torch.Tensor, want_logits: bool = False,
+                         want_second: bool = True, workspace: Optional[torch.Tensor] = None):
+    """hidden [M][H] bf16, weight [V][H] bf16.
+
+    Returns dict(max, argmax, lse, second, logits) (second/logits may be None)."""
+    lib = load()
+    dev = hidden.device
+    _need(hidden, "hidden", torch.bfloat16, dev)
+    _need(weight, "weight", torch.bfloat16, dev)
+    M, H = hidden.shape
+    V = weight.shape[0]
+    if weight.shape[1] != H:
+        raise ValueError("hidden and weight disagree on H")
+    f = dict(device=dev)
+    res = {"max": torch.empty(M, dtype=torch.float32, **f),
+           "argmax": torch.empty(M, dtype=torch.int32, **f),
+           "lse": torch.empty(M, dtype=torch.float32, **f),
+           "second": torch.empty(M, dtype=torch.float32, **f) if want_second else None,
+           "logits": torch.empty((M, V), dtype=torch.float32, **f) if want_logits else None}
+    if workspace is None:
+        workspace = _workspace(lib.eagle_lm_head_workspace(M, H, V), dev)
+    st = lib.eagle_lm_head_argmax(hidden.data_ptr(), weight.data_ptr(), M, H, V,
+                                  res["max"].data_ptr(), res["argmax"].data_ptr(),
+                                  res["lse"].data_ptr(), _ptr(res["second"]), _ptr(res["logits"]),
+                                  workspace.data_ptr(), workspace.numel(), _stream())
+    _check(st, "eagle_lm_head_argmax")
+    return res
+
+
+def eagle_accept_greedy(tokens: torch.Tensor, parents: torch.Tensor, target_argmax: torch.Tensor,
+                        max_depth: int):
+    """tokens, parents, target_argmax [B][N] int32 -> (accept_len [B], accept_path, out_tokens
+    [B][max_depth+1])."""
+    lib = load()
+    dev = tokens.device
+    for t, n in ((tokens, "tokens"), (parents, "parents"), (target_argmax, "target_argmax")):
+        _need(t, n, torch.int32, dev)
+    B, N = tokens.shape
+    if tuple(parents.shape) != (B, N) or tuple(target_argmax.shape) != (B, N):
+        raise ValueError("inconsistent shapes")
+    alen = torch.empty(B, dtype=torch.int32, device=dev)
+    path = torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev)
+    out = torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev)
+    st = lib.eagle_accept_greedy(tokens.data_ptr(), parents.data_ptr(), target_argmax.data_ptr(),
+                                 B, N, max_depth, alen.data_ptr(), path.data_ptr(), out.data_ptr(),
+                                 _stream())
+    _check(st, "eagle_accept_greedy")
+    return alen, path, out
+
+
+def eagle_accept_spec(tokens: torch.Tensor, parents: torch.Tensor, draft_row: torch.Tensor,
+                      target_logits: torch.Tensor, draft_logits: torch.Tensor,
+                      u_accept: torch.Tensor, u_sample: torch.Tensor, max_depth: int,
+                      workspace: Optional[torch.Tensor] = None):
+    """tokens, parents, draft_row [B][N] int32; target_logits [B][N][V] fp32;
+    draft_logits [B][R][V] fp32; u_accept, u_sample [B][N] fp32."""
+    lib = load()
+    dev = tokens.device
+    for t, n in ((tokens, "tokens"), (parents, "parents"), (draft_row, "draft_row")):
+        _need(t, n, torch.int32, dev)
+    for t, n in ((target_logits, "target_logits"), (draft_logits, "draft_logits"),
+                 (u_accept, "u_accept"), (u_sample, "u_sample")):
+        _need(t, n, torch.float32, dev)
+    B, N = tokens.shape
+    V = target_logits.shape[-1]
+    R = draft_logits.shape[1]
+    if tuple(target_logits.shape) != (B, N, V) or tuple(draft_logits.shape) != (B, R, V):
+        raise ValueError("inconsistent logits shapes")
+    alen = torch.empty(B, dtype=torch.int32, device=dev)
+    path = torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev)
+    out = torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = _workspace(lib.eagle_accept_spec_workspace(B, N, V), dev)
+    st = lib.eagle_accept_spec(tokens.data_ptr(), parents.data_ptr(), draft_row.data_ptr(),
+                               target_logits.data_ptr(), draft_logits.data_ptr(), R,
+                               u_accept.data_ptr(), u_sample.data_ptr(), B, N, V, max_depth,
+                               alen.data_ptr(), path.data_ptr(), out.data_ptr(),
+                               workspace.data_ptr(), workspace.numel(), _stream())
+    _check(st, "eagle_accept_spec")
+    return alen, path, out
+
+
+def eagle2_rerank(draft_logits: torch.Tensor, root_token: torch.Tensor, top_k: int, depth: int,
+                  n_nodes: int, workspace: Optional[torch.Tensor] = None):
+    """draft_logits [B][R][V] fp32 (R = 1 + (depth-1)*top_k); root_token [B] int32.
+
+    Returns dict(tokens, parents, depths, scores, draft_row, draft_lse)."""
+    lib = load()
+    dev = draft_logits.device
+    _need(draft_logits, "draft_logits", torch.float32, dev)
+    _need(root_token, "root_token", torch.int32, dev)
+    B, R, V = draft_logits.shape
+    if R != 1 + (depth - 1) * top_k:
+        raise ValueError(f"draft_logits has {R} rows, expected {1 + (depth - 1) * top_k}")
+    f = dict(device=dev)
+    res = {"tokens": torch.empty((B, n_nodes), dtype=torch.int32, **f),
+           "parents": torch.empty((B, n_nodes), dtype=torch.int32, **f),
+           "depths": torch.empty((B, n_nodes), dtype=torch.int32, **f),
+           "scores": torch.empty((B, n_nodes), dtype=torch.float32, **f),
+           "draft_row": torch.empty((B, n_nodes), dtype=torch.int32, **f),
+           "draft_lse": torch.empty((B, R), dtype=torch.float32, **f)}
+    if workspace is None:
+        workspace = _workspace(lib.eagle2_rerank_workspace(B, V, top_k, depth), dev)
+    st = lib.eagle2_rerank(draft_logits.data_ptr(), root_token.data_ptr(), B, V, top_k, depth,
+                           n_nodes, res["tokens"].data_ptr(), res["parents"].data_ptr(),
+                           res["depths"].data_ptr(), res["scores"].data_ptr(),
+                           res["draft_row"].data_ptr(), res["draft_lse"].data_ptr(),
+                           workspace.data_ptr(), workspace.numel(), _stream())
+    _check(st, "eagle2_rerank")
+    return res

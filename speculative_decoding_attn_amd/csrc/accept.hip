@@ -1,0 +1,472 @@
+// Acceptance of a verified draft tree: greedy and multi-round speculative sampling.
+#include "common.h"
+#include "internal.h"
+
+namespace eagle {
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Greedy.  [P1] greedy decoding paragraph (match the target's top-1 from the first
+// draft on, cut at the first mismatch) and [P2] speculative sampling paragraph
+// (alpha accepted drafts give alpha + 1 tokens).  One wave per sequence, lane i =
+// node i: each lane walks its root path (at most 64 links, stopping at any link
+// that breaks the tree rules) to get its depth and whether every edge matches.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+accept_greedy_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict__ parents,
+                     const int32_t* __restrict__ top1, int B, int N, int max_depth,
+                     int32_t* __restrict__ accept_len, int32_t* __restrict__ accept_path,
+                     int32_t* __restrict__ out_tokens) {
+  const int lane = threadIdx.x & 63;
+  const int b = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+  if (b >= B) return;
+  const int32_t* tok = tokens + (size_t)b * N;
+  const int32_t* par = parents + (size_t)b * N;
+  const int32_t* am = top1 + (size_t)b * N;
+
+  int key = -1;
+  if (lane < N) {
+    bool ok = true;
+    bool reached = (lane == 0);
+    int depth = 0;
+    int n = lane;
+    for (int step = 0; step < 64 && n > 0; ++step) {
+      const int p = par[n];
+      if (p < 0 || p >= n) {
+        ok = false;
+        break;
+      }
+      if (tok[n] != am[p]) ok = false;
+      ++depth;
+      n = p;
+      if (n == 0) reached = true;
+    }
+    if (ok && reached && depth <= max_depth) key = depth * 64 + (63 - lane);
+  }
+  const int best = wave_max_i(key);   // >= 63: the root always qualifies
+  const int vstar = 63 - (best & 63);
+  const int alpha = best >> 6;
+
+  const int cap = max_depth + 1;
+  int32_t* path_out = accept_path + (size_t)b * cap;
+  int32_t* tok_out = out_tokens + (size_t)b * cap;
+  for (int j = lane; j < cap; j += 64) {
+    if (j <= alpha) {
+      int n = vstar;
+      for (int s = 0; s < alpha - j; ++s) n = par[n];   // the node at depth j on the path
+      path_out[j] = n;
+      if (j < alpha) {
+        int c = vstar;
+        for (int s = 0; s < alpha - j - 1; ++s) c = par[c];   // the node at depth j + 1
+        tok_out[j] = tok[c];
+      } else {
+        tok_out[j] = am[vstar];
+      }
+    } else {
+      path_out[j] = -1;
+      tok_out[j] = -1;
+    }
+  }
+  if (lane == 0) accept_len[b] = alpha;
+}
+
+// ---------------------------------------------------------------------------
+// Multi-round speculative sampling.  [P1] stochastic verification paragraph (q
+// target, p draft; accept below min(1, q/p), else resample from the corrected
+// distribution), [P2] multi-round speculative sampling section (the recursive
+// tree form), [P3] section 2 (rejection sampling keeps the output law).
+//
+// Closed form used on the device.  With q the target and p the draft at the current
+// node, after j rejections the corrected target is
+//     q_j = max(0, q - c_j p) / S(c_j),  S(c) = sum_x max(0, q(x) - c p(x)),
+// with c_0 = 0 and c_{j+1} = c_j + S(c_j): one rejection maps max(0, q - c p)/S to
+// the normalised positive part of (that - p), which is max(0, q - (c + S) p) up to
+// its normaliser.  So each rejection round is one vocabulary reduction of
+// max(0, q - c p) with the next c, and the acceptance ratio of token t is
+// max(0, q(t) - c p(t)) / (S p(t)).  All of it runs in fp64 on fp64 q and p.
+//
+// Parallel layout.  Each sequence gets `chunks` workgroups, each owning a contiguous
+// slice of the vocabulary.  Every workgroup follows the same control flow; the
+// vocabulary reductions are exchanged through the workspace and a per-sequence
+// counter barrier (release/acquire at agent scope).  Every spin is bounded: on
+// timeout the sequence's accept_len is set to -1 and all its workgroups leave.
+// ---------------------------------------------------------------------------
+constexpr int kSpecThreads = 256;
+constexpr unsigned kSpinLimit = 1u << 22;
+
+struct SpecWs {
+  unsigned* counters;   // [B] barrier arrivals
+  int* abort_flags;     // [B]
+  double* slots;        // [B][2][chunks][4] exchanged partials
+  double* qbuf;         // [B][V] fp64 q of the current node
+  double* pbuf;         // [B][V] fp64 p of the current node
+};
+
+__device__ __forceinline__ SpecWs spec_ws(void* ws, int B, int chunks, int V) {
+  SpecWs w;
+  char* base = (char*)ws;
+  w.counters = (unsigned*)base;
+  w.abort_flags = (int*)(base + 256 * ((B * 4 + 255) / 256));
+  size_t off = 2 * 256 * (size_t)((B * 4 + 255) / 256);
+  w.slots = (double*)(base + off);
+  off += (size_t)B * 2 * chunks * 4 * sizeof(double);
+  off = (off + 255) / 256 * 256;
+  w.qbuf = (double*)(base + off);
+  off += (size_t)B * V * sizeof(double);
+  w.pbuf = (double*)(base + off);
+  return w;
+}
+
+__global__ void spec_init_kernel(void* ws, int B, int chunks, int V) {
+  SpecWs w = spec_ws(ws, B, chunks, V);
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < B; i += gridDim.x * blockDim.x) {
+    w.counters[i] = 0u;
+    w.abort_flags[i] = 0;
+  }
+}
+
+// Workgroup-wide sum of a double (all threads get the result).
+__device__ __forceinline__ double wg_sum_d(double x, double* red) {
+  x = wave_sum_d(x);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wid] = x;
+  __syncthreads();
+  double t = 0.0;
+#pragma unroll
+  for (int i = 0; i < kSpecThreads / 64; ++i) t += red[i];
+  return t;
+}
+
+__device__ __forceinline__ double wg_max_d(double x, double* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmax(x, __shfl_xor(x, o));
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wid] = x;
+  __syncthreads();
+  double t = red[0];
+#pragma unroll
+  for (int i = 1; i < kSpecThreads / 64; ++i) t = fmax(t, red[i]);
+  return t;
+}
+
+// Publish this workgroup's 4 partials for generation `gen`, wait for all chunks of
+// the sequence, and return the chunk-ordered partials in lds_all[chunks][4].
+// Returns false on timeout.
+__device__ bool exchange(const SpecWs& w, int b, int chunks, int me, unsigned gen,
+                         const double (&mine)[4], double* lds_all, int* lds_flag) {
+  double* slot = w.slots + (((size_t)b * 2 + (gen & 1)) * chunks) * 4;
+  if (threadIdx.x < 4) slot[me * 4 + threadIdx.x] = mine[threadIdx.x];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int ok = 1;
+    if (chunks > 1) {
+      __hip_atomic_fetch_add(&w.counters[b], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned target = (gen + 1) * (unsigned)chunks;
+      unsigned spins = 0;
+      while (__hip_atomic_load(&w.counters[b], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
+        if (__hip_atomic_load(&w.abort_flags[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+          ok = 0;
+          break;
+        }
+        if (++spins > kSpinLimit) {
+          __hip_atomic_store(&w.abort_flags[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ok = 0;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    *lds_flag = ok;
+  }
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const bool ok = *lds_flag != 0;
+  if (ok) {
+    for (int i = threadIdx.x; i < chunks * 4; i += blockDim.x)
+      lds_all[i] = __hip_atomic_load(&slot[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  return ok;
+}
+
+__global__ void __launch_bounds__(kSpecThreads)
+accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict__ parents,
+                   const int32_t* __restrict__ draft_row, const float* __restrict__ target_logits,
+                   const float* __restrict__ draft_logits, const float* __restrict__ u_accept,
+                   const float* __restrict__ u_sample, SpecPlan pl, int32_t* __restrict__ accept_len,
+                   int32_t* __restrict__ accept_path, int32_t* __restrict__ out_tokens, void* ws) {
+  __shared__ double lds_all[4 * 64];
+  __shared__ double red[kSpecThreads / 64];
+  __shared__ int lds_flag;
+  __shared__ int kids[64];
+  __shared__ int nkids_s;
+  __shared__ int path_s[65];
+
+  const int chunks = pl.chunks;
+  const int b = blockIdx.x / chunks;
+  const int me = blockIdx.x % chunks;
+  const int N = pl.N, V = pl.V;
+  const int chunk_len = (V + chunks - 1) / chunks;
+  const int x0 = me * chunk_len;
+  const int x1 = min(V, x0 + chunk_len);
+  SpecWs w = spec_ws(ws, pl.B, chunks, V);
+  double* qb = w.qbuf + (size_t)b * V;
+  double* pb = w.pbuf + (size_t)b * V;
+  const int32_t* tok = tokens + (size_t)b * N;
+  const int32_t* par = parents + (size_t)b * N;
+  const int tid = threadIdx.x;
+
+  unsigned gen = 0;
+  int v = 0;
+  int alpha = 0;
+  if (tid == 0) path_s[0] = 0;
+  bool aborted = false;
+
+  double sample_c = 0.0;   // corrected target for the final draw: max(0, q - c p) / S
+  int sample_node = 0;
+
+  for (;;) {
+    // children of v in ascending index (none at max_depth)
+    if (tid < 64) {
+      const bool is_kid = tid < N && tid > 0 && par[tid] == v && alpha < pl.max_depth;
+      const unsigned long long mask = __ballot(is_kid);
+      if (is_kid) kids[__popcll(mask & ((1ull << tid) - 1ull))] = tid;
+      if (tid == 0) nkids_s = __popcll(mask);
+    }
+    __syncthreads();
+    const int nk = nkids_s;
+    int row = draft_row[(size_t)b * N + v];
+    const bool has_draft = nk > 0 && row >= 0 && row < pl.R;
+
+    // ---- q and p of node v: chunk max / exp-sum, exchanged, then fp64 values
+    const float* tl = target_logits + ((size_t)b * N + v) * V;
+    const float* dl = has_draft ? draft_logits + ((size_t)b * pl.R + row) * V : tl;
+    double mq = -INFINITY, mp = -INFINITY;
+    for (int x = x0 + tid; x < x1; x += kSpecThreads) {
+      mq = fmax(mq, (double)tl[x]);
+      mp = fmax(mp, (double)dl[x]);
+    }
+    mq = wg_max_d(mq, red);
+    mp = wg_max_d(mp, red);
+    double zq = 0.0, zp = 0.0;
+    for (int x = x0 + tid; x < x1; x += kSpecThreads) {
+      zq += exp((double)tl[x] - mq);
+      zp += exp((double)dl[x] - mp);
+    }
+    zq = wg_sum_d(zq, red);
+    zp = wg_sum_d(zp, red);
+    {
+      const double mine[4] = {mq, zq, mp, zp};
+      if (!exchange(w, b, chunks, me, gen++, mine, lds_all, &lds_flag)) { aborted = true; break; }
+    }
+    double Mq = -INFINITY, Mp = -INFINITY;
+    for (int c = 0; c < chunks; ++c) {
+      Mq = fmax(Mq, lds_all[4 * c]);
+      Mp = fmax(Mp, lds_all[4 * c + 2]);
+    }
+    double Zq = 0.0, Zp = 0.0;
+    for (int c = 0; c < chunks; ++c) {
+      if (lds_all[4 * c] > -INFINITY) Zq += lds_all[4 * c + 1] * exp(lds_all[4 * c] - Mq);
+      if (lds_all[4 * c + 2] > -INFINITY) Zp += lds_all[4 * c + 3] * exp(lds_all[4 * c + 2] - Mp);
+    }
+    const double lse_q = Mq + log(Zq);
+    const double lse_p = Mp + log(Zp);
+    for (int x = x0 + tid; x < x1; x += kSpecThreads) {
+      qb[x] = exp((double)tl[x] - lse_q);
+      pb[x] = exp((double)dl[x] - lse_p);
+    }
+    __syncthreads();
+
+    if (!has_draft) {
+      sample_c = 0.0;
+      sample_node = v;
+      break;
+    }
+
+    // ---- children in order against the corrected target
+    double cst = 0.0, S = 1.0;
+    int accepted = -1;
+    for (int j = 0; j < nk; ++j) {
+      const int kid = kids[j];
+      const int t = tok[kid];
+      double qt = 0.0, pt = 0.0;
+      if (t >= 0 && t < V) {
+        qt = exp((double)tl[t] - lse_q);
+        pt = exp((double)dl[t] - lse_p);
+      }
+      const double resid = fmax(0.0, qt - cst * pt);
+      const double ratio = pt > 0.0 ? fmin(1.0, resid / (S * pt)) : (resid > 0.0 ? 1.0 : 0.0);
+      if ((double)u_accept[(size_t)b * N + kid] < ratio) {
+        accepted = kid;
+        break;
+      }
+      const double c2 = cst + S;
+      double part = 0.0;
+      for (int x = x0 + tid; x < x1; x += kSpecThreads) part += fmax(0.0, qb[x] - c2 * pb[x]);
+      part = wg_sum_d(part, red);
+      const double mine[4] = {part, 0.0, 0.0, 0.0};
+      if (!exchange(w, b, chunks, me, gen++, mine, lds_all, &lds_flag)) { aborted = true; break; }
+      double S2 = 0.0;
+      for (int c = 0; c < chunks; ++c) S2 += lds_all[4 * c];
+      if (S2 > 0.0) {
+        cst = c2;
+        S = S2;
+      }
+    }
+    if (aborted) break;
+    if (accepted < 0) {
+      sample_c = cst;
+      sample_node = v;
+      break;
+    }
+    v = accepted;
+    ++alpha;
+    if (tid == 0) path_s[alpha] = v;
+    __syncthreads();
+  }
+
+  const int cap = pl.max_depth + 1;
+  if (!aborted) {
+    // ---- inverse-CDF draw from max(0, q - c p) (c = 0: q itself)
+    const double c = sample_c;
+    // contiguous per-thread ranges so that the scan runs in index order
+    const int span = x1 - x0;
+    const int per = (span + kSpecThreads - 1) / kSpecThreads;
+    const int t0 = x0 + tid * per;
+    const int t1 = min(x1, t0 + per);
+    double tsum = 0.0;
+    int tlast = -1;
+    for (int x = t0; x < t1; ++x) {
+      const double m = fmax(0.0, qb[x] - c * pb[x]);
+      tsum += m;
+      if (m > 0.0) tlast = x;
+    }
+    // exclusive scan of thread sums (index order) and the chunk total
+    __shared__ double scan_s[kSpecThreads];
+    __shared__ int last_s[kSpecThreads];
+    scan_s[tid] = tsum;
+    last_s[tid] = tlast;
+    __syncthreads();
+    double chunk_total = 0.0;
+    double before = 0.0;
+    int chunk_last = -1;
+    for (int i = 0; i < kSpecThreads; ++i) {
+      if (i == tid) before = chunk_total;
+      chunk_total += scan_s[i];
+      chunk_last = max(chunk_last, last_s[i]);
+    }
+    __syncthreads();
+    const double mine[4] = {chunk_total, (double)chunk_last, 0.0, 0.0};
+    if (!exchange(w, b, chunks, me, gen++, mine, lds_all, &lds_flag)) {
+      aborted = true;
+    } else {
+      double total = 0.0, offset = 0.0;
+      int glast = -1, glast_owner = 0;
+      for (int cc = 0; cc < chunks; ++cc) {
+        if (cc == me) offset = total;
+        total += lds_all[4 * cc];
+        if ((int)lds_all[4 * cc + 1] >= 0) {
+          glast = (int)lds_all[4 * cc + 1];
+          glast_owner = cc;
+        }
+      }
+      const double T = (double)u_sample[(size_t)b * N + sample_node] * total;
+      __shared__ int found_s;
+      if (tid == 0) found_s = -1;
+      __syncthreads();
+      if (T < total && T >= offset && T < offset + chunk_total) {
+        const double Tl = T - offset;
+        if (Tl >= before && Tl < before + tsum) {
+          double run = before;
+          for (int x = t0; x < t1; ++x) {
+            run += fmax(0.0, qb[x] - c * pb[x]);
+            if (run > Tl) {
+              found_s = x;
+              break;
+            }
+          }
+        }
+        __syncthreads();
+        if (tid == 0 && found_s < 0) found_s = chunk_last;   // rounding inside the chunk
+      } else if (!(T < total) && me == glast_owner) {
+        if (tid == 0) found_s = glast;                         // rounding past the total
+      }
+      __syncthreads();
+      if (tid == 0 && found_s >= 0) out_tokens[(size_t)b * cap + alpha] = found_s;
+    }
+  }
+
+  if (me == 0 && tid < 64) {
+    const bool bad = aborted;
+    for (int j = tid; j < cap; j += 64) {
+      if (bad) {
+        accept_path[(size_t)b * cap + j] = -1;
+        out_tokens[(size_t)b * cap + j] = -1;
+      } else if (j <= alpha) {
+        accept_path[(size_t)b * cap + j] = path_s[j];
+        if (j < alpha) out_tokens[(size_t)b * cap + j] = tok[path_s[j + 1]];
+      } else {
+        accept_path[(size_t)b * cap + j] = -1;
+        out_tokens[(size_t)b * cap + j] = -1;
+      }
+    }
+    if (tid == 0) accept_len[b] = bad ? -1 : alpha;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_accept_greedy(const int32_t* tokens, const int32_t* parents,
+                                const int32_t* target_argmax, int B, int N, int max_depth,
+                                int32_t* accept_len, int32_t* accept_path, int32_t* out_tokens,
+                                hipStream_t stream) {
+  hipLaunchKernelGGL(accept_greedy_kernel, dim3((B + 3) / 4), dim3(256), 0, stream, tokens, parents,
+                     target_argmax, B, N, max_depth, accept_len, accept_path, out_tokens);
+  return hipGetLastError();
+}
+
+SpecPlan plan_accept_spec(int B, int N, int V) {
+  SpecPlan pl{};
+  pl.B = B;
+  pl.N = N;
+  pl.V = V;
+  // about 4K vocabulary entries per workgroup, at most 64 per sequence, and at most
+  // 256 workgroups in all so that every workgroup of a sequence is resident at once
+  int c = (V + 4095) / 4096;
+  if (c > 64) c = 64;
+  int cap = 256 / (B > 0 ? B : 1);
+  if (cap < 1) cap = 1;
+  if (c > cap) c = cap;
+  if (c < 1) c = 1;
+  pl.chunks = c;
+  return pl;
+}
+
+size_t accept_spec_workspace_bytes(const SpecPlan& pl) {
+  size_t off = 2 * 256 * (size_t)((pl.B * 4 + 255) / 256);
+  off += (size_t)pl.B * 2 * pl.chunks * 4 * sizeof(double);
+  off = (off + 255) / 256 * 256;
+  off += 2 * (size_t)pl.B * pl.V * sizeof(double);
+  return off + 256;
+}
+
+hipError_t launch_accept_spec(const SpecPlan& pl, const int32_t* tokens, const int32_t* parents,
+                              const int32_t* draft_row, const float* target_logits,
+                              const float* draft_logits, const float* u_accept,
+                              const float* u_sample, int32_t* accept_len, int32_t* accept_path,
+                              int32_t* out_tokens, void* workspace, hipStream_t stream) {
+  hipLaunchKernelGGL(spec_init_kernel, dim3(1), dim3(256), 0, stream, workspace, pl.B, pl.chunks,
+                     pl.V);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(accept_spec_kernel, dim3(pl.B * pl.chunks), dim3(kSpecThreads), 0, stream,
+                     tokens, parents, draft_row, target_logits, draft_logits, u_accept, u_sample, pl,
+                     accept_len, accept_path, out_tokens, workspace);
+  return hipGetLastError();
+}
+
+}  // namespace eagle

@@ -1,0 +1,93 @@
+// Device-side helpers shared by the gfx950 kernels: vector types for the bf16
+// MFMA operands, bf16 conversion, wave64 reductions, status plumbing.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace eagle {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// D(32x32 fp32) += A(32x16 bf16) * B(16x32 bf16).  Lane l supplies A row l%32 and
+// B column l%32, each with k = 8*(l/32) .. 8*(l/32)+7; it receives D column l%32,
+// rows 8*(r/4) + 4*(l/32) + r%4 for r = 0..15.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+__device__ __forceinline__ u32x4 as_u32x4(bf16x8 x) { return __builtin_bit_cast(u32x4, x); }
+
+// fp32 -> bf16, round to nearest even (the hardware conversion on gfx950).
+__device__ __forceinline__ bf16x2 to_bf16x2(float a, float b) {
+  f32x2 v = {a, b};
+  return __builtin_convertvector(v, bf16x2);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, to_bf16x2(a, b));
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t x) {
+  return __builtin_bit_cast(float, (uint32_t)x << 16);
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+__device__ __forceinline__ double wave_sum_d(double x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+__device__ __forceinline__ int wave_min_i(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = min(x, __shfl_xor(x, o));
+  return x;
+}
+
+__device__ __forceinline__ int wave_max_i(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = max(x, __shfl_xor(x, o));
+  return x;
+}
+
+// Ancestor-or-self bitmask of node i (bit a set for every a on the root path of
+// i).  Walks at most 64 parent links and stops at any link that breaks the tree
+// rules, so it is memory-safe for any parent content.
+__device__ __forceinline__ uint64_t ancestor_mask(const int32_t* par, int i, int N) {
+  uint64_t m = 0;
+  int n = i;
+  for (int step = 0; step < 64; ++step) {
+    if (n < 0 || n >= N) break;
+    m |= 1ull << n;
+    int p = par[n];
+    if (p >= n) break;
+    n = p;
+  }
+  return m;
+}
+
+}  // namespace eagle

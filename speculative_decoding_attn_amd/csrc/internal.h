@@ -1,0 +1,80 @@
+// Host-side launch plans and launchers shared between the kernel files and the
+// C-ABI entry points.  Plans are pure functions of the problem sizes (the
+// workspace queries use them without touching the GPU).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace eagle {
+
+// MI355X: 256 CUs x 4 SIMDs.  Split-KV aims at about one wave per SIMD.
+constexpr int kTargetWaves = 1024;
+constexpr int kMinSplitKeys = 256;
+
+struct AttnPlan {
+  int B, N, Hq, Hkv, G, D, P, kv_cap;
+  int R;          // query rows per (sequence, KV head) = N * G
+  int waves;      // waves per workgroup (64 rows each)
+  int RB;         // row blocks per pair
+  int Rpad;       // RB * waves * 64
+  int S;          // key splits
+  int split_len;  // keys per split (multiple of 32); the last split also takes the tree
+  float c;        // scale * log2(e)
+};
+
+AttnPlan plan_tree_attn(int B, int N, int Hq, int Hkv, int D, int P, int kv_cap);
+size_t tree_attn_workspace_bytes(const AttnPlan& pl);
+hipError_t launch_tree_attn(const AttnPlan& pl, float scale, const void* q, const void* k,
+                            const void* v, const int32_t* parents, void* out, float* lse,
+                            void* workspace, hipStream_t stream);
+
+struct LmPlan {
+  int M, H, V;
+  int variant;    // tile-shape variant
+  int mrows;      // hidden rows per workgroup
+  int vrows;      // vocabulary rows per workgroup
+  int nvt;        // vocabulary tiles
+  int nmb;        // hidden-row blocks
+};
+
+LmPlan plan_lm_head(int M, int H, int V);
+size_t lm_head_workspace_bytes(const LmPlan& pl);
+hipError_t launch_lm_head(const LmPlan& pl, const void* hidden, const void* W, float* out_max,
+                          int32_t* out_argmax, float* out_lse, float* out_second, float* out_logits,
+                          void* workspace, hipStream_t stream);
+
+hipError_t launch_accept_greedy(const int32_t* tokens, const int32_t* parents,
+                                const int32_t* target_argmax, int B, int N, int max_depth,
+                                int32_t* accept_len, int32_t* accept_path, int32_t* out_tokens,
+                                hipStream_t stream);
+
+struct SpecPlan {
+  int B, N, V, R, max_depth;
+  int chunks;     // vocabulary chunks (one workgroup each) per sequence
+};
+SpecPlan plan_accept_spec(int B, int N, int V);
+size_t accept_spec_workspace_bytes(const SpecPlan& pl);
+hipError_t launch_accept_spec(const SpecPlan& pl, const int32_t* tokens, const int32_t* parents,
+                              const int32_t* draft_row, const float* target_logits,
+                              const float* draft_logits, const float* u_accept,
+                              const float* u_sample, int32_t* accept_len, int32_t* accept_path,
+                              int32_t* out_tokens, void* workspace, hipStream_t stream);
+
+struct RerankPlan {
+  int B, V, k, depth, R, n_nodes;
+  int chunks;     // vocabulary chunks per row for the top-k / log-sum-exp pass
+  int chunk_len;  // vocabulary entries per chunk
+};
+RerankPlan plan_rerank(int B, int V, int top_k, int depth, int n_nodes);
+size_t rerank_workspace_bytes(const RerankPlan& pl);
+hipError_t launch_rerank(const RerankPlan& pl, const float* draft_logits, const int32_t* root_token,
+                         int32_t* tokens, int32_t* parents, int32_t* depths, float* scores,
+                         int32_t* draft_row, float* draft_lse, void* workspace, hipStream_t stream);
+
+}  // namespace eagle
+
+namespace eagle {
+int rerank_max_candidates();
+}  // namespace eagle

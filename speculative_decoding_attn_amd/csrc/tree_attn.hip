@@ -1,0 +1,456 @@
+// Tree-verify attention for gfx950.
+//
+// [P1] innovations list item 2 / [P2] workflow paragraph: the target verifies
+// every path of the draft tree in one pass by masking attention with the tree.
+// Node i at query head h attends to the whole prefix and to its own root path.
+//
+// Work decomposition.  For one (sequence b, KV head g) pair the R = N*G query rows
+// (row r = node r/G, head g*G + r%G) share every K/V row, so a workgroup takes a
+// block of WAVES*64 rows of one pair and one contiguous range of keys ("split"):
+// K and V tiles of 32 keys are staged once in LDS and read by all of its waves.
+// Each wave owns 64 rows as two 32-row MFMA tiles.
+//
+// Orientation.  Scores are formed transposed, S^T = K * Q^T, with the 32x32x16 bf16
+// MFMA: lane l then holds 16 keys of ONE query row (l % 32), so the row max, the
+// exponentials and the row sum stay inside the lane (plus one exchange with lane
+// l ^ 32), and the output O^T = V^T * P^T again gives each lane one row.  P^T is fed
+// straight from the score registers; V is stored transposed in LDS with its key
+// positions permuted (bits 2 and 3 of the key index swapped) so that the key order
+// of the P^T registers and of the V^T operand agree.
+//
+// Mask.  The ancestor-or-self set of each lane's node is a 64-bit mask in
+// registers; only the key chunks that reach past the prefix are masked.
+//
+// Softmax.  Online max/sum in base 2 with scale*log2(e) folded into one FMA.  The
+// running max is only raised when a chunk exceeds it by more than 2^8 (values then
+// stay below 256), so O is rescaled rarely; the branch is taken per wave when any
+// lane needs it.
+//
+// Splits.  The prefix is cut into S ranges of whole 32-key chunks; the last range
+// also covers the tree keys.  With S > 1 every workgroup writes its normalised
+// partial output and log-sum-exp in fp32 and a merge kernel combines them.
+#include "common.h"
+#include "internal.h"
+
+namespace eagle {
+
+namespace {
+
+constexpr int KC = 32;            // keys per chunk
+constexpr float kLazy = 8.0f;     // log2 headroom before the running max is raised
+
+template <int D>
+struct AttnLds {
+  static constexpr int KSTR = D + 8;    // bf16 per K row (16 B pad: conflict-free b128 reads)
+  static constexpr int VSTR = KC + 8;   // bf16 per V^T row
+  static constexpr int KELEMS = KC * KSTR;
+  static constexpr int VELEMS = D * VSTR;
+  static constexpr int STAGE = KELEMS + VELEMS;
+};
+
+// key index within a 16-key group -> position in the V^T row (swap bits 2 and 3)
+__device__ __forceinline__ int vt_pos(int key) {
+  return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+}
+
+template <int D, int WAVES>
+__global__ void __launch_bounds__(WAVES * 64, 1)
+tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+              const uint16_t* __restrict__ v, const int32_t* __restrict__ parents,
+              AttnPlan pl, uint16_t* __restrict__ out, float* __restrict__ lse_out,
+              float* __restrict__ part_o, float* __restrict__ part_lse) {
+  using L = AttnLds<D>;
+  constexpr int THREADS = WAVES * 64;
+  constexpr int KSTEPS = D / 16;
+  constexpr int DBLK = D / 32;
+  constexpr int K_UNITS = KC * D / 8;          // 16-byte pieces of a K chunk
+  constexpr int V_UNITS = (KC / 2) * (D / 8);  // key pairs x 16-byte pieces of a V chunk
+  constexpr int K_PER = (K_UNITS + THREADS - 1) / THREADS;
+  constexpr int V_PER = (V_UNITS + THREADS - 1) / THREADS;
+
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * L::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = tid >> 6;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+
+  // blocks are dealt to the 8 XCDs round-robin; renumber so that consecutive
+  // logical blocks (the row blocks of one pair and split) share an XCD's L2
+  const int nwg = gridDim.x;
+  const int w = blockIdx.x;
+  const int logical = (nwg % 8 == 0) ? (w % 8) * (nwg / 8) + (w / 8) : w;
+  const int rb = logical % pl.RB;
+  const int split = (logical / pl.RB) % pl.S;
+  const int pair = logical / (pl.RB * pl.S);
+  const int b = pair / pl.Hkv;
+  const int g = pair % pl.Hkv;
+  const int G = pl.G;
+  const int N = pl.N;
+  const int P = pl.P;
+  const int key_begin = split * pl.split_len;
+  const int key_end = (split == pl.S - 1) ? P + N : min(P, (split + 1) * pl.split_len);
+  const int key_lim = P + N;
+
+  const uint16_t* kbase = k + (size_t)pair * pl.kv_cap * D;
+  const uint16_t* vbase = v + (size_t)pair * pl.kv_cap * D;
+  const int32_t* par = parents + (size_t)b * N;
+
+  // ---- Q^T operands (B side of S^T = K Q^T) and ancestor masks, per row tile
+  const int rowbase = rb * (WAVES * 64) + wid * 64;
+  bf16x8 qf[2][KSTEPS];
+  uint64_t anc[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int r = rowbase + 32 * t + l32;
+    if (r < pl.R) {
+      const int i = r / G;
+      const int h = g * G + (r - i * G);
+      const uint16_t* qp = q + ((size_t)(b * N + i) * pl.Hq + h) * D + 8 * half;
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) qf[t][s] = as_bf16x8(*(const u32x4*)(qp + 16 * s));
+      anc[t] = ancestor_mask(par, i, N);
+    } else {
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) qf[t][s] = as_bf16x8(u32x4{0, 0, 0, 0});
+      anc[t] = 1;
+    }
+  }
+
+  f32x16 oacc[2][DBLK];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[t][db][r] = 0.f;
+  float mc[2] = {-INFINITY, -INFINITY};   // running max of scale*log2e*s
+  float lsum[2] = {0.f, 0.f};             // this lane's half of the row sum
+
+  const float c = pl.c;
+
+  // ---- global -> registers for one chunk
+  u32x4 kreg[K_PER];
+  u32x4 vreg[V_PER][2];
+  auto load_chunk = [&](int kb) {
+#pragma unroll
+    for (int it = 0; it < K_PER; ++it) {
+      const int u = tid + it * THREADS;
+      kreg[it] = u32x4{0, 0, 0, 0};
+      if (u < K_UNITS) {
+        const int key = kb + u / (D / 8);
+        const int col = (u % (D / 8)) * 8;
+        if (key < key_lim) kreg[it] = *(const u32x4*)(kbase + (size_t)key * D + col);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < V_PER; ++it) {
+      const int u = tid + it * THREADS;
+      vreg[it][0] = u32x4{0, 0, 0, 0};
+      vreg[it][1] = u32x4{0, 0, 0, 0};
+      if (u < V_UNITS) {
+        const int kp = u % (KC / 2);
+        const int col = (u / (KC / 2)) * 8;
+        const int key = kb + 2 * kp;
+        if (key < key_lim) vreg[it][0] = *(const u32x4*)(vbase + (size_t)key * D + col);
+        if (key + 1 < key_lim) vreg[it][1] = *(const u32x4*)(vbase + (size_t)(key + 1) * D + col);
+      }
+    }
+  };
+  // ---- registers -> LDS stage (K as [key][d], V transposed as [d][permuted key])
+  auto store_chunk = [&](int st) {
+    uint16_t* Ks = lds + st * L::STAGE;
+    uint16_t* Vs = Ks + L::KELEMS;
+#pragma unroll
+    for (int it = 0; it < K_PER; ++it) {
+      const int u = tid + it * THREADS;
+      if (u < K_UNITS) {
+        const int key = u / (D / 8);
+        const int col = (u % (D / 8)) * 8;
+        *(u32x4*)(Ks + key * L::KSTR + col) = kreg[it];
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < V_PER; ++it) {
+      const int u = tid + it * THREADS;
+      if (u < V_UNITS) {
+        const int kp = u % (KC / 2);
+        const int col = (u / (KC / 2)) * 8;
+        const int key = 2 * kp;
+        const int pos = (key & 16) | vt_pos(key & 15);
+        const u32x4 a = vreg[it][0];
+        const u32x4 bb = vreg[it][1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // elements 2e and 2e+1 of each key's 8-wide piece
+          const uint32_t lo = (a[e] & 0xFFFFu) | (bb[e] << 16);
+          const uint32_t hi = (a[e] >> 16) | (bb[e] & 0xFFFF0000u);
+          *(uint32_t*)(Vs + (col + 2 * e) * L::VSTR + pos) = lo;
+          *(uint32_t*)(Vs + (col + 2 * e + 1) * L::VSTR + pos) = hi;
+        }
+      }
+    }
+  };
+
+  const int n_chunks = (key_end - key_begin + KC - 1) / KC;
+  if (n_chunks > 0) {
+    load_chunk(key_begin);
+    store_chunk(0);
+  }
+  __syncthreads();
+
+  for (int ch = 0; ch < n_chunks; ++ch) {
+    const int kb = key_begin + ch * KC;
+    const int st = ch & 1;
+    if (ch + 1 < n_chunks) load_chunk(kb + KC);
+
+    const uint16_t* Ks = lds + st * L::STAGE;
+    const uint16_t* Vs = Ks + L::KELEMS;
+
+    // S^T tile for 32 keys x 2 row tiles
+    f32x16 sacc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      const bf16x8 kf = *(const bf16x8*)(Ks + l32 * L::KSTR + 16 * s + 8 * half);
+      sacc[0] = mfma32(kf, qf[0][s], sacc[0]);
+      sacc[1] = mfma32(kf, qf[1][s], sacc[1]);
+    }
+
+    if (kb + KC > P) {
+      // chunk reaches into the tree (or past it): apply the ancestor mask
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb + 8 * (r >> 2) + 4 * half + (r & 3);
+          const int a = key - P;
+          const bool ok = key < P || (a < N && key < key_end && ((anc[t] >> (a & 63)) & 1ull));
+          if (!ok) sacc[t][r] = -INFINITY;
+        }
+    }
+
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      float mx = sacc[t][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[t][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mxc = mx * c;
+      const bool need = mxc > mc[t] + kLazy;
+      if (__ballot(need)) {
+        const float mnew = need ? mxc : mc[t];
+        const float alpha = need ? exp2f(mc[t] - mnew) : 1.f;
+        lsum[t] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[t][db][r] *= alpha;
+        mc[t] = mnew;
+      }
+      const float mcu = (mc[t] == -INFINITY) ? 0.f : mc[t];
+      float pr[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        pr[r] = __builtin_amdgcn_exp2f(fmaf(sacc[t][r], c, -mcu));
+        lsum[t] += pr[r];
+      }
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        u32x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pk[e] = pack_bf16x2(pr[8 * cc + 2 * e], pr[8 * cc + 2 * e + 1]);
+        pf[t][cc] = as_bf16x8(pk);
+      }
+    }
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const bf16x8 vf = *(const bf16x8*)(Vs + (32 * db + l32) * L::VSTR + 16 * cc + 8 * half);
+        oacc[0][db] = mfma32(vf, pf[0][cc], oacc[0][db]);
+        oacc[1][db] = mfma32(vf, pf[1][cc], oacc[1][db]);
+      }
+
+    if (ch + 1 < n_chunks) store_chunk(st ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int r = rowbase + 32 * t + l32;
+    const float ltot = lsum[t] + __shfl_xor(lsum[t], 32);
+    if (r >= pl.R) continue;
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    const float lse = (mc[t] + log2f(ltot)) * kLn2;
+    const int i = r / G;
+    const int h = g * G + (r - i * G);
+    if (pl.S == 1) {
+      uint16_t* op = out + ((size_t)(b * N + i) * pl.Hq + h) * D;
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d0 = 32 * db + 8 * j + 4 * half;
+          u32x2 pk;
+          pk[0] = pack_bf16x2(oacc[t][db][4 * j] * inv, oacc[t][db][4 * j + 1] * inv);
+          pk[1] = pack_bf16x2(oacc[t][db][4 * j + 2] * inv, oacc[t][db][4 * j + 3] * inv);
+          *(u32x2*)(op + d0) = pk;
+        }
+      if (half == 0 && lse_out) lse_out[(size_t)(b * N + i) * pl.Hq + h] = lse;
+    } else {
+      const size_t prow = ((size_t)pair * pl.S + split) * pl.Rpad + r;
+      float* op = part_o + prow * D;
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d0 = 32 * db + 8 * j + 4 * half;
+          f32x4 vv = {oacc[t][db][4 * j] * inv, oacc[t][db][4 * j + 1] * inv,
+                      oacc[t][db][4 * j + 2] * inv, oacc[t][db][4 * j + 3] * inv};
+          *(f32x4*)(op + d0) = vv;
+        }
+      if (half == 0) part_lse[prow] = lse;
+    }
+  }
+}
+
+// One wave per (pair, row): combine the S split partials with their lse weights.
+template <int D>
+__global__ void __launch_bounds__(256)
+tree_attn_merge(AttnPlan pl, const float* __restrict__ part_o, const float* __restrict__ part_lse,
+                uint16_t* __restrict__ out, float* __restrict__ lse_out) {
+  constexpr int PER = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+  const int pairs = pl.B * pl.Hkv;
+  if (gw >= pairs * pl.R) return;
+  const int pair = gw / pl.R;
+  const int r = gw % pl.R;
+  const int b = pair / pl.Hkv;
+  const int g = pair % pl.Hkv;
+  const size_t base = (size_t)pair * pl.S * pl.Rpad + r;
+  float mx = -INFINITY;
+  for (int s = 0; s < pl.S; ++s) mx = fmaxf(mx, part_lse[base + (size_t)s * pl.Rpad]);
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  float wsum = 0.f;
+  for (int s = 0; s < pl.S; ++s) {
+    const size_t prow = base + (size_t)s * pl.Rpad;
+    const float wgt = expf(part_lse[prow] - mx);
+    wsum += wgt;
+    const float* op = part_o + prow * D + lane * PER;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] += wgt * op[e];
+  }
+  const float inv = 1.f / wsum;
+  const int i = r / pl.G;
+  const int h = g * pl.G + (r - i * pl.G);
+  uint16_t* o = out + ((size_t)(b * pl.N + i) * pl.Hq + h) * D + lane * PER;
+  if (PER == 2) {
+    *(uint32_t*)o = pack_bf16x2(acc[0] * inv, acc[PER - 1] * inv);
+  } else {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const uint32_t pk = pack_bf16x2(acc[e] * inv, 0.f);
+      o[e] = (uint16_t)(pk & 0xFFFFu);
+    }
+  }
+  if (lane == 0 && lse_out) lse_out[(size_t)(b * pl.N + i) * pl.Hq + h] = mx + logf(wsum);
+}
+
+template <int D, int WAVES>
+hipError_t launch_fwd(const AttnPlan& pl, const void* q, const void* k, const void* v,
+                      const int32_t* parents, void* out, float* lse, float* part_o,
+                      float* part_lse, hipStream_t stream) {
+  const int nwg = pl.B * pl.Hkv * pl.RB * pl.S;
+  hipLaunchKernelGGL((tree_attn_fwd<D, WAVES>), dim3(nwg), dim3(WAVES * 64), 0, stream,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, parents, pl,
+                     (uint16_t*)out, lse, part_o, part_lse);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+AttnPlan plan_tree_attn(int B, int N, int Hq, int Hkv, int D, int P, int kv_cap) {
+  AttnPlan pl{};
+  pl.B = B;
+  pl.N = N;
+  pl.Hq = Hq;
+  pl.Hkv = Hkv;
+  pl.G = Hq / Hkv;
+  pl.D = D;
+  pl.P = P;
+  pl.kv_cap = kv_cap;
+  pl.R = N * pl.G;
+  pl.waves = pl.R > 128 ? 4 : (pl.R > 64 ? 2 : 1);
+  pl.RB = (pl.R + pl.waves * 64 - 1) / (pl.waves * 64);
+  pl.Rpad = pl.RB * pl.waves * 64;
+  const long long unit_waves = (long long)B * Hkv * pl.RB * pl.waves;
+  int s_target = (int)((kTargetWaves + unit_waves - 1) / unit_waves);
+  int s_max = P / kMinSplitKeys;
+  int S = s_target < s_max ? s_target : s_max;
+  if (S < 1) S = 1;
+  if (P <= 0) {
+    S = 1;
+    pl.split_len = 0;
+  } else {
+    int len = (P + S - 1) / S;
+    len = (len + KC - 1) / KC * KC;
+    S = (P + len - 1) / len;
+    pl.split_len = len;
+  }
+  pl.S = S;
+  return pl;
+}
+
+size_t tree_attn_workspace_bytes(const AttnPlan& pl) {
+  if (pl.S <= 1) return 0;
+  const size_t rows = (size_t)pl.B * pl.Hkv * pl.S * pl.Rpad;
+  return rows * (size_t)pl.D * sizeof(float) + rows * sizeof(float) + 256;
+}
+
+hipError_t launch_tree_attn(const AttnPlan& pl0, float scale, const void* q, const void* k,
+                            const void* v, const int32_t* parents, void* out, float* lse,
+                            void* workspace, hipStream_t stream) {
+  AttnPlan pl = pl0;
+  pl.c = scale * kLog2e;
+  float* part_o = nullptr;
+  float* part_lse = nullptr;
+  if (pl.S > 1) {
+    const size_t rows = (size_t)pl.B * pl.Hkv * pl.S * pl.Rpad;
+    part_o = (float*)workspace;
+    part_lse = part_o + rows * pl.D;
+  }
+  hipError_t e;
+  if (pl.D == 128) {
+    if (pl.waves == 4) e = launch_fwd<128, 4>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
+    else if (pl.waves == 2) e = launch_fwd<128, 2>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
+    else e = launch_fwd<128, 1>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
+  } else {
+    if (pl.waves == 4) e = launch_fwd<64, 4>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
+    else if (pl.waves == 2) e = launch_fwd<64, 2>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
+    else e = launch_fwd<64, 1>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
+  }
+  if (e != hipSuccess || pl.S == 1) return e;
+  const int rows = pl.B * pl.Hkv * pl.R;
+  const int blocks = (rows + 3) / 4;
+  if (pl.D == 128)
+    hipLaunchKernelGGL(tree_attn_merge<128>, dim3(blocks), dim3(256), 0, stream, pl, part_o, part_lse,
+                       (uint16_t*)out, lse);
+  else
+    hipLaunchKernelGGL(tree_attn_merge<64>, dim3(blocks), dim3(256), 0, stream, pl, part_o, part_lse,
+                       (uint16_t*)out, lse);
+  return hipGetLastError();
+}
+
+}  // namespace eagle

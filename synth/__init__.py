@@ -16,6 +16,8 @@ values (the oracle widens them to fp64).
 from .gen import (  # noqa: F401
     CHUNK,
     bf16_bits_to_f32,
+    chain_parents,
+    random_parents,
     bf16_bits_to_f64,
     integers,
     normal_bf16_bits,

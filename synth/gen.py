@@ -126,3 +126,16 @@ def plant_tokens(parents: np.ndarray, parent_argmax: np.ndarray, prob: float, vo
             if u[b, i] < prob:
                 tok[b, i] = parent_argmax[b, parents[b, i]]
     return tok.astype(np.int32)
+
+
+def random_parents(B: int, N: int, seed: int, cfg: int, tensor: int) -> np.ndarray:
+    """B random trees of N nodes: parents[b][0] = -1, parents[b][i] uniform in [0, i)."""
+    u = uniform_f32((B, N), seed, cfg, tensor).astype(np.float64)
+    par = np.floor(u * np.arange(N)[None, :]).astype(np.int32)
+    par = np.minimum(par, np.maximum(np.arange(N)[None, :] - 1, 0)).astype(np.int32)
+    par[:, 0] = -1
+    return par
+
+
+def chain_parents(B: int, N: int) -> np.ndarray:
+    return np.tile(np.arange(-1, N - 1, dtype=np.int32), (B, 1))

@@ -1,0 +1,144 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before launching anything."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import speculative_decoding_attn_amd as sda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "eagle_mi355.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(eagle\w*)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return sda.load()
+
+
+def test_header_declares_the_five_calls():
+    names = _declared()
+    for n in ("eagle_tree_verify_attn", "eagle_lm_head_argmax", "eagle_accept_greedy",
+              "eagle_accept_spec", "eagle2_rerank"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_binding_covers_every_symbol():
+    assert set(_declared()) == set(sda._SIGNATURES)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.eagle_abi_version() == 1
+    assert lib.eagle_status_string(0) == b"ok"
+    assert lib.eagle_status_string(99) == b"unknown status"
+
+
+def _tree(arr):
+    a = np.ascontiguousarray(np.asarray(arr, dtype=np.int32))
+    return a, a.ctypes.data
+
+
+def test_check_tree(lib):
+    a, p = _tree([[-1, 0, 0, 1, 3], [-1, 0, 1, 1, 2]])
+    assert lib.eagle_check_tree(p, 2, 5) == 0
+    a, p = _tree([[-1, 0, 2]])
+    assert lib.eagle_check_tree(p, 1, 3) == 5
+    assert b"parents[2]" in lib.eagle_last_error()
+    a, p = _tree([[0, 0]])
+    assert lib.eagle_check_tree(p, 1, 2) == 5
+    assert lib.eagle_check_tree(None, 1, 2) == 1
+    assert lib.eagle_check_tree(p, 0, 2) == 2
+    assert sda.eagle_check_tree([-1, 0, 1]) is True
+    assert sda.eagle_check_tree([-1, 1, 1]) is False
+
+
+FAKE = 1 << 20   # a non-NULL, 16-byte aligned address that is never dereferenced
+
+
+def test_attention_argument_errors(lib):
+    f = lib.eagle_tree_verify_attn
+    ok = dict(B=1, N=10, Hq=2, Hkv=1, D=64, P=128, cap=138, scale=0.125)
+
+    def call(q=FAKE, parents=FAKE, out=FAKE, B=1, N=10, Hq=2, Hkv=1, D=64, P=128, cap=138,
+             scale=0.125, ws=None, wsb=0):
+        return f(q, FAKE, FAKE, parents, B, N, Hq, Hkv, D, P, cap, scale, out, None, ws, wsb, None)
+
+    assert call(q=None) == 1
+    assert call(out=None) == 1
+    assert call(B=0) == 2
+    assert call(Hq=3, Hkv=2) == 2
+    assert call(N=65, cap=200) == 3
+    assert call(D=96) == 3
+    assert call(cap=137) == 2
+    assert call(scale=0.0) == 2
+    assert call(scale=float("nan")) == 2
+    assert call(q=FAKE + 2) == 2
+    # a shape that needs split-KV partials, without workspace
+    need = lib.eagle_tree_verify_attn_workspace(1, 60, 32, 8, 128, 4096)
+    assert need > 0
+    assert call(N=60, Hq=32, Hkv=8, D=128, P=4096, cap=4156) == 4
+    assert call(N=60, Hq=32, Hkv=8, D=128, P=4096, cap=4156, ws=FAKE, wsb=need - 1) == 4
+    assert b"need" in lib.eagle_last_error()
+
+
+def test_workspace_queries_are_pure_and_consistent(lib):
+    assert lib.eagle_tree_verify_attn_workspace(1, 10, 2, 1, 64, 128) == 0      # no split
+    a = lib.eagle_tree_verify_attn_workspace(4, 60, 64, 8, 128, 32768)
+    assert a > 0 and a == lib.eagle_tree_verify_attn_workspace(4, 60, 64, 8, 128, 32768)
+    assert lib.eagle_tree_verify_attn_workspace(1, 65, 2, 1, 64, 128) == 0     # unsupported
+    assert lib.eagle_lm_head_workspace(240, 8192, 128256) >= 240 * 16
+    assert lib.eagle_lm_head_workspace(10, 100, 1000) == 0                     # H % 64 != 0
+    assert lib.eagle_accept_spec_workspace(1, 60, 128256) >= 2 * 8 * 128256
+    assert lib.eagle2_rerank_workspace(4, 128256, 10, 6) > 0
+
+
+def test_lm_head_argument_errors(lib):
+    f = lib.eagle_lm_head_argmax
+
+    def call(hidden=FAKE, M=4, H=64, V=100, out=FAKE, ws=FAKE, wsb=1 << 20):
+        return f(hidden, FAKE, M, H, V, out, FAKE, FAKE, None, None, ws, wsb, None)
+
+    assert call(hidden=None) == 1
+    assert call(out=None) == 1
+    assert call(M=0) == 2
+    assert call(V=1) == 2
+    assert call(H=100) == 3
+    assert call(ws=None) == 4
+    assert call(wsb=16) == 4
+
+
+def test_accept_and_rerank_argument_errors(lib):
+    g = lib.eagle_accept_greedy
+    assert g(None, FAKE, FAKE, 1, 5, 4, FAKE, FAKE, FAKE, None) == 1
+    assert g(FAKE, FAKE, FAKE, 1, 65, 4, FAKE, FAKE, FAKE, None) == 3
+    assert g(FAKE, FAKE, FAKE, 1, 5, -1, FAKE, FAKE, FAKE, None) == 2
+    s = lib.eagle_accept_spec
+    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, None, 1, 5, 8, 3, FAKE, FAKE, FAKE, FAKE,
+             1 << 20, None) == 1
+    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 1, 5, 8, 3, FAKE, FAKE, FAKE, None, 0,
+             None) == 4
+    r = lib.eagle2_rerank
+
+    def rr(B=1, V=100, k=10, depth=3, n=20, ws=FAKE, wsb=1 << 24):
+        return r(FAKE, FAKE, B, V, k, depth, n, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, wsb, None)
+
+    assert rr(k=0) == 2
+    assert rr(k=65, V=1000) == 3
+    assert rr(k=10, V=5) == 2
+    assert rr(n=65) == 3
+    assert rr(k=2, depth=2, n=8) == 2          # only 2 + 4 = 6 candidates
+    assert rr(k=64, depth=3, V=1000, n=10) == 3  # too many candidates
+    assert rr(ws=None) == 4

@@ -1,0 +1,166 @@
+"""GPU parity: eagle_accept_greedy (bit-exact) and eagle_accept_spec (decisions
+bit-exact for the same uniforms; the resampled token in distribution)."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy.stats import chi2
+
+import oracle
+import synth
+from inputs import to_dev
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _greedy_gpu(lib, tokens, parents, top1, max_depth):
+    a, p, o = lib.eagle_accept_greedy(to_dev(tokens), to_dev(parents), to_dev(top1), max_depth)
+    torch.cuda.synchronize()
+    return a.cpu().numpy(), p.cpu().numpy(), o.cpu().numpy()
+
+
+def _padded(seq, cap):
+    return list(seq) + [-1] * (cap - len(seq))
+
+
+def test_greedy_worked_example(gpu_lib):
+    g = json.load(open(os.path.join(GOLDEN, "greedy_worked_example.json")))
+    a, p, o = _greedy_gpu(gpu_lib, np.array([g["tokens"]], np.int32),
+                          np.array([g["parents"]], np.int32),
+                          np.array([g["target_argmax"]], np.int32), g["max_depth"])
+    cap = g["max_depth"] + 1
+    assert a[0] == g["expect"]["alpha"]
+    assert list(p[0]) == _padded(g["expect"]["path"], cap)
+    assert list(o[0]) == _padded(g["expect"]["out_tokens"], cap)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_greedy_random_trees(gpu_lib, seed):
+    B, N, V = 97, int([5, 26, 60, 64][seed]), 7
+    parents = synth.random_parents(B, N, seed, 500, 1)
+    top1 = synth.integers((B, N), 0, V, seed, 500, 2)
+    noise = synth.integers((B, N), 0, V, seed, 500, 3)
+    u = synth.uniform_f32((B, N), seed, 500, 4)
+    tokens = np.where(u < 0.7, np.take_along_axis(top1, np.maximum(parents, 0), 1), noise)
+    tokens = tokens.astype(np.int32)
+    max_depth = [2, 5, 8, 63][seed]
+    a, p, o = _greedy_gpu(gpu_lib, tokens, parents, top1, max_depth)
+    cap = max_depth + 1
+    for b in range(B):
+        alpha, path, out = oracle.accept_greedy(tokens[b], parents[b], top1[b], max_depth)
+        assert a[b] == alpha and len(out) == alpha + 1
+        assert list(p[b]) == _padded(path, cap)
+        assert list(o[b]) == _padded(out, cap)
+
+
+def _spec_gpu(lib, tokens, parents, draft_row, tl, dl, ua, us, max_depth):
+    a, p, o = lib.eagle_accept_spec(to_dev(tokens), to_dev(parents), to_dev(draft_row), to_dev(tl),
+                                    to_dev(dl), to_dev(ua), to_dev(us), max_depth)
+    torch.cuda.synchronize()
+    return a.cpu().numpy(), p.cpu().numpy(), o.cpu().numpy()
+
+
+def _spec_case(seed, B, N, V, R_per, k_sib, tl_std, dl_std, plant_p):
+    """Trees whose internal nodes have their own draft row; sibling tokens drawn
+    from the parent's draft distribution (a mix of i.i.d. draws and fixed tokens)."""
+    parents = synth.random_parents(B, N, seed, 600, 1)
+    tl = synth.normal_f32((B, N, V), tl_std, seed, 600, 2)
+    dl = synth.normal_f32((B, R_per, V), dl_std, seed, 600, 3)
+    ua = synth.uniform_f32((B, N), seed, 600, 4)
+    us = synth.uniform_f32((B, N), seed, 600, 5)
+    rowpick = synth.integers((B, N), 0, R_per, seed, 600, 6)
+    draft_row = np.full((B, N), -1, np.int32)
+    for b in range(B):
+        internal = sorted(set(parents[b, 1:].tolist()))
+        for v in internal:
+            draft_row[b, v] = rowpick[b, v]
+    # tokens: draft samples from the parent's draft row
+    pu = synth.uniform_f32((B, N), seed, 600, 7)
+    tokens = np.zeros((B, N), np.int32)
+    for b in range(B):
+        for i in range(1, N):
+            row = dl[b, draft_row[b, parents[b, i]]].astype(np.float64)
+            p = np.exp(row - row.max())
+            p /= p.sum()
+            tokens[b, i] = min(int(np.searchsorted(np.cumsum(p), pu[b, i] * p.sum(), side="right")), V - 1)
+    return tokens, parents, draft_row, tl, dl, ua, us
+
+
+@pytest.mark.parametrize("seed,B,N,V", [(0, 64, 8, 8), (1, 16, 20, 1000), (2, 4, 60, 5003),
+                                        (3, 2, 64, 40000)])
+def test_spec_decisions_match_oracle(gpu_lib, seed, B, N, V):
+    tokens, parents, draft_row, tl, dl, ua, us = _spec_case(seed, B, N, V, 5, 0, 1.0, 1.5, 0)
+    max_depth = 64
+    print(f"spec parity seed={seed} B={B} N={N} V={V}", flush=True)
+    a, p, o = _spec_gpu(gpu_lib, tokens, parents, draft_row, tl, dl, ua, us, max_depth)
+    cap = max_depth + 1
+    near = 0
+    tok_diff = 0
+    for b in range(B):
+        trace = []
+        alpha, path, out = oracle.accept_spec(tokens[b], parents[b], tl[b], dl[b], draft_row[b],
+                                              ua[b], us[b], max_depth, trace=trace)
+        margins = [abs(float(ua[b, kid]) - r) for (_, kids, ratios, _) in trace
+                   for kid, r in zip(kids, ratios)]
+        if margins and min(margins) <= 1e-6:
+            near += 1
+            continue
+        assert a[b] == alpha
+        assert list(p[b]) == _padded(path, cap)
+        assert list(o[b, :alpha]) == out[:alpha]
+        assert 0 <= o[b, alpha] < V
+        tok_diff += int(o[b, alpha] != out[alpha])
+    assert near <= max(1, B // 20)
+    # the resampled token is compared in distribution (chi-square test below); with
+    # fp64 arithmetic on both sides it also agrees here except next to a CDF boundary
+    assert tok_diff <= max(1, B // 20)
+
+
+def test_spec_chi_square_on_gpu(gpu_lib):
+    """2e5 independent trials in one launch, V = 8, root with 3 children drawn i.i.d.
+    from the draft: the first emitted token must follow q."""
+    T, V, N = 200_000, 8, 4
+    tlrow = synth.normal_f32((V,), 1.2, 0, 650, 1)
+    dlrow = synth.normal_f32((V,), 2.0, 0, 650, 2)
+    q = np.exp(tlrow - tlrow.max()); q /= q.sum()
+    p = np.exp(dlrow - dlrow.max()); p /= p.sum()
+    parents = np.tile(np.array([-1, 0, 0, 0], np.int32), (T, 1))
+    draft_row = np.tile(np.array([0, -1, -1, -1], np.int32), (T, 1))
+    pu = synth.uniform_f32((T, N), 0, 650, 3)
+    tokens = np.minimum(np.searchsorted(np.cumsum(p), pu, side="right"), V - 1).astype(np.int32)
+    tokens[:, 0] = 0
+    tl = np.broadcast_to(tlrow, (T, N, V)).copy()
+    dl = np.broadcast_to(dlrow, (T, 1, V)).copy()
+    ua = synth.uniform_f32((T, N), 0, 650, 4)
+    us = synth.uniform_f32((T, N), 0, 650, 5)
+    a, path, o = _spec_gpu(gpu_lib, tokens, parents, draft_row, tl, dl, ua, us, 5)
+    first = np.bincount(o[:, 0], minlength=V)[:V].astype(np.float64)
+    stat = ((first - T * q) ** 2 / (T * q)).sum()
+    assert chi2.sf(stat, V - 1) > 1e-3, (first / T, q)
+
+
+def test_spec_full_c4_tree(gpu_lib):
+    """C4 shapes: a 60-node tree from the oracle's rerank of the C4 draft logits; target
+    logits N(0,1) over 128256 tokens, draft logits N(0,9): every root child is rejected
+    (q is flat, p peaky), so this runs the 10 residual rounds."""
+    cfg = synth.CONFIGS["C4"]
+    V = cfg.V
+    dl = synth.normal_f32((1, cfg.rows, V), cfg.draft_std, 0, cfg.index, 6)
+    root = int(synth.integers((1,), 0, V, 0, cfg.index, 7)[0])
+    tree = oracle.eagle2_rerank(dl[0], root, cfg.top_k, cfg.depth, cfg.N)
+    tl = synth.normal_f32((1, cfg.N, V), 1.0, 0, cfg.index, 10)
+    ua = synth.uniform_f32((1, cfg.N), 0, cfg.index, 8)
+    us = synth.uniform_f32((1, cfg.N), 0, cfg.index, 9)
+    toks = tree["tokens"][None].astype(np.int32)
+    par = tree["parents"][None].astype(np.int32)
+    drow = tree["draft_row"][None].astype(np.int32)
+    a, p, o = _spec_gpu(gpu_lib, toks, par, drow, tl, dl, ua, us, cfg.max_depth)
+    trace = []
+    alpha, path, out = oracle.accept_spec(toks[0], par[0], tl[0], dl[0], drow[0], ua[0], us[0],
+                                          cfg.max_depth, trace=trace)
+    assert a[0] == alpha and list(p[0, :alpha + 1]) == path
+    assert len(trace[0][2]) == 10 and trace[0][3] == -1       # ten rejections at the root
+    assert 0 <= o[0, alpha] < V

@@ -1,0 +1,116 @@
+"""GPU parity: eagle_tree_verify_attn against the fp64 oracle on identical bf16 inputs.
+
+Tolerance (bf16 inputs, fp32 accumulation, bf16 output): max-abs 2e-2 and relative
+L2 5e-3 on the output; lse within 2e-3 absolute."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from inputs import assert_close_attn, bf16, to_dev, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(cfg_id, B, N, Hq, Hkv, D, P, parents, cap_extra=0, seed=0):
+    qb, q = bf16((B, N, Hq, D), 1.0, seed, cfg_id, 1)
+    kb, k = bf16((B, Hkv, P + N + cap_extra, D), 1.0, seed, cfg_id, 2)
+    vb, v = bf16((B, Hkv, P + N + cap_extra, D), 1.0, seed, cfg_id, 3)
+    if cap_extra:
+        # capacity rows past P+N hold NaN: they must never be read
+        kb[:, :, P + N:] = 0x7FC0
+        vb[:, :, P + N:] = 0x7FC0
+    return (qb, kb, vb), (q, k, v), np.asarray(parents, dtype=np.int32)
+
+
+def _run(gpu_lib, bits, parents, P, scale):
+    qb, kb, vb = bits
+    out, lse = gpu_lib.eagle_tree_verify_attn(to_dev_bf16(qb), to_dev_bf16(kb), to_dev_bf16(vb),
+                                              to_dev(parents), P, scale)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), lse.cpu().numpy()
+
+
+CASES = [
+    # (B, N, Hq, Hkv, D, P, tree)
+    (1, 10, 2, 1, 64, 128, "c1"),
+    (1, 1, 4, 1, 128, 0, "chain"),
+    (1, 7, 4, 4, 128, 0, "rand"),
+    (2, 33, 8, 2, 128, 31, "rand"),
+    (1, 64, 4, 1, 64, 32, "rand"),
+    (1, 64, 2, 2, 128, 33, "chain"),
+    (3, 17, 6, 3, 64, 300, "rand"),
+    (1, 26, 32, 32, 128, 1024, "c2"),
+    (2, 60, 8, 1, 128, 777, "rand"),
+    (1, 40, 16, 2, 128, 2048, "rand"),
+    (1, 5, 12, 4, 64, 5000, "rand"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_attention_parity(gpu_lib, case):
+    B, N, Hq, Hkv, D, P, kind = CASES[case]
+    if kind == "c1":
+        parents = np.array([synth.CONFIGS["C1"].parents], dtype=np.int32)
+    elif kind == "c2":
+        parents = np.array([synth.CONFIGS["C2"].parents], dtype=np.int32)
+    elif kind == "chain":
+        parents = synth.chain_parents(B, N)
+    else:
+        parents = synth.random_parents(B, N, 0, 200 + case, 9)
+    bits, vals, parents = _case(300 + case, B, N, Hq, Hkv, D, P, parents)
+    scale = D ** -0.5
+    print(f"attention case {case}: B={B} N={N} Hq={Hq} Hkv={Hkv} D={D} P={P} {kind}", flush=True)
+    got, lse = _run(gpu_lib, bits, parents, P, scale)
+    ref, ref_lse = oracle.tree_verify_attention(*vals, parents, P, scale)
+    assert_close_attn(got, ref)
+    np.testing.assert_allclose(lse, ref_lse, atol=2e-3, rtol=0)
+
+
+def test_capacity_rows_are_not_read(gpu_lib):
+    B, N, Hq, Hkv, D, P = 2, 20, 4, 2, 128, 200
+    parents = synth.random_parents(B, N, 0, 250, 9)
+    bits, vals, parents = _case(251, B, N, Hq, Hkv, D, P, parents, cap_extra=37)
+    got, lse = _run(gpu_lib, bits, parents, P, 0.1)
+    assert np.isfinite(got).all()
+    ref, ref_lse = oracle.tree_verify_attention(*vals, parents, P, 0.1)
+    assert_close_attn(got, ref)
+
+
+def test_chain_is_causal_and_deterministic(gpu_lib):
+    B, N, Hq, Hkv, D, P = 1, 48, 8, 2, 128, 1000
+    parents = synth.chain_parents(B, N)
+    bits, vals, parents = _case(252, B, N, Hq, Hkv, D, P, parents)
+    a, la = _run(gpu_lib, bits, parents, P, D ** -0.5)
+    b, lb = _run(gpu_lib, bits, parents, P, D ** -0.5)
+    assert (a == b).all() and (la == lb).all()          # no atomics: bitwise repeatable
+    ref, _ = oracle.tree_verify_attention(*vals, parents, P, D ** -0.5)
+    assert_close_attn(a, ref)
+
+
+@pytest.mark.parametrize("name", ["C3", "C5"])
+def test_attention_full_size_sampled(gpu_lib, name):
+    """Full C3 / C5 shapes in the benchmark's launch configuration; the oracle checks
+    a sample of (sequence, node, KV head) outputs one by one."""
+    cfg = synth.CONFIGS[name]
+    B, N, Hq, Hkv, D, P = cfg.B, cfg.N, cfg.Hq, cfg.Hkv, cfg.D, cfg.P
+    parents = synth.random_parents(B, N, 0, cfg.index, 20)
+    qb = synth.normal_bf16_bits((B, N, Hq, D), 1.0, 0, cfg.index, 1)
+    kb = synth.normal_bf16_bits((B, Hkv, P + N, D), 1.0, 0, cfg.index, 2)
+    vb = synth.normal_bf16_bits((B, Hkv, P + N, D), 1.0, 0, cfg.index, 3)
+    print(f"attention full size {name}", flush=True)
+    got, lse = _run(gpu_lib, (qb, kb, vb), parents, P, D ** -0.5)
+    rng = np.random.default_rng(7)
+    G = Hq // Hkv
+    picks = [(int(rng.integers(B)), int(rng.integers(N)), int(rng.integers(Hkv))) for _ in range(12)]
+    picks += [(B - 1, N - 1, Hkv - 1), (0, 0, 0)]
+    errs = []
+    for b, i, g in picks:
+        anc = oracle.ancestor_sets(parents[b])[i]
+        ref, ref_lse = oracle.tree_verify_attention_node(
+            synth.bf16_bits_to_f64(qb[b, i, g * G:(g + 1) * G]), synth.bf16_bits_to_f64(kb[b, g]),
+            synth.bf16_bits_to_f64(vb[b, g]), anc, P, D ** -0.5)
+        assert_close_attn(got[b, i, g * G:(g + 1) * G], ref)
+        np.testing.assert_allclose(lse[b, i, g * G:(g + 1) * G], ref_lse, atol=2e-3)
+    assert np.isfinite(got).all() and np.isfinite(lse).all()
