@@ -1,0 +1,333 @@
+#!/usr/bin/env python3
+"""Benchmark of one EAGLE-2 tree-verification step on one MI355X.
+
+A step is the whole hot path over one batch of synthetic input at the
+Llama-3-70B-shaped workload (4 sequences, 60-node EAGLE-2 trees, 64 query / 8 KV
+heads, head dim 128, 32768-token KV prefix, hidden 8192, vocabulary 128256, bf16):
+
+    eagle2_rerank          -> tree (tokens, parents, draft rows) from draft logits
+    eagle_tree_verify_attn -> one layer of tree attention over prefix + tree
+    eagle_lm_head_argmax   -> LM head + per-node max/argmax/lse over the tree's hidden states
+    eagle_accept_greedy    -> accepted path and emitted tokens
+
+Inputs are resident in HBM before timing.  Every step streams 2.1 GB of LM-head
+weights, 538 MB of KV and 105 MB of draft logits, more than the 256 MB Infinity
+Cache, so nothing is served warm from one step to the next.
+
+Prints ONE JSON line.  `value` is tree-verify tokens/s = B*N tree tokens verified
+per step / step time.  The per-kernel breakdown, the roofline of the dominant
+kernel (LM head, HBM-bound) and of the attention kernel, the speculative-sampling
+acceptance latency at the Llama-3-8B-shaped workload and the timed CPU oracle
+baseline are added as extra fields.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+METRIC = "tree-verify tokens/s + HBM GB/s (% peak) at 8B/70B shapes; accept+rerank µs"
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {
+    "lm_head": "speculative_decoding_attn_amd/csrc/lm_head.hip",
+    "tree_attn": "speculative_decoding_attn_amd/csrc/tree_attn.hip",
+}
+
+
+def _src_hash(rel: str) -> str:
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None if
+    the summary is missing or was taken on a different kernel source."""
+    path = os.path.join(PROFILE_DIR, f"{kernel}_C5_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != _src_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def make_inputs(cfg, torch, dev):
+    """Synthetic C5 inputs as device tensors (bf16 where the GPU reads bf16)."""
+    B, N, Hq, Hkv, D, P, H, V = cfg.B, cfg.N, cfg.Hq, cfg.Hkv, cfg.D, cfg.P, cfg.H, cfg.V
+
+    def dbf(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x = {}
+    x["q"] = dbf(synth.normal_bf16_bits((B, N, Hq, D), 1.0, 0, cfg.index, 1))
+    x["k"] = dbf(synth.normal_bf16_bits((B, Hkv, P + N, D), 1.0, 0, cfg.index, 2))
+    x["v"] = dbf(synth.normal_bf16_bits((B, Hkv, P + N, D), 1.0, 0, cfg.index, 3))
+    x["hidden"] = dbf(synth.normal_bf16_bits((B * N, H), 1.0, 0, cfg.index, 4))
+    x["W"] = dbf(synth.normal_bf16_bits((V, H), cfg.w_std, 0, cfg.index, 5))
+    x["draft_logits"] = torch.from_numpy(
+        synth.normal_f32((B, cfg.rows, V), cfg.draft_std, 0, cfg.index, 6)).to(dev)
+    x["root"] = torch.from_numpy(synth.integers((B,), 0, V, 0, cfg.index, 7)).to(dev)
+    return x
+
+
+def attn_flops(parents_np, cfg) -> float:
+    """Algorithmic flops of tree attention: 2*D for q.k and 2*D for p*v per (query, key);
+    node i of depth d sees P + d + 1 keys."""
+    total_keys = 0
+    for b in range(parents_np.shape[0]):
+        depth = [0] * cfg.N
+        for i in range(1, cfg.N):
+            depth[i] = depth[parents_np[b, i]] + 1
+        total_keys += sum(cfg.P + d + 1 for d in depth)
+    return 4.0 * cfg.D * cfg.Hq * total_keys
+
+
+def cpu_baseline(cfg):
+    """Time the fp64 oracle on a bounded sample of the C5 step and scale to one step."""
+    import oracle
+    try:
+        import threadpoolctl
+        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
+    except Exception:  # pragma: no cover
+        threads = 1
+    B, N, Hq, Hkv, D, P, H, V = cfg.B, cfg.N, cfg.Hq, cfg.Hkv, cfg.D, cfg.P, cfg.H, cfg.V
+    G = Hq // Hkv
+    f64 = synth.bf16_bits_to_f64
+    n_pairs, n_slices, n_rerank = 6, 24, 2
+    slice_rows = (V + 63) // 64
+
+    # attention: n_pairs of the B*Hkv (sequence, KV head) pairs, all nodes and heads
+    parents = synth.random_parents(B, N, 0, cfg.index, 20)
+    t_attn = 0.0
+    for j in range(n_pairs):
+        b, g = j % B, (j * 3) % Hkv
+        qb = synth.normal_bf16_bits((N, G, D), 1.0, 0, cfg.index, 1001 + j)
+        kb = synth.normal_bf16_bits((P + N, D), 1.0, 0, cfg.index, 1101 + j)
+        vb = synth.normal_bf16_bits((P + N, D), 1.0, 0, cfg.index, 1201 + j)
+        q, k, v = f64(qb), f64(kb), f64(vb)
+        anc = oracle.ancestor_sets(parents[b])
+        t0 = time.perf_counter()
+        for i in range(N):
+            oracle.tree_verify_attention_node(q[i], k, v, anc[i], P, D ** -0.5)
+        t_attn += time.perf_counter() - t0
+    t_attn *= (B * Hkv) / n_pairs
+
+    # LM head: n_slices vocabulary slices of 1/64 of the vocabulary, all rows
+    hidden = f64(synth.normal_bf16_bits((B * N, H), 1.0, 0, cfg.index, 4))
+    t_lm = 0.0
+    for j in range(n_slices):
+        wb = synth.normal_bf16_bits((slice_rows, H), cfg.w_std, 0, cfg.index, 1301 + j)
+        t0 = time.perf_counter()
+        lg = oracle.lm_head_logits(hidden, wb, to_f64=f64)
+        oracle.lm_head_row_stats(lg)
+        t_lm += time.perf_counter() - t0
+    t_lm *= 64.0 / n_slices
+
+    # rerank: n_rerank sequences
+    t_rr = 0.0
+    for j in range(n_rerank):
+        dl = synth.normal_f32((cfg.rows, V), cfg.draft_std, 0, cfg.index, 1401 + j)
+        t0 = time.perf_counter()
+        oracle.eagle2_rerank(dl, 1, cfg.top_k, cfg.depth, N)
+        t_rr += time.perf_counter() - t0
+    t_rr *= B / n_rerank
+
+    # greedy acceptance: all sequences
+    t0 = time.perf_counter()
+    for b in range(B):
+        oracle.accept_greedy(np.zeros(N, np.int64), parents[b], np.zeros(N, np.int64), cfg.max_depth)
+    t_acc = time.perf_counter() - t0
+
+    step = t_attn + t_lm + t_rr + t_acc
+    return {"value": round(B * N / step, 3), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"fp64 numpy oracle on {n_pairs}/{B * Hkv} attention (sequence, KV head) "
+                       f"pairs, {n_slices}/64 LM-head vocabulary slices, {n_rerank}/{B} rerank "
+                       f"sequences and all {B} greedy acceptances of the C5 step, each scaled "
+                       f"to the full step"),
+            "step_seconds": round(step, 3),
+            "parts_seconds": {"tree_attn": round(t_attn, 3), "lm_head": round(t_lm, 3),
+                              "rerank": round(t_rr, 3), "accept_greedy": round(t_acc, 4)}}
+
+
+def copy_calibration(torch, dev, nbytes=1 << 30, reps=5):
+    """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}))
+
+
+def spec_latency(torch, sda, dev, iters=20):
+    """eagle_accept_spec at the Llama-3-8B-shaped speculative-sampling workload (C4): a
+    60-node tree from eagle2_rerank, target logits N(0,1) over 128256 tokens."""
+    cfg = synth.CONFIGS["C4"]
+    dl = torch.from_numpy(synth.normal_f32((1, cfg.rows, cfg.V), cfg.draft_std, 0, cfg.index, 6)).to(dev)
+    root = torch.from_numpy(synth.integers((1,), 0, cfg.V, 0, cfg.index, 7)).to(dev)
+    tree = sda.eagle2_rerank(dl, root, cfg.top_k, cfg.depth, cfg.N)
+    tl = torch.from_numpy(synth.normal_f32((1, cfg.N, cfg.V), 1.0, 0, cfg.index, 10)).to(dev)
+    ua = torch.from_numpy(synth.uniform_f32((1, cfg.N), 0, cfg.index, 8)).to(dev)
+    us = torch.from_numpy(synth.uniform_f32((1, cfg.N), 0, cfg.index, 9)).to(dev)
+    ws = torch.empty(sda.load().eagle_accept_spec_workspace(1, cfg.N, cfg.V), dtype=torch.uint8,
+                     device=dev)
+    for _ in range(3):
+        sda.eagle_accept_spec(tree["tokens"], tree["parents"], tree["draft_row"], tl, dl, ua, us,
+                              cfg.max_depth, workspace=ws)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(iters):
+        sda.eagle_accept_spec(tree["tokens"], tree["parents"], tree["draft_row"], tl, dl, ua, us,
+                              cfg.max_depth, workspace=ws)
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1000.0 / iters
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-spec", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU sharding is described in DESIGN.md, not implemented)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import speculative_decoding_attn_amd as sda
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    sda.load()
+    dev = torch.device("cuda:0")
+    if args.copy_calib:
+        copy_calibration(torch, dev)
+        return 0
+
+    cfg = synth.CONFIGS["C5"]
+    B, N, Hq, Hkv, D, P, H, V = cfg.B, cfg.N, cfg.Hq, cfg.Hkv, cfg.D, cfg.P, cfg.H, cfg.V
+    t_gen = time.perf_counter()
+    x = make_inputs(cfg, torch, dev)
+    torch.cuda.synchronize()
+    print(f"# inputs resident in HBM ({time.perf_counter() - t_gen:.1f} s)", file=sys.stderr,
+          flush=True)
+    lib = sda.load()
+    ws_attn = torch.empty(max(1, lib.eagle_tree_verify_attn_workspace(B, N, Hq, Hkv, D, P)),
+                          dtype=torch.uint8, device=dev)
+    ws_lm = torch.empty(lib.eagle_lm_head_workspace(B * N, H, V), dtype=torch.uint8, device=dev)
+    ws_rr = torch.empty(lib.eagle2_rerank_workspace(B, V, cfg.top_k, cfg.depth), dtype=torch.uint8,
+                        device=dev)
+    attn_out = torch.empty((B, N, Hq, D), dtype=torch.bfloat16, device=dev)
+    attn_lse = torch.empty((B, N, Hq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        tree = sda.eagle2_rerank(x["draft_logits"], x["root"], cfg.top_k, cfg.depth, N, workspace=ws_rr)
+        if ev:
+            ev[1].record(stream)
+        sda.eagle_tree_verify_attn(x["q"], x["k"], x["v"], tree["parents"], P, D ** -0.5,
+                                   out=attn_out, lse=attn_lse, workspace=ws_attn)
+        if ev:
+            ev[2].record(stream)
+        res = sda.eagle_lm_head_argmax(x["hidden"], x["W"], want_logits=False, workspace=ws_lm)
+        if ev:
+            ev[3].record(stream)
+        acc = sda.eagle_accept_greedy(tree["tokens"], tree["parents"], res["argmax"].view(B, N),
+                                      cfg.max_depth)
+        if ev:
+            ev[4].record(stream)
+        return tree, acc
+
+    for _ in range(args.warmup):
+        tree, _ = step()
+    torch.cuda.synchronize()
+    parents_np = tree["parents"].cpu().numpy()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    total_ms = evs[0][0].elapsed_time(evs[-1][4])
+    names = ["rerank", "tree_attn", "lm_head", "accept_greedy"]
+    per = {n: 1000.0 * sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps
+           for j, n in enumerate(names)}
+    ms_per_step = total_ms / args.steps
+    value = B * N / (ms_per_step / 1000.0)
+
+    # rooflines
+    lm_bytes = V * H * 2 + B * N * H * 2 + B * N * 16
+    lm_gbs = lm_bytes / (per["lm_head"] * 1e-6) / 1e9
+    attn_bytes = 2 * B * Hkv * (P + N) * D * 2 + 2 * B * N * Hq * D * 2 + B * N * Hq * 4
+    a_flops = attn_flops(parents_np, cfg)
+    attn_tflops = a_flops / (per["tree_attn"] * 1e-6) / 1e12
+    attn_gbs = attn_bytes / (per["tree_attn"] * 1e-6) / 1e9
+    rr_bytes = B * cfg.rows * V * 4
+    dominant = max(("lm_head", "tree_attn"), key=lambda n: per[n])
+    roof_lm = {"kernel": "lm_head (eagle_lm_head_argmax)", "bound": "hbm",
+               "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+               "frac": round(lm_gbs / HBM_PEAK_GBS, 4), "traffic": _traffic("lm_head"),
+               "algorithmic_bytes": lm_bytes, "avg_us": round(per["lm_head"], 2)}
+    roof_attn = {"kernel": "tree_attn (eagle_tree_verify_attn)", "bound": "mfma",
+                 "achieved": round(attn_tflops, 1), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": round(attn_tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": _traffic("tree_attn"),
+                 "algorithmic_flops": a_flops, "algorithmic_bytes": attn_bytes,
+                 "hbm_gbs": round(attn_gbs, 1), "hbm_frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+                 "avg_us": round(per["tree_attn"], 2)}
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "C5 Llama-3-70B-shaped tree verification: 4 sequences x 60-node "
+                               "EAGLE-2 trees (top-k 10, depth 6), GQA 64/8 heads, head dim 128, "
+                               "KV prefix 32768, hidden 8192, vocab 128256, greedy acceptance",
+                   "B": B, "N": N, "Hq": Hq, "Hkv": Hkv, "D": D, "P": P, "H": H, "V": V,
+                   "top_k": cfg.top_k, "depth": cfg.depth, "parallelism": "single GPU"},
+        "roofline": roof_lm if dominant == "lm_head" else roof_attn,
+        "roofline_attn": roof_attn,
+        "roofline_lm_head": roof_lm,
+        "breakdown_us": {k: round(v, 2) for k, v in per.items()},
+        "rerank_hbm_gbs": round(rr_bytes / (per["rerank"] * 1e-6) / 1e9, 1),
+    }
+    if not args.no_spec:
+        out["accept_spec_us_C4"] = round(spec_latency(torch, sda, dev), 2)
+    if not args.no_cpu_baseline:
+        print("# timing the CPU oracle baseline", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(cfg)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
