@@ -93,7 +93,7 @@ accept_greedy_kernel(const int32_t* __restrict__ tokens, const int32_t* __restri
 // timeout the sequence's accept_len is set to -1 and all its workgroups leave.
 // ---------------------------------------------------------------------------
 constexpr int kSpecThreads = 256;
-constexpr unsigned kSpinLimit = 1u << 22;
+constexpr unsigned kSpinLimit = 1u << 24;
 
 struct SpecWs {
   unsigned* counters;   // [B] barrier arrivals
@@ -154,20 +154,27 @@ __device__ __forceinline__ double wg_max_d(double x, double* red) {
 
 // Publish this workgroup's 4 partials for generation `gen`, wait for all chunks of
 // the sequence, and return the chunk-ordered partials in lds_all[chunks][4].
-// Returns false on timeout.
+// Returns false on timeout.  The partials and the arrival counter are accessed with
+// relaxed agent-scope atomics, which are coherent across the XCDs' L2 caches without
+// cache-wide write-back or invalidation; the partial stores are complete (s_waitcnt
+// vmcnt(0)) before the counter increment that announces them, and the partial loads
+// are issued only after the counter has been seen complete.
 __device__ bool exchange(const SpecWs& w, int b, int chunks, int me, unsigned gen,
                          const double (&mine)[4], double* lds_all, int* lds_flag) {
-  double* slot = w.slots + (((size_t)b * 2 + (gen & 1)) * chunks) * 4;
-  if (threadIdx.x < 4) slot[me * 4 + threadIdx.x] = mine[threadIdx.x];
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  unsigned long long* slot =
+      (unsigned long long*)(w.slots + (((size_t)b * 2 + (gen & 1)) * chunks) * 4);
+  if (threadIdx.x < 4)
+    __hip_atomic_store(&slot[me * 4 + threadIdx.x], __double_as_longlong(mine[threadIdx.x]),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
     int ok = 1;
     if (chunks > 1) {
-      __hip_atomic_fetch_add(&w.counters[b], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(&w.counters[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const unsigned target = (gen + 1) * (unsigned)chunks;
       unsigned spins = 0;
-      while (__hip_atomic_load(&w.counters[b], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      while (__hip_atomic_load(&w.counters[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
         if (__hip_atomic_load(&w.abort_flags[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
           ok = 0;
           break;
@@ -177,17 +184,17 @@ __device__ bool exchange(const SpecWs& w, int b, int chunks, int me, unsigned ge
           ok = 0;
           break;
         }
-        __builtin_amdgcn_s_sleep(2);
+        __builtin_amdgcn_s_sleep(1);
       }
     }
     *lds_flag = ok;
   }
   __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   const bool ok = *lds_flag != 0;
   if (ok) {
     for (int i = threadIdx.x; i < chunks * 4; i += blockDim.x)
-      lds_all[i] = __hip_atomic_load(&slot[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      lds_all[i] = __longlong_as_double(
+          (long long)__hip_atomic_load(&slot[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
   }
   __syncthreads();
   return ok;

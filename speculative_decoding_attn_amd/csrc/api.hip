@@ -202,6 +202,11 @@ static eagle_status_t check_rerank_dims(int32_t B, int32_t V, int32_t top_k, int
   if (cand > eagle::rerank_max_candidates())
     return fail(EAGLE_ERR_UNSUPPORTED, "top_k + (depth-1)*top_k^2 = %lld candidates > %d", cand,
                 eagle::rerank_max_candidates());
+  const long long rows = 1 + (long long)(depth - 1) * top_k;
+  const long long chunks = (V + 4095) / 4096;
+  if (rows * top_k > eagle::rerank_max_row_list() || rows > 512 || chunks * top_k > 1024)
+    return fail(EAGLE_ERR_UNSUPPORTED, "rerank sizes past the kernel limits (rows*top_k=%lld, rows=%lld, "
+                "chunks*top_k=%lld)", rows * top_k, rows, chunks * top_k);
   if (n_nodes - 1 > cand)
     return fail(EAGLE_ERR_INVALID_ARG, "n_nodes-1=%d exceeds the %lld candidates", n_nodes - 1, cand);
   return EAGLE_OK;

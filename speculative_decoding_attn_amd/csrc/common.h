@@ -17,6 +17,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
+// s_waitcnt immediate for "vmcnt(0)" with expcnt and lgkmcnt left at their maxima
+constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

@@ -9,16 +9,21 @@
 
 namespace eagle {
 
-// MI355X: 256 CUs x 4 SIMDs.  Split-KV aims at about one wave per SIMD.
-constexpr int kTargetWaves = 1024;
+// MI355X: 256 CUs.  Split-KV aims at about one attention workgroup per CU.
+constexpr int kNumCUs = 256;
 constexpr int kMinSplitKeys = 256;
+#ifndef EAGLE_ATTN_ROW_TILES
+#define EAGLE_ATTN_ROW_TILES 1
+#endif
+constexpr int kAttnRowTiles = EAGLE_ATTN_ROW_TILES;   // 32-row MFMA tiles per wave
 
 struct AttnPlan {
   int B, N, Hq, Hkv, G, D, P, kv_cap;
   int R;          // query rows per (sequence, KV head) = N * G
-  int waves;      // waves per workgroup (64 rows each)
+  int rowt;       // 32-row tiles per wave (1 or 2)
+  int waves;      // waves per workgroup
   int RB;         // row blocks per pair
-  int Rpad;       // RB * waves * 64
+  int Rpad;       // RB * waves * rowt * 32
   int S;          // key splits
   int split_len;  // keys per split (multiple of 32); the last split also takes the tree
   float c;        // scale * log2(e)
@@ -77,4 +82,5 @@ hipError_t launch_rerank(const RerankPlan& pl, const float* draft_logits, const 
 
 namespace eagle {
 int rerank_max_candidates();
+int rerank_max_row_list();   // R * top_k limit (also caps R at 512 and chunks * top_k at 1024)
 }  // namespace eagle

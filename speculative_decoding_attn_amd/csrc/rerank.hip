@@ -28,8 +28,10 @@ namespace {
 constexpr int kRowThreads = 256;
 constexpr int kRowPer = 16;                        // elements per thread in rerank_rows
 constexpr int kChunk = kRowThreads * kRowPer;      // vocabulary entries per chunk
-constexpr int kTreeThreads = 256;
-constexpr int kMaxCand = 4096;                     // candidates per sequence in rerank_tree
+constexpr int kTreeThreads = 1024;
+constexpr int kMaxCand = 2048;                     // candidates per sequence in rerank_tree
+constexpr int kMaxRowList = 1024;                  // R * k row-list entries staged in rerank_tree
+constexpr int kMaxRows = 512;                      // draft rows per sequence
 
 // (value, index) order: larger value first, then smaller index
 __device__ __forceinline__ bool better(float v1, int i1, float v2, int i2) {
@@ -40,6 +42,20 @@ struct VI {
   float v;
   int i;
 };
+
+// (value desc, index asc) as one unsigned 64-bit key: larger key = better.
+__device__ __forceinline__ uint32_t ordered_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint64_t key) {
+  const uint32_t o = (uint32_t)(key >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+__device__ __forceinline__ int key_index(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
+__device__ __forceinline__ uint64_t vi_key(float v, int i) {
+  return ((uint64_t)ordered_bits(v) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
+}
 
 __device__ __forceinline__ VI wave_best(VI a) {
 #pragma unroll
@@ -79,10 +95,36 @@ __host__ __device__ inline RrWs rr_ws(void* ws, const RerankPlan& pl) {
   return w;
 }
 
+// Descending bitonic sort of one float per lane across the wave.
+__device__ __forceinline__ float wave_sort_desc(float v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1)
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const float o = __shfl_xor(v, j);
+      const bool lower = (lane & j) == 0;
+      const bool desc = (lane & k) == 0;
+      v = (lower == desc) ? fmaxf(v, o) : fminf(v, o);
+    }
+  return v;
+}
+
+// One workgroup per (row, vocabulary chunk of 4096).  Max and exp-sum of the chunk,
+// and its top-k: every wave keeps the elements not below the k-th largest of its
+// 64 lane maxima (at least k of its elements are that large, so its top-k is among
+// them) and appends them to a short LDS list; one wave then extracts the chunk's k
+// best from that list in (logit desc, token asc) order.  If ties make the list
+// overflow, the whole chunk is searched instead (same order, same result).
+constexpr int kCandCap = 512;
+
 __global__ void __launch_bounds__(kRowThreads)
 rerank_rows(const float* __restrict__ logits, RerankPlan pl, void* ws) {
-  __shared__ VI red[kRowThreads / 64];
   __shared__ float redf[kRowThreads / 64];
+  __shared__ float cand_v[kCandCap];
+  __shared__ int cand_i[kCandCap];
+  __shared__ int wave_cnt[kRowThreads / 64];
+  __shared__ VI red[kRowThreads / 64];
   RrWs w = rr_ws(ws, pl);
   const int chunk = blockIdx.x % pl.chunks;
   const size_t row = blockIdx.x / pl.chunks;
@@ -91,20 +133,22 @@ rerank_rows(const float* __restrict__ logits, RerankPlan pl, void* ws) {
   const int x0 = chunk * pl.chunk_len;
   const float* src = logits + row * (size_t)V;
 
+  // element e of thread tid is x0 + e*256 + tid: every load instruction is coalesced
   float val[kRowPer];
   int idx[kRowPer];
 #pragma unroll
   for (int e = 0; e < kRowPer; ++e) {
     const int x = x0 + e * kRowThreads + tid;
-    const bool ok = x < V && e * kRowThreads + tid < pl.chunk_len;
+    const bool ok = x < V;
     val[e] = ok ? src[x] : -INFINITY;
     idx[e] = ok ? x : 0x7fffffff;
   }
-  // max and exp-sum of the chunk
-  float mx = val[0];
+  float lmax = val[0];
 #pragma unroll
-  for (int e = 1; e < kRowPer; ++e) mx = fmaxf(mx, val[e]);
-  mx = wave_max(mx);
+  for (int e = 1; e < kRowPer; ++e) lmax = fmaxf(lmax, val[e]);
+
+  // chunk max and exp-sum
+  float mx = wave_max(lmax);
   if (lane == 0) redf[wid] = mx;
   __syncthreads();
   mx = redf[0];
@@ -113,22 +157,77 @@ rerank_rows(const float* __restrict__ logits, RerankPlan pl, void* ws) {
   float z = 0.f;
   if (mx > -INFINITY) {
 #pragma unroll
-    for (int e = 0; e < kRowPer; ++e)
-      z += __builtin_amdgcn_exp2f((val[e] - mx) * kLog2e);
+    for (int e = 0; e < kRowPer; ++e) z += __builtin_amdgcn_exp2f((val[e] - mx) * kLog2e);
   }
   z = wave_sum(z);
   __syncthreads();
   if (lane == 0) redf[wid] = z;
+
+  // candidates of this wave: elements >= the k-th largest lane maximum
+  const int k = pl.k;
+  const float sorted = wave_sort_desc(lmax);
+  const float thr = k >= 64 ? -INFINITY : __shfl(sorted, k - 1);
+  int mine = 0;
+#pragma unroll
+  for (int e = 0; e < kRowPer; ++e) mine += val[e] >= thr ? 1 : 0;
+  int pre = mine;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(pre, o);
+    if (lane >= o) pre += t;
+  }
+  const int wtotal = __shfl(pre, 63);
+  pre -= mine;
+  if (lane == 0) wave_cnt[wid] = wtotal;
   __syncthreads();
+  int off = 0, ncand = 0;
+#pragma unroll
+  for (int i = 0; i < kRowThreads / 64; ++i) {
+    if (i < wid) off += wave_cnt[i];
+    ncand += wave_cnt[i];
+  }
   if (tid == 0) {
     float zt = 0.f;
     for (int i = 0; i < kRowThreads / 64; ++i) zt += redf[i];
     w.chunk_mz[blockIdx.x] = make_float2(mx, zt);
   }
-  // top-k by repeated extraction
+  float* out_v = w.chunk_v + (size_t)blockIdx.x * k;
+  int* out_i = w.chunk_i + (size_t)blockIdx.x * k;
+  if (ncand <= kCandCap) {
+    int pos = off + pre;
+#pragma unroll
+    for (int e = 0; e < kRowPer; ++e)
+      if (val[e] >= thr) {
+        cand_v[pos] = val[e];
+        cand_i[pos] = idx[e];
+        ++pos;
+      }
+    __syncthreads();
+    if (wid != 0) return;
+    float pv = INFINITY;
+    int pi = -1;
+    for (int r = 0; r < k; ++r) {
+      VI best{-INFINITY, 0x7fffffff};
+      for (int c = lane; c < ncand; c += 64) {
+        const float v = cand_v[c];
+        const int i = cand_i[c];
+        const bool after = v < pv || (v == pv && i > pi);
+        if (after && better(v, i, best.v, best.i)) best = VI{v, i};
+      }
+      best = wave_best(best);
+      if (lane == 0) {
+        out_v[r] = best.v;
+        out_i[r] = best.i;
+      }
+      pv = best.v;
+      pi = best.i;
+    }
+    return;
+  }
+  // many ties: k rounds over the whole chunk
   float pv = INFINITY;
   int pi = -1;
-  for (int r = 0; r < pl.k; ++r) {
+  for (int r = 0; r < k; ++r) {
     VI best{-INFINITY, 0x7fffffff};
 #pragma unroll
     for (int e = 0; e < kRowPer; ++e) {
@@ -139,58 +238,95 @@ rerank_rows(const float* __restrict__ logits, RerankPlan pl, void* ws) {
     __syncthreads();
     if (lane == 0) red[wid] = best;
     __syncthreads();
-    VI b = red[0];
+    VI bb = red[0];
 #pragma unroll
     for (int i = 1; i < kRowThreads / 64; ++i)
-      if (better(red[i].v, red[i].i, b.v, b.i)) b = red[i];
+      if (better(red[i].v, red[i].i, bb.v, bb.i)) bb = red[i];
     if (tid == 0) {
-      w.chunk_v[(size_t)blockIdx.x * pl.k + r] = b.v;
-      w.chunk_i[(size_t)blockIdx.x * pl.k + r] = b.i;
+      out_v[r] = bb.v;
+      out_i[r] = bb.i;
     }
-    pv = b.v;
-    pi = b.i;
+    pv = bb.v;
+    pi = bb.i;
   }
 }
 
+// One wave per row: merges the chunk results into the row's lse and top-k.  The
+// row's k best are not below T = the k-th largest chunk maximum (the k chunks with
+// the largest maxima hold k elements >= T), so only chunk entries >= T are kept; each
+// kept entry's rank among them is counted, and entries of rank < k are written in
+// rank order.
+constexpr int kMergeCap = 256;   // kept entries per row (more: every entry is kept and ranked)
+
 __global__ void __launch_bounds__(256)
 rerank_merge(RerankPlan pl, void* ws, float* __restrict__ draft_lse) {
+  __shared__ uint64_t keys[4][1024];
   RrWs w = rr_ws(ws, pl);
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int row = blockIdx.x * 4 + wid;
   if (row >= pl.B * pl.R) return;
-  // lse
+  const int k = pl.k, chunks = pl.chunks;
   float mx = -INFINITY;
-  for (int c = lane; c < pl.chunks; c += 64) mx = fmaxf(mx, w.chunk_mz[(size_t)row * pl.chunks + c].x);
+  for (int c = lane; c < chunks; c += 64) mx = fmaxf(mx, w.chunk_mz[(size_t)row * chunks + c].x);
   mx = wave_max(mx);
   float z = 0.f;
-  for (int c = lane; c < pl.chunks; c += 64) {
-    const float2 e = w.chunk_mz[(size_t)row * pl.chunks + c];
+  for (int c = lane; c < chunks; c += 64) {
+    const float2 e = w.chunk_mz[(size_t)row * chunks + c];
     if (e.x > -INFINITY) z += e.y * __builtin_amdgcn_exp2f((e.x - mx) * kLog2e);
   }
   z = wave_sum(z);
   if (lane == 0) draft_lse[row] = mx + logf(z);
-  // top-k over chunks * k candidates
-  const int ncand = pl.chunks * pl.k;
-  const float* cv = w.chunk_v + (size_t)row * ncand;
-  const int* ci = w.chunk_i + (size_t)row * ncand;
-  float pv = INFINITY;
-  int pi = -1;
-  for (int r = 0; r < pl.k; ++r) {
-    VI best{-INFINITY, 0x7fffffff};
-    for (int c = lane; c < ncand; c += 64) {
-      const float v = cv[c];
-      const int i = ci[c];
-      const bool after = v < pv || (v == pv && i > pi);
-      if (after && better(v, i, best.v, best.i)) best = VI{v, i};
-    }
-    best = wave_best(best);
-    if (lane == 0) {
-      w.row_v[(size_t)row * pl.k + r] = best.v;
-      w.row_i[(size_t)row * pl.k + r] = best.i;
-    }
-    pv = best.v;
-    pi = best.i;
+
+  const float* cv = w.chunk_v + (size_t)row * chunks * k;
+  const int* ci = w.chunk_i + (size_t)row * chunks * k;
+  // threshold: k-th largest chunk maximum (entry 0 of each chunk list); chunks <= 64
+  // whenever chunks * k <= 1024 and k >= 16, otherwise keep everything
+  float thr = -INFINITY;
+  if (chunks <= 64 && k <= chunks) {
+    const float cm = lane < chunks ? cv[(size_t)lane * k] : -INFINITY;
+    thr = __shfl(wave_sort_desc(cm), k - 1);
   }
+  // keep entries >= thr (lane-major over the chunks * k entries)
+  uint64_t* kk = keys[wid];
+  const int n_all = chunks * k;
+  int kept = 0;
+  for (int base = 0; base < n_all; base += 64) {
+    const int e = base + lane;
+    const float v = e < n_all ? cv[e] : -INFINITY;
+    const bool keep = e < n_all && v >= thr;
+    const uint64_t m = __ballot(keep);
+    if (keep) kk[kept + __popcll(m & ((1ull << lane) - 1ull))] = vi_key(v, ci[e]);
+    kept += __popcll(m);
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the wave's own LDS writes are done
+  // rank by counting; distinct keys (distinct token ids) give distinct ranks
+  for (int e = lane; e < kept; e += 64) {
+    const uint64_t key = kk[e];
+    int rank = 0;
+    for (int o = 0; o < kept; ++o) rank += kk[o] > key ? 1 : 0;
+    if (rank < k) {
+      w.row_v[(size_t)row * k + rank] = key_value(key);
+      w.row_i[(size_t)row * k + rank] = key_index(key);
+    }
+  }
+}
+
+// Rank of candidate (s, c) among candidates lb .. lb+n-1 of the LDS score list: how
+// many come first in (score desc, id asc) order.  Independent LDS reads, unrolled,
+// so the loop is not bound by one read's latency per comparison.
+__device__ __forceinline__ int rank_in(const uint64_t* keys, int lb, int n, uint64_t key) {
+  int rank = 0;
+  int o = lb;
+  const int end = lb + n;
+  for (; o + 8 <= end; o += 8) {
+    uint64_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = keys[o + e];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rank += v[e] > key ? 1 : 0;
+  }
+  for (; o < end; ++o) rank += keys[o] > key ? 1 : 0;
+  return rank;
 }
 
 __global__ void __launch_bounds__(kTreeThreads)
@@ -198,19 +334,31 @@ rerank_tree(RerankPlan pl, const int32_t* __restrict__ root_token, const float* 
             void* ws, int32_t* __restrict__ tokens, int32_t* __restrict__ parents,
             int32_t* __restrict__ depths, float* __restrict__ scores, int32_t* __restrict__ draft_row) {
   __shared__ float c_score[kMaxCand];
+  __shared__ uint64_t c_key[kMaxCand];
   __shared__ int c_tok[kMaxCand];
   __shared__ short c_par[kMaxCand];
   __shared__ short c_row[kMaxCand];
   __shared__ short c_pos[kMaxCand];
 
+  __shared__ float s_rv[kMaxRowList];
+  __shared__ int s_ri[kMaxRowList];
+  __shared__ float s_lse[kMaxRows];
+
   RrWs w = rr_ws(ws, pl);
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int k = pl.k, R = pl.R;
-  const float* rv = w.row_v + (size_t)b * R * k;
-  const int* ri = w.row_i + (size_t)b * R * k;
-  const float* lse = draft_lse + (size_t)b * R;
   const int total = k + (pl.depth - 1) * k * k;
+  // the sequence's row lists and normalisers, staged once in LDS
+  for (int e = tid; e < R * k; e += kTreeThreads) {
+    s_rv[e] = w.row_v[(size_t)b * R * k + e];
+    s_ri[e] = w.row_i[(size_t)b * R * k + e];
+  }
+  for (int r = tid; r < R; r += kTreeThreads) s_lse[r] = draft_lse[(size_t)b * R + r];
+  __syncthreads();
+  const float* rv = s_rv;
+  const int* ri = s_ri;
+  const float* lse = s_lse;
 
   for (int c = tid; c < total; c += kTreeThreads) c_row[c] = -1;
   // depth 1: the root's proposals
@@ -223,9 +371,10 @@ rerank_tree(RerankPlan pl, const int32_t* __restrict__ root_token, const float* 
   int lb = 0, ln = k, base = k;
   for (int d = 1; d < pl.depth; ++d) {
     // frontier: rank within the level
+    for (int c = lb + tid; c < lb + ln; c += kTreeThreads) c_key[c] = vi_key(c_score[c], c);
+    __syncthreads();
     for (int c = lb + tid; c < lb + ln; c += kTreeThreads) {
-      int rank = 0;
-      for (int o = lb; o < lb + ln; ++o) rank += better(c_score[o], o, c_score[c], c) ? 1 : 0;
+      const int rank = rank_in(c_key, lb, ln, c_key[c]);
       if (rank < k) c_row[c] = (short)(1 + (d - 1) * k + rank);
     }
     __syncthreads();
@@ -247,29 +396,23 @@ rerank_tree(RerankPlan pl, const int32_t* __restrict__ root_token, const float* 
   }
   // final selection by overall rank, then breadth-first positions
   const int keep = pl.n_nodes - 1;
+  for (int c = tid; c < total; c += kTreeThreads) c_key[c] = vi_key(c_score[c], c);
+  __syncthreads();
   for (int c = tid; c < total; c += kTreeThreads) {
-    int rank = 0;
-    const float s = c_score[c];
-    for (int o = 0; o < total; ++o) rank += better(c_score[o], o, s, c) ? 1 : 0;
+    const int rank = rank_in(c_key, 0, total, c_key[c]);
     c_pos[c] = (short)(rank < keep ? 1 : 0);
   }
   __syncthreads();
-  // exclusive scan of the selection flags in id order (one pass per thread range)
-  const int per = (total + kTreeThreads - 1) / kTreeThreads;
-  const int c0 = tid * per, c1 = min(total, c0 + per);
-  int cnt = 0;
-  for (int c = c0; c < c1; ++c) cnt += c_pos[c];
-  __shared__ int tcount[kTreeThreads];
-  tcount[tid] = cnt;
-  __syncthreads();
-  int before = 0;
-  for (int i = 0; i < tid; ++i) before += tcount[i];
-  __syncthreads();
-  int run = before;
-  for (int c = c0; c < c1; ++c) {
-    const bool s = c_pos[c] != 0;
-    c_pos[c] = s ? (short)(1 + run) : (short)0;
-    run += s ? 1 : 0;
+  // breadth-first positions: 1 + number of selected candidates with a smaller id
+  if (tid < 64) {
+    int run = 0;
+    for (int base = 0; base < total; base += 64) {
+      const int c = base + tid;
+      const bool sel = c < total && c_pos[c] != 0;
+      const uint64_t m = __ballot(sel);
+      if (sel) c_pos[c] = (short)(1 + run + __popcll(m & ((1ull << tid) - 1ull)));
+      run += __popcll(m);
+    }
   }
   __syncthreads();
   const size_t ob = (size_t)b * pl.n_nodes;
@@ -318,6 +461,7 @@ size_t rerank_workspace_bytes(const RerankPlan& pl) {
 }
 
 int rerank_max_candidates() { return kMaxCand; }
+int rerank_max_row_list() { return kMaxRowList; }
 
 hipError_t launch_rerank(const RerankPlan& pl, const float* draft_logits, const int32_t* root_token,
                          int32_t* tokens, int32_t* parents, int32_t* depths, float* scores,

@@ -53,7 +53,7 @@ __device__ __forceinline__ int vt_pos(int key) {
   return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
 }
 
-template <int D, int WAVES>
+template <int D, int WAVES, int ROWT>
 __global__ void __launch_bounds__(WAVES * 64, 1)
 tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
               const uint16_t* __restrict__ v, const int32_t* __restrict__ parents,
@@ -98,11 +98,11 @@ tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int32_t* par = parents + (size_t)b * N;
 
   // ---- Q^T operands (B side of S^T = K Q^T) and ancestor masks, per row tile
-  const int rowbase = rb * (WAVES * 64) + wid * 64;
-  bf16x8 qf[2][KSTEPS];
-  uint64_t anc[2];
+  const int rowbase = rb * (WAVES * ROWT * 32) + wid * ROWT * 32;
+  bf16x8 qf[ROWT][KSTEPS];
+  uint64_t anc[ROWT];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < ROWT; ++t) {
     const int r = rowbase + 32 * t + l32;
     if (r < pl.R) {
       const int i = r / G;
@@ -118,17 +118,21 @@ tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     }
   }
 
-  f32x16 oacc[2][DBLK];
+  f32x16 oacc[ROWT][DBLK];
+  float mc[ROWT];     // running max of scale*log2e*s
+  float lsum[ROWT];   // this lane's half of the row sum
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < ROWT; ++t) {
 #pragma unroll
     for (int db = 0; db < DBLK; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[t][db][r] = 0.f;
-  float mc[2] = {-INFINITY, -INFINITY};   // running max of scale*log2e*s
-  float lsum[2] = {0.f, 0.f};             // this lane's half of the row sum
+    mc[t] = -INFINITY;
+    lsum[t] = 0.f;
+  }
 
   const float c = pl.c;
+  const uint64_t node_mask = N >= 64 ? ~0ull : ((1ull << N) - 1ull);
 
   // ---- global -> registers for one chunk
   u32x4 kreg[K_PER];
@@ -193,6 +197,10 @@ tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     }
   };
 
+  // let the Q loads land before the loop, so that the compiler's wait counters do
+  // not make the loop wait on the next chunk's prefetch when it reads Q
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+
   const int n_chunks = (key_end - key_begin + KC - 1) / KC;
   if (n_chunks > 0) {
     load_chunk(key_begin);
@@ -208,38 +216,49 @@ tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* Ks = lds + st * L::STAGE;
     const uint16_t* Vs = Ks + L::KELEMS;
 
-    // S^T tile for 32 keys x 2 row tiles
-    f32x16 sacc[2];
+    // S^T tile for 32 keys x ROWT row tiles
+    f32x16 sacc[ROWT];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < ROWT; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
       const bf16x8 kf = *(const bf16x8*)(Ks + l32 * L::KSTR + 16 * s + 8 * half);
-      sacc[0] = mfma32(kf, qf[0][s], sacc[0]);
-      sacc[1] = mfma32(kf, qf[1][s], sacc[1]);
+#pragma unroll
+      for (int t = 0; t < ROWT; ++t) sacc[t] = mfma32(kf, qf[t][s], sacc[t]);
     }
 
-    if (kb + KC > P) {
-      // chunk reaches into the tree (or past it): apply the ancestor mask
+    // scores of this lane's 16 keys; chunks that reach into the tree (or past it) get
+    // the ancestor mask: bit j of `allowed` says whether key kb + j is visible
+    float sv[ROWT][16];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < ROWT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sv[t][r] = sacc[t][r];
+    if (kb + KC > P) {
+      const int off = kb - P;   // >= -31
+#pragma unroll
+      for (int t = 0; t < ROWT; ++t) {
+        const uint64_t tm = anc[t] & node_mask;
+        const uint32_t tree_bits = off >= 0 ? (off < 64 ? (uint32_t)(tm >> off) : 0u)
+                                            : (uint32_t)(tm << (-off));
+        const uint32_t prefix_bits = off < 0 ? ((1u << (-off)) - 1u) : 0u;
+        const uint32_t allowed = (tree_bits | prefix_bits) >> (4 * half);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = kb + 8 * (r >> 2) + 4 * half + (r & 3);
-          const int a = key - P;
-          const bool ok = key < P || (a < N && key < key_end && ((anc[t] >> (a & 63)) & 1ull));
-          if (!ok) sacc[t][r] = -INFINITY;
+          const int bit = 8 * (r >> 2) + (r & 3);
+          sv[t][r] = ((allowed >> bit) & 1u) ? sv[t][r] : -INFINITY;
         }
+      }
     }
 
-    bf16x8 pf[2][2];
+    bf16x8 pf[ROWT][2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      float mx = sacc[t][0];
+    for (int t = 0; t < ROWT; ++t) {
+      float mx = sv[t][0];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[t][r]);
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sv[t][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float mxc = mx * c;
       const bool need = mxc > mc[t] + kLazy;
@@ -257,7 +276,7 @@ tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       float pr[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        pr[r] = __builtin_amdgcn_exp2f(fmaf(sacc[t][r], c, -mcu));
+        pr[r] = __builtin_amdgcn_exp2f(fmaf(sv[t][r], c, -mcu));
         lsum[t] += pr[r];
       }
 #pragma unroll
@@ -275,8 +294,8 @@ tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
         const bf16x8 vf = *(const bf16x8*)(Vs + (32 * db + l32) * L::VSTR + 16 * cc + 8 * half);
-        oacc[0][db] = mfma32(vf, pf[0][cc], oacc[0][db]);
-        oacc[1][db] = mfma32(vf, pf[1][cc], oacc[1][db]);
+#pragma unroll
+        for (int t = 0; t < ROWT; ++t) oacc[t][db] = mfma32(vf, pf[t][cc], oacc[t][db]);
       }
 
     if (ch + 1 < n_chunks) store_chunk(st ^ 1);
@@ -285,7 +304,7 @@ tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 
   // ---- epilogue
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < ROWT; ++t) {
     const int r = rowbase + 32 * t + l32;
     const float ltot = lsum[t] + __shfl_xor(lsum[t], 32);
     if (r >= pl.R) continue;
@@ -368,15 +387,30 @@ tree_attn_merge(AttnPlan pl, const float* __restrict__ part_o, const float* __re
   if (lane == 0 && lse_out) lse_out[(size_t)(b * pl.N + i) * pl.Hq + h] = mx + logf(wsum);
 }
 
-template <int D, int WAVES>
+template <int D, int WAVES, int ROWT>
 hipError_t launch_fwd(const AttnPlan& pl, const void* q, const void* k, const void* v,
                       const int32_t* parents, void* out, float* lse, float* part_o,
                       float* part_lse, hipStream_t stream) {
   const int nwg = pl.B * pl.Hkv * pl.RB * pl.S;
-  hipLaunchKernelGGL((tree_attn_fwd<D, WAVES>), dim3(nwg), dim3(WAVES * 64), 0, stream,
+  hipLaunchKernelGGL((tree_attn_fwd<D, WAVES, ROWT>), dim3(nwg), dim3(WAVES * 64), 0, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, parents, pl,
                      (uint16_t*)out, lse, part_o, part_lse);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_fwd_d(const AttnPlan& pl, const void* q, const void* k, const void* v,
+                        const int32_t* parents, void* out, float* lse, float* part_o,
+                        float* part_lse, hipStream_t stream) {
+  if (pl.rowt == 2) {
+    if (pl.waves == 4) return launch_fwd<D, 4, 2>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
+    if (pl.waves == 2) return launch_fwd<D, 2, 2>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
+    return launch_fwd<D, 1, 2>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
+  }
+  if (pl.waves == 8) return launch_fwd<D, 8, 1>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
+  if (pl.waves == 4) return launch_fwd<D, 4, 1>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
+  if (pl.waves == 2) return launch_fwd<D, 2, 1>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
+  return launch_fwd<D, 1, 1>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
 }
 
 }  // namespace
@@ -392,11 +426,18 @@ AttnPlan plan_tree_attn(int B, int N, int Hq, int Hkv, int D, int P, int kv_cap)
   pl.P = P;
   pl.kv_cap = kv_cap;
   pl.R = N * pl.G;
-  pl.waves = pl.R > 128 ? 4 : (pl.R > 64 ? 2 : 1);
-  pl.RB = (pl.R + pl.waves * 64 - 1) / (pl.waves * 64);
-  pl.Rpad = pl.RB * pl.waves * 64;
-  const long long unit_waves = (long long)B * Hkv * pl.RB * pl.waves;
-  int s_target = (int)((kTargetWaves + unit_waves - 1) / unit_waves);
+  // rows per wave: 32 (one MFMA row tile, 2 waves per SIMD) or 64 (two row tiles, 1 wave
+  // per SIMD: half the LDS reads per MFMA)
+  pl.rowt = kAttnRowTiles;
+  const int wave_rows = 32 * pl.rowt;
+  const int max_waves = pl.rowt == 2 ? 4 : 8;
+  pl.waves = 1;
+  while (pl.waves < max_waves && pl.waves * wave_rows < pl.R) pl.waves *= 2;
+  pl.RB = (pl.R + pl.waves * wave_rows - 1) / (pl.waves * wave_rows);
+  pl.Rpad = pl.RB * pl.waves * wave_rows;
+  // about one workgroup per CU
+  const long long units = (long long)B * Hkv * pl.RB;
+  int s_target = (int)((kNumCUs + units - 1) / units);
   int s_max = P / kMinSplitKeys;
   int S = s_target < s_max ? s_target : s_max;
   if (S < 1) S = 1;
@@ -431,16 +472,9 @@ hipError_t launch_tree_attn(const AttnPlan& pl0, float scale, const void* q, con
     part_o = (float*)workspace;
     part_lse = part_o + rows * pl.D;
   }
-  hipError_t e;
-  if (pl.D == 128) {
-    if (pl.waves == 4) e = launch_fwd<128, 4>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
-    else if (pl.waves == 2) e = launch_fwd<128, 2>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
-    else e = launch_fwd<128, 1>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
-  } else {
-    if (pl.waves == 4) e = launch_fwd<64, 4>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
-    else if (pl.waves == 2) e = launch_fwd<64, 2>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
-    else e = launch_fwd<64, 1>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
-  }
+  const hipError_t e =
+      pl.D == 128 ? launch_fwd_d<128>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream)
+                  : launch_fwd_d<64>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
   if (e != hipSuccess || pl.S == 1) return e;
   const int rows = pl.B * pl.Hkv * pl.R;
   const int blocks = (rows + 3) / 4;

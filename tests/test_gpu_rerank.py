@@ -70,3 +70,15 @@ def test_rerank_ties_go_to_lower_token(gpu_lib):
     logits = logits.astype(np.float32)
     roots = np.array([3], np.int32)
     _compare(_gpu(gpu_lib, logits, roots, k, depth, n), logits, roots, k, depth, n)
+
+
+def test_rerank_constant_rows_take_lowest_tokens(gpu_lib):
+    """Rows where every logit ties (thousands of equal candidates per vocabulary
+    chunk): each row's proposals are its lowest token ids, on both sides."""
+    V, k, depth, n = 9000, 4, 3, 15
+    R = 1 + (depth - 1) * k
+    logits = synth.normal_f32((2, R, V), 1.0, 0, 770, 6)
+    logits[0, 0, :] = 0.5          # root row of sequence 0 is constant
+    logits[1, 1:, 4096:] = 7.0     # a constant tail across chunks in sequence 1
+    roots = np.array([1, 2], np.int32)
+    _compare(_gpu(gpu_lib, logits, roots, k, depth, n), logits, roots, k, depth, n)
