@@ -203,6 +203,95 @@ def spec_latency(torch, sda, dev, iters=20):
     return e0.elapsed_time(e1) * 1000.0 / iters
 
 
+PROFILE_RUNS = {
+    "prof": "rocprofv3 --kernel-trace --stats -T -d gpurun_out/prof -o run --output-format csv "
+            "-- python -u bench.py --steps 10 --warmup 2 --no-cpu-baseline",
+    "pmc_fetch": "rocprofv3 --pmc FETCH_SIZE -T -d gpurun_out/pmc_fetch -o run --output-format csv "
+                 "-- python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-spec",
+    "pmc_write": "rocprofv3 --pmc WRITE_SIZE -T -d gpurun_out/pmc_write -o run --output-format csv "
+                 "-- python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-spec",
+    "pmc_copy_fetch": "rocprofv3 --pmc FETCH_SIZE -T -d gpurun_out/pmc_copy_fetch -o run "
+                      "--output-format csv -- python -u bench.py --copy-calib",
+    "pmc_copy_write": "rocprofv3 --pmc WRITE_SIZE -T -d gpurun_out/pmc_copy_write -o run "
+                      "--output-format csv -- python -u bench.py --copy-calib",
+}
+TRACE_MD = "c5_step_kernel_trace.md"
+TRAFFIC_MD = "c5_step_hbm_traffic.md"
+
+
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_profiles(root):
+    """Turn the five rocprofv3 runs of PROFILE_RUNS (under `root`) into the committed
+    text summaries under profiles/ and the per-kernel traffic records bench.py reads."""
+    cfg = synth.CONFIGS["C5"]
+    B, N, Hq, Hkv, D, P, H, V = cfg.B, cfg.N, cfg.Hq, cfg.Hkv, cfg.D, cfg.P, cfg.H, cfg.V
+    stats = _read_csv(os.path.join(root, "prof", "run_kernel_stats.csv"))
+    total = sum(float(r["TotalDurationNs"]) for r in stats)
+    lines = ["# rocprofv3 kernel trace: C5 verification step", "",
+             "Command (repository root, one MI355X):", "", "    " + PROFILE_RUNS["prof"], "",
+             f"Workload: C5 (B={B}, N={N}, Hq={Hq}, Hkv={Hkv}, D={D}, P={P}, H={H}, V={V}); "
+             "12 steps (2 warmup + 10 timed)",
+             "plus the speculative-sampling latency loop at C4 shapes (accept_spec_kernel, "
+             "spec_init_kernel).", "",
+             "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"| {r['Name']} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{100.0 * float(r['TotalDurationNs']) / total:.1f} |")
+    with open(os.path.join(PROFILE_DIR, TRACE_MD), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    def per_kernel(run, counter):
+        acc = {}
+        for r in _read_csv(os.path.join(root, run, "run_counter_collection.csv")):
+            if r["Counter_Name"] == counter:
+                acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+
+    copy_bytes = 1 << 30
+    cf = per_kernel("pmc_copy_fetch", "FETCH_SIZE")
+    cw = per_kernel("pmc_copy_write", "WRITE_SIZE")
+    copy_name = max(cf, key=cf.get)
+    f_fac = copy_bytes / 1024.0 / cf[copy_name]
+    w_fac = copy_bytes / 1024.0 / cw[copy_name]
+    fetch = per_kernel("pmc_fetch", "FETCH_SIZE")
+    write = per_kernel("pmc_write", "WRITE_SIZE")
+    algo = {"tree_attn_fwd": 2 * B * Hkv * (P + N) * D * 2 + 2 * B * N * Hq * D * 2 + B * N * Hq * 4,
+            "lm_head_gemm": V * H * 2 + B * N * H * 2 + B * N * 16}
+    cmds = [PROFILE_RUNS[k] for k in ("pmc_fetch", "pmc_write", "pmc_copy_fetch", "pmc_copy_write")]
+    rows = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE), C5 verification step", "",
+            "Commands (repository root, one MI355X; each counter in a run of its own):", ""]
+    rows += ["    " + c for c in cmds]
+    rows += ["", f"Calibration: a plain 1 GiB device copy (`bench.py --copy-calib`, `{copy_name}`) reads",
+             f"FETCH_SIZE = {cf[copy_name]:.0f} KiB and WRITE_SIZE = {cw[copy_name]:.0f} KiB per dispatch,",
+             f"so HBM bytes = FETCH_SIZE x 1024 x {f_fac:.3f} + WRITE_SIZE x 1024 x {w_fac:.3f}.", "",
+             "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (calibrated) | algorithmic bytes | ratio |",
+             "|---|---|---|---|---|---|"]
+    for k in fetch:
+        if k.startswith("__amd"):
+            continue
+        hbm = fetch[k] * 1024 * f_fac + write.get(k, 0.0) * 1024 * w_fac
+        a = algo.get(k)
+        rows.append(f"| {k} | {fetch[k]:.0f} | {write.get(k, 0.0):.0f} | {hbm / 1e6:.1f} MB | "
+                    + (f"{a / 1e6:.1f} MB | {hbm / a:.3f} |" if a else " |  |"))
+    with open(os.path.join(PROFILE_DIR, TRAFFIC_MD), "w") as f:
+        f.write("\n".join(rows) + "\n")
+    for short, kname in (("lm_head", "lm_head_gemm"), ("tree_attn", "tree_attn_fwd")):
+        hbm = fetch[kname] * 1024 * f_fac + write[kname] * 1024 * w_fac
+        rec = {"kernel": kname, "workload": "C5", "fetch_kib": fetch[kname], "write_kib": write[kname],
+               "fetch_factor": f_fac, "write_factor": w_fac, "bytes_per_launch": int(round(hbm)),
+               "algorithmic_bytes": algo[kname], "source": KERNEL_SOURCES[short],
+               "source_sha256_16": _src_hash(KERNEL_SOURCES[short]), "commands": cmds}
+        with open(os.path.join(PROFILE_DIR, f"{short}_C5_traffic.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+    print("\n".join(lines + [""] + rows))
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -212,7 +301,13 @@ def main(argv=None):
     ap.add_argument("--no-spec", action="store_true")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="write profiles/ summaries from the rocprofv3 runs listed in "
+                         "PROFILE_RUNS, found under DIR (no GPU needed)")
     args = ap.parse_args(argv)
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return 0
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the multi-GPU sharding is described in DESIGN.md, not implemented)", file=sys.stderr)

@@ -23,23 +23,6 @@ namespace eagle {
 
 namespace {
 
-// 16-byte global load whose completion the caller waits for with wait_vmcnt<N>():
-// the compiler does not track it, so the destination must not be read before then.
-__device__ __forceinline__ u32x4 gload_async(const void* p) {
-  u32x4 v;
-  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
-  return v;
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Redefine a register after a wait_vmcnt so that its readers cannot be scheduled
-// above the wait (an empty asm that the compiler must treat as writing it).
-__device__ __forceinline__ void after_wait(u32x4& r) { asm volatile("" : "+v"(r)); }
-
 struct Top2 {
   float mx;
   float sec;
@@ -237,7 +220,22 @@ lm_head_gemm(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W
       __syncthreads();
     }
   }
-  wait_vmcnt<0>();   // the last (unused) loads land before the registers are reused
+  // The last loads of the rings are never read, so to the compiler their
+  // destination registers are dead and free for reuse while the loads are still in
+  // flight.  Waiting here and then touching every ring register keeps them reserved
+  // until the data has landed.
+  wait_vmcnt<0>();
+#pragma unroll
+  for (int u = 0; u < PF; ++u)
+#pragma unroll
+    for (int j = 0; j < VT; ++j)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) after_wait(wbuf[u][j][s]);
+#pragma unroll
+  for (int it = 0; it < H_PER; ++it) {
+    after_wait(hreg[0][it]);
+    after_wait(hreg[1][it]);
+  }
 
   // ---- epilogue: per-lane top-2 / exp-sum over its 16*VT vocabulary entries
   f32x4* red = (f32x4*)lds;   // [WV][MROWS] partials of this workgroup (reuses the staging LDS)

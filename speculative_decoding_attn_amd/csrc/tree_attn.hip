@@ -63,10 +63,15 @@ tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   constexpr int THREADS = WAVES * 64;
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
-  constexpr int K_UNITS = KC * D / 8;          // 16-byte pieces of a K chunk
-  constexpr int V_UNITS = (KC / 2) * (D / 8);  // key pairs x 16-byte pieces of a V chunk
-  constexpr int K_PER = (K_UNITS + THREADS - 1) / THREADS;
-  constexpr int V_PER = (V_UNITS + THREADS - 1) / THREADS;
+  // per chunk: 4D K units (16 bytes of one key row) and 4D V units (8 bytes of a key
+  // pair, i.e. two 8-byte loads); every thread takes the same number of each, so the
+  // per-wave load count of a chunk is a constant (the vmcnt arithmetic below)
+  constexpr int UNITS = 4 * D;
+  static_assert(UNITS % THREADS == 0, "chunk staging must divide evenly over the threads");
+  constexpr int K_PER = UNITS / THREADS;
+  constexpr int V_PER = UNITS / THREADS;
+  constexpr int LOADS = K_PER + 2 * V_PER;   // vector-memory loads per thread per chunk
+  static_assert(LOADS <= 63, "vmcnt is a 6-bit counter");
 
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * L::STAGE];
 
@@ -134,174 +139,174 @@ tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const float c = pl.c;
   const uint64_t node_mask = N >= 64 ? ~0ull : ((1ull << N) - 1ull);
 
-  // ---- global -> registers for one chunk
-  u32x4 kreg[K_PER];
-  u32x4 vreg[V_PER][2];
-  auto load_chunk = [&](int kb) {
+  // ---- chunk staging: a ring of two register slots.  Chunk c is loaded two
+  // iterations before it is computed (slot c%2), stored to LDS stage c%2 at the end of
+  // iteration c-1, and computed in iteration c, so each wave keeps one chunk of loads
+  // in flight across a whole chunk of compute.  The slots are indexed with
+  // compile-time constants only (the chunk loop is unrolled by two), which lets the
+  // compiler keep them in registers and wait for exactly the older slot's loads.
+  // Rows past P+N are clamped on load and zeroed on store.
+  u32x4 kreg[2][K_PER];
+  u32x2 vreg[2][V_PER][2];
+  auto load_chunk = [&](int slot, int kb) {
 #pragma unroll
     for (int it = 0; it < K_PER; ++it) {
       const int u = tid + it * THREADS;
-      kreg[it] = u32x4{0, 0, 0, 0};
-      if (u < K_UNITS) {
-        const int key = kb + u / (D / 8);
-        const int col = (u % (D / 8)) * 8;
-        if (key < key_lim) kreg[it] = *(const u32x4*)(kbase + (size_t)key * D + col);
-      }
+      const int key = min(kb + u / (D / 8), key_lim - 1);
+      const int col = (u % (D / 8)) * 8;
+      kreg[slot][it] = *(const u32x4*)(kbase + (size_t)key * D + col);
     }
 #pragma unroll
     for (int it = 0; it < V_PER; ++it) {
       const int u = tid + it * THREADS;
-      vreg[it][0] = u32x4{0, 0, 0, 0};
-      vreg[it][1] = u32x4{0, 0, 0, 0};
-      if (u < V_UNITS) {
-        const int kp = u % (KC / 2);
-        const int col = (u / (KC / 2)) * 8;
-        const int key = kb + 2 * kp;
-        if (key < key_lim) vreg[it][0] = *(const u32x4*)(vbase + (size_t)key * D + col);
-        if (key + 1 < key_lim) vreg[it][1] = *(const u32x4*)(vbase + (size_t)(key + 1) * D + col);
-      }
+      const int kp = u % (KC / 2);
+      const int d0 = (u / (KC / 2)) * 4;
+      const int key = kb + 2 * kp;
+      vreg[slot][it][0] = *(const u32x2*)(vbase + (size_t)min(key, key_lim - 1) * D + d0);
+      vreg[slot][it][1] = *(const u32x2*)(vbase + (size_t)min(key + 1, key_lim - 1) * D + d0);
     }
   };
-  // ---- registers -> LDS stage (K as [key][d], V transposed as [d][permuted key])
-  auto store_chunk = [&](int st) {
+  // registers -> LDS stage (K as [key][d], V transposed as [d][permuted key])
+  auto store_chunk = [&](int slot, int st, int kb) {
     uint16_t* Ks = lds + st * L::STAGE;
     uint16_t* Vs = Ks + L::KELEMS;
 #pragma unroll
     for (int it = 0; it < K_PER; ++it) {
       const int u = tid + it * THREADS;
-      if (u < K_UNITS) {
-        const int key = u / (D / 8);
-        const int col = (u % (D / 8)) * 8;
-        *(u32x4*)(Ks + key * L::KSTR + col) = kreg[it];
-      }
+      const int key = u / (D / 8);
+      const int col = (u % (D / 8)) * 8;
+      *(u32x4*)(Ks + key * L::KSTR + col) =
+          kb + key < key_lim ? kreg[slot][it] : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int it = 0; it < V_PER; ++it) {
       const int u = tid + it * THREADS;
-      if (u < V_UNITS) {
-        const int kp = u % (KC / 2);
-        const int col = (u / (KC / 2)) * 8;
-        const int key = 2 * kp;
-        const int pos = (key & 16) | vt_pos(key & 15);
-        const u32x4 a = vreg[it][0];
-        const u32x4 bb = vreg[it][1];
+      const int kp = u % (KC / 2);
+      const int d0 = (u / (KC / 2)) * 4;
+      const int key = 2 * kp;
+      const int pos = (key & 16) | vt_pos(key & 15);
+      const u32x2 a = kb + key < key_lim ? vreg[slot][it][0] : u32x2{0, 0};
+      const u32x2 bb = kb + key + 1 < key_lim ? vreg[slot][it][1] : u32x2{0, 0};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // elements 2e and 2e+1 of each key's 8-wide piece
-          const uint32_t lo = (a[e] & 0xFFFFu) | (bb[e] << 16);
-          const uint32_t hi = (a[e] >> 16) | (bb[e] & 0xFFFF0000u);
-          *(uint32_t*)(Vs + (col + 2 * e) * L::VSTR + pos) = lo;
-          *(uint32_t*)(Vs + (col + 2 * e + 1) * L::VSTR + pos) = hi;
-        }
+      for (int e = 0; e < 2; ++e) {
+        // elements 2e and 2e+1 of each key's 4-wide piece
+        const uint32_t lo = (a[e] & 0xFFFFu) | (bb[e] << 16);
+        const uint32_t hi = (a[e] >> 16) | (bb[e] & 0xFFFF0000u);
+        *(uint32_t*)(Vs + (d0 + 2 * e) * L::VSTR + pos) = lo;
+        *(uint32_t*)(Vs + (d0 + 2 * e + 1) * L::VSTR + pos) = hi;
       }
     }
   };
 
-  // let the Q loads land before the loop, so that the compiler's wait counters do
-  // not make the loop wait on the next chunk's prefetch when it reads Q
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-
   const int n_chunks = (key_end - key_begin + KC - 1) / KC;
   if (n_chunks > 0) {
-    load_chunk(key_begin);
-    store_chunk(0);
+    load_chunk(0, key_begin);
+    load_chunk(1, key_begin + KC);   // clamped (and zeroed) if it does not exist
+    store_chunk(0, 0, key_begin);
   }
   __syncthreads();
 
-  for (int ch = 0; ch < n_chunks; ++ch) {
-    const int kb = key_begin + ch * KC;
-    const int st = ch & 1;
-    if (ch + 1 < n_chunks) load_chunk(kb + KC);
+  // unrolled by two: the ring slot and LDS stage of each chunk are compile-time
+  // indices (a runtime index would move the ring to scratch memory)
+  for (int ch0 = 0; ch0 < n_chunks; ch0 += 2) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int ch = ch0 + st;
+      if (st == 1 && ch >= n_chunks) break;   // chunk ch0 always exists
+      const int kb = key_begin + ch * KC;
+      // chunk ch+2 into the slot chunk ch came from (its data is in LDS already)
+      load_chunk(st, kb + 2 * KC);
+      const uint16_t* Ks = lds + st * L::STAGE;
+      const uint16_t* Vs = Ks + L::KELEMS;
 
-    const uint16_t* Ks = lds + st * L::STAGE;
-    const uint16_t* Vs = Ks + L::KELEMS;
+      // S^T tile for 32 keys x ROWT row tiles
+      f32x16 sacc[ROWT];
+#pragma unroll
+      for (int t = 0; t < ROWT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        const bf16x8 kf = *(const bf16x8*)(Ks + l32 * L::KSTR + 16 * s + 8 * half);
+#pragma unroll
+        for (int t = 0; t < ROWT; ++t) sacc[t] = mfma32(kf, qf[t][s], sacc[t]);
+      }
 
-    // S^T tile for 32 keys x ROWT row tiles
-    f32x16 sacc[ROWT];
+      // scores of this lane's 16 keys; chunks that reach into the tree (or past it) get
+      // the ancestor mask: bit j of `allowed` says whether key kb + j is visible
+      float sv[ROWT][16];
 #pragma unroll
-    for (int t = 0; t < ROWT; ++t)
+      for (int t = 0; t < ROWT; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
+        for (int r = 0; r < 16; ++r) sv[t][r] = sacc[t][r];
+      if (kb + KC > P) {
+        const int off = kb - P;   // >= -31
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      const bf16x8 kf = *(const bf16x8*)(Ks + l32 * L::KSTR + 16 * s + 8 * half);
+        for (int t = 0; t < ROWT; ++t) {
+          const uint64_t tm = anc[t] & node_mask;
+          const uint32_t tree_bits = off >= 0 ? (off < 64 ? (uint32_t)(tm >> off) : 0u)
+                                              : (uint32_t)(tm << (-off));
+          const uint32_t prefix_bits = off < 0 ? ((1u << (-off)) - 1u) : 0u;
+          const uint32_t allowed = (tree_bits | prefix_bits) >> (4 * half);
 #pragma unroll
-      for (int t = 0; t < ROWT; ++t) sacc[t] = mfma32(kf, qf[t][s], sacc[t]);
-    }
-
-    // scores of this lane's 16 keys; chunks that reach into the tree (or past it) get
-    // the ancestor mask: bit j of `allowed` says whether key kb + j is visible
-    float sv[ROWT][16];
-#pragma unroll
-    for (int t = 0; t < ROWT; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sv[t][r] = sacc[t][r];
-    if (kb + KC > P) {
-      const int off = kb - P;   // >= -31
-#pragma unroll
-      for (int t = 0; t < ROWT; ++t) {
-        const uint64_t tm = anc[t] & node_mask;
-        const uint32_t tree_bits = off >= 0 ? (off < 64 ? (uint32_t)(tm >> off) : 0u)
-                                            : (uint32_t)(tm << (-off));
-        const uint32_t prefix_bits = off < 0 ? ((1u << (-off)) - 1u) : 0u;
-        const uint32_t allowed = (tree_bits | prefix_bits) >> (4 * half);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int bit = 8 * (r >> 2) + (r & 3);
-          sv[t][r] = ((allowed >> bit) & 1u) ? sv[t][r] : -INFINITY;
+          for (int r = 0; r < 16; ++r) {
+            const int bit = 8 * (r >> 2) + (r & 3);
+            sv[t][r] = ((allowed >> bit) & 1u) ? sv[t][r] : -INFINITY;
+          }
         }
       }
+
+      bf16x8 pf[ROWT][2];
+#pragma unroll
+      for (int t = 0; t < ROWT; ++t) {
+        float mx = sv[t][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sv[t][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mxc = mx * c;
+        const bool need = mxc > mc[t] + kLazy;
+        if (__ballot(need)) {
+          const float mnew = need ? mxc : mc[t];
+          const float alpha = need ? exp2f(mc[t] - mnew) : 1.f;
+          lsum[t] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[t][db][r] *= alpha;
+          mc[t] = mnew;
+        }
+        const float mcu = (mc[t] == -INFINITY) ? 0.f : mc[t];
+        float pr[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          pr[r] = __builtin_amdgcn_exp2f(fmaf(sv[t][r], c, -mcu));
+          lsum[t] += pr[r];
+        }
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          u32x4 pk;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pk[e] = pack_bf16x2(pr[8 * cc + 2 * e], pr[8 * cc + 2 * e + 1]);
+          pf[t][cc] = as_bf16x8(pk);
+        }
+      }
+
+      // O^T += V^T P^T
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          const bf16x8 vf = *(const bf16x8*)(Vs + (32 * db + l32) * L::VSTR + 16 * cc + 8 * half);
+#pragma unroll
+          for (int t = 0; t < ROWT; ++t) oacc[t][db] = mfma32(vf, pf[t][cc], oacc[t][db]);
+        }
+
+      // chunk ch+1 (loaded during iteration ch-1) -> LDS stage st^1, while chunk ch+2's
+      // loads stay in flight
+      if (ch + 1 < n_chunks) store_chunk(st ^ 1, st ^ 1, kb + KC);
+      __syncthreads();
     }
-
-    bf16x8 pf[ROWT][2];
-#pragma unroll
-    for (int t = 0; t < ROWT; ++t) {
-      float mx = sv[t][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sv[t][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mxc = mx * c;
-      const bool need = mxc > mc[t] + kLazy;
-      if (__ballot(need)) {
-        const float mnew = need ? mxc : mc[t];
-        const float alpha = need ? exp2f(mc[t] - mnew) : 1.f;
-        lsum[t] *= alpha;
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[t][db][r] *= alpha;
-        mc[t] = mnew;
-      }
-      const float mcu = (mc[t] == -INFINITY) ? 0.f : mc[t];
-      float pr[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        pr[r] = __builtin_amdgcn_exp2f(fmaf(sv[t][r], c, -mcu));
-        lsum[t] += pr[r];
-      }
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        u32x4 pk;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pk[e] = pack_bf16x2(pr[8 * cc + 2 * e], pr[8 * cc + 2 * e + 1]);
-        pf[t][cc] = as_bf16x8(pk);
-      }
-    }
-
-    // O^T += V^T P^T
-#pragma unroll
-    for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const bf16x8 vf = *(const bf16x8*)(Vs + (32 * db + l32) * L::VSTR + 16 * cc + 8 * half);
-#pragma unroll
-        for (int t = 0; t < ROWT; ++t) oacc[t][db] = mfma32(vf, pf[t][cc], oacc[t][db]);
-      }
-
-    if (ch + 1 < n_chunks) store_chunk(st ^ 1);
-    __syncthreads();
   }
-
   // ---- epilogue
 #pragma unroll
   for (int t = 0; t < ROWT; ++t) {
@@ -407,7 +412,9 @@ hipError_t launch_fwd_d(const AttnPlan& pl, const void* q, const void* k, const 
     if (pl.waves == 2) return launch_fwd<D, 2, 2>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
     return launch_fwd<D, 1, 2>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
   }
-  if (pl.waves == 8) return launch_fwd<D, 8, 1>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
+  if constexpr (D == 128) {   // D=64 uses at most 4 waves (chunk staging must divide evenly)
+    if (pl.waves == 8) return launch_fwd<D, 8, 1>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
+  }
   if (pl.waves == 4) return launch_fwd<D, 4, 1>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
   if (pl.waves == 2) return launch_fwd<D, 2, 1>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
   return launch_fwd<D, 1, 1>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
@@ -430,7 +437,7 @@ AttnPlan plan_tree_attn(int B, int N, int Hq, int Hkv, int D, int P, int kv_cap)
   // per SIMD: half the LDS reads per MFMA)
   pl.rowt = kAttnRowTiles;
   const int wave_rows = 32 * pl.rowt;
-  const int max_waves = pl.rowt == 2 ? 4 : 8;
+  const int max_waves = (pl.rowt == 2 || D == 64) ? 4 : 8;
   pl.waves = 1;
   while (pl.waves < max_waves && pl.waves * wave_rows < pl.R) pl.waves *= 2;
   pl.RB = (pl.R + pl.waves * wave_rows - 1) / (pl.waves * wave_rows);
