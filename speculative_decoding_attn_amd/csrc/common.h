@@ -76,32 +76,13 @@ __device__ __forceinline__ int wave_max_i(int x) {
   return x;
 }
 
-// Global loads whose completion the caller waits for explicitly with wait_vmcnt<N>()
-// (the number of vector-memory loads allowed to remain outstanding).  The compiler
-// does not track them, so a destination must not be read before that wait; call
-// after_wait() on it after the wait so that its readers stay below the wait.  Used
-// for register-ring prefetch across loop iterations, where the compiler's own wait
-// counters would drain every outstanding load at each iteration.
-__device__ __forceinline__ u32x4 gload_async(const void* p) {
-  u32x4 v;
-  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
-  return v;
-}
-
-__device__ __forceinline__ u32x2 gload_async8(const void* p) {
-  u32x2 v;
-  asm volatile("global_load_dwordx2 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
-  return v;
-}
-
+// Waits until at most N vector-memory operations of this wave are outstanding
+// (loads complete in issue order), for loads the compiler does not track.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N <= 63, "vmcnt is a 6-bit counter");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
-
-__device__ __forceinline__ void after_wait(u32x4& r) { asm volatile("" : "+v"(r)); }
-__device__ __forceinline__ void after_wait(u32x2& r) { asm volatile("" : "+v"(r)); }
 
 // Ancestor-or-self bitmask of node i (bit a set for every a on the root path of
 // i).  Walks at most 64 parent links and stops at any link that breaks the tree

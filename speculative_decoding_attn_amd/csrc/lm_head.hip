@@ -5,17 +5,17 @@
 // node; [P1] greedy decoding needs its top-1.
 //
 // logits^T tile = W (vocab rows, A operand) x hidden^T (tree rows, B operand) on the
-// 32x32x16 bf16 MFMA.  A workgroup of WV waves owns WV*VT*32 vocabulary rows and
-// MT*32 hidden rows; every wave multiplies its own VT vocabulary tiles with all MT
-// row tiles.  W is streamed from HBM exactly once, straight into registers in the
-// MFMA operand layout, PF 64-column blocks ahead (enough bytes in flight per CU to
-// cover HBM latency), while the hidden rows of the current 64-column block are
-// staged in LDS (XOR-swizzled 16-byte chunks, conflict-free reads) and shared by
-// all waves.  In the output layout every lane holds 16
-// vocabulary entries of ONE row, so the epilogue reduces in registers, then across
-// lane l ^ 32, then across the waves of the workgroup, and writes one partial
-// (max, second, sum of exp(x - max), argmax) per (row, vocabulary tile).  A second
-// kernel merges the partials of a row.  No atomics: the result is deterministic.
+// 32x32x16 bf16 MFMA.  A workgroup of 4 waves (one per SIMD) owns 4*VT*32 vocabulary
+// rows and MT*32 hidden rows; every wave multiplies its own VT vocabulary tiles with
+// all MT row tiles.  Both operands are staged in LDS, 64 columns (128 bytes per row) at
+// a time, by global->LDS DMA loads that read whole 128-byte lines (8 rows per wave
+// instruction) into XOR-swizzled rows; W is streamed from HBM exactly once and runs
+// three blocks ahead, the hidden rows (L2-resident) two blocks ahead.  In the output
+// layout every lane holds 16 vocabulary entries of ONE row, so the epilogue reduces
+// in registers, then across lane l ^ 32, then across the waves of the workgroup, and
+// writes one partial (max, second, sum of exp(x - max), argmax) per (row, vocabulary
+// tile).  A second kernel merges the partials of a row.  No atomics: the result is
+// deterministic.
 #include "common.h"
 #include "internal.h"
 
@@ -53,23 +53,61 @@ __device__ __forceinline__ Top2 shfl_xor_top2(Top2 a, int m) {
   return r;
 }
 
-template <int MT, int VT, int WV, int PF, int OCC>
-__global__ void __launch_bounds__(WV * 64, OCC)
+// global -> LDS copy of 16 bytes per lane: lane i's bytes land at LDS byte address
+// m0 + 16*i, one contiguous KiB per wave.  Issued through inline assembly: for the
+// compiler's own form of this load it waits for every outstanding load before any
+// later LDS read, which would drain the pipeline each block.  Completion is waited
+// for with wait_vmcnt<N>() and published to the other waves with a barrier.
+// (m0 is a reserved register to the compiler, hence the warning about its clobber;
+// the kernels' assembly is checked to use m0 nowhere else.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_byte_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_byte_addr))
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
+}
+
+// 16-byte chunk position of logical chunk c (of 8) in row r of a 128-byte-row LDS
+// tile: XOR-swizzled so that any 16 consecutive lanes reading rows r..r+15 at one
+// logical chunk hit 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+template <int MT, int VT, int NW>
+constexpr int lm_lds_bytes() {
+  return NW * (4 * VT * 32) * 128 + 2 * (MT * 32) * 128;
+}
+
+template <int MT, int VT, int NW, int LA>
+__global__ void __launch_bounds__(256)
 lm_head_gemm(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W, LmPlan pl,
              f32x4* __restrict__ part, float* __restrict__ logits) {
+  constexpr int WV = 4;
   constexpr int THREADS = WV * 64;
   constexpr int MROWS = MT * 32;
   constexpr int VROWS = WV * VT * 32;
-  constexpr int HB = 64;                               // hidden columns per block
-  constexpr int HSTAGE = MROWS * HB;                   // bf16 per LDS stage
-  constexpr int H_PER = MROWS * (HB / 8) / THREADS;    // 16-byte loads per thread per block
-  static_assert(MROWS * (HB / 8) % THREADS == 0, "hidden staging must cover the block exactly");
+  constexpr int RB = 128;                    // bytes per row of a 64-column block
+  constexpr int WSTAGE = VROWS * RB;
+  constexpr int HSTAGE = MROWS * RB;
+  constexpr int W_DMA = VT * 32 / 8;         // per wave and block: 8 rows per instruction
+  constexpr int H_DMA = MROWS / (8 * WV);
+  static_assert(NW == 3, "W block b+3 is loaded into the stage of block b");
+  static_assert(MROWS % (8 * WV) == 0, "each wave loads whole 8-row groups of hidden rows");
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * HSTAGE];
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint8_t* const wst = smem;                 // [NW][VROWS][128 B] W blocks
+  uint8_t* const hst = smem + NW * WSTAGE;   // [2][MROWS][128 B] hidden blocks
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (DMA bases)
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
@@ -82,13 +120,36 @@ lm_head_gemm(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W
   const int m0 = mb * MROWS;
   const int v0 = vt * VROWS + wv * VT * 32;
 
-  // W rows of this lane (A operand rows); rows past V read row 0 and are masked later
-  const uint16_t* wrow[VT];
+  // DMA sources for block 0 (a block adds 128 bytes).  Instruction t of a wave fills
+  // 8 whole rows (full 128-byte lines): lane i takes row 8t + i/8 and stores its
+  // chunk at position i%8, i.e. it reads the logical chunk that position holds.
+  // Rows past V / M re-read the last row; those outputs are never written.
+  const uint32_t base = lds_addr(smem);
+  const uint8_t* wsrc[W_DMA];
 #pragma unroll
-  for (int j = 0; j < VT; ++j) {
-    const int row = v0 + 32 * j + l32;
-    wrow[j] = W + (size_t)(row < V ? row : 0) * H + 8 * half;
+  for (int t = 0; t < W_DMA; ++t) {
+    const int r = wv * VT * 32 + 8 * t + (lane >> 3);          // row within the W tile
+    const int row = min(vt * VROWS + r, V - 1);
+    wsrc[t] = (const uint8_t*)(W + (size_t)row * H) + 16 * swz(r, lane & 7);
   }
+  const uint8_t* hsrc[H_DMA];
+#pragma unroll
+  for (int t = 0; t < H_DMA; ++t) {
+    const int r = wv * (MROWS / WV) + 8 * t + (lane >> 3);     // row within the hidden tile
+    const int row = min(m0 + r, M - 1);
+    hsrc[t] = (const uint8_t*)(hidden + (size_t)row * H) + 16 * swz(r, lane & 7);
+  }
+  auto issue_w = [&](int blk, int st) {
+#pragma unroll
+    for (int t = 0; t < W_DMA; ++t)
+      dma16(wsrc[t] + (size_t)blk * RB, base + st * WSTAGE + (wv * VT * 32 + 8 * t) * RB);
+  };
+  auto issue_h = [&](int blk, int st) {
+#pragma unroll
+    for (int t = 0; t < H_DMA; ++t)
+      dma16(hsrc[t] + (size_t)blk * RB,
+            base + NW * WSTAGE + st * HSTAGE + (wv * (MROWS / WV) + 8 * t) * RB);
+  };
 
   f32x16 acc[VT][MT];
 #pragma unroll
@@ -98,147 +159,80 @@ lm_head_gemm(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.f;
 
-  // Software pipeline.  W blocks stay in flight in a ring of PF register slots (W
-  // streams from HBM) and hidden blocks in a ring of 2 register slots (a hidden block
-  // is loaded two iterations before it is stored to LDS; it comes from L2 / Infinity
-  // Cache).  The loop's global loads are issued with inline assembly and waited for
-  // with explicit vmcnt counts: the compiler's wait-counter tracking cannot follow a
-  // register ring across the loop back-edge and would drain every load at each block.
-  // Issue order per iteration i: hidden loads H_i (block i+2), then W loads W_i (block
-  // i+PF).  Loads past the last block re-read it (addresses are clamped), so every
-  // iteration issues the same count and the counts below are exact; their data is
-  // never used (the hidden rows of a padding block are zeroed).
-  static_assert(PF % 2 == 0, "the loop is unrolled by PF and the hidden ring has 2 slots");
-  constexpr int W_LOADS = VT * 4;
-  constexpr int H_LOADS = H_PER;
-  // compute(i) needs W_{i-PF}; issued after it: (PF-1) x (H + W) of later iterations + H_i
-  constexpr int WAIT_W = (PF - 1) * (H_LOADS + W_LOADS) + H_LOADS;
-  // store of hidden block i+1 needs H_{i-1}; issued after it: W_{i-1}, H_i, W_i
-  constexpr int WAIT_H = 2 * W_LOADS + H_LOADS;
-  static_assert(WAIT_W <= 63 && WAIT_H <= 63, "vmcnt is a 6-bit counter");
-  u32x4 wbuf[PF][VT][4];
-  u32x4 hreg[2][H_PER];
+  // LDS fragment reads.  A block is NG = 4*MT groups g = (k-step s, row tile i); group
+  // g multiplies the VT W fragments of step s with hidden fragment (s, i).
+  constexpr int NG = 4 * MT;
+  auto w_frag = [&](int stage, int s, int j) {
+    const int r = wv * VT * 32 + 32 * j + l32;
+    return *(const bf16x8*)(wst + stage * WSTAGE + r * RB + 16 * swz(r, 2 * s + half));
+  };
+  auto h_frag = [&](int stage, int g) {
+    const int s = g / MT, i = g % MT;
+    const int r = 32 * i + l32;
+    return *(const bf16x8*)(hst + stage * HSTAGE + r * RB + 16 * swz(r, 2 * s + half));
+  };
 
-  const int nhb = H / HB;
-  const int nhb_pad = (nhb + PF - 1) / PF * PF;   // blocks past nhb are zero blocks
-  auto load_w = [&](u32x4 (&dst)[VT][4], int hbi) {
-    const int hb = min(hbi, nhb - 1) * HB;
+  // Pipeline.  Block b's W is in stage b%NW, its hidden rows in stage b%2.  Hidden
+  // fragments are read LA groups ahead of their MFMAs and W fragments one k-step
+  // ahead.  Once the last read of block b is issued (group NG-LA), the waves wait for
+  // it, meet at a barrier that also publishes block b+1, put hidden block b+2 and W
+  // block b+3 in flight into block b's stages, and start reading block b+1 while the
+  // last LA groups of block b are multiplied: the matrix cores never wait for the
+  // barrier.  Issue order per iteration: hidden b+2, then W b+3, so at block b's
+  // barrier only W b+2 may still be outstanding beyond what block b+1 needs.
+  static_assert(NG % (LA + 1) == 0, "the hidden fragment ring continues across blocks");
+  static_assert(LA <= MT, "the barrier falls in step 3, after step 2 last used wf[0]");
+  const int nhb = H / 64;
+  issue_w(0, 0);
+  issue_h(0, 0);
+  if (nhb > 1) {
+    issue_w(1, 1 % NW);
+    issue_h(1, 1);
+  }
+  if (nhb > 2) issue_w(2, 2 % NW);
+  if (nhb > 2) wait_vmcnt<2 * W_DMA + H_DMA>();
+  else if (nhb > 1) wait_vmcnt<W_DMA + H_DMA>();
+  else wait_vmcnt<0>();
+  __syncthreads();
+
+  bf16x8 wf[2][VT];
+  bf16x8 hf[LA + 1];
 #pragma unroll
-    for (int j = 0; j < VT; ++j)
+  for (int j = 0; j < VT; ++j) wf[0][j] = w_frag(0, 0, j);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) dst[j][s] = gload_async(wrow[j] + hb + 16 * s);
-  };
-  auto load_h = [&](u32x4 (&dst)[H_PER], int hbi) {
-    const int hb = min(hbi, nhb - 1) * HB;
-#pragma unroll
-    for (int it = 0; it < H_PER; ++it) {
-      const int u = tid + it * THREADS;
-      const int m = m0 + u / (HB / 8);
-      const int ch = u % (HB / 8);
-      dst[it] = gload_async(hidden + (size_t)min(m, M - 1) * H + hb + 8 * ch);
-    }
-  };
-  // zero the rows past M and the blocks past nhb, then store to LDS (after the wait)
-  auto store_h = [&](const u32x4 (&src)[H_PER], int st, int hbi) {
-    uint16_t* base = lds + st * HSTAGE;
-#pragma unroll
-    for (int it = 0; it < H_PER; ++it) {
-      const int u = tid + it * THREADS;
-      const int m = u / (HB / 8);
-      const int ch = u % (HB / 8);
-      const u32x4 v = (m0 + m < M && hbi < nhb) ? src[it] : u32x4{0, 0, 0, 0};
-      *(u32x4*)(base + m * HB + ((ch ^ (m & 7)) * 8)) = v;
-    }
-  };
-  // One block: 4 k-steps x MT row tiles = 4*MT operand reads from LDS, each feeding
-  // VT MFMAs.  The reads run LA groups ahead of the MFMAs that consume them; a
-  // scheduling fence after each group keeps that order (the scheduler would otherwise
-  // sink each read to its use and wait for it).
-  auto compute = [&](int st, const u32x4 (&wb)[VT][4]) {
-    const uint16_t* hs = lds + st * HSTAGE;
-    constexpr int NG = 4 * MT;   // groups: g = s * MT + i
-    constexpr int LA = 3;        // reads in flight ahead of the MFMAs
-    auto rd = [&](int g) {
-      const int s = g / MT, i = g % MT;
-      const int m = 32 * i + l32;
-      const int ch = 2 * s + half;
-      return *(const bf16x8*)(hs + m * HB + ((ch ^ (m & 7)) * 8));
-    };
-    bf16x8 hf[LA + 1];
-#pragma unroll
-    for (int g = 0; g < LA; ++g) hf[g] = rd(g);
+  for (int g = 0; g < LA; ++g) hf[g] = h_frag(0, g);
+
+  for (int b = 0; b < nhb; ++b) {
+    const int sw = b % NW, sh = b & 1;
+    const int sw1 = (b + 1) % NW, sh1 = sh ^ 1;   // block b+1 (stale past the last block)
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      if (g + LA < NG) hf[(g + LA) % (LA + 1)] = rd(g + LA);
       const int s = g / MT, i = g % MT;
+      if (g + LA < NG) hf[(g + LA) % (LA + 1)] = h_frag(sh, g + LA);
+      if (i == 0 && s < 3) {
 #pragma unroll
-      for (int j = 0; j < VT; ++j) acc[j][i] = mfma32(as_bf16x8(wb[j][s]), hf[g % (LA + 1)], acc[j][i]);
-      __builtin_amdgcn_sched_barrier(0);   // keep program order: read g+LA, then the MFMAs of g
-    }
-  };
-
-  // prologue: W blocks 0..PF-1 and hidden blocks 0, 1; drained before the loop
+        for (int j = 0; j < VT; ++j) wf[(s + 1) & 1][j] = w_frag(sw, s + 1, j);
+      }
+      if (g == NG - LA) {
+        if (b + 2 < nhb) wait_vmcnt<W_DMA>();
+        else wait_vmcnt<0>();
+        __syncthreads();   // block b+1 visible; every wave is done reading block b
+        if (b + 2 < nhb) issue_h(b + 2, sh);
+        if (b + 3 < nhb) issue_w(b + 3, sw);   // (b+3) % NW == b % NW for NW == 3
 #pragma unroll
-  for (int u = 0; u < PF; ++u) load_w(wbuf[u], u);
-  load_h(hreg[0], 0);
-  load_h(hreg[1], 1);
-  wait_vmcnt<0>();
+        for (int j = 0; j < VT; ++j) wf[0][j] = w_frag(sw1, 0, j);   // step 3 uses wf[1]
+      }
+      if (g >= NG - LA) hf[(g + LA) % (LA + 1)] = h_frag(sh1, g + LA - NG);
 #pragma unroll
-  for (int u = 0; u < PF; ++u)
-#pragma unroll
-    for (int j = 0; j < VT; ++j)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) after_wait(wbuf[u][j][s]);
-#pragma unroll
-  for (int it = 0; it < H_PER; ++it) {
-    after_wait(hreg[0][it]);
-    after_wait(hreg[1][it]);
-  }
-  store_h(hreg[0], 0, 0);
-  __syncthreads();
-
-  // iteration i: issue H_i into ring slot i%2 (its block i was stored last
-  // iteration), compute block i from LDS stage i%2 with W slot i%PF, refill that
-  // slot with block i+PF, store hidden block i+1 into LDS stage (i+1)%2
-  for (int hb0 = 0; hb0 < nhb_pad; hb0 += PF) {
-#pragma unroll
-    for (int u = 0; u < PF; ++u) {
-      const int hbi = hb0 + u;
-      load_h(hreg[u & 1], hbi + 2);
-      wait_vmcnt<WAIT_W>();
-#pragma unroll
-      for (int j = 0; j < VT; ++j)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) after_wait(wbuf[u][j][s]);
-      compute(u & 1, wbuf[u]);
-      load_w(wbuf[u], hbi + PF);
-      wait_vmcnt<WAIT_H>();
-#pragma unroll
-      for (int it = 0; it < H_PER; ++it) after_wait(hreg[(u + 1) & 1][it]);
-      store_h(hreg[(u + 1) & 1], (u + 1) & 1, hbi + 1);
-      __syncthreads();
+      for (int j = 0; j < VT; ++j) acc[j][i] = mfma32(wf[s & 1][j], hf[g % (LA + 1)], acc[j][i]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
-  // The last loads of the rings are never read, so to the compiler their
-  // destination registers are dead and free for reuse while the loads are still in
-  // flight.  Waiting here and then touching every ring register keeps them reserved
-  // until the data has landed.
-  wait_vmcnt<0>();
-#pragma unroll
-  for (int u = 0; u < PF; ++u)
-#pragma unroll
-    for (int j = 0; j < VT; ++j)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) after_wait(wbuf[u][j][s]);
-#pragma unroll
-  for (int it = 0; it < H_PER; ++it) {
-    after_wait(hreg[0][it]);
-    after_wait(hreg[1][it]);
-  }
+  __syncthreads();   // every wave is done with the stages; the epilogue reuses them
 
   // ---- epilogue: per-lane top-2 / exp-sum over its 16*VT vocabulary entries
-  f32x4* red = (f32x4*)lds;   // [WV][MROWS] partials of this workgroup (reuses the staging LDS)
+  f32x4* red = (f32x4*)smem;   // [WV][MROWS] partials of this workgroup (reuses the staging LDS)
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
     const int mloc = 32 * i + l32;
@@ -325,11 +319,21 @@ lm_head_merge(LmPlan pl, const f32x4* __restrict__ part, float* __restrict__ out
   }
 }
 
-template <int MT, int VT, int WV, int PF, int OCC>
+template <int MT, int VT, int NW, int LA>
 hipError_t launch_gemm(const LmPlan& pl, const void* hidden, const void* W, f32x4* part,
                        float* logits, hipStream_t stream) {
-  hipLaunchKernelGGL((lm_head_gemm<MT, VT, WV, PF, OCC>), dim3(pl.nvt * pl.nmb), dim3(WV * 64), 0,
-                     stream, (const uint16_t*)hidden, (const uint16_t*)W, pl, part, logits);
+  constexpr int bytes = lm_lds_bytes<MT, VT, NW>();
+  static_assert(bytes <= 160 * 1024, "MI355X LDS is 160 KiB per workgroup");
+  static_assert(4 * MT * 32 * 16 <= bytes, "the epilogue's partials reuse the staging LDS");
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)lm_head_gemm<MT, VT, NW, LA>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((lm_head_gemm<MT, VT, NW, LA>), dim3(pl.nvt * pl.nmb), dim3(256), bytes, stream,
+                     (const uint16_t*)hidden, (const uint16_t*)W, pl, part, logits);
   return hipGetLastError();
 }
 
@@ -374,10 +378,10 @@ hipError_t launch_lm_head(const LmPlan& pl, const void* hidden, const void* W, f
   f32x4* part = (f32x4*)workspace;
   hipError_t e;
   switch (pl.variant) {
-    case 3: e = launch_gemm<8, 2, 4, 4, 1>(pl, hidden, W, part, out_logits, stream); break;
-    case 2: e = launch_gemm<4, 2, 4, 4, 1>(pl, hidden, W, part, out_logits, stream); break;
-    case 1: e = launch_gemm<2, 2, 4, 4, 2>(pl, hidden, W, part, out_logits, stream); break;
-    default: e = launch_gemm<1, 1, 4, 4, 2>(pl, hidden, W, part, out_logits, stream); break;
+    case 3: e = launch_gemm<8, 2, 3, 3>(pl, hidden, W, part, out_logits, stream); break;
+    case 2: e = launch_gemm<4, 2, 3, 3>(pl, hidden, W, part, out_logits, stream); break;
+    case 1: e = launch_gemm<2, 2, 3, 1>(pl, hidden, W, part, out_logits, stream); break;
+    default: e = launch_gemm<1, 1, 3, 1>(pl, hidden, W, part, out_logits, stream); break;
   }
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(lm_head_merge, dim3((pl.M + 3) / 4), dim3(256), 0, stream, pl,

@@ -13,8 +13,11 @@ in-order vector-memory counter (every global/buffer/flat/scratch access incremen
 it; `s_waitcnt vmcnt(N)` retires the oldest until N remain), and reports each
 instruction that touches a register an inline-assembly load is still writing.
 Loads the compiler emitted itself are counted but not flagged: the compiler inserts
-their waits.  It also counts indirect register indexing (`movrel`,
-`s_set_gpr_idx`), which inline-asm destinations cannot survive.
+their waits.  Global-to-LDS loads (`global_load_lds_*`) write no register, so they
+only count.  It also counts indirect register indexing (`movrel`, `s_set_gpr_idx`),
+which inline-asm destinations cannot survive, and lists compiler-generated uses of
+m0 in kernels whose inline assembly sets m0 for global-to-LDS loads (the compiler
+treats m0 as reserved and may not honour a clobber of it).
 """
 import re
 from collections import defaultdict
@@ -98,7 +101,14 @@ def _blocks(lines):
 
 
 def kernel_hazards(lines, max_states=256):
-    """Instructions that touch an inline-asm load destination before its wait."""
+    """Instructions that touch an inline-asm load destination before its wait.
+
+    The state carried along the control-flow graph is the list of outstanding
+    vector-memory operations, oldest first, from the oldest inline-asm register load
+    on: an entry is that load's destination registers, or None for any other
+    operation (only its place in the order matters).  Operations older than every
+    inline-asm load cannot change when such a load retires, so they are dropped.
+    """
     blocks, succ = _blocks(lines)
     hazards = []
     seen = defaultdict(set)
@@ -108,7 +118,7 @@ def kernel_hazards(lines, max_states=256):
         if state in seen[bi] or len(seen[bi]) >= max_states:
             continue
         seen[bi].add(state)
-        pending = list(state)   # oldest first: (dest registers, untracked?, text)
+        pending = list(state)
         for ins, from_asm in blocks[bi][1]:
             op = ins.split()[0]
             operands = ins[len(op):]
@@ -118,20 +128,42 @@ def kernel_hazards(lines, max_states=256):
                     keep = int(m.group(1))
                     while len(pending) > keep:
                         pending.pop(0)
+                    while pending and pending[0] is None:
+                        pending.pop(0)
                 continue
-            touched = regs_of(operands)
-            for dest, untracked, src in pending:
-                if untracked and touched & dest:
-                    hazards.append((ins, src))
+            if pending:
+                touched = regs_of(operands)
+                for dest in pending:
+                    if dest is not None and touched & dest:
+                        hazards.append((ins, op))
             vm = _VMEM.match(op)
             if vm:
                 loads = vm.group(2) == 'load' or (vm.group(2) == 'atomic' and 'glc' in ins)
-                dest = regs_of(operands.split(',')[0]) if loads else frozenset()
-                pending.append((dest, from_asm and loads, ins))
+                if '_lds_' in op:
+                    loads = False   # writes LDS at m0; its first operand is the address
+                if from_asm and loads:
+                    pending.append(regs_of(operands.split(',')[0]))
+                elif pending:
+                    pending.append(None)
         nxt = tuple(pending)
         for s in succ[bi]:
             work.append((s, nxt))
     return hazards
+
+
+def m0_writers(lines):
+    """Instructions other than the inline-asm `s_mov_b32 m0, ...` that name m0."""
+    out, in_asm = [], False
+    for ln in lines:
+        if ';;#ASMSTART' in ln:
+            in_asm = True
+        elif ';;#ASMEND' in ln:
+            in_asm = False
+        else:
+            s = ln.split(';')[0]
+            if re.search(r'\bm0\b', s) and not in_asm:
+                out.append(s.strip())
+    return out
 
 
 def indirect_indexing(lines):

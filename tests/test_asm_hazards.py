@@ -40,6 +40,23 @@ def test_checker_catches_planted_reuse():
     assert [h[0] for h in hz] == ["v_add_u32_e32 v14, 1, v1"]
 
 
+def test_checker_lds_loads_write_no_register():
+    text = """\
+_Z3dmav:
+\t;;#ASMSTART
+\ts_mov_b32 m0, s4
+\tglobal_load_lds_dwordx4 v[2:3], off
+\t;;#ASMEND
+\tv_add_u32_e32 v2, 16, v2
+\ts_mov_b32 m0, s5
+\ts_endpgm
+.Lfunc_end2:
+"""
+    k = ah.split_kernels(text)["_Z3dmav"]
+    assert ah.kernel_hazards(k) == []          # the address register may be reused at once
+    assert ah.m0_writers(k) == ["s_mov_b32 m0, s5"]
+
+
 def test_checker_follows_loop_back_edges():
     text = """\
 _Z4loopv:
@@ -82,6 +99,8 @@ def test_inline_asm_loads_are_safe(kernel_asm, src):
             continue
         if ah.indirect_indexing(lines):
             problems.append((name, "indirect register indexing"))
-        for ins, src_load in ah.kernel_hazards(lines)[:3]:
-            problems.append((name, ins, src_load))
+        if any('global_load_lds' in ln for ln in lines):
+            problems += [(name, "compiler use of m0", x) for x in ah.m0_writers(lines)[:3]]
+        for ins, _ in ah.kernel_hazards(lines)[:3]:
+            problems.append((name, ins))
     assert not problems, problems
