@@ -5,12 +5,13 @@
 // node; [P1] greedy decoding needs its top-1.
 //
 // logits^T tile = W (vocab rows, A operand) x hidden^T (tree rows, B operand) on the
-// 32x32x16 bf16 MFMA.  A workgroup of 4 waves (one per SIMD) owns 4*VT*32 vocabulary
-// rows and MT*32 hidden rows; every wave multiplies its own VT vocabulary tiles with
-// all MT row tiles.  Both operands are staged in LDS, 64 columns (128 bytes per row) at
+// 32x32x16 bf16 MFMA.  A workgroup's waves form a grid over its vocabulary rows and
+// hidden rows; every wave multiplies its VT vocabulary tiles with its MT row tiles
+// (for the largest M: 8 waves, two per SIMD, so one wave's MFMAs cover the other's
+// waits).  Both operands are staged in LDS, 64 columns (128 bytes per row) at
 // a time, by global->LDS DMA loads that read whole 128-byte lines (8 rows per wave
 // instruction) into XOR-swizzled rows; W is streamed from HBM exactly once and runs
-// three blocks ahead, the hidden rows (L2-resident) two blocks ahead.  In the output
+// two to three blocks ahead, the hidden rows (L2-resident) one to two.  In the output
 // layout every lane holds 16 vocabulary entries of ONE row, so the epilogue reduces
 // in registers, then across lane l ^ 32, then across the waves of the workgroup, and
 // writes one partial (max, second, sum of exp(x - max), argmax) per (row, vocabulary
@@ -80,26 +81,31 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // logical chunk hit 16 distinct 16-byte bank groups.
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-template <int MT, int VT, int NW>
+constexpr int kLmStagesW = 3;   // W blocks: b+2 in flight while b and b+1 are resident
+
+template <int MT, int VT, int WVV, int WVM>
 constexpr int lm_lds_bytes() {
-  return NW * (4 * VT * 32) * 128 + 2 * (MT * 32) * 128;
+  return kLmStagesW * (WVV * VT * 32) * 128 + 2 * (WVM * MT * 32) * 128;
 }
 
-template <int MT, int VT, int NW, int LA>
-__global__ void __launch_bounds__(256)
+// Waves form a WVV x WVM grid: wave (wvv, wvm) multiplies vocabulary tiles
+// wvv*VT .. wvv*VT+VT-1 with hidden row tiles wvm*MT .. wvm*MT+MT-1 of the workgroup.
+template <int MT, int VT, int WVV, int WVM, int LA>
+__global__ void __launch_bounds__(WVV * WVM * 64)
 lm_head_gemm(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W, LmPlan pl,
              f32x4* __restrict__ part, float* __restrict__ logits) {
-  constexpr int WV = 4;
+  constexpr int WV = WVV * WVM;
   constexpr int THREADS = WV * 64;
-  constexpr int MROWS = MT * 32;
-  constexpr int VROWS = WV * VT * 32;
+  constexpr int NW = kLmStagesW;
+  constexpr int MROWS = WVM * MT * 32;
+  constexpr int VROWS = WVV * VT * 32;
   constexpr int RB = 128;                    // bytes per row of a 64-column block
   constexpr int WSTAGE = VROWS * RB;
   constexpr int HSTAGE = MROWS * RB;
-  constexpr int W_DMA = VT * 32 / 8;         // per wave and block: 8 rows per instruction
+  constexpr int W_DMA = VROWS / (8 * WV);    // per wave and block: 8 rows per instruction
   constexpr int H_DMA = MROWS / (8 * WV);
-  static_assert(NW == 3, "W block b+3 is loaded into the stage of block b");
-  static_assert(MROWS % (8 * WV) == 0, "each wave loads whole 8-row groups of hidden rows");
+  static_assert(W_DMA * 8 * WV == VROWS && H_DMA * 8 * WV == MROWS,
+                "the waves load whole 8-row groups of both tiles");
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t* const wst = smem;                 // [NW][VROWS][128 B] W blocks
@@ -108,6 +114,7 @@ lm_head_gemm(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (DMA bases)
+  const int wvv = wv % WVV, wvm = wv / WVV;
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
@@ -118,37 +125,36 @@ lm_head_gemm(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W
   const int vt = logical / pl.nmb;
   const int M = pl.M, H = pl.H, V = pl.V;
   const int m0 = mb * MROWS;
-  const int v0 = vt * VROWS + wv * VT * 32;
+  const int v0 = vt * VROWS + wvv * VT * 32;   // this wave's first vocabulary row
 
-  // DMA sources for block 0 (a block adds 128 bytes).  Instruction t of a wave fills
-  // 8 whole rows (full 128-byte lines): lane i takes row 8t + i/8 and stores its
-  // chunk at position i%8, i.e. it reads the logical chunk that position holds.
-  // Rows past V / M re-read the last row; those outputs are never written.
+  // DMA sources for block 0 (a block adds 128 bytes).  Instruction t of wave wv fills
+  // the 8 whole rows 8*(wv*N + t) .. +7 of a stage (full 128-byte lines): lane i
+  // takes row +i/8 and stores its chunk at position i%8, i.e. it reads the logical
+  // chunk that position holds.  Rows past V / M re-read the last row; those outputs
+  // are never written.
   const uint32_t base = lds_addr(smem);
   const uint8_t* wsrc[W_DMA];
 #pragma unroll
   for (int t = 0; t < W_DMA; ++t) {
-    const int r = wv * VT * 32 + 8 * t + (lane >> 3);          // row within the W tile
+    const int r = 8 * (wv * W_DMA + t) + (lane >> 3);          // row within the W tile
     const int row = min(vt * VROWS + r, V - 1);
     wsrc[t] = (const uint8_t*)(W + (size_t)row * H) + 16 * swz(r, lane & 7);
   }
   const uint8_t* hsrc[H_DMA];
 #pragma unroll
   for (int t = 0; t < H_DMA; ++t) {
-    const int r = wv * (MROWS / WV) + 8 * t + (lane >> 3);     // row within the hidden tile
+    const int r = 8 * (wv * H_DMA + t) + (lane >> 3);          // row within the hidden tile
     const int row = min(m0 + r, M - 1);
     hsrc[t] = (const uint8_t*)(hidden + (size_t)row * H) + 16 * swz(r, lane & 7);
   }
-  auto issue_w = [&](int blk, int st) {
-#pragma unroll
-    for (int t = 0; t < W_DMA; ++t)
-      dma16(wsrc[t] + (size_t)blk * RB, base + st * WSTAGE + (wv * VT * 32 + 8 * t) * RB);
+  // one DMA instruction t (8 rows) of W / hidden block blk into stage st; hidden
+  // groups wholly past M are skipped (their rows are never written out)
+  auto issue_w = [&](int blk, int st, int t) {
+    dma16(wsrc[t] + (size_t)blk * RB, base + st * WSTAGE + 8 * (wv * W_DMA + t) * RB);
   };
-  auto issue_h = [&](int blk, int st) {
-#pragma unroll
-    for (int t = 0; t < H_DMA; ++t)
-      dma16(hsrc[t] + (size_t)blk * RB,
-            base + NW * WSTAGE + st * HSTAGE + (wv * (MROWS / WV) + 8 * t) * RB);
+  auto issue_h = [&](int blk, int st, int t) {
+    if (m0 + 8 * (wv * H_DMA + t) < M)
+      dma16(hsrc[t] + (size_t)blk * RB, base + NW * WSTAGE + st * HSTAGE + 8 * (wv * H_DMA + t) * RB);
   };
 
   f32x16 acc[VT][MT];
@@ -163,37 +169,47 @@ lm_head_gemm(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W
   // g multiplies the VT W fragments of step s with hidden fragment (s, i).
   constexpr int NG = 4 * MT;
   auto w_frag = [&](int stage, int s, int j) {
-    const int r = wv * VT * 32 + 32 * j + l32;
+    const int r = wvv * VT * 32 + 32 * j + l32;
     return *(const bf16x8*)(wst + stage * WSTAGE + r * RB + 16 * swz(r, 2 * s + half));
   };
   auto h_frag = [&](int stage, int g) {
     const int s = g / MT, i = g % MT;
-    const int r = 32 * i + l32;
+    const int r = wvm * MT * 32 + 32 * i + l32;
     return *(const bf16x8*)(hst + stage * HSTAGE + r * RB + 16 * swz(r, 2 * s + half));
   };
 
-  // Pipeline.  Block b's W is in stage b%NW, its hidden rows in stage b%2.  Hidden
+  // Pipeline.  Block b's W is in stage b%3, its hidden rows in stage b%2.  Hidden
   // fragments are read LA groups ahead of their MFMAs and W fragments one k-step
-  // ahead.  Once the last read of block b is issued (group NG-LA), the waves wait for
-  // it, meet at a barrier that also publishes block b+1, put hidden block b+2 and W
-  // block b+3 in flight into block b's stages, and start reading block b+1 while the
-  // last LA groups of block b are multiplied: the matrix cores never wait for the
-  // barrier.  Issue order per iteration: hidden b+2, then W b+3, so at block b's
-  // barrier only W b+2 may still be outstanding beyond what block b+1 needs.
+  // ahead.  Once the last read of block b is issued (group NG-LA) the waves wait for
+  // it and meet at a barrier that also publishes block b+1, then read block b+1
+  // while the last LA groups of block b are multiplied, so the matrix cores do not
+  // wait for the barrier.  The DMA instructions are spread over the block instead of
+  // issued in bursts (a burst fills the vector L1's miss queue and stalls the wave's
+  // in-order issue, MFMAs included): W block b+2 over groups 0..NG-LA-1 (its stage
+  // was freed at block b-1's barrier), hidden block b+2 over the last LA groups (its
+  // stage is block b's, freed at this barrier).  Hidden loads are issued after the W
+  // loads of the same block, so at block b's barrier only W block b+2 may be
+  // outstanding beyond what block b+1 needs.
   static_assert(NG % (LA + 1) == 0, "the hidden fragment ring continues across blocks");
   static_assert(LA <= MT, "the barrier falls in step 3, after step 2 last used wf[0]");
+  constexpr int NGI = NG - LA;
   const int nhb = H / 64;
-  issue_w(0, 0);
-  issue_h(0, 0);
+#pragma unroll
+  for (int t = 0; t < W_DMA; ++t) issue_w(0, 0, t);
+#pragma unroll
+  for (int t = 0; t < H_DMA; ++t) issue_h(0, 0, t);
   if (nhb > 1) {
-    issue_w(1, 1 % NW);
-    issue_h(1, 1);
+#pragma unroll
+    for (int t = 0; t < W_DMA; ++t) issue_w(1, 1, t);
+    wait_vmcnt<W_DMA>();   // W 0 and hidden 0
+  } else {
+    wait_vmcnt<0>();
   }
-  if (nhb > 2) issue_w(2, 2 % NW);
-  if (nhb > 2) wait_vmcnt<2 * W_DMA + H_DMA>();
-  else if (nhb > 1) wait_vmcnt<W_DMA + H_DMA>();
-  else wait_vmcnt<0>();
   __syncthreads();
+  if (nhb > 1) {
+#pragma unroll
+    for (int t = 0; t < H_DMA; ++t) issue_h(1, 1, t);
+  }
 
   bf16x8 wf[2][VT];
   bf16x8 hf[LA + 1];
@@ -205,6 +221,8 @@ lm_head_gemm(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W
   for (int b = 0; b < nhb; ++b) {
     const int sw = b % NW, sh = b & 1;
     const int sw1 = (b + 1) % NW, sh1 = sh ^ 1;   // block b+1 (stale past the last block)
+    const int sw2 = (b + 2) % NW;                 // == (b-1) % NW
+    const bool more = b + 2 < nhb;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
@@ -214,16 +232,20 @@ lm_head_gemm(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W
 #pragma unroll
         for (int j = 0; j < VT; ++j) wf[(s + 1) & 1][j] = w_frag(sw, s + 1, j);
       }
-      if (g == NG - LA) {
-        if (b + 2 < nhb) wait_vmcnt<W_DMA>();
+#pragma unroll
+      for (int t = 0; t < W_DMA; ++t)
+        if ((t * NGI) / W_DMA == g && more) issue_w(b + 2, sw2, t);
+      if (g == NGI) {
+        if (more) wait_vmcnt<W_DMA>();
         else wait_vmcnt<0>();
         __syncthreads();   // block b+1 visible; every wave is done reading block b
-        if (b + 2 < nhb) issue_h(b + 2, sh);
-        if (b + 3 < nhb) issue_w(b + 3, sw);   // (b+3) % NW == b % NW for NW == 3
 #pragma unroll
         for (int j = 0; j < VT; ++j) wf[0][j] = w_frag(sw1, 0, j);   // step 3 uses wf[1]
       }
-      if (g >= NG - LA) hf[(g + LA) % (LA + 1)] = h_frag(sh1, g + LA - NG);
+#pragma unroll
+      for (int t = 0; t < H_DMA; ++t)
+        if (NGI + (t * LA) / H_DMA == g && more) issue_h(b + 2, sh, t);
+      if (g >= NGI) hf[(g + LA) % (LA + 1)] = h_frag(sh1, g + LA - NG);
 #pragma unroll
       for (int j = 0; j < VT; ++j) acc[j][i] = mfma32(wf[s & 1][j], hf[g % (LA + 1)], acc[j][i]);
       __builtin_amdgcn_sched_barrier(0);
@@ -232,10 +254,10 @@ lm_head_gemm(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W
   __syncthreads();   // every wave is done with the stages; the epilogue reuses them
 
   // ---- epilogue: per-lane top-2 / exp-sum over its 16*VT vocabulary entries
-  f32x4* red = (f32x4*)smem;   // [WV][MROWS] partials of this workgroup (reuses the staging LDS)
+  f32x4* red = (f32x4*)smem;   // [WVV][MROWS] partials of this workgroup (reuses the staging LDS)
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
-    const int mloc = 32 * i + l32;
+    const int mloc = wvm * MT * 32 + 32 * i + l32;
     const int m = m0 + mloc;
     Top2 t{-INFINITY, -INFINITY, 0.f, 0x7fffffff};
 #pragma unroll
@@ -279,7 +301,7 @@ lm_head_gemm(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W
         }
     }
     t = merge_top2(t, shfl_xor_top2(t, 32));
-    if (half == 0) red[wv * MROWS + mloc] = f32x4{t.mx, t.sec, t.z, __int_as_float(t.idx)};
+    if (half == 0) red[wvv * MROWS + mloc] = f32x4{t.mx, t.sec, t.z, __int_as_float(t.idx)};
   }
   __syncthreads();
   for (int mloc = tid; mloc < MROWS; mloc += THREADS) {
@@ -288,7 +310,7 @@ lm_head_gemm(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W
     f32x4 e0 = red[mloc];
     Top2 t{e0[0], e0[1], e0[2], __float_as_int(e0[3])};
 #pragma unroll
-    for (int q = 1; q < WV; ++q) {
+    for (int q = 1; q < WVV; ++q) {
       const f32x4 e = red[q * MROWS + mloc];
       t = merge_top2(t, Top2{e[0], e[1], e[2], __float_as_int(e[3])});
     }
@@ -319,21 +341,22 @@ lm_head_merge(LmPlan pl, const f32x4* __restrict__ part, float* __restrict__ out
   }
 }
 
-template <int MT, int VT, int NW, int LA>
+template <int MT, int VT, int WVV, int WVM, int LA>
 hipError_t launch_gemm(const LmPlan& pl, const void* hidden, const void* W, f32x4* part,
                        float* logits, hipStream_t stream) {
-  constexpr int bytes = lm_lds_bytes<MT, VT, NW>();
+  constexpr int bytes = lm_lds_bytes<MT, VT, WVV, WVM>();
   static_assert(bytes <= 160 * 1024, "MI355X LDS is 160 KiB per workgroup");
-  static_assert(4 * MT * 32 * 16 <= bytes, "the epilogue's partials reuse the staging LDS");
+  static_assert(WVV * WVM * MT * 32 * 16 <= bytes, "the epilogue's partials reuse the staging LDS");
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)lm_head_gemm<MT, VT, NW, LA>,
+    hipError_t e = hipFuncSetAttribute((const void*)lm_head_gemm<MT, VT, WVV, WVM, LA>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((lm_head_gemm<MT, VT, NW, LA>), dim3(pl.nvt * pl.nmb), dim3(256), bytes, stream,
-                     (const uint16_t*)hidden, (const uint16_t*)W, pl, part, logits);
+  hipLaunchKernelGGL((lm_head_gemm<MT, VT, WVV, WVM, LA>), dim3(pl.nvt * pl.nmb),
+                     dim3(WVV * WVM * 64), bytes, stream, (const uint16_t*)hidden,
+                     (const uint16_t*)W, pl, part, logits);
   return hipGetLastError();
 }
 
@@ -344,22 +367,22 @@ LmPlan plan_lm_head(int M, int H, int V) {
   pl.M = M;
   pl.H = H;
   pl.V = V;
-  // tile shapes: every wave covers all MT m-tiles of the workgroup's rows and VT
-  // 32-row vocabulary tiles; W blocks 4 deep in flight
+  // tile shapes (LDS holds 3 W stages of vrows x 128 B and 2 hidden stages of
+  // mrows x 128 B)
   if (M > 128) {
-    pl.variant = 3;          // MT=8 VT=2: 256 rows x 256 vocab, 1 wave/SIMD (accumulators in AGPRs)
+    pl.variant = 3;          // 8 waves (4 vocab x 2 row halves), 2 per SIMD: 256 rows x 256 vocab
     pl.mrows = 256;
     pl.vrows = 256;
   } else if (M > 64) {
-    pl.variant = 2;          // MT=4 VT=2: 128 rows x 256 vocab
+    pl.variant = 2;          // 4 waves, MT=4 VT=2: 128 rows x 256 vocab
     pl.mrows = 128;
     pl.vrows = 256;
   } else if (M > 32) {
-    pl.variant = 1;          // MT=2 VT=2: 64 rows x 256 vocab, 2 waves/SIMD
+    pl.variant = 1;          // 4 waves, MT=2 VT=2: 64 rows x 256 vocab
     pl.mrows = 64;
     pl.vrows = 256;
   } else {
-    pl.variant = 0;          // MT=1 VT=1: 32 rows x 128 vocab, 2 waves/SIMD
+    pl.variant = 0;          // 4 waves, MT=1 VT=1: 32 rows x 128 vocab
     pl.mrows = 32;
     pl.vrows = 128;
   }
@@ -378,10 +401,10 @@ hipError_t launch_lm_head(const LmPlan& pl, const void* hidden, const void* W, f
   f32x4* part = (f32x4*)workspace;
   hipError_t e;
   switch (pl.variant) {
-    case 3: e = launch_gemm<8, 2, 3, 3>(pl, hidden, W, part, out_logits, stream); break;
-    case 2: e = launch_gemm<4, 2, 3, 3>(pl, hidden, W, part, out_logits, stream); break;
-    case 1: e = launch_gemm<2, 2, 3, 1>(pl, hidden, W, part, out_logits, stream); break;
-    default: e = launch_gemm<1, 1, 3, 1>(pl, hidden, W, part, out_logits, stream); break;
+    case 3: e = launch_gemm<4, 2, 4, 2, 3>(pl, hidden, W, part, out_logits, stream); break;
+    case 2: e = launch_gemm<4, 2, 4, 1, 3>(pl, hidden, W, part, out_logits, stream); break;
+    case 1: e = launch_gemm<2, 2, 4, 1, 1>(pl, hidden, W, part, out_logits, stream); break;
+    default: e = launch_gemm<1, 1, 4, 1, 1>(pl, hidden, W, part, out_logits, stream); break;
   }
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(lm_head_merge, dim3((pl.M + 3) / 4), dim3(256), 0, stream, pl,
