@@ -205,7 +205,7 @@ def spec_latency(torch, sda, dev, iters=20):
 
 PROFILE_RUNS = {
     "prof": "rocprofv3 --kernel-trace --stats -T -d gpurun_out/prof -o run --output-format csv "
-            "-- python -u bench.py --steps 10 --warmup 2 --no-cpu-baseline",
+            "-- python -u bench.py --steps 50 --warmup 5 --no-cpu-baseline",
     "pmc_fetch": "rocprofv3 --pmc FETCH_SIZE -T -d gpurun_out/pmc_fetch -o run --output-format csv "
                  "-- python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-spec",
     "pmc_write": "rocprofv3 --pmc WRITE_SIZE -T -d gpurun_out/pmc_write -o run --output-format csv "
@@ -235,7 +235,7 @@ def summarize_profiles(root):
     lines = ["# rocprofv3 kernel trace: C5 verification step", "",
              "Command (repository root, one MI355X):", "", "    " + PROFILE_RUNS["prof"], "",
              f"Workload: C5 (B={B}, N={N}, Hq={Hq}, Hkv={Hkv}, D={D}, P={P}, H={H}, V={V}); "
-             "12 steps (2 warmup + 10 timed)",
+             "55 steps (5 warmup + 50 timed, as bench.py times them)",
              "plus the speculative-sampling latency loop at C4 shapes (accept_spec_kernel, "
              "spec_init_kernel).", "",
              "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
