@@ -23,3 +23,4 @@ from .attention import tree_verify_attention, tree_verify_attention_node  # noqa
 from .lm_head import lm_head_logits, lm_head_row_stats, lm_head  # noqa: F401
 from .accept import accept_greedy, accept_spec, sample_inverse_cdf, spec_node_round  # noqa: F401
 from .rerank import eagle2_rerank  # noqa: F401
+from .kv_commit import kv_commit  # noqa: F401
