@@ -203,6 +203,49 @@ def spec_latency(torch, sda, dev, iters=20):
     return e0.elapsed_time(e1) * 1000.0 / iters
 
 
+def kv_commit_latency(torch, sda, dev, parents, iters=50, layers=80):
+    """eagle_kv_commit over the caches of every layer of a Llama-3-70B-shaped model
+    (80 layers x 4 sequences x 8 KV heads x head dim 128) after accepting, in each
+    sequence, the root path of the tree's deepest node.  The commit only touches rows
+    P .. P+N, so the caches hold a short prefix (P = 64) plus the 60 tree rows."""
+    cfg = synth.CONFIGS["C5"]
+    B, N, Hkv, D, P = cfg.B, cfg.N, cfg.Hkv, cfg.D, 64
+    par = parents.cpu().numpy()
+    maxd = cfg.max_depth
+    alen = np.zeros(B, dtype=np.int32)
+    path = np.full((B, maxd + 1), -1, dtype=np.int32)
+    for b in range(B):
+        depth = [0] * N
+        for i in range(1, N):
+            depth[i] = depth[par[b, i]] + 1
+        node = max(range(N), key=lambda i: (min(depth[i], maxd), -i) if depth[i] <= maxd else (-1, 0))
+        chain = [node]
+        while chain[-1] != 0:
+            chain.append(int(par[b, chain[-1]]))
+        chain.reverse()
+        alen[b] = len(chain) - 1
+        path[b, :len(chain)] = chain
+    shape = (layers, B, Hkv, P + N, D)
+    k = torch.empty(shape, dtype=torch.bfloat16, device=dev).normal_()
+    v = torch.empty(shape, dtype=torch.bfloat16, device=dev).normal_()
+    a = torch.from_numpy(alen).to(dev)
+    p = torch.from_numpy(path).to(dev)
+    for _ in range(5):
+        sda.eagle_kv_commit(k, v, a, p, P)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(iters):
+        sda.eagle_kv_commit(k, v, a, p, P)
+    e1.record(s)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / iters
+    moved = 2 * 2 * layers * Hkv * D * 2 * int((alen + 1).sum())   # K and V, read + write
+    return {"us": round(us, 2), "layers": layers, "accepted_rows_per_seq": [int(x) + 1 for x in alen],
+            "bytes": moved, "gbs": round(moved / (us * 1e-6) / 1e9, 1)}
+
+
 PROFILE_RUNS = {
     "prof": "rocprofv3 --kernel-trace --stats -T -d gpurun_out/prof -o run --output-format csv "
             "-- python -u bench.py --steps 50 --warmup 5 --no-cpu-baseline",
@@ -415,6 +458,7 @@ def main(argv=None):
     }
     if not args.no_spec:
         out["accept_spec_us_C4"] = round(spec_latency(torch, sda, dev), 2)
+        out["kv_commit_80_layers"] = kv_commit_latency(torch, sda, dev, tree["parents"])
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg)

@@ -8,6 +8,8 @@
  *   eagle_lm_head_argmax   frozen LM head fused with per-row max/argmax/softmax stats
  *   eagle_accept_greedy    greedy acceptance (longest matching root path)
  *   eagle_accept_spec      multi-round speculative sampling acceptance
+ * and, after acceptance:
+ *   eagle_kv_commit        move the accepted path's K/V rows to the end of the prefix
  *
  * Sources (web pages on the method), cited per call below:
  *   [P1] "大模型推理效率突破：EAGLE推测解码算法在摩尔线程GPU的实践与优化" (adg.csdn.net)
@@ -209,6 +211,28 @@ eagle_status_t eagle2_rerank(const float* draft_logits, const int32_t* root_toke
                              int32_t* tokens, int32_t* parents, int32_t* depths, float* scores,
                              int32_t* draft_row, float* draft_lse, void* workspace,
                              size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * KV-cache commit after acceptance.  [P3] section 4 (limitations: the dynamic
+ * draft tree fragments the KV cache).  The tree's K/V rows follow the prefix in node
+ * order (row P + i holds node i, as eagle_tree_verify_attn reads them).  After a
+ * root path path[0] = 0, path[1], ..., path[alpha] is accepted, its rows become the
+ * next prefix rows in path order, in place, in every layer, sequence and KV head:
+ *     cache[l][b][g][P + i] = old cache[l][b][g][P + path[b][i]],  i = 0 .. alpha;
+ * every other row keeps its contents, so the next step's prefix is P + alpha + 1.
+ *
+ *   k_cache, v_cache bf16 [L][B][Hkv][kv_cap][D] (device, 16-byte aligned), updated
+ *     in place; D in {64, 128}
+ *   accept_len int32 [B] (alpha; sequences with alpha < 0 are left unchanged) and
+ *   accept_path int32 [B][path_len] as written by eagle_accept_greedy /
+ *     eagle_accept_spec (path_len = max_depth + 1 <= 65); alpha is capped at
+ *     path_len - 1, and path entries that name no row of the cache are skipped
+ *   P + path_len <= kv_cap
+ */
+eagle_status_t eagle_kv_commit(void* k_cache, void* v_cache, const int32_t* accept_len,
+                               const int32_t* accept_path, int32_t L, int32_t B, int32_t Hkv,
+                               int32_t D, int32_t P, int32_t kv_cap, int32_t path_len,
+                               hipStream_t stream);
 
 #ifdef __cplusplus
 }

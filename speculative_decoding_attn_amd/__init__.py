@@ -45,6 +45,8 @@ _SIGNATURES = {
     "eagle_lm_head_workspace": ([_i32] * 3, _sz),
     "eagle_lm_head_argmax": ([_vp, _vp, _i32, _i32, _i32] + [_vp] * 6 + [_sz, _vp], ctypes.c_int),
     "eagle_accept_greedy": ([_vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "eagle_kv_commit": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp],
+                        ctypes.c_int),
     "eagle_accept_spec_workspace": ([_i32] * 3, _sz),
     "eagle_accept_spec": ([_vp] * 5 + [_i32, _vp, _vp, _i32, _i32, _i32, _i32] + [_vp] * 4
                           + [_sz, _vp], ctypes.c_int),
@@ -193,6 +195,29 @@ def eagle_accept_greedy(tokens: torch.Tensor, parents: torch.Tensor, target_argm
                                  _stream())
     _check(st, "eagle_accept_greedy")
     return alen, path, out
+
+
+def eagle_kv_commit(k_cache: torch.Tensor, v_cache: torch.Tensor, accept_len: torch.Tensor,
+                    accept_path: torch.Tensor, P: int) -> None:
+    """In place: the accepted path's tree rows P + path[b][i] -> P + i in every layer.
+
+    k_cache, v_cache bf16 [L][B][Hkv][kv_cap][D]; accept_len int32 [B];
+    accept_path int32 [B][path_len]."""
+    lib = load()
+    dev = k_cache.device
+    _need(k_cache, "k_cache", torch.bfloat16, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, dev)
+    _need(accept_len, "accept_len", torch.int32, dev)
+    _need(accept_path, "accept_path", torch.int32, dev)
+    if k_cache.dim() != 5 or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache and v_cache must both be [L][B][Hkv][kv_cap][D]")
+    L, B, Hkv, cap, D = k_cache.shape
+    if tuple(accept_len.shape) != (B,) or accept_path.dim() != 2 or accept_path.shape[0] != B:
+        raise ValueError("accept_len must be [B] and accept_path [B][path_len]")
+    st = lib.eagle_kv_commit(k_cache.data_ptr(), v_cache.data_ptr(), accept_len.data_ptr(),
+                             accept_path.data_ptr(), L, B, Hkv, D, P, cap, accept_path.shape[1],
+                             _stream())
+    _check(st, "eagle_kv_commit")
 
 
 def eagle_accept_spec(tokens: torch.Tensor, parents: torch.Tensor, draft_row: torch.Tensor,

@@ -237,4 +237,29 @@ eagle_status_t eagle2_rerank(const float* draft_logits, const int32_t* root_toke
                     "eagle2_rerank launch");
 }
 
+// ---------------------------------------------------------------- KV commit
+eagle_status_t eagle_kv_commit(void* k_cache, void* v_cache, const int32_t* accept_len,
+                               const int32_t* accept_path, int32_t L, int32_t B, int32_t Hkv,
+                               int32_t D, int32_t P, int32_t kv_cap, int32_t path_len,
+                               hipStream_t stream) {
+  if (!k_cache || !v_cache || !accept_len || !accept_path)
+    return fail(EAGLE_ERR_NULL, "all pointers must be non-NULL");
+  if (L < 1 || B < 1 || Hkv < 1 || P < 0 || path_len < 1)
+    return fail(EAGLE_ERR_INVALID_ARG, "need L,B,Hkv,path_len >= 1 and P >= 0 (L=%d B=%d Hkv=%d P=%d path_len=%d)",
+                L, B, Hkv, P, path_len);
+  if (D != 64 && D != 128) return fail(EAGLE_ERR_UNSUPPORTED, "D=%d (supported: 64, 128)", D);
+  if (path_len > eagle::kMaxCommitRows)
+    return fail(EAGLE_ERR_UNSUPPORTED, "path_len=%d > %d", path_len, eagle::kMaxCommitRows);
+  if ((long long)P + path_len > kv_cap)
+    return fail(EAGLE_ERR_INVALID_ARG, "P + path_len = %lld exceeds kv_cap=%d", (long long)P + path_len, kv_cap);
+  if ((long long)L * B * Hkv > 0x7fffffffLL ||
+      (double)L * B * Hkv * (double)kv_cap * D > 9.0e18)
+    return fail(EAGLE_ERR_INVALID_ARG, "cache too large");
+  if (!aligned16(k_cache) || !aligned16(v_cache))
+    return fail(EAGLE_ERR_INVALID_ARG, "caches must be 16-byte aligned");
+  return hip_status(eagle::launch_kv_commit(k_cache, v_cache, accept_len, accept_path, L, B, Hkv,
+                                            D, P, kv_cap, path_len, stream),
+                    "eagle_kv_commit launch");
+}
+
 }  // extern "C"

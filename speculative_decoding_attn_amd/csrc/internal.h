@@ -78,9 +78,16 @@ hipError_t launch_rerank(const RerankPlan& pl, const float* draft_logits, const 
                          int32_t* tokens, int32_t* parents, int32_t* depths, float* scores,
                          int32_t* draft_row, float* draft_lse, void* workspace, hipStream_t stream);
 
+// KV commit: at most max_depth + 1 <= 65 accepted rows per (layer, sequence, head)
+constexpr int kMaxCommitRows = 65;
+hipError_t launch_kv_commit(void* k_cache, void* v_cache, const int32_t* accept_len,
+                            const int32_t* accept_path, int L, int B, int Hkv, int D, int P,
+                            int kv_cap, int path_len, hipStream_t stream);
+
 }  // namespace eagle
 
 namespace eagle {
 int rerank_max_candidates();
 int rerank_max_row_list();   // R * top_k limit (also caps R at 512 and chunks * top_k at 1024)
+
 }  // namespace eagle

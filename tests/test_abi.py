@@ -142,3 +142,19 @@ def test_accept_and_rerank_argument_errors(lib):
     assert rr(k=2, depth=2, n=8) == 2          # only 2 + 4 = 6 candidates
     assert rr(k=64, depth=3, V=1000, n=10) == 3  # too many candidates
     assert rr(ws=None) == 4
+
+
+def test_kv_commit_argument_errors(lib):
+    c = lib.eagle_kv_commit
+
+    def kc(k=FAKE, L=2, B=1, H=2, D=128, P=10, cap=80, path_len=7):
+        return c(k, FAKE, FAKE, FAKE, L, B, H, D, P, cap, path_len, None)
+
+    assert kc(k=None) == 1
+    assert kc(L=0) == 2
+    assert kc(P=-1) == 2
+    assert kc(D=96) == 3
+    assert kc(path_len=66, cap=200) == 3
+    assert kc(P=75, cap=80, path_len=7) == 2   # rows P .. P+6 do not fit
+    assert kc(k=FAKE + 8) == 2                 # misaligned cache
+    assert b"aligned" in lib.eagle_last_error()
