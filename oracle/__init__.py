@@ -24,3 +24,4 @@ from .lm_head import lm_head_logits, lm_head_row_stats, lm_head  # noqa: F401
 from .accept import accept_greedy, accept_spec, sample_inverse_cdf, spec_node_round  # noqa: F401
 from .rerank import eagle2_rerank  # noqa: F401
 from .kv_commit import kv_commit  # noqa: F401
+from .ragged import accept_greedy_ragged, accept_spec_ragged, tree_verify_attention_ragged  # noqa: F401
