@@ -246,6 +246,66 @@ def kv_commit_latency(torch, sda, dev, parents, iters=50, layers=80):
             "bytes": moved, "gbs": round(moved / (us * 1e-6) / 1e9, 1)}
 
 
+RAGGED_PREFIX = [32768, 8192, 24576, 2048]
+RAGGED_TREE = [60, 40, 60, 25]
+
+
+def ragged_step(torch, sda, dev, x, steps=20):
+    """The verification step (attention, LM head, greedy acceptance) on a ragged C5
+    batch: the four sequences keep C5's shapes but have prefixes of RAGGED_PREFIX
+    tokens and trees of RAGGED_TREE nodes (rows of the C5 tensors past them are
+    padding).  The LM head takes only the real rows, packed."""
+    cfg = synth.CONFIGS["C5"]
+    B, N, P, D, H, V = cfg.B, cfg.N, cfg.P, cfg.D, cfg.H, cfg.V
+    plen = torch.tensor(RAGGED_PREFIX, dtype=torch.int32, device=dev)
+    tlen = torch.tensor(RAGGED_TREE, dtype=torch.int32, device=dev)
+    M = sum(RAGGED_TREE)
+    lib = sda.load()
+    ws_attn = torch.empty(max(1, lib.eagle_tree_verify_attn_workspace(B, N, cfg.Hq, cfg.Hkv, D, P)),
+                          dtype=torch.uint8, device=dev)
+    ws_lm = torch.empty(lib.eagle_lm_head_workspace(M, H, V), dtype=torch.uint8, device=dev)
+    attn_out = torch.empty((B, N, cfg.Hq, D), dtype=torch.bfloat16, device=dev)
+    attn_lse = torch.empty((B, N, cfg.Hq), dtype=torch.float32, device=dev)
+    hidden = x["hidden"][:M]
+    amax = torch.zeros((B, N), dtype=torch.int32, device=dev)
+    rows = []
+    for b, n in enumerate(RAGGED_TREE):
+        rows += [b * N + i for i in range(n)]
+    idx = torch.tensor(rows, dtype=torch.long, device=dev)
+    parents = torch.from_numpy(synth.random_parents(B, N, 0, cfg.index, 20)).to(dev)
+    tokens = torch.from_numpy(synth.integers((B, N), 0, V, 0, cfg.index, 21)).to(dev)
+    stream = torch.cuda.current_stream()
+
+    def one(ev=None):
+        if ev:
+            ev[0].record(stream)
+        sda.eagle_tree_verify_attn(x["q"], x["k"], x["v"], parents, P, D ** -0.5, out=attn_out,
+                                   lse=attn_lse, workspace=ws_attn, prefix_len=plen, tree_len=tlen)
+        if ev:
+            ev[1].record(stream)
+        res = sda.eagle_lm_head_argmax(hidden, x["W"], want_logits=False, workspace=ws_lm)
+        if ev:
+            ev[2].record(stream)
+        amax.view(-1).index_copy_(0, idx, res["argmax"])
+        sda.eagle_accept_greedy(tokens, parents, amax, cfg.max_depth, tree_len=tlen)
+        if ev:
+            ev[3].record(stream)
+
+    for _ in range(3):
+        one()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for i in range(steps):
+        one(evs[i])
+    torch.cuda.synchronize()
+    ms = evs[0][0].elapsed_time(evs[-1][3]) / steps
+    per = {n: 1000.0 * sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps
+           for j, n in enumerate(["tree_attn", "lm_head", "accept_greedy"])}
+    return {"prefix_len": RAGGED_PREFIX, "tree_len": RAGGED_TREE,
+            "tokens_per_s": round(M / (ms / 1000.0), 1), "ms_per_step": round(ms, 4),
+            "breakdown_us": {k: round(v, 2) for k, v in per.items()}}
+
+
 PROFILE_RUNS = {
     "prof": "rocprofv3 --kernel-trace --stats -T -d gpurun_out/prof -o run --output-format csv "
             "-- python -u bench.py --steps 50 --warmup 5 --no-cpu-baseline",
@@ -459,6 +519,7 @@ def main(argv=None):
     if not args.no_spec:
         out["accept_spec_us_C4"] = round(spec_latency(torch, sda, dev), 2)
         out["kv_commit_80_layers"] = kv_commit_latency(torch, sda, dev, tree["parents"])
+        out["ragged_C5"] = ragged_step(torch, sda, dev, x)
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg)

@@ -8,7 +8,8 @@
  *   eagle_lm_head_argmax   frozen LM head fused with per-row max/argmax/softmax stats
  *   eagle_accept_greedy    greedy acceptance (longest matching root path)
  *   eagle_accept_spec      multi-round speculative sampling acceptance
- * and, after acceptance:
+ * with _ragged forms of the attention and the acceptances for batches whose
+ * sequences have different prefix and tree sizes, and, after acceptance:
  *   eagle_kv_commit        move the accepted path's K/V rows to the end of the prefix
  *
  * Sources (web pages on the method), cited per call below:
@@ -181,6 +182,44 @@ eagle_status_t eagle_accept_spec(const int32_t* tokens, const int32_t* parents,
                                  int32_t N, int32_t V, int32_t max_depth, int32_t* accept_len,
                                  int32_t* accept_path, int32_t* out_tokens, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Ragged batches.  [P3] section 4 (batch sizes above one are the method's weak spot)
+ * and its closing remarks (continuous batching): the sequences of one batch carry
+ * prefixes and trees of different sizes.  These calls take the same arguments as
+ * the uniform ones, where N and P are now the largest tree and prefix the layouts
+ * are sized for, plus device arrays
+ *   prefix_len int32 [B]  this sequence's prefix length (clamped to [0, P])
+ *   tree_len   int32 [B]  this sequence's tree size     (clamped to [1, N])
+ * (for attention either may be NULL, meaning "all equal to the maximum").  Sequence
+ * b's tree rows follow its own prefix: k, v row prefix_len[b] + i holds node i.  Only
+ * nodes i < tree_len[b] exist: rows of q, parents, tokens, target_argmax, draft_row,
+ * u_accept, u_sample and target_logits past them are padding (never read as nodes),
+ * and the attention writes no output or lse for them.  The LM head needs no ragged
+ * form: its rows are independent, so the trees' rows are passed as one [M][H] block.
+ * Workspace sizes: those of the uniform calls at the maxima.
+ */
+eagle_status_t eagle_tree_verify_attn_ragged(const void* q, const void* k, const void* v,
+                                             const int32_t* parents, const int32_t* prefix_len,
+                                             const int32_t* tree_len, int32_t B, int32_t N,
+                                             int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
+                                             int32_t kv_cap, float scale, void* out, float* lse,
+                                             void* workspace, size_t workspace_bytes,
+                                             hipStream_t stream);
+eagle_status_t eagle_accept_greedy_ragged(const int32_t* tokens, const int32_t* parents,
+                                          const int32_t* target_argmax, const int32_t* tree_len,
+                                          int32_t B, int32_t N, int32_t max_depth,
+                                          int32_t* accept_len, int32_t* accept_path,
+                                          int32_t* out_tokens, hipStream_t stream);
+eagle_status_t eagle_accept_spec_ragged(const int32_t* tokens, const int32_t* parents,
+                                        const int32_t* draft_row, const float* target_logits,
+                                        const float* draft_logits, int32_t draft_rows,
+                                        const float* u_accept, const float* u_sample,
+                                        const int32_t* tree_len, int32_t B, int32_t N, int32_t V,
+                                        int32_t max_depth, int32_t* accept_len,
+                                        int32_t* accept_path, int32_t* out_tokens,
+                                        void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream);
 
 /*
  * EAGLE-2 dynamic draft tree.  [P3] section 2 (dynamic draft tree: confidence

@@ -50,6 +50,11 @@ _SIGNATURES = {
     "eagle_accept_spec_workspace": ([_i32] * 3, _sz),
     "eagle_accept_spec": ([_vp] * 5 + [_i32, _vp, _vp, _i32, _i32, _i32, _i32] + [_vp] * 4
                           + [_sz, _vp], ctypes.c_int),
+    "eagle_tree_verify_attn_ragged": ([_vp] * 6 + [_i32] * 7 + [_f32, _vp, _vp, _vp, _sz, _vp],
+                                      ctypes.c_int),
+    "eagle_accept_greedy_ragged": ([_vp] * 4 + [_i32, _i32, _i32] + [_vp] * 4, ctypes.c_int),
+    "eagle_accept_spec_ragged": ([_vp] * 5 + [_i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32]
+                                 + [_vp] * 4 + [_sz, _vp], ctypes.c_int),
     "eagle2_rerank_workspace": ([_i32] * 4, _sz),
     "eagle2_rerank": ([_vp, _vp] + [_i32] * 5 + [_vp] * 7 + [_sz, _vp], ctypes.c_int),
 }
@@ -115,9 +120,13 @@ def eagle_check_tree(parents) -> bool:
 def eagle_tree_verify_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, parents: torch.Tensor,
                            P: int, scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
                            lse: Optional[torch.Tensor] = None, want_lse: bool = True,
-                           workspace: Optional[torch.Tensor] = None):
+                           workspace: Optional[torch.Tensor] = None,
+                           prefix_len: Optional[torch.Tensor] = None,
+                           tree_len: Optional[torch.Tensor] = None):
     """q [B][N][Hq][D] bf16; k, v [B][Hkv][kv_cap][D] bf16; parents [B][N] int32.
 
+    With prefix_len / tree_len (int32 [B]) the batch is ragged (P and N are then the
+    maxima) and eagle_tree_verify_attn_ragged is called.
     Returns (out [B][N][Hq][D] bf16, lse [B][N][Hq] fp32 or None)."""
     lib = load()
     dev = q.device
@@ -139,12 +148,30 @@ def eagle_tree_verify_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pa
     ws_bytes = lib.eagle_tree_verify_attn_workspace(B, N, Hq, Hkv, D, P)
     if workspace is None and ws_bytes:
         workspace = _workspace(ws_bytes, dev)
-    st = lib.eagle_tree_verify_attn(q.data_ptr(), k.data_ptr(), v.data_ptr(), parents.data_ptr(),
-                                    B, N, Hq, Hkv, D, P, kv_cap, float(scale), out.data_ptr(),
-                                    _ptr(lse), _ptr(workspace),
-                                    0 if workspace is None else workspace.numel(), _stream())
-    _check(st, "eagle_tree_verify_attn")
+    wsb = 0 if workspace is None else workspace.numel()
+    if prefix_len is None and tree_len is None:
+        st = lib.eagle_tree_verify_attn(q.data_ptr(), k.data_ptr(), v.data_ptr(), parents.data_ptr(),
+                                        B, N, Hq, Hkv, D, P, kv_cap, float(scale), out.data_ptr(),
+                                        _ptr(lse), _ptr(workspace), wsb, _stream())
+        _check(st, "eagle_tree_verify_attn")
+        return out, lse
+    for t, n in ((prefix_len, "prefix_len"), (tree_len, "tree_len")):
+        if t is not None:
+            _need(t, n, torch.int32, dev)
+            if tuple(t.shape) != (B,):
+                raise ValueError(f"{n} must be [B]")
+    st = lib.eagle_tree_verify_attn_ragged(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                           parents.data_ptr(), _ptr(prefix_len), _ptr(tree_len),
+                                           B, N, Hq, Hkv, D, P, kv_cap, float(scale),
+                                           out.data_ptr(), _ptr(lse), _ptr(workspace), wsb,
+                                           _stream())
+    _check(st, "eagle_tree_verify_attn_ragged")
     return out, lse
+
+
+def eagle_tree_verify_attn_ragged(q, k, v, parents, prefix_len, tree_len, P: int, **kw):
+    """eagle_tree_verify_attn with per-sequence prefix_len / tree_len (int32 [B])."""
+    return eagle_tree_verify_attn(q, k, v, parents, P, prefix_len=prefix_len, tree_len=tree_len, **kw)
 
 
 def eagle_lm_head_argmax(hidden: torch.Tensor, weight: torch.Tensor, want_logits: bool = False,
@@ -177,9 +204,9 @@ def eagle_lm_head_argmax(hidden: torch.Tensor, weight: torch.Tensor, want_logits
 
 
 def eagle_accept_greedy(tokens: torch.Tensor, parents: torch.Tensor, target_argmax: torch.Tensor,
-                        max_depth: int):
+                        max_depth: int, tree_len: Optional[torch.Tensor] = None):
     """tokens, parents, target_argmax [B][N] int32 -> (accept_len [B], accept_path, out_tokens
-    [B][max_depth+1])."""
+    [B][max_depth+1]).  With tree_len (int32 [B]) eagle_accept_greedy_ragged is called."""
     lib = load()
     dev = tokens.device
     for t, n in ((tokens, "tokens"), (parents, "parents"), (target_argmax, "target_argmax")):
@@ -190,11 +217,26 @@ def eagle_accept_greedy(tokens: torch.Tensor, parents: torch.Tensor, target_argm
     alen = torch.empty(B, dtype=torch.int32, device=dev)
     path = torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev)
     out = torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev)
-    st = lib.eagle_accept_greedy(tokens.data_ptr(), parents.data_ptr(), target_argmax.data_ptr(),
-                                 B, N, max_depth, alen.data_ptr(), path.data_ptr(), out.data_ptr(),
-                                 _stream())
-    _check(st, "eagle_accept_greedy")
+    if tree_len is None:
+        st = lib.eagle_accept_greedy(tokens.data_ptr(), parents.data_ptr(), target_argmax.data_ptr(),
+                                     B, N, max_depth, alen.data_ptr(), path.data_ptr(),
+                                     out.data_ptr(), _stream())
+        _check(st, "eagle_accept_greedy")
+        return alen, path, out
+    _need(tree_len, "tree_len", torch.int32, dev)
+    if tuple(tree_len.shape) != (B,):
+        raise ValueError("tree_len must be [B]")
+    st = lib.eagle_accept_greedy_ragged(tokens.data_ptr(), parents.data_ptr(),
+                                        target_argmax.data_ptr(), tree_len.data_ptr(), B, N,
+                                        max_depth, alen.data_ptr(), path.data_ptr(), out.data_ptr(),
+                                        _stream())
+    _check(st, "eagle_accept_greedy_ragged")
     return alen, path, out
+
+
+def eagle_accept_greedy_ragged(tokens, parents, target_argmax, tree_len, max_depth: int):
+    """eagle_accept_greedy with per-sequence tree sizes tree_len (int32 [B])."""
+    return eagle_accept_greedy(tokens, parents, target_argmax, max_depth, tree_len=tree_len)
 
 
 def eagle_kv_commit(k_cache: torch.Tensor, v_cache: torch.Tensor, accept_len: torch.Tensor,
@@ -223,9 +265,11 @@ def eagle_kv_commit(k_cache: torch.Tensor, v_cache: torch.Tensor, accept_len: to
 def eagle_accept_spec(tokens: torch.Tensor, parents: torch.Tensor, draft_row: torch.Tensor,
                       target_logits: torch.Tensor, draft_logits: torch.Tensor,
                       u_accept: torch.Tensor, u_sample: torch.Tensor, max_depth: int,
-                      workspace: Optional[torch.Tensor] = None):
+                      workspace: Optional[torch.Tensor] = None,
+                      tree_len: Optional[torch.Tensor] = None):
     """tokens, parents, draft_row [B][N] int32; target_logits [B][N][V] fp32;
-    draft_logits [B][R][V] fp32; u_accept, u_sample [B][N] fp32."""
+    draft_logits [B][R][V] fp32; u_accept, u_sample [B][N] fp32.  With tree_len
+    (int32 [B]) eagle_accept_spec_ragged is called."""
     lib = load()
     dev = tokens.device
     for t, n in ((tokens, "tokens"), (parents, "parents"), (draft_row, "draft_row")):
@@ -243,13 +287,32 @@ def eagle_accept_spec(tokens: torch.Tensor, parents: torch.Tensor, draft_row: to
     out = torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev)
     if workspace is None:
         workspace = _workspace(lib.eagle_accept_spec_workspace(B, N, V), dev)
-    st = lib.eagle_accept_spec(tokens.data_ptr(), parents.data_ptr(), draft_row.data_ptr(),
-                               target_logits.data_ptr(), draft_logits.data_ptr(), R,
-                               u_accept.data_ptr(), u_sample.data_ptr(), B, N, V, max_depth,
-                               alen.data_ptr(), path.data_ptr(), out.data_ptr(),
-                               workspace.data_ptr(), workspace.numel(), _stream())
-    _check(st, "eagle_accept_spec")
+    if tree_len is None:
+        st = lib.eagle_accept_spec(tokens.data_ptr(), parents.data_ptr(), draft_row.data_ptr(),
+                                   target_logits.data_ptr(), draft_logits.data_ptr(), R,
+                                   u_accept.data_ptr(), u_sample.data_ptr(), B, N, V, max_depth,
+                                   alen.data_ptr(), path.data_ptr(), out.data_ptr(),
+                                   workspace.data_ptr(), workspace.numel(), _stream())
+        _check(st, "eagle_accept_spec")
+        return alen, path, out
+    _need(tree_len, "tree_len", torch.int32, dev)
+    if tuple(tree_len.shape) != (B,):
+        raise ValueError("tree_len must be [B]")
+    st = lib.eagle_accept_spec_ragged(tokens.data_ptr(), parents.data_ptr(), draft_row.data_ptr(),
+                                      target_logits.data_ptr(), draft_logits.data_ptr(), R,
+                                      u_accept.data_ptr(), u_sample.data_ptr(), tree_len.data_ptr(),
+                                      B, N, V, max_depth, alen.data_ptr(), path.data_ptr(),
+                                      out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                      _stream())
+    _check(st, "eagle_accept_spec_ragged")
     return alen, path, out
+
+
+def eagle_accept_spec_ragged(tokens, parents, draft_row, target_logits, draft_logits, u_accept,
+                             u_sample, tree_len, max_depth: int, workspace=None):
+    """eagle_accept_spec with per-sequence tree sizes tree_len (int32 [B])."""
+    return eagle_accept_spec(tokens, parents, draft_row, target_logits, draft_logits, u_accept,
+                             u_sample, max_depth, workspace=workspace, tree_len=tree_len)
 
 
 def eagle2_rerank(draft_logits: torch.Tensor, root_token: torch.Tensor, top_k: int, depth: int,

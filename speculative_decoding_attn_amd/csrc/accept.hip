@@ -15,18 +15,20 @@ namespace {
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256)
 accept_greedy_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict__ parents,
-                     const int32_t* __restrict__ top1, int B, int N, int max_depth,
-                     int32_t* __restrict__ accept_len, int32_t* __restrict__ accept_path,
-                     int32_t* __restrict__ out_tokens) {
+                     const int32_t* __restrict__ top1, const int32_t* __restrict__ tree_len, int B,
+                     int N, int max_depth, int32_t* __restrict__ accept_len,
+                     int32_t* __restrict__ accept_path, int32_t* __restrict__ out_tokens) {
   const int lane = threadIdx.x & 63;
   const int b = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
   if (b >= B) return;
   const int32_t* tok = tokens + (size_t)b * N;
   const int32_t* par = parents + (size_t)b * N;
   const int32_t* am = top1 + (size_t)b * N;
+  // ragged batches: nodes past this sequence's tree do not exist
+  const int Nb = tree_len ? min(max(tree_len[b], 1), N) : N;
 
   int key = -1;
-  if (lane < N) {
+  if (lane < Nb) {
     bool ok = true;
     bool reached = (lane == 0);
     int depth = 0;
@@ -226,6 +228,8 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
   const int32_t* tok = tokens + (size_t)b * N;
   const int32_t* par = parents + (size_t)b * N;
   const int tid = threadIdx.x;
+  // ragged batches: nodes past this sequence's tree do not exist
+  const int Nb = pl.tree_len ? min(max(pl.tree_len[b], 1), N) : N;
 
   unsigned gen = 0;
   int v = 0;
@@ -239,7 +243,7 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
   for (;;) {
     // children of v in ascending index (none at max_depth)
     if (tid < 64) {
-      const bool is_kid = tid < N && tid > 0 && par[tid] == v && alpha < pl.max_depth;
+      const bool is_kid = tid < Nb && tid > 0 && par[tid] == v && alpha < pl.max_depth;
       const unsigned long long mask = __ballot(is_kid);
       if (is_kid) kids[__popcll(mask & ((1ull << tid) - 1ull))] = tid;
       if (tid == 0) nkids_s = __popcll(mask);
@@ -428,11 +432,11 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
 }  // namespace
 
 hipError_t launch_accept_greedy(const int32_t* tokens, const int32_t* parents,
-                                const int32_t* target_argmax, int B, int N, int max_depth,
-                                int32_t* accept_len, int32_t* accept_path, int32_t* out_tokens,
-                                hipStream_t stream) {
+                                const int32_t* target_argmax, const int32_t* tree_len, int B,
+                                int N, int max_depth, int32_t* accept_len, int32_t* accept_path,
+                                int32_t* out_tokens, hipStream_t stream) {
   hipLaunchKernelGGL(accept_greedy_kernel, dim3((B + 3) / 4), dim3(256), 0, stream, tokens, parents,
-                     target_argmax, B, N, max_depth, accept_len, accept_path, out_tokens);
+                     target_argmax, tree_len, B, N, max_depth, accept_len, accept_path, out_tokens);
   return hipGetLastError();
 }
 

@@ -86,11 +86,12 @@ size_t eagle_tree_verify_attn_workspace(int32_t B, int32_t N, int32_t Hq, int32_
   return eagle::tree_attn_workspace_bytes(eagle::plan_tree_attn(B, N, Hq, Hkv, D, P, P + N));
 }
 
-eagle_status_t eagle_tree_verify_attn(const void* q, const void* k, const void* v,
-                                      const int32_t* parents, int32_t B, int32_t N, int32_t Hq,
-                                      int32_t Hkv, int32_t D, int32_t P, int32_t kv_cap,
-                                      float scale, void* out, float* lse, void* workspace,
-                                      size_t workspace_bytes, hipStream_t stream) {
+static eagle_status_t attn_impl(const void* q, const void* k, const void* v,
+                                const int32_t* parents, const int32_t* prefix_len,
+                                const int32_t* tree_len, int32_t B, int32_t N, int32_t Hq,
+                                int32_t Hkv, int32_t D, int32_t P, int32_t kv_cap, float scale,
+                                void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream, const char* name) {
   if (!q || !k || !v || !parents || !out)
     return fail(EAGLE_ERR_NULL, "q, k, v, parents and out must be non-NULL");
   eagle_status_t st = check_attn_dims(B, N, Hq, Hkv, D, P);
@@ -100,13 +101,39 @@ eagle_status_t eagle_tree_verify_attn(const void* q, const void* k, const void* 
     return fail(EAGLE_ERR_INVALID_ARG, "scale must be a positive finite number");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return fail(EAGLE_ERR_INVALID_ARG, "q, k, v, out must be 16-byte aligned");
-  const eagle::AttnPlan pl = eagle::plan_tree_attn(B, N, Hq, Hkv, D, P, kv_cap);
+  eagle::AttnPlan pl = eagle::plan_tree_attn(B, N, Hq, Hkv, D, P, kv_cap);
+  pl.prefix_len = prefix_len;
+  pl.tree_len = tree_len;
   const size_t need = eagle::tree_attn_workspace_bytes(pl);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(EAGLE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
   if (need > 0 && !aligned16(workspace)) return fail(EAGLE_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  char what[96];
+  snprintf(what, sizeof(what), "%s launch", name);
   return hip_status(eagle::launch_tree_attn(pl, scale, q, k, v, parents, out, lse, workspace, stream),
-                    "eagle_tree_verify_attn launch");
+                    what);
+}
+
+eagle_status_t eagle_tree_verify_attn(const void* q, const void* k, const void* v,
+                                      const int32_t* parents, int32_t B, int32_t N, int32_t Hq,
+                                      int32_t Hkv, int32_t D, int32_t P, int32_t kv_cap,
+                                      float scale, void* out, float* lse, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+  return attn_impl(q, k, v, parents, nullptr, nullptr, B, N, Hq, Hkv, D, P, kv_cap, scale, out, lse,
+                   workspace, workspace_bytes, stream, "eagle_tree_verify_attn");
+}
+
+eagle_status_t eagle_tree_verify_attn_ragged(const void* q, const void* k, const void* v,
+                                             const int32_t* parents, const int32_t* prefix_len,
+                                             const int32_t* tree_len, int32_t B, int32_t N,
+                                             int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
+                                             int32_t kv_cap, float scale, void* out, float* lse,
+                                             void* workspace, size_t workspace_bytes,
+                                             hipStream_t stream) {
+  if (!prefix_len && !tree_len)
+    return fail(EAGLE_ERR_NULL, "prefix_len and tree_len are both NULL (use eagle_tree_verify_attn)");
+  return attn_impl(q, k, v, parents, prefix_len, tree_len, B, N, Hq, Hkv, D, P, kv_cap, scale, out,
+                   lse, workspace, workspace_bytes, stream, "eagle_tree_verify_attn_ragged");
 }
 
 // ---------------------------------------------------------------- LM head
@@ -143,19 +170,38 @@ eagle_status_t eagle_lm_head_argmax(const void* hidden, const void* weight, int3
 }
 
 // ---------------------------------------------------------------- acceptance
-eagle_status_t eagle_accept_greedy(const int32_t* tokens, const int32_t* parents,
-                                   const int32_t* target_argmax, int32_t B, int32_t N,
-                                   int32_t max_depth, int32_t* accept_len, int32_t* accept_path,
-                                   int32_t* out_tokens, hipStream_t stream) {
+static eagle_status_t greedy_impl(const int32_t* tokens, const int32_t* parents,
+                                  const int32_t* target_argmax, const int32_t* tree_len, int32_t B,
+                                  int32_t N, int32_t max_depth, int32_t* accept_len,
+                                  int32_t* accept_path, int32_t* out_tokens, hipStream_t stream) {
   if (!tokens || !parents || !target_argmax || !accept_len || !accept_path || !out_tokens)
     return fail(EAGLE_ERR_NULL, "all pointers must be non-NULL");
   if (B < 1 || N < 1 || max_depth < 0)
     return fail(EAGLE_ERR_INVALID_ARG, "need B,N >= 1 and max_depth >= 0");
   if (N > EAGLE_MAX_TREE) return fail(EAGLE_ERR_UNSUPPORTED, "N=%d > %d", N, EAGLE_MAX_TREE);
   if (max_depth > EAGLE_MAX_TREE) return fail(EAGLE_ERR_INVALID_ARG, "max_depth=%d > %d", max_depth, EAGLE_MAX_TREE);
-  return hip_status(eagle::launch_accept_greedy(tokens, parents, target_argmax, B, N, max_depth,
-                                                accept_len, accept_path, out_tokens, stream),
+  return hip_status(eagle::launch_accept_greedy(tokens, parents, target_argmax, tree_len, B, N,
+                                                max_depth, accept_len, accept_path, out_tokens,
+                                                stream),
                     "eagle_accept_greedy launch");
+}
+
+eagle_status_t eagle_accept_greedy(const int32_t* tokens, const int32_t* parents,
+                                   const int32_t* target_argmax, int32_t B, int32_t N,
+                                   int32_t max_depth, int32_t* accept_len, int32_t* accept_path,
+                                   int32_t* out_tokens, hipStream_t stream) {
+  return greedy_impl(tokens, parents, target_argmax, nullptr, B, N, max_depth, accept_len,
+                     accept_path, out_tokens, stream);
+}
+
+eagle_status_t eagle_accept_greedy_ragged(const int32_t* tokens, const int32_t* parents,
+                                          const int32_t* target_argmax, const int32_t* tree_len,
+                                          int32_t B, int32_t N, int32_t max_depth,
+                                          int32_t* accept_len, int32_t* accept_path,
+                                          int32_t* out_tokens, hipStream_t stream) {
+  if (!tree_len) return fail(EAGLE_ERR_NULL, "tree_len is NULL (use eagle_accept_greedy)");
+  return greedy_impl(tokens, parents, target_argmax, tree_len, B, N, max_depth, accept_len,
+                     accept_path, out_tokens, stream);
 }
 
 size_t eagle_accept_spec_workspace(int32_t B, int32_t N, int32_t V) {
@@ -163,13 +209,14 @@ size_t eagle_accept_spec_workspace(int32_t B, int32_t N, int32_t V) {
   return eagle::accept_spec_workspace_bytes(eagle::plan_accept_spec(B, N, V));
 }
 
-eagle_status_t eagle_accept_spec(const int32_t* tokens, const int32_t* parents,
-                                 const int32_t* draft_row, const float* target_logits,
-                                 const float* draft_logits, int32_t draft_rows,
-                                 const float* u_accept, const float* u_sample, int32_t B,
-                                 int32_t N, int32_t V, int32_t max_depth, int32_t* accept_len,
-                                 int32_t* accept_path, int32_t* out_tokens, void* workspace,
-                                 size_t workspace_bytes, hipStream_t stream) {
+static eagle_status_t spec_impl(const int32_t* tokens, const int32_t* parents,
+                                const int32_t* draft_row, const float* target_logits,
+                                const float* draft_logits, int32_t draft_rows,
+                                const float* u_accept, const float* u_sample,
+                                const int32_t* tree_len, int32_t B, int32_t N, int32_t V,
+                                int32_t max_depth, int32_t* accept_len, int32_t* accept_path,
+                                int32_t* out_tokens, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
   if (!tokens || !parents || !draft_row || !target_logits || !draft_logits || !u_accept ||
       !u_sample || !accept_len || !accept_path || !out_tokens)
     return fail(EAGLE_ERR_NULL, "all pointers must be non-NULL");
@@ -180,6 +227,7 @@ eagle_status_t eagle_accept_spec(const int32_t* tokens, const int32_t* parents,
   eagle::SpecPlan pl = eagle::plan_accept_spec(B, N, V);
   pl.R = draft_rows;
   pl.max_depth = max_depth;
+  pl.tree_len = tree_len;
   const size_t need = eagle::accept_spec_workspace_bytes(pl);
   if (!workspace || workspace_bytes < need)
     return fail(EAGLE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
@@ -188,6 +236,33 @@ eagle_status_t eagle_accept_spec(const int32_t* tokens, const int32_t* parents,
                                               draft_logits, u_accept, u_sample, accept_len,
                                               accept_path, out_tokens, workspace, stream),
                     "eagle_accept_spec launch");
+}
+
+eagle_status_t eagle_accept_spec(const int32_t* tokens, const int32_t* parents,
+                                 const int32_t* draft_row, const float* target_logits,
+                                 const float* draft_logits, int32_t draft_rows,
+                                 const float* u_accept, const float* u_sample, int32_t B,
+                                 int32_t N, int32_t V, int32_t max_depth, int32_t* accept_len,
+                                 int32_t* accept_path, int32_t* out_tokens, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  return spec_impl(tokens, parents, draft_row, target_logits, draft_logits, draft_rows, u_accept,
+                   u_sample, nullptr, B, N, V, max_depth, accept_len, accept_path, out_tokens,
+                   workspace, workspace_bytes, stream);
+}
+
+eagle_status_t eagle_accept_spec_ragged(const int32_t* tokens, const int32_t* parents,
+                                        const int32_t* draft_row, const float* target_logits,
+                                        const float* draft_logits, int32_t draft_rows,
+                                        const float* u_accept, const float* u_sample,
+                                        const int32_t* tree_len, int32_t B, int32_t N, int32_t V,
+                                        int32_t max_depth, int32_t* accept_len,
+                                        int32_t* accept_path, int32_t* out_tokens,
+                                        void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream) {
+  if (!tree_len) return fail(EAGLE_ERR_NULL, "tree_len is NULL (use eagle_accept_spec)");
+  return spec_impl(tokens, parents, draft_row, target_logits, draft_logits, draft_rows, u_accept,
+                   u_sample, tree_len, B, N, V, max_depth, accept_len, accept_path, out_tokens,
+                   workspace, workspace_bytes, stream);
 }
 
 // ---------------------------------------------------------------- rerank

@@ -27,6 +27,10 @@ struct AttnPlan {
   int S;          // key splits
   int split_len;  // keys per split (multiple of 32); the last split also takes the tree
   float c;        // scale * log2(e)
+  // ragged batches (may be null): per-sequence prefix length (<= P) and tree size
+  // (<= N); P and N above are then the maxima the plan and the layouts are sized for
+  const int32_t* prefix_len;
+  const int32_t* tree_len;
 };
 
 AttnPlan plan_tree_attn(int B, int N, int Hq, int Hkv, int D, int P, int kv_cap);
@@ -51,13 +55,14 @@ hipError_t launch_lm_head(const LmPlan& pl, const void* hidden, const void* W, f
                           void* workspace, hipStream_t stream);
 
 hipError_t launch_accept_greedy(const int32_t* tokens, const int32_t* parents,
-                                const int32_t* target_argmax, int B, int N, int max_depth,
-                                int32_t* accept_len, int32_t* accept_path, int32_t* out_tokens,
-                                hipStream_t stream);
+                                const int32_t* target_argmax, const int32_t* tree_len, int B,
+                                int N, int max_depth, int32_t* accept_len, int32_t* accept_path,
+                                int32_t* out_tokens, hipStream_t stream);
 
 struct SpecPlan {
   int B, N, V, R, max_depth;
   int chunks;     // vocabulary chunks (one workgroup each) per sequence
+  const int32_t* tree_len;   // ragged batches: per-sequence tree size (<= N), may be null
 };
 SpecPlan plan_accept_spec(int B, int N, int V);
 size_t accept_spec_workspace_bytes(const SpecPlan& pl);

@@ -92,15 +92,20 @@ tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int b = pair / pl.Hkv;
   const int g = pair % pl.Hkv;
   const int G = pl.G;
-  const int N = pl.N;
-  const int P = pl.P;
-  const int key_begin = split * pl.split_len;
+  // this sequence's prefix and tree (ragged batches: clamped to the plan's maxima,
+  // so every access stays inside the layouts the plan was sized for)
+  const int P = pl.prefix_len ? min(max(pl.prefix_len[b], 0), pl.P) : pl.P;
+  const int N = pl.tree_len ? min(max(pl.tree_len[b], 1), pl.N) : pl.N;
+  const int R = N * G;   // this sequence's query rows; rows past R are padding
+  // split s covers prefix keys [s*len, (s+1)*len) below P (possibly none); the last
+  // split also takes the tree keys P .. P+N-1
+  const int key_begin = (split == pl.S - 1) ? min(split * pl.split_len, P) : split * pl.split_len;
   const int key_end = (split == pl.S - 1) ? P + N : min(P, (split + 1) * pl.split_len);
   const int key_lim = P + N;
 
   const uint16_t* kbase = k + (size_t)pair * pl.kv_cap * D;
   const uint16_t* vbase = v + (size_t)pair * pl.kv_cap * D;
-  const int32_t* par = parents + (size_t)b * N;
+  const int32_t* par = parents + (size_t)b * pl.N;
 
   // ---- Q^T operands (B side of S^T = K Q^T) and ancestor masks, per row tile
   const int rowbase = rb * (WAVES * ROWT * 32) + wid * ROWT * 32;
@@ -109,10 +114,10 @@ tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
   for (int t = 0; t < ROWT; ++t) {
     const int r = rowbase + 32 * t + l32;
-    if (r < pl.R) {
+    if (r < R) {
       const int i = r / G;
       const int h = g * G + (r - i * G);
-      const uint16_t* qp = q + ((size_t)(b * N + i) * pl.Hq + h) * D + 8 * half;
+      const uint16_t* qp = q + ((size_t)(b * pl.N + i) * pl.Hq + h) * D + 8 * half;
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) qf[t][s] = as_bf16x8(*(const u32x4*)(qp + 16 * s));
       anc[t] = ancestor_mask(par, i, N);
@@ -198,7 +203,7 @@ tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     }
   };
 
-  const int n_chunks = (key_end - key_begin + KC - 1) / KC;
+  const int n_chunks = key_end > key_begin ? (key_end - key_begin + KC - 1) / KC : 0;
   if (n_chunks > 0) {
     load_chunk(0, key_begin);
     load_chunk(1, key_begin + KC);   // clamped (and zeroed) if it does not exist
@@ -243,7 +248,9 @@ tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         const int off = kb - P;   // >= -31
 #pragma unroll
         for (int t = 0; t < ROWT; ++t) {
-          const uint64_t tm = anc[t] & node_mask;
+          // only the last split owns the tree keys: in a ragged batch an earlier split
+          // can end inside a chunk at this sequence's prefix end
+          const uint64_t tm = (split == pl.S - 1) ? (anc[t] & node_mask) : 0ull;
           const uint32_t tree_bits = off >= 0 ? (off < 64 ? (uint32_t)(tm >> off) : 0u)
                                               : (uint32_t)(tm << (-off));
           const uint32_t prefix_bits = off < 0 ? ((1u << (-off)) - 1u) : 0u;
@@ -312,13 +319,13 @@ tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   for (int t = 0; t < ROWT; ++t) {
     const int r = rowbase + 32 * t + l32;
     const float ltot = lsum[t] + __shfl_xor(lsum[t], 32);
-    if (r >= pl.R) continue;
+    if (r >= R) continue;
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     const float lse = (mc[t] + log2f(ltot)) * kLn2;
     const int i = r / G;
     const int h = g * G + (r - i * G);
     if (pl.S == 1) {
-      uint16_t* op = out + ((size_t)(b * N + i) * pl.Hq + h) * D;
+      uint16_t* op = out + ((size_t)(b * pl.N + i) * pl.Hq + h) * D;
 #pragma unroll
       for (int db = 0; db < DBLK; ++db)
 #pragma unroll
@@ -329,7 +336,7 @@ tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
           pk[1] = pack_bf16x2(oacc[t][db][4 * j + 2] * inv, oacc[t][db][4 * j + 3] * inv);
           *(u32x2*)(op + d0) = pk;
         }
-      if (half == 0 && lse_out) lse_out[(size_t)(b * N + i) * pl.Hq + h] = lse;
+      if (half == 0 && lse_out) lse_out[(size_t)(b * pl.N + i) * pl.Hq + h] = lse;
     } else {
       const size_t prow = ((size_t)pair * pl.S + split) * pl.Rpad + r;
       float* op = part_o + prow * D;
@@ -361,6 +368,7 @@ tree_attn_merge(AttnPlan pl, const float* __restrict__ part_o, const float* __re
   const int r = gw % pl.R;
   const int b = pair / pl.Hkv;
   const int g = pair % pl.Hkv;
+  if (pl.tree_len && r >= min(max(pl.tree_len[b], 1), pl.N) * pl.G) return;   // past this tree
   const size_t base = (size_t)pair * pl.S * pl.Rpad + r;
   float mx = -INFINITY;
   for (int s = 0; s < pl.S; ++s) mx = fmaxf(mx, part_lse[base + (size_t)s * pl.Rpad]);

@@ -158,3 +158,19 @@ def test_kv_commit_argument_errors(lib):
     assert kc(P=75, cap=80, path_len=7) == 2   # rows P .. P+6 do not fit
     assert kc(k=FAKE + 8) == 2                 # misaligned cache
     assert b"aligned" in lib.eagle_last_error()
+
+
+def test_ragged_argument_errors(lib):
+    a = lib.eagle_tree_verify_attn_ragged
+    # both per-sequence arrays NULL: the uniform call is the right one
+    assert a(FAKE, FAKE, FAKE, FAKE, None, None, 1, 4, 2, 1, 64, 16, 64, 0.1, FAKE, None, None, 0,
+             None) == 1
+    # layouts must hold the maxima
+    assert a(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 2, 1, 64, 16, 19, 0.1, FAKE, None, None, 0,
+             None) == 2
+    g = lib.eagle_accept_greedy_ragged
+    assert g(FAKE, FAKE, FAKE, None, 1, 5, 4, FAKE, FAKE, FAKE, None) == 1
+    assert g(FAKE, FAKE, FAKE, FAKE, 1, 65, 4, FAKE, FAKE, FAKE, None) == 3
+    s = lib.eagle_accept_spec_ragged
+    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, None, 1, 5, 8, 3, FAKE, FAKE, FAKE, FAKE,
+             1 << 20, None) == 1
