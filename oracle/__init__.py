@@ -25,3 +25,4 @@ from .accept import accept_greedy, accept_spec, sample_inverse_cdf, spec_node_ro
 from .rerank import eagle2_rerank  # noqa: F401
 from .kv_commit import kv_commit  # noqa: F401
 from .ragged import accept_greedy_ragged, accept_spec_ragged, tree_verify_attention_ragged  # noqa: F401
+from .paged import gather_pages, tree_verify_attention_paged  # noqa: F401
