@@ -246,6 +246,42 @@ def kv_commit_latency(torch, sda, dev, parents, iters=50, layers=80):
             "bytes": moved, "gbs": round(moved / (us * 1e-6) / 1e9, 1)}
 
 
+def paged_attention(torch, sda, dev, x, parents, page_size=16, iters=20):
+    """Tree attention at C5 with the KV cache in pages of `page_size` rows scattered
+    over a pool by a seeded permutation (the same rows as the contiguous cache)."""
+    cfg = synth.CONFIGS["C5"]
+    B, N, Hkv, D, P = cfg.B, cfg.N, cfg.Hkv, cfg.D, cfg.P
+    L = P + N
+    pages = (L + page_size - 1) // page_size
+    nblk = B * pages
+    perm = torch.from_numpy(np.random.default_rng(5).permutation(nblk).astype(np.int64)).to(dev)
+    table = perm.view(B, pages).to(torch.int32).contiguous()
+
+    def pool_of(c):
+        pad = torch.zeros((B, Hkv, pages * page_size - L, D), dtype=c.dtype, device=dev)
+        blocks = torch.cat([c, pad], dim=2).view(B, Hkv, pages, page_size, D).permute(0, 2, 1, 3, 4)
+        pool = torch.empty((nblk, Hkv, page_size, D), dtype=c.dtype, device=dev)
+        pool[perm] = blocks.reshape(nblk, Hkv, page_size, D)
+        return pool
+
+    kp, vp = pool_of(x["k"]), pool_of(x["v"])
+    ws = torch.empty(max(1, sda.load().eagle_tree_verify_attn_paged_workspace(
+        B, N, cfg.Hq, Hkv, D, P, page_size)), dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        sda.eagle_tree_verify_attn_paged(x["q"], kp, vp, table, parents, P, workspace=ws)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(iters):
+        sda.eagle_tree_verify_attn_paged(x["q"], kp, vp, table, parents, P, workspace=ws)
+    e1.record(s)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / iters
+    del kp, vp
+    return {"page_size": page_size, "us": round(us, 2)}
+
+
 RAGGED_PREFIX = [32768, 8192, 24576, 2048]
 RAGGED_TREE = [60, 40, 60, 25]
 
@@ -520,6 +556,7 @@ def main(argv=None):
         out["accept_spec_us_C4"] = round(spec_latency(torch, sda, dev), 2)
         out["kv_commit_80_layers"] = kv_commit_latency(torch, sda, dev, tree["parents"])
         out["ragged_C5"] = ragged_step(torch, sda, dev, x)
+        out["paged_attention_C5"] = paged_attention(torch, sda, dev, x, tree["parents"])
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg)

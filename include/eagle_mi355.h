@@ -9,7 +9,8 @@
  *   eagle_accept_greedy    greedy acceptance (longest matching root path)
  *   eagle_accept_spec      multi-round speculative sampling acceptance
  * with _ragged forms of the attention and the acceptances for batches whose
- * sequences have different prefix and tree sizes, and, after acceptance:
+ * sequences have different prefix and tree sizes, a _paged form of the attention
+ * for KV caches kept in fixed-size pages, and, after acceptance:
  *   eagle_kv_commit        move the accepted path's K/V rows to the end of the prefix
  *
  * Sources (web pages on the method), cited per call below:
@@ -220,6 +221,31 @@ eagle_status_t eagle_accept_spec_ragged(const int32_t* tokens, const int32_t* pa
                                         int32_t* accept_path, int32_t* out_tokens,
                                         void* workspace, size_t workspace_bytes,
                                         hipStream_t stream);
+
+/*
+ * Paged KV cache.  [P3] section 4 (limitations: dynamic draft trees strain paged
+ * cache management such as PagedAttention).  Same computation as
+ * eagle_tree_verify_attn, but the K and V rows of each (sequence, KV head) sit in
+ * fixed-size pages of shared pools:
+ *   k_pool, v_pool bf16 [num_blocks][Hkv][page_size][D]   (16-byte aligned)
+ *   block_table int32 [B][max_pages]: row r (prefix rows, then tree rows in node
+ *     order, r < P + N) of sequence b lives in block block_table[b][r / page_size]
+ *     at slot r % page_size.  Entries are clamped to [0, num_blocks - 1] on the
+ *     device, so any table content stays inside the pools.
+ *   page_size: a power of two, 1 .. 4096; max_pages * page_size >= P + N.
+ * Very small pages with a long prefix are rejected (EAGLE_ERR_UNSUPPORTED) when a
+ * split's slice of the block table would not fit on chip.
+ * Workspace: eagle_tree_verify_attn_paged_workspace(B, N, Hq, Hkv, D, P, page_size).
+ */
+size_t eagle_tree_verify_attn_paged_workspace(int32_t B, int32_t N, int32_t Hq, int32_t Hkv,
+                                              int32_t D, int32_t P, int32_t page_size);
+eagle_status_t eagle_tree_verify_attn_paged(const void* q, const void* k_pool, const void* v_pool,
+                                            const int32_t* block_table, const int32_t* parents,
+                                            int32_t B, int32_t N, int32_t Hq, int32_t Hkv,
+                                            int32_t D, int32_t P, int32_t page_size,
+                                            int32_t max_pages, int32_t num_blocks, float scale,
+                                            void* out, float* lse, void* workspace,
+                                            size_t workspace_bytes, hipStream_t stream);
 
 /*
  * EAGLE-2 dynamic draft tree.  [P3] section 2 (dynamic draft tree: confidence

@@ -52,6 +52,9 @@ _SIGNATURES = {
                           + [_sz, _vp], ctypes.c_int),
     "eagle_tree_verify_attn_ragged": ([_vp] * 6 + [_i32] * 7 + [_f32, _vp, _vp, _vp, _sz, _vp],
                                       ctypes.c_int),
+    "eagle_tree_verify_attn_paged_workspace": ([_i32] * 7, _sz),
+    "eagle_tree_verify_attn_paged": ([_vp] * 5 + [_i32] * 9 + [_f32, _vp, _vp, _vp, _sz, _vp],
+                                     ctypes.c_int),
     "eagle_accept_greedy_ragged": ([_vp] * 4 + [_i32, _i32, _i32] + [_vp] * 4, ctypes.c_int),
     "eagle_accept_spec_ragged": ([_vp] * 5 + [_i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32]
                                  + [_vp] * 4 + [_sz, _vp], ctypes.c_int),
@@ -166,6 +169,41 @@ def eagle_tree_verify_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pa
                                            out.data_ptr(), _ptr(lse), _ptr(workspace), wsb,
                                            _stream())
     _check(st, "eagle_tree_verify_attn_ragged")
+    return out, lse
+
+
+def eagle_tree_verify_attn_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                                 block_table: torch.Tensor, parents: torch.Tensor, P: int,
+                                 scale: Optional[float] = None, want_lse: bool = True,
+                                 workspace: Optional[torch.Tensor] = None):
+    """q [B][N][Hq][D] bf16; k_pool, v_pool [num_blocks][Hkv][page_size][D] bf16;
+    block_table [B][max_pages] int32; parents [B][N] int32.
+    Returns (out [B][N][Hq][D] bf16, lse [B][N][Hq] fp32 or None)."""
+    lib = load()
+    dev = q.device
+    _need(q, "q", torch.bfloat16, dev)
+    _need(k_pool, "k_pool", torch.bfloat16, dev)
+    _need(v_pool, "v_pool", torch.bfloat16, dev)
+    _need(block_table, "block_table", torch.int32, dev)
+    _need(parents, "parents", torch.int32, dev)
+    B, N, Hq, D = q.shape
+    nblk, Hkv, ps, Dk = k_pool.shape
+    if v_pool.shape != k_pool.shape or Dk != D or block_table.dim() != 2 or block_table.shape[0] != B \
+            or tuple(parents.shape) != (B, N):
+        raise ValueError("inconsistent shapes")
+    if scale is None:
+        scale = D ** -0.5
+    out = torch.empty((B, N, Hq, D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, N, Hq), dtype=torch.float32, device=dev) if want_lse else None
+    ws_bytes = lib.eagle_tree_verify_attn_paged_workspace(B, N, Hq, Hkv, D, P, ps)
+    if workspace is None and ws_bytes:
+        workspace = _workspace(ws_bytes, dev)
+    st = lib.eagle_tree_verify_attn_paged(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                          block_table.data_ptr(), parents.data_ptr(), B, N, Hq, Hkv,
+                                          D, P, ps, block_table.shape[1], nblk, float(scale),
+                                          out.data_ptr(), _ptr(lse), _ptr(workspace),
+                                          0 if workspace is None else workspace.numel(), _stream())
+    _check(st, "eagle_tree_verify_attn_paged")
     return out, lse
 
 

@@ -123,6 +123,62 @@ eagle_status_t eagle_tree_verify_attn(const void* q, const void* k, const void* 
                    workspace, workspace_bytes, stream, "eagle_tree_verify_attn");
 }
 
+static int page_shift_of(int32_t page_size) {
+  for (int s = 0; s <= 12; ++s)
+    if (page_size == (1 << s)) return s;
+  return -1;
+}
+
+size_t eagle_tree_verify_attn_paged_workspace(int32_t B, int32_t N, int32_t Hq, int32_t Hkv,
+                                              int32_t D, int32_t P, int32_t page_size) {
+  if (check_attn_dims(B, N, Hq, Hkv, D, P) != EAGLE_OK) return 0;
+  const int shift = page_shift_of(page_size);
+  if (shift < 0) return 0;
+  return eagle::tree_attn_workspace_bytes(eagle::plan_tree_attn_paged(B, N, Hq, Hkv, D, P, shift));
+}
+
+eagle_status_t eagle_tree_verify_attn_paged(const void* q, const void* k_pool, const void* v_pool,
+                                            const int32_t* block_table, const int32_t* parents,
+                                            int32_t B, int32_t N, int32_t Hq, int32_t Hkv,
+                                            int32_t D, int32_t P, int32_t page_size,
+                                            int32_t max_pages, int32_t num_blocks, float scale,
+                                            void* out, float* lse, void* workspace,
+                                            size_t workspace_bytes, hipStream_t stream) {
+  if (!q || !k_pool || !v_pool || !block_table || !parents || !out)
+    return fail(EAGLE_ERR_NULL, "q, k_pool, v_pool, block_table, parents and out must be non-NULL");
+  eagle_status_t st = check_attn_dims(B, N, Hq, Hkv, D, P);
+  if (st != EAGLE_OK) return st;
+  const int shift = page_shift_of(page_size);
+  if (shift < 0) return fail(EAGLE_ERR_UNSUPPORTED, "page_size=%d (a power of two up to 4096)", page_size);
+  if (num_blocks < 1 || max_pages < 1)
+    return fail(EAGLE_ERR_INVALID_ARG, "num_blocks=%d and max_pages=%d must be >= 1", num_blocks, max_pages);
+  if ((long long)max_pages * page_size < (long long)P + N)
+    return fail(EAGLE_ERR_INVALID_ARG, "max_pages * page_size = %lld < P+N=%d",
+                (long long)max_pages * page_size, P + N);
+  if ((double)num_blocks * Hkv * page_size * (double)D > 4.0e18)
+    return fail(EAGLE_ERR_INVALID_ARG, "pool too large");
+  if (!(scale > 0.f) || scale != scale || scale > 1e30f)
+    return fail(EAGLE_ERR_INVALID_ARG, "scale must be a positive finite number");
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
+    return fail(EAGLE_ERR_INVALID_ARG, "q, k_pool, v_pool, out must be 16-byte aligned");
+  eagle::AttnPlan pl = eagle::plan_tree_attn_paged(B, N, Hq, Hkv, D, P, shift);
+  const int last_range = (P - (pl.S - 1) * pl.split_len) + N;
+  const int range = (pl.split_len > last_range ? pl.split_len : last_range) + 64;
+  if ((range >> shift) + 2 > eagle::kMaxSplitPages)
+    return fail(EAGLE_ERR_UNSUPPORTED, "page_size=%d too small for P=%d (block-table slice per split)",
+                page_size, P);
+  pl.block_table = block_table;
+  pl.max_pages = max_pages;
+  pl.num_blocks = num_blocks;
+  const size_t need = eagle::tree_attn_workspace_bytes(pl);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(EAGLE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  if (need > 0 && !aligned16(workspace)) return fail(EAGLE_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  return hip_status(eagle::launch_tree_attn(pl, scale, q, k_pool, v_pool, parents, out, lse,
+                                            workspace, stream),
+                    "eagle_tree_verify_attn_paged launch");
+}
+
 eagle_status_t eagle_tree_verify_attn_ragged(const void* q, const void* k, const void* v,
                                              const int32_t* parents, const int32_t* prefix_len,
                                              const int32_t* tree_len, int32_t B, int32_t N,

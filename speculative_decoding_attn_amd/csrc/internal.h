@@ -31,7 +31,17 @@ struct AttnPlan {
   // (<= N); P and N above are then the maxima the plan and the layouts are sized for
   const int32_t* prefix_len;
   const int32_t* tree_len;
+  // paged KV (may be null): k, v are pools [num_blocks][Hkv][page_size][D] and row r
+  // of sequence b lives in block block_table[b][r / page_size] at slot r % page_size
+  const int32_t* block_table;
+  int page_shift;   // log2(page_size)
+  int max_pages;    // row stride of block_table
+  int num_blocks;
 };
+
+// paged KV: a split's slice of the block table is staged in LDS
+constexpr int kMaxSplitPages = 1024;
+AttnPlan plan_tree_attn_paged(int B, int N, int Hq, int Hkv, int D, int P, int page_shift);
 
 AttnPlan plan_tree_attn(int B, int N, int Hq, int Hkv, int D, int P, int kv_cap);
 size_t tree_attn_workspace_bytes(const AttnPlan& pl);

@@ -53,7 +53,7 @@ __device__ __forceinline__ int vt_pos(int key) {
   return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
 }
 
-template <int D, int WAVES, int ROWT>
+template <int D, int WAVES, int ROWT, bool PAGED>
 __global__ void __launch_bounds__(WAVES * 64, 1)
 tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
               const uint16_t* __restrict__ v, const int32_t* __restrict__ parents,
@@ -74,6 +74,7 @@ tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   static_assert(LOADS <= 63, "vmcnt is a 6-bit counter");
 
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * L::STAGE];
+  __shared__ int32_t ptab[PAGED ? kMaxSplitPages : 1];   // paged KV: this split's blocks
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -103,9 +104,20 @@ tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int key_end = (split == pl.S - 1) ? P + N : min(P, (split + 1) * pl.split_len);
   const int key_lim = P + N;
 
-  const uint16_t* kbase = k + (size_t)pair * pl.kv_cap * D;
-  const uint16_t* vbase = v + (size_t)pair * pl.kv_cap * D;
+  const uint16_t* kbase = PAGED ? k : k + (size_t)pair * pl.kv_cap * D;
+  const uint16_t* vbase = PAGED ? v : v + (size_t)pair * pl.kv_cap * D;
   const int32_t* par = parents + (size_t)b * pl.N;
+  // element offset of cache row `key` (< key_lim) of this (sequence, KV head)
+  const int first_page = PAGED ? (key_begin >> pl.page_shift) : 0;
+  auto row_off = [&](int key) -> size_t {
+    if constexpr (PAGED) {
+      const int blk = ptab[(key >> pl.page_shift) - first_page];
+      const int slot = key & ((1 << pl.page_shift) - 1);
+      return (((size_t)blk * pl.Hkv + g) << pl.page_shift | (size_t)slot) * D;
+    } else {
+      return (size_t)key * D;
+    }
+  };
 
   // ---- Q^T operands (B side of S^T = K Q^T) and ancestor masks, per row tile
   const int rowbase = rb * (WAVES * ROWT * 32) + wid * ROWT * 32;
@@ -159,7 +171,7 @@ tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       const int u = tid + it * THREADS;
       const int key = min(kb + u / (D / 8), key_lim - 1);
       const int col = (u % (D / 8)) * 8;
-      kreg[slot][it] = *(const u32x4*)(kbase + (size_t)key * D + col);
+      kreg[slot][it] = *(const u32x4*)(kbase + row_off(key) + col);
     }
 #pragma unroll
     for (int it = 0; it < V_PER; ++it) {
@@ -167,8 +179,8 @@ tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       const int kp = u % (KC / 2);
       const int d0 = (u / (KC / 2)) * 4;
       const int key = kb + 2 * kp;
-      vreg[slot][it][0] = *(const u32x2*)(vbase + (size_t)min(key, key_lim - 1) * D + d0);
-      vreg[slot][it][1] = *(const u32x2*)(vbase + (size_t)min(key + 1, key_lim - 1) * D + d0);
+      vreg[slot][it][0] = *(const u32x2*)(vbase + row_off(min(key, key_lim - 1)) + d0);
+      vreg[slot][it][1] = *(const u32x2*)(vbase + row_off(min(key + 1, key_lim - 1)) + d0);
     }
   };
   // registers -> LDS stage (K as [key][d], V transposed as [d][permuted key])
@@ -204,6 +216,15 @@ tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   };
 
   const int n_chunks = key_end > key_begin ? (key_end - key_begin + KC - 1) / KC : 0;
+  if constexpr (PAGED) {
+    // rows loaded by this split (prefetches run up to two chunks past its end, all
+    // clamped below key_lim); their blocks, clamped to the pool
+    const int last = min(key_lim - 1, key_begin + (n_chunks + 2) * KC - 1);
+    const int npages = min((last >> pl.page_shift) - first_page + 1, kMaxSplitPages);
+    const int32_t* bt = pl.block_table + (size_t)b * pl.max_pages + first_page;
+    for (int j = tid; j < npages; j += THREADS) ptab[j] = min(max(bt[j], 0), pl.num_blocks - 1);
+    __syncthreads();
+  }
   if (n_chunks > 0) {
     load_chunk(0, key_begin);
     load_chunk(1, key_begin + KC);   // clamped (and zeroed) if it does not exist
@@ -405,9 +426,14 @@ hipError_t launch_fwd(const AttnPlan& pl, const void* q, const void* k, const vo
                       const int32_t* parents, void* out, float* lse, float* part_o,
                       float* part_lse, hipStream_t stream) {
   const int nwg = pl.B * pl.Hkv * pl.RB * pl.S;
-  hipLaunchKernelGGL((tree_attn_fwd<D, WAVES, ROWT>), dim3(nwg), dim3(WAVES * 64), 0, stream,
-                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, parents, pl,
-                     (uint16_t*)out, lse, part_o, part_lse);
+  if (pl.block_table)
+    hipLaunchKernelGGL((tree_attn_fwd<D, WAVES, ROWT, true>), dim3(nwg), dim3(WAVES * 64), 0,
+                       stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, parents,
+                       pl, (uint16_t*)out, lse, part_o, part_lse);
+  else
+    hipLaunchKernelGGL((tree_attn_fwd<D, WAVES, ROWT, false>), dim3(nwg), dim3(WAVES * 64), 0,
+                       stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, parents,
+                       pl, (uint16_t*)out, lse, part_o, part_lse);
   return hipGetLastError();
 }
 
@@ -466,6 +492,24 @@ AttnPlan plan_tree_attn(int B, int N, int Hq, int Hkv, int D, int P, int kv_cap)
     pl.split_len = len;
   }
   pl.S = S;
+  return pl;
+}
+
+// Paged KV: as plan_tree_attn, with more splits where a split's slice of the block
+// table would not fit the LDS table (rows of one split plus two chunks of prefetch).
+AttnPlan plan_tree_attn_paged(int B, int N, int Hq, int Hkv, int D, int P, int page_shift) {
+  AttnPlan pl = plan_tree_attn(B, N, Hq, Hkv, D, P, P + N);
+  auto fits = [&](int len, int S) {
+    const int last_range = (P - (S - 1) * len) + N;   // the last split also has the tree
+    const int range = (len > last_range ? len : last_range) + 2 * KC;
+    return (range >> page_shift) + 2 <= kMaxSplitPages;
+  };
+  while (P > 0 && !fits(pl.split_len, pl.S) && pl.split_len > KC) {
+    int len = ((pl.split_len / 2) + KC - 1) / KC * KC;
+    pl.S = (P + len - 1) / len;
+    pl.split_len = len;
+  }
+  pl.page_shift = page_shift;
   return pl;
 }
 

@@ -174,3 +174,20 @@ def test_ragged_argument_errors(lib):
     s = lib.eagle_accept_spec_ragged
     assert s(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, None, 1, 5, 8, 3, FAKE, FAKE, FAKE, FAKE,
              1 << 20, None) == 1
+
+
+def test_paged_argument_errors(lib):
+    a = lib.eagle_tree_verify_attn_paged
+
+    def pg(ps=16, max_pages=8, nblk=100, P=100, N=10, k=FAKE):
+        return a(FAKE, k, FAKE, FAKE, FAKE, 1, N, 2, 1, 64, P, ps, max_pages, nblk, 0.1, FAKE, None,
+                 FAKE, 1 << 30, None)
+
+    assert pg(k=None) == 1
+    assert pg(ps=24) == 3                  # not a power of two
+    assert pg(max_pages=6) == 2            # 6 * 16 < P + N
+    assert pg(nblk=0) == 2
+    assert lib.eagle_tree_verify_attn_paged_workspace(1, 10, 2, 1, 64, 100, 24) == 0
+    # with one-row pages the plan splits a long prefix finely enough for the on-chip
+    # slice of the block table, which then needs a split-KV workspace
+    assert lib.eagle_tree_verify_attn_paged_workspace(1, 10, 2, 1, 64, 30000, 1) > 0
