@@ -47,9 +47,16 @@ KERNEL_SOURCES = {
 }
 
 
+COMMON_HEADER = "speculative_decoding_attn_amd/csrc/common.h"
+
+
 def _src_hash(rel: str) -> str:
-    with open(os.path.join(ROOT, rel), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of a kernel source together with the device header it includes."""
+    h = hashlib.sha256()
+    for path in (rel, COMMON_HEADER):
+        with open(os.path.join(ROOT, path), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def _traffic(kernel: str):
@@ -400,7 +407,9 @@ def summarize_profiles(root):
     w_fac = copy_bytes / 1024.0 / cw[copy_name]
     fetch = per_kernel("pmc_fetch", "FETCH_SIZE")
     write = per_kernel("pmc_write", "WRITE_SIZE")
-    algo = {"tree_attn_fwd": 2 * B * Hkv * (P + N) * D * 2 + 2 * B * N * Hq * D * 2 + B * N * Hq * 4,
+    # the C5 attention kernel (the eight-wave ping-pong kernel at these shapes)
+    attn_name = next(k for k in fetch if k.startswith("tree_attn_") and "merge" not in k)
+    algo = {attn_name: 2 * B * Hkv * (P + N) * D * 2 + 2 * B * N * Hq * D * 2 + B * N * Hq * 4,
             "lm_head_gemm": V * H * 2 + B * N * H * 2 + B * N * 16}
     cmds = [PROFILE_RUNS[k] for k in ("pmc_fetch", "pmc_write", "pmc_copy_fetch", "pmc_copy_write")]
     rows = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE), C5 verification step", "",
@@ -420,7 +429,7 @@ def summarize_profiles(root):
                     + (f"{a / 1e6:.1f} MB | {hbm / a:.3f} |" if a else " |  |"))
     with open(os.path.join(PROFILE_DIR, TRAFFIC_MD), "w") as f:
         f.write("\n".join(rows) + "\n")
-    for short, kname in (("lm_head", "lm_head_gemm"), ("tree_attn", "tree_attn_fwd")):
+    for short, kname in (("lm_head", "lm_head_gemm"), ("tree_attn", attn_name)):
         hbm = fetch[kname] * 1024 * f_fac + write[kname] * 1024 * w_fac
         rec = {"kernel": kname, "workload": "C5", "fetch_kib": fetch[kname], "write_kib": write[kname],
                "fetch_factor": f_fac, "write_factor": w_fac, "bytes_per_launch": int(round(hbm)),

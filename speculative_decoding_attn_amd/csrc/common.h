@@ -84,6 +84,29 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// global -> LDS copy of 16 bytes per lane: lane i's bytes land at LDS byte address
+// m0 + 16*i, one contiguous KiB per wave.  Issued through inline assembly: for the
+// compiler's own form of this load it waits for every outstanding load before any
+// later LDS read, which would drain the pipeline each block.  Completion is waited
+// for with wait_vmcnt<N>() and published to the other waves with a barrier.
+// (m0 is a reserved register to the compiler, hence the warning about its clobber;
+// the kernels' assembly is checked to use m0 nowhere else.  The s_nop is the wait
+// state the ISA asks for between an SALU write of m0 and an LDS DMA that reads it.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_byte_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_byte_addr))
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
+}
+
 // Ancestor-or-self bitmask of node i (bit a set for every a on the root path of
 // i).  Walks at most 64 parent links and stops at any link that breaks the tree
 // rules, so it is memory-safe for any parent content.

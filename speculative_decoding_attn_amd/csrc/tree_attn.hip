@@ -32,6 +32,7 @@
 #include "common.h"
 #include "internal.h"
 
+
 namespace eagle {
 
 namespace {
@@ -421,6 +422,359 @@ tree_attn_merge(AttnPlan pl, const float* __restrict__ part_o, const float* __re
   if (lane == 0 && lse_out) lse_out[(size_t)(b * pl.N + i) * pl.Hq + h] = mx + logf(wsum);
 }
 
+// ---------------------------------------------------------------------------
+// D = 128 with eight waves: the two halves of the workgroup in ping-pong.
+//
+// Each wave owns 32 query rows and walks the split in chunks of 64 keys.  Per chunk
+// a wave has a matrix phase (the scores of the next chunk, S^T = K Q^T, and the
+// output update of this one, O^T += V^T P^T: 32 MFMAs) and a vector phase (mask,
+// online max and sum, exponentials and bf16 packing of those scores).  Waves 0-3
+// and 4-7 (one of each per SIMD) run these phases half a chunk apart, separated by
+// workgroup barriers, so on every SIMD one wave issues MFMAs while the other one
+// runs the exponentials.
+//
+// K and V chunks reach LDS by global-to-LDS DMA (each lane moves 16 bytes to
+// m0 + 16*lane), four chunks deep.  Rows are stored whole (256 bytes) with their
+// 16-byte pieces permuted: K piece c of row r sits at c ^ (r & 15), which makes the
+// b128 fragment reads of 16 consecutive rows hit every bank once; V piece c of row r
+// sits at c ^ 4*(r & 3), which does the same for the transposing reads
+// (ds_read_b64_tr_b16) that hand each lane 4 keys of one V column, the V^T operand
+// of the output MFMA, without a transpose in registers.
+constexpr int XC = 64;               // keys per chunk
+constexpr int XNB = 4;               // LDS stages
+constexpr int XROW = 256;            // bytes per K or V row
+constexpr int XHALF = XC * XROW;     // one chunk of K (or of V): 16 KB
+constexpr int XSTAGE = 2 * XHALF;
+constexpr int XLDS = XNB * XSTAGE;   // 128 KB of dynamic LDS
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+
+__device__ __forceinline__ v4i16 lds_read_tr(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p);
+}
+
+template <bool PAGED>
+__global__ void __launch_bounds__(512, 1)
+tree_attn_pingpong(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                   const uint16_t* __restrict__ v, const int32_t* __restrict__ parents,
+                   AttnPlan pl, uint16_t* __restrict__ out, float* __restrict__ lse_out,
+                   float* __restrict__ part_o, float* __restrict__ part_lse) {
+  constexpr int D = 128;
+  constexpr int KSTEPS = D / 16;
+  constexpr int DBLK = D / 32;
+  extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
+  __shared__ int32_t ptab[PAGED ? kMaxSplitPages : 1];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wv >> 2;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int nwg = gridDim.x;
+  const int w = blockIdx.x;
+  const int logical = (nwg % 8 == 0) ? (w % 8) * (nwg / 8) + (w / 8) : w;
+  const int rb = logical % pl.RB;
+  const int split = (logical / pl.RB) % pl.S;
+  const int pair = logical / (pl.RB * pl.S);
+  const int b = pair / pl.Hkv;
+  const int g = pair % pl.Hkv;
+  const int G = pl.G;
+  const int P = pl.prefix_len ? min(max(pl.prefix_len[b], 0), pl.P) : pl.P;
+  const int N = pl.tree_len ? min(max(pl.tree_len[b], 1), pl.N) : pl.N;
+  const int R = N * G;
+  const bool last = split == pl.S - 1;
+  const int key_begin = last ? min(split * pl.split_len, P) : split * pl.split_len;
+  const int key_end = last ? P + N : min(P, (split + 1) * pl.split_len);
+  const int key_lim = P + N;
+  // keys at or past mask_from are masked: the tree part of the last split, and the
+  // tail of a chunk that runs past the end of an earlier split
+  const int mask_from = last ? P : key_end;
+
+  const uint16_t* kbase = PAGED ? k : k + (size_t)pair * pl.kv_cap * D;
+  const uint16_t* vbase = PAGED ? v : v + (size_t)pair * pl.kv_cap * D;
+  const int32_t* par = parents + (size_t)b * pl.N;
+  const int first_page = PAGED ? (key_begin >> pl.page_shift) : 0;
+  auto row_off = [&](int key) -> size_t {
+    if constexpr (PAGED) {
+      const int blk = ptab[(key >> pl.page_shift) - first_page];
+      const int slot = key & ((1 << pl.page_shift) - 1);
+      return (((size_t)blk * pl.Hkv + g) << pl.page_shift | (size_t)slot) * D;
+    } else {
+      return (size_t)key * D;
+    }
+  };
+
+  // ---- Q^T operand and ancestor mask of this wave's 32 rows
+  const int r_row = rb * 256 + wv * 32 + l32;
+  bf16x8 qf[KSTEPS];
+  uint64_t anc;
+  if (r_row < R) {
+    const int i = r_row / G;
+    const int h = g * G + (r_row - i * G);
+    const uint16_t* qp = q + ((size_t)(b * pl.N + i) * pl.Hq + h) * D + 8 * half;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) qf[s] = as_bf16x8(*(const u32x4*)(qp + 16 * s));
+    anc = ancestor_mask(par, i, N);
+  } else {
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) qf[s] = as_bf16x8(u32x4{0, 0, 0, 0});
+    anc = 1;
+  }
+  const uint64_t tmask = last ? (anc & (N >= 64 ? ~0ull : ((1ull << N) - 1ull))) : 0ull;
+
+  f32x16 oacc[DBLK];
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  float mc = -INFINITY;   // running max of scale*log2e*s
+  float lsum = 0.f;       // this lane's half of the row sum
+  const float c = pl.c;
+
+  const int n = key_end > key_begin ? (key_end - key_begin + XC - 1) / XC : 0;
+  if constexpr (PAGED) {
+    const int lastkey = min(key_lim - 1, key_begin + n * XC - 1);
+    const int npages = min((lastkey >> pl.page_shift) - first_page + 1, kMaxSplitPages);
+    const int32_t* bt = pl.block_table + (size_t)b * pl.max_pages + first_page;
+    for (int j = tid; j < npages; j += 512) ptab[j] = min(max(bt[j], 0), pl.num_blocks - 1);
+    __syncthreads();
+  }
+
+  const uint32_t xbase = lds_addr(xs);
+  // chunk cidx -> LDS stage cidx % XNB; wave wv moves rows 8wv .. 8wv+7 of K and V,
+  // rows past the last key are clamped (their scores are masked)
+  auto issue = [&](int cidx) {
+    const int kb = key_begin + cidx * XC;
+    const uint32_t st = xbase + (uint32_t)(cidx % XNB) * XSTAGE;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int row = 8 * wv + 4 * t + (lane >> 4);
+      const size_t off = row_off(min(kb + row, key_lim - 1));
+      const uint32_t dst = st + (uint32_t)(8 * wv + 4 * t) * XROW;
+      dma16(kbase + off + 8 * ((lane & 15) ^ (row & 15)), dst);
+      dma16(vbase + off + 8 * ((lane & 15) ^ (4 * (row & 3))), dst + XHALF);
+    }
+  };
+
+  f32x16 sacc[2];   // S^T of one chunk: keys 32t .. 32t+31 in tile t
+  bf16x8 pf[4];     // P^T of one chunk, 16 keys per operand
+  // Matrix phase of chunk cidx: O^T += V^T P^T for chunk cidx (16 MFMAs) and the scores
+  // of chunk cidx+1 (16 MFMAs).  The LDS operand of MFMA i is fetched LA MFMAs ahead
+  // (a ring of LA fragments, indexed with compile-time constants), and the scheduler
+  // is told to keep that order, so the reads of later MFMAs overlap the earlier ones.
+  auto matrix_phase = [&](int cidx) {
+    const uint8_t* Vs = xs + (cidx % XNB) * XSTAGE + XHALF;
+    const uint8_t* Ks = xs + ((cidx + 1) % XNB) * XSTAGE;
+    const int m = lane & 15;
+    const int vrow = 4 * half + (m >> 2);
+    const int vcol = 2 * ((lane >> 4) & 1) + ((m & 3) >> 1);
+    const uint8_t* vp = Vs + vrow * XROW + 8 * (m & 1);
+    const int vx = 4 * (m >> 2);
+    const uint8_t* kp = Ks + l32 * XROW;
+    const int kx = l32 & 15;
+    auto fetch = [&](int i) -> bf16x8 {
+      if (i < 16) {   // V^T operand of (cc, db)
+        const int cc = i >> 2, db = i & 3;
+        const uint8_t* p0 = vp + 16 * cc * XROW + 16 * ((4 * db + vcol) ^ vx);
+        const v4i16 both[2] = {lds_read_tr(p0), lds_read_tr(p0 + 8 * XROW)};
+        return __builtin_bit_cast(bf16x8, both);
+      }
+      const int s = (i - 16) >> 1, t = (i - 16) & 1;   // K operand of (s, t)
+      return *(const bf16x8*)(kp + 32 * t * XROW + 16 * ((2 * s + half) ^ kx));
+    };
+    constexpr int LA = 4;
+    bf16x8 ring[LA];
+#pragma unroll
+    for (int i = 0; i < LA; ++i) ring[i] = fetch(i);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const bf16x8 a = ring[i % LA];
+      if (i + LA < 32) ring[i % LA] = fetch(i + LA);
+      if (i < 16) {
+        oacc[i & 3] = mfma32(a, pf[i >> 2], oacc[i & 3]);
+      } else {
+        const int s = (i - 16) >> 1, t = (i - 16) & 1;
+        sacc[t] = mfma32(a, qf[s], sacc[t]);
+      }
+    }
+    // LA operands' reads first, then per MFMA: the MFMA and the reads LA ahead
+    __builtin_amdgcn_sched_group_barrier(0x100, LA <= 16 ? 2 * LA : 32 + (LA - 16), 0);
+#pragma unroll
+    for (int i = 0; i < 16 - LA; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < LA; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  };
+  auto softmax = [&](int cidx) {
+    const int kb = key_begin + cidx * XC;
+    float sv[2][16];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sv[t][r] = sacc[t][r];
+    if (kb + XC > mask_from) {
+      const int npre = mask_from - kb;   // < 64
+      uint64_t allowed = npre <= 0 ? 0ull : ((1ull << npre) - 1ull);
+      const int off = kb - P;
+      allowed |= off >= 0 ? (off < 64 ? tmask >> off : 0ull) : (-off < 64 ? tmask << (-off) : 0ull);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int bit = 32 * t + 8 * (r >> 2) + 4 * half + (r & 3);
+          sv[t][r] = ((allowed >> bit) & 1ull) ? sv[t][r] : -INFINITY;
+        }
+    }
+    float mx = sv[0][0];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv[t][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mxc = mx * c;
+    const bool need = mxc > mc + kLazy;
+    if (__ballot(need)) {
+      const float mnew = need ? mxc : mc;
+      const float alpha = need ? exp2f(mc - mnew) : 1.f;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      mc = mnew;
+    }
+    const float mcu = (mc == -INFINITY) ? 0.f : mc;
+    float pr[2][16];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        pr[t][r] = __builtin_amdgcn_exp2f(fmaf(sv[t][r], c, -mcu));
+        lsum += pr[t][r];
+      }
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      u32x4 pk;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        pk[e] = pack_bf16x2(pr[cc >> 1][8 * (cc & 1) + 2 * e], pr[cc >> 1][8 * (cc & 1) + 2 * e + 1]);
+      pf[cc] = as_bf16x8(pk);
+    }
+  };
+
+  // ---- prologue: chunks 0..2 in flight, 0 and 1 landed; scores and P of chunk 0
+  if (n > 0) issue(0);
+  if (n > 1) issue(1);
+  if (n > 2) {
+    issue(2);
+    wait_vmcnt<4>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  __syncthreads();
+  if (n > 0) {
+    const uint8_t* Ks = xs;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const bf16x8 kf =
+            *(const bf16x8*)(Ks + (32 * t + l32) * XROW + 16 * ((2 * s + half) ^ (l32 & 15)));
+        sacc[t] = mfma32(kf, qf[s], sacc[t]);
+      }
+    softmax(0);
+  }
+  // waves 4-7 start half a chunk behind waves 0-3
+  if (grp == 1) __builtin_amdgcn_s_barrier();
+
+  for (int j = 0; j < n; ++j) {
+    // matrix phase: chunk j+3 to stage (j-1)%4 (read by both halves before the last
+    // barrier), scores of chunk j+1 (unused after the last chunk), output of chunk j
+    const bool more = j + 3 < n;
+    if (more) issue(j + 3);
+    matrix_phase(j);
+    // chunk j+2 must have landed before the next matrix phase of either half
+    if (more) wait_vmcnt<4>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    // vector phase
+    if (j + 1 < n) softmax(j + 1);
+    __syncthreads();
+  }
+  if (grp == 0) __builtin_amdgcn_s_barrier();
+
+  // ---- epilogue
+  const float ltot = lsum + __shfl_xor(lsum, 32);
+  if (r_row >= R) return;
+  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+  const float lse = (mc + log2f(ltot)) * kLn2;
+  const int i = r_row / G;
+  const int h = g * G + (r_row - i * G);
+  if (pl.S == 1) {
+    uint16_t* op = out + ((size_t)(b * pl.N + i) * pl.Hq + h) * D;
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int d0 = 32 * db + 8 * jj + 4 * half;
+        u32x2 pk;
+        pk[0] = pack_bf16x2(oacc[db][4 * jj] * inv, oacc[db][4 * jj + 1] * inv);
+        pk[1] = pack_bf16x2(oacc[db][4 * jj + 2] * inv, oacc[db][4 * jj + 3] * inv);
+        *(u32x2*)(op + d0) = pk;
+      }
+    if (half == 0 && lse_out) lse_out[(size_t)(b * pl.N + i) * pl.Hq + h] = lse;
+  } else {
+    const size_t prow = ((size_t)pair * pl.S + split) * pl.Rpad + r_row;
+    float* op = part_o + prow * D;
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int d0 = 32 * db + 8 * jj + 4 * half;
+        f32x4 vv = {oacc[db][4 * jj] * inv, oacc[db][4 * jj + 1] * inv, oacc[db][4 * jj + 2] * inv,
+                    oacc[db][4 * jj + 3] * inv};
+        *(f32x4*)(op + d0) = vv;
+      }
+    if (half == 0) part_lse[prow] = lse;
+  }
+}
+
+template <bool PAGED>
+hipError_t launch_pingpong(const AttnPlan& pl, const void* q, const void* k, const void* v,
+                           const int32_t* parents, void* out, float* lse, float* part_o,
+                           float* part_lse, hipStream_t stream) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute((const void*)tree_attn_pingpong<PAGED>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, XLDS);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int nwg = pl.B * pl.Hkv * pl.RB * pl.S;
+  hipLaunchKernelGGL(tree_attn_pingpong<PAGED>, dim3(nwg), dim3(512), XLDS, stream,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, parents, pl,
+                     (uint16_t*)out, lse, part_o, part_lse);
+  return hipGetLastError();
+}
+
 template <int D, int WAVES, int ROWT>
 hipError_t launch_fwd(const AttnPlan& pl, const void* q, const void* k, const void* v,
                       const int32_t* parents, void* out, float* lse, float* part_o,
@@ -447,7 +801,11 @@ hipError_t launch_fwd_d(const AttnPlan& pl, const void* q, const void* k, const 
     return launch_fwd<D, 1, 2>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
   }
   if constexpr (D == 128) {   // D=64 uses at most 4 waves (chunk staging must divide evenly)
-    if (pl.waves == 8) return launch_fwd<D, 8, 1>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
+    if (pl.waves == 8) {
+      if (pl.block_table)
+        return launch_pingpong<true>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
+      return launch_pingpong<false>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
+    }
   }
   if (pl.waves == 4) return launch_fwd<D, 4, 1>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
   if (pl.waves == 2) return launch_fwd<D, 2, 1>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
