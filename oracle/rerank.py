@@ -45,24 +45,34 @@ def _topk_tokens(row, k: int):
     return [int(t) for t in order[:k]]
 
 
-def eagle2_rerank(draft_logits, root_token: int, top_k: int, depth: int, n_nodes: int):
-    """One sequence.  draft_logits [R][V] with R = 1 + (depth-1)*top_k.
+def grow_tree(row_fn, root_token: int, top_k: int, depth: int, n_nodes: int):
+    """The expansion and selection above, with the rows produced on demand.
 
-    Returns dict with tokens, parents, depths, scores (fp64), draft_row (row of the
-    node's own expansion, -1 if it was not expanded; 0 for the root), draft_lse [R].
+    row_fn(r, token, parent_row) returns the logits of row r at the moment the tree
+    first needs them: r = 0 for the root (token = root_token, parent_row = -1), and
+    r = 1 + (d-1)*top_k + j for frontier slot j at depth d, whose node carries
+    `token` and was proposed by the node expanded in row `parent_row`.  A row is
+    requested only after every row of the depths above it, so a draft model can
+    compute it from its ancestors.  Returns what eagle2_rerank returns.
     """
     R = 1 + (depth - 1) * top_k
-    logits = np.asarray(draft_logits, dtype=np.float64)
-    assert logits.shape[0] == R
-    lse = [_logsumexp(logits[r]) for r in range(R)]
-    props = [_topk_tokens(logits[r], top_k) for r in range(R)]
+    lse = [0.0] * R
+    props = [None] * R
+    rows = {}
 
-    # candidate records: id -> (depth, score, token, parent_id or -1 for root, row or -1)
+    def need(r, token, parent_row):
+        x = np.asarray(row_fn(r, token, parent_row), dtype=np.float64)
+        rows[r] = x
+        lse[r] = _logsumexp(x)
+        props[r] = _topk_tokens(x, top_k)
+
+    # candidate records: id -> [depth, score, token, parent_id or -1 for root, row or -1]
+    need(0, root_token, -1)
     cand = {}
     level = []
     for rank, t in enumerate(props[0]):
         cid = rank
-        cand[cid] = [1, logits[0, t] - lse[0], t, -1, -1]
+        cand[cid] = [1, rows[0][t] - lse[0], t, -1, -1]
         level.append(cid)
     base = top_k
     for d in range(1, depth):
@@ -71,9 +81,11 @@ def eagle2_rerank(draft_logits, root_token: int, top_k: int, depth: int, n_nodes
         for j, fid in enumerate(frontier):
             row = 1 + (d - 1) * top_k + j
             cand[fid][4] = row
+            par = cand[fid][3]
+            need(row, cand[fid][2], 0 if par < 0 else cand[par][4])
             for rank, t in enumerate(props[row]):
                 cid = base + j * top_k + rank
-                cand[cid] = [d + 1, cand[fid][1] + (logits[row, t] - lse[row]), t, fid, -1]
+                cand[cid] = [d + 1, cand[fid][1] + (rows[row][t] - lse[row]), t, fid, -1]
                 level.append(cid)
         base += top_k * top_k
 
@@ -97,3 +109,15 @@ def eagle2_rerank(draft_logits, root_token: int, top_k: int, depth: int, n_nodes
         draft_row[i] = row
     return {"tokens": tokens, "parents": parents, "depths": depths, "scores": scores,
             "draft_row": draft_row, "draft_lse": np.array(lse)}
+
+
+def eagle2_rerank(draft_logits, root_token: int, top_k: int, depth: int, n_nodes: int):
+    """One sequence.  draft_logits [R][V] with R = 1 + (depth-1)*top_k.
+
+    Returns dict with tokens, parents, depths, scores (fp64), draft_row (row of the
+    node's own expansion, -1 if it was not expanded; 0 for the root), draft_lse [R].
+    """
+    R = 1 + (depth - 1) * top_k
+    logits = np.asarray(draft_logits, dtype=np.float64)
+    assert logits.shape[0] == R
+    return grow_tree(lambda r, token, parent_row: logits[r], root_token, top_k, depth, n_nodes)
