@@ -289,6 +289,61 @@ def paged_attention(torch, sda, dev, x, parents, page_size=16, iters=20):
     return {"page_size": page_size, "us": round(us, 2)}
 
 
+DRAFT_SHAPES = {
+    # name: (B, H, Hq, Hkv, D, I, V, P)  draft head = one decoder layer of the target family
+    "C3": (1, 4096, 32, 8, 128, 14336, 128256, 4096),
+    "C5": (4, 8192, 64, 8, 128, 28672, 128256, 32768),
+}
+
+
+def draft_expansion(torch, sda, dev, name="C5", top_k=10, depth=6, n_nodes=60, iters=3):
+    """Per-depth EAGLE-2 draft expansion (eagle_draft_expand) with a one-layer draft head
+    of the target family's shape (random bf16 weights drawn on the device, seeded) over
+    a draft prefix of P rows.  Reports the time of one whole expansion and the weight
+    bytes it streams: every depth reads W_fc, W_qkv, W_o, W_gate_up, W_down and the LM
+    head once."""
+    B, H, Hq, Hkv, D, I, V, P = DRAFT_SHAPES[name]
+    R = 1 + (depth - 1) * top_k
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+
+    def w(rows, cols, std):
+        return (torch.randn((rows, cols), generator=gen, device=dev) * std).to(torch.bfloat16)
+
+    qkvn = (Hq + 2 * Hkv) * D
+    head = {"embed": w(V, H, 1.0), "w_fc": w(H, 2 * H, (2 * H) ** -0.5), "w_qkv": w(qkvn, H, H ** -0.5),
+            "w_o": w(H, Hq * D, (Hq * D) ** -0.5), "w_gate_up": w(2 * I, H, H ** -0.5),
+            "w_down": w(H, I, I ** -0.5), "w_lm": w(V, H, H ** -0.5),
+            "g1": torch.ones(H, device=dev), "g2": torch.ones(H, device=dev)}
+    f0 = w(B, H, 1.0)
+    root = torch.randint(0, V, (B,), generator=gen, device=dev, dtype=torch.int32)
+    kc = torch.randn((B, Hkv, P + R, D), generator=gen, device=dev).to(torch.bfloat16)
+    vc = torch.randn((B, Hkv, P + R, D), generator=gen, device=dev).to(torch.bfloat16)
+    ws = torch.empty(max(1, sda.eagle_draft_expand_workspace(B, H, Hq, Hkv, D, I, V, P, P + R, top_k,
+                                                             depth)), dtype=torch.uint8, device=dev)
+    out = sda.eagle_draft_expand(head, f0, root, kc, vc, P, Hq, top_k, depth, n_nodes, D ** -0.5, 1e-5,
+                                 workspace=ws)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(iters):
+        sda.eagle_draft_expand(head, f0, root, kc, vc, P, Hq, top_k, depth, n_nodes, D ** -0.5, 1e-5,
+                               workspace=ws, out=out)
+    e1.record(s)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / iters
+    weights = sum(head[k].numel() * 2 for k in ("w_fc", "w_qkv", "w_o", "w_gate_up", "w_down", "w_lm"))
+    streamed = depth * weights
+    del head, kc, vc, ws, out
+    torch.cuda.empty_cache()
+    return {"shape": f"B={B} H={H} Hq={Hq} Hkv={Hkv} D={D} I={I} V={V} draft prefix {P}",
+            "top_k": top_k, "depth": depth, "n_nodes": n_nodes, "us": round(us, 1),
+            "weight_bytes_per_expansion": streamed,
+            "weight_stream_gbs": round(streamed / us / 1e3, 1),
+            "weight_stream_frac_of_hbm_peak": round(streamed / us / 1e3 / HBM_PEAK_GBS, 4)}
+
+
 RAGGED_PREFIX = [32768, 8192, 24576, 2048]
 RAGGED_TREE = [60, 40, 60, 25]
 
@@ -351,7 +406,9 @@ def ragged_step(torch, sda, dev, x, steps=20):
 
 PROFILE_RUNS = {
     "prof": "rocprofv3 --kernel-trace --stats -T -d gpurun_out/prof -o run --output-format csv "
-            "-- python -u bench.py --steps 50 --warmup 5 --no-cpu-baseline",
+            "-- python -u bench.py --steps 50 --warmup 5 --no-cpu-baseline --no-spec",
+    "prof_draft": "rocprofv3 --kernel-trace --stats -T -d gpurun_out/prof_draft -o run --output-format csv "
+                  "-- python -u bench.py --only-draft",
     "pmc_fetch": "rocprofv3 --pmc FETCH_SIZE -T -d gpurun_out/pmc_fetch -o run --output-format csv "
                  "-- python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-spec",
     "pmc_write": "rocprofv3 --pmc WRITE_SIZE -T -d gpurun_out/pmc_write -o run --output-format csv "
@@ -362,6 +419,7 @@ PROFILE_RUNS = {
                       "--output-format csv -- python -u bench.py --copy-calib",
 }
 TRACE_MD = "c5_step_kernel_trace.md"
+DRAFT_TRACE_MD = "c5_draft_expand_kernel_trace.md"
 TRAFFIC_MD = "c5_step_hbm_traffic.md"
 
 
@@ -381,9 +439,7 @@ def summarize_profiles(root):
     lines = ["# rocprofv3 kernel trace: C5 verification step", "",
              "Command (repository root, one MI355X):", "", "    " + PROFILE_RUNS["prof"], "",
              f"Workload: C5 (B={B}, N={N}, Hq={Hq}, Hkv={Hkv}, D={D}, P={P}, H={H}, V={V}); "
-             "55 steps (5 warmup + 50 timed, as bench.py times them)",
-             "plus the speculative-sampling latency loop at C4 shapes (accept_spec_kernel, "
-             "spec_init_kernel).", "",
+             "55 steps (5 warmup + 50 timed, as bench.py times them), nothing else.", "",
              "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
         lines.append(f"| {r['Name']} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
@@ -391,6 +447,25 @@ def summarize_profiles(root):
                      f"{100.0 * float(r['TotalDurationNs']) / total:.1f} |")
     with open(os.path.join(PROFILE_DIR, TRACE_MD), "w") as f:
         f.write("\n".join(lines) + "\n")
+    dpath = os.path.join(root, "prof_draft", "run_kernel_stats.csv")
+    if os.path.exists(dpath):
+        dstats = _read_csv(dpath)
+        dtotal = sum(float(r["TotalDurationNs"]) for r in dstats)
+        B_, H_, Hq_, Hkv_, D_, I_, V_, P_ = DRAFT_SHAPES["C5"]
+        dl = ["# rocprofv3 kernel trace: per-depth draft expansion, C5 shapes", "",
+              "Command (repository root, one MI355X):", "", "    " + PROFILE_RUNS["prof_draft"], "",
+              f"Workload: eagle_draft_expand with a one-layer draft head (B={B_}, H={H_}, Hq={Hq_}, "
+              f"Hkv={Hkv_}, D={D_}, MLP {I_}, V={V_}, draft prefix {P_}), top-k 10, depth 6, 60 nodes; "
+              "4 expansions (1 warmup + 3 timed).  lm_head_gemm runs every projection and the LM head "
+              "(6 GEMMs per depth).", "",
+              "| kernel | calls | avg us | total ms | share % |", "|---|---|---|---|---|"]
+        for r in sorted(dstats, key=lambda r: -float(r["TotalDurationNs"])):
+            dl.append(f"| {r['Name']} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                      f"{float(r['TotalDurationNs']) / 1e6:.3f} | "
+                      f"{100.0 * float(r['TotalDurationNs']) / dtotal:.1f} |")
+        with open(os.path.join(PROFILE_DIR, DRAFT_TRACE_MD), "w") as f:
+            f.write("\n".join(dl) + "\n")
+        lines += ["", *dl]
 
     def per_kernel(run, counter):
         acc = {}
@@ -446,7 +521,11 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-spec", action="store_true")
+    ap.add_argument("--no-spec", action="store_true",
+                    help="only the C5 step: skip the spec latency, KV commit, ragged, paged and "
+                         "draft-expansion measurements")
+    ap.add_argument("--only-draft", action="store_true",
+                    help="only the C5-shaped draft expansion (eagle_draft_expand)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--summarize-profiles", metavar="DIR",
@@ -471,6 +550,9 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     if args.copy_calib:
         copy_calibration(torch, dev)
+        return 0
+    if args.only_draft:
+        print(json.dumps({"draft_expand_C5": draft_expansion(torch, sda, dev, "C5")}))
         return 0
 
     cfg = synth.CONFIGS["C5"]
@@ -566,6 +648,7 @@ def main(argv=None):
         out["kv_commit_80_layers"] = kv_commit_latency(torch, sda, dev, tree["parents"])
         out["ragged_C5"] = ragged_step(torch, sda, dev, x)
         out["paged_attention_C5"] = paged_attention(torch, sda, dev, x, tree["parents"])
+        out["draft_expand_C5"] = draft_expansion(torch, sda, dev, "C5")
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg)

@@ -12,6 +12,9 @@
  * sequences have different prefix and tree sizes, a _paged form of the attention
  * for KV caches kept in fixed-size pages, and, after acceptance:
  *   eagle_kv_commit        move the accepted path's K/V rows to the end of the prefix
+ * and, before the step, the draft side that feeds eagle2_rerank:
+ *   eagle_draft_expand     grow the EAGLE-2 draft tree depth by depth with a one-layer
+ *                          draft head and the frozen LM head
  *
  * Sources (web pages on the method), cited per call below:
  *   [P1] "大模型推理效率突破：EAGLE推测解码算法在摩尔线程GPU的实践与优化" (adg.csdn.net)
@@ -276,6 +279,71 @@ eagle_status_t eagle2_rerank(const float* draft_logits, const int32_t* root_toke
                              int32_t* tokens, int32_t* parents, int32_t* depths, float* scores,
                              int32_t* draft_row, float* draft_lse, void* workspace,
                              size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Per-depth EAGLE-2 draft expansion.  [P2] auto-regression head and workflow
+ * paragraphs (the head reads the parent's feature and the embedding of the node's
+ * token, predicts the node's feature, and the target's frozen LM head gives the next
+ * token distribution; repeated, this grows the draft tree); [P2] training paragraph
+ * (the head is one transformer layer); [P3] section 2 (dynamic tree under a token
+ * budget).  The layer, for expansion row r with parent feature f and token t:
+ *     u = [f ; E[t]];  x = W_fc u;  a = rms(x) g1;  q, k, v = W_qkv a
+ *     h = x + W_o Attn_r(q, k, v);  b = rms(h) g2
+ *     y = h + W_down( silu(W_gate b) * (W_up b) );  logits_r = W_lm y
+ * rms(z) = z / sqrt(mean(z^2) + eps); GEMM inputs are bf16, accumulation and the
+ * residual stream fp32, y is stored in bf16.  Attn_r: grouped-query attention with
+ * the given scale over the draft cache's prefix rows 0..P-1 and the rows P + a of the
+ * ancestors a of r in the expansion (itself included); no position encoding.
+ *
+ * Rows: row 0 is the root (feature f0[b], token root_token[b]); depth by depth, the
+ * top_k best candidates of depth d (by cumulative log-probability, ties to the lower
+ * candidate id, exactly as eagle2_rerank ranks them) take rows 1 + (d-1)*top_k + j,
+ * read the feature y of the row that proposed them and run the head.  Row r's
+ * logits are written to draft_logits[b][r]; after the last depth the tree is built
+ * from them as eagle2_rerank would (same outputs), so the tree, draft_logits and
+ * draft_lse can go straight to eagle_tree_verify_attn / eagle_accept_spec.
+ *
+ *   head: the weights, bf16 row-major ([out][in], 16-byte aligned) except the fp32
+ *     gains: embed [V][H]; w_fc [H][2H]; w_qkv [(Hq + 2 Hkv) D][H] (q rows, then k
+ *     rows, then v rows, head-major); w_o [H][Hq D]; w_gate_up [2I][H] (gate rows,
+ *     then up rows); w_down [H][I]; w_lm [V][H] (the frozen LM head); g1, g2 [H]
+ *   f0 bf16 [B][H]: the target's feature at the root; root_token int32 [B]
+ *   k_cache, v_cache bf16 [B][Hkv][kv_cap][D]: the draft layer's cache; rows 0..P-1
+ *     are read, rows P .. P + R - 1 (R = 1 + (depth-1)*top_k) are overwritten with
+ *     the expansion rows' keys and values; kv_cap >= P + R
+ *   H, I multiples of 64; D in {64, 128}; Hq % Hkv == 0; R <= 64; the eagle2_rerank
+ *     limits on V, top_k, depth, n_nodes
+ *   outputs: tokens, parents, depths, scores, draft_row [B][n_nodes] and draft_lse
+ *     [B][R] as eagle2_rerank; draft_logits fp32 [B][R][V]; features bf16 [B][R][H]
+ *     (y of every row); row_token, parent_row int32 [B][R] (the token of each row and
+ *     the row that proposed it; -1 for the root)
+ * Workspace: eagle_draft_expand_workspace(B, H, Hq, Hkv, D, I, V, P, kv_cap, top_k,
+ * depth) bytes (0 for invalid sizes).  All launches go to `stream`.
+ */
+typedef struct {
+  const void* embed;
+  const void* w_fc;
+  const void* w_qkv;
+  const void* w_o;
+  const void* w_gate_up;
+  const void* w_down;
+  const void* w_lm;
+  const float* g1;
+  const float* g2;
+} eagle_draft_head;
+
+size_t eagle_draft_expand_workspace(int32_t B, int32_t H, int32_t Hq, int32_t Hkv, int32_t D,
+                                    int32_t I, int32_t V, int32_t P, int32_t kv_cap, int32_t top_k,
+                                    int32_t depth);
+eagle_status_t eagle_draft_expand(const eagle_draft_head* head, const void* f0,
+                                  const int32_t* root_token, void* k_cache, void* v_cache, int32_t B,
+                                  int32_t H, int32_t Hq, int32_t Hkv, int32_t D, int32_t I, int32_t V,
+                                  int32_t P, int32_t kv_cap, int32_t top_k, int32_t depth,
+                                  int32_t n_nodes, float scale, float eps, int32_t* tokens,
+                                  int32_t* parents, int32_t* depths, float* scores,
+                                  int32_t* draft_row, float* draft_logits, float* draft_lse,
+                                  void* features, int32_t* row_token, int32_t* parent_row,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * KV-cache commit after acceptance.  [P3] section 4 (limitations: the dynamic

@@ -60,7 +60,16 @@ _SIGNATURES = {
                                  + [_vp] * 4 + [_sz, _vp], ctypes.c_int),
     "eagle2_rerank_workspace": ([_i32] * 4, _sz),
     "eagle2_rerank": ([_vp, _vp] + [_i32] * 5 + [_vp] * 7 + [_sz, _vp], ctypes.c_int),
+    "eagle_draft_expand_workspace": ([_i32] * 11, _sz),
+    "eagle_draft_expand": ([_vp] * 5 + [_i32] * 12 + [_f32, _f32] + [_vp] * 11 + [_sz, _vp],
+                           ctypes.c_int),
 }
+
+
+class DraftHead(ctypes.Structure):
+    """The C struct eagle_draft_head: device pointers of the draft head's weights."""
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("embed", "w_fc", "w_qkv", "w_o", "w_gate_up", "w_down", "w_lm", "g1", "g2")]
 
 
 def load(path: Optional[str] = None):
@@ -76,6 +85,7 @@ def load(path: Optional[str] = None):
         f = getattr(lib, name)
         f.argtypes = args
         f.restype = res
+    lib.eagle_draft_expand.argtypes = [ctypes.POINTER(DraftHead)] + _SIGNATURES["eagle_draft_expand"][0][1:]
     _lib = lib
     return lib
 
@@ -380,4 +390,66 @@ def eagle2_rerank(draft_logits: torch.Tensor, root_token: torch.Tensor, top_k: i
                            res["draft_row"].data_ptr(), res["draft_lse"].data_ptr(),
                            workspace.data_ptr(), workspace.numel(), _stream())
     _check(st, "eagle2_rerank")
+    return res
+
+
+DRAFT_HEAD_KEYS = ("embed", "w_fc", "w_qkv", "w_o", "w_gate_up", "w_down", "w_lm")
+
+
+def eagle_draft_expand_workspace(B, H, Hq, Hkv, D, I, V, P, kv_cap, top_k, depth) -> int:
+    return load().eagle_draft_expand_workspace(B, H, Hq, Hkv, D, I, V, P, kv_cap, top_k, depth)
+
+
+def eagle_draft_expand(head: dict, f0: torch.Tensor, root_token: torch.Tensor, k_cache: torch.Tensor,
+                       v_cache: torch.Tensor, P: int, Hq: int, top_k: int, depth: int, n_nodes: int,
+                       scale: float, eps: float, workspace: Optional[torch.Tensor] = None,
+                       out: Optional[dict] = None):
+    """Per-depth EAGLE-2 draft expansion with a one-layer draft head.
+
+    head: dict of device tensors embed [V][H], w_fc [H][2H], w_qkv [(Hq+2Hkv)D][H],
+    w_o [H][Hq D], w_gate_up [2I][H], w_down [H][I], w_lm [V][H] (bf16) and g1, g2 [H]
+    (fp32).  f0 [B][H] bf16; root_token [B] int32; k_cache, v_cache [B][Hkv][kv_cap][D]
+    bf16 (rows P.. are overwritten).  Returns dict(tokens, parents, depths, scores,
+    draft_row, draft_logits, draft_lse, features, row_token, parent_row)."""
+    lib = load()
+    dev = f0.device
+    for name in DRAFT_HEAD_KEYS:
+        _need(head[name], name, torch.bfloat16, dev)
+    for name in ("g1", "g2"):
+        _need(head[name], name, torch.float32, dev)
+    _need(f0, "f0", torch.bfloat16, dev)
+    _need(root_token, "root_token", torch.int32, dev)
+    _need(k_cache, "k_cache", torch.bfloat16, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, dev)
+    B, H = f0.shape
+    V = head["embed"].shape[0]
+    I = head["w_down"].shape[1]
+    _, Hkv, kv_cap, D = k_cache.shape
+    R = 1 + (depth - 1) * top_k
+    f = dict(device=dev)
+    res = out if out is not None else {
+        "tokens": torch.empty((B, n_nodes), dtype=torch.int32, **f),
+        "parents": torch.empty((B, n_nodes), dtype=torch.int32, **f),
+        "depths": torch.empty((B, n_nodes), dtype=torch.int32, **f),
+        "scores": torch.empty((B, n_nodes), dtype=torch.float32, **f),
+        "draft_row": torch.empty((B, n_nodes), dtype=torch.int32, **f),
+        "draft_logits": torch.empty((B, R, V), dtype=torch.float32, **f),
+        "draft_lse": torch.empty((B, R), dtype=torch.float32, **f),
+        "features": torch.empty((B, R, H), dtype=torch.bfloat16, **f),
+        "row_token": torch.empty((B, R), dtype=torch.int32, **f),
+        "parent_row": torch.empty((B, R), dtype=torch.int32, **f)}
+    if workspace is None:
+        workspace = _workspace(lib.eagle_draft_expand_workspace(B, H, Hq, Hkv, D, I, V, P, kv_cap,
+                                                                top_k, depth), dev)
+    hd = DraftHead(*[head[k].data_ptr() for k in DRAFT_HEAD_KEYS + ("g1", "g2")])
+    st = lib.eagle_draft_expand(ctypes.byref(hd), f0.data_ptr(), root_token.data_ptr(),
+                                k_cache.data_ptr(), v_cache.data_ptr(), B, H, Hq, Hkv, D, I, V, P,
+                                kv_cap, top_k, depth, n_nodes, scale, eps, res["tokens"].data_ptr(),
+                                res["parents"].data_ptr(), res["depths"].data_ptr(),
+                                res["scores"].data_ptr(), res["draft_row"].data_ptr(),
+                                res["draft_logits"].data_ptr(), res["draft_lse"].data_ptr(),
+                                res["features"].data_ptr(), res["row_token"].data_ptr(),
+                                res["parent_row"].data_ptr(), workspace.data_ptr(),
+                                workspace.numel(), _stream())
+    _check(st, "eagle_draft_expand")
     return res

@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libeagle_mi355.so")
-SOURCES = ["api.hip", "tree_attn.hip", "lm_head.hip", "accept.hip", "rerank.hip", "kv_commit.hip"]
+SOURCES = ["api.hip", "tree_attn.hip", "lm_head.hip", "accept.hip", "rerank.hip", "kv_commit.hip",
+           "draft.hip"]
 ARCH = "gfx950"
 
 

@@ -368,6 +368,181 @@ eagle_status_t eagle2_rerank(const float* draft_logits, const int32_t* root_toke
                     "eagle2_rerank launch");
 }
 
+// ---------------------------------------------------------------- draft expansion
+namespace {
+
+struct DraftLayout {
+  eagle::DraftDims dd;
+  eagle::RerankPlan rpl;
+  int Mmax, maxN, maxW;
+  size_t off_rerank, off_X, off_G, off_x, off_h, off_n, off_y, off_q, off_att, off_attws, off_stats,
+      off_lm, total;
+  size_t attn_ws, lm_ws;
+};
+
+size_t a256(size_t x) { return (x + 255) / 256 * 256; }
+
+DraftLayout draft_layout(int B, int H, int Hq, int Hkv, int D, int I, int V, int P, int kv_cap,
+                         int top_k, int depth, int n_nodes) {
+  DraftLayout L{};
+  const int R = 1 + (depth - 1) * top_k;
+  L.dd = eagle::DraftDims{B, H, Hq, Hkv, D, I, V, P, kv_cap, R};
+  L.rpl = eagle::plan_rerank(B, V, top_k, depth, n_nodes);
+  L.Mmax = B * (depth > 1 ? top_k : 1);
+  const int qkvn = (Hq + 2 * Hkv) * D;
+  L.maxN = V;
+  for (int n : {H, qkvn, 2 * I}) L.maxN = n > L.maxN ? n : L.maxN;
+  L.maxW = H;
+  for (int w : {Hq * D, I}) L.maxW = w > L.maxW ? w : L.maxW;
+  // the attention runs over all R rows of the expansion at every depth
+  L.attn_ws = eagle::tree_attn_workspace_bytes(eagle::plan_tree_attn(B, R, Hq, Hkv, D, P, kv_cap));
+  L.lm_ws = 0;
+  const int shapes[5][2] = {{2 * H, H}, {H, qkvn}, {Hq * D, H}, {H, 2 * I}, {I, H}};
+  for (int m : {B, L.Mmax}) {
+    for (auto& kn : shapes) {
+      const size_t w = eagle::lm_head_workspace_bytes(eagle::plan_lm_head(m, kn[0], kn[1]));
+      L.lm_ws = w > L.lm_ws ? w : L.lm_ws;
+    }
+    const size_t w = eagle::lm_head_workspace_bytes(eagle::plan_lm_head(m, H, V));
+    L.lm_ws = w > L.lm_ws ? w : L.lm_ws;
+  }
+  const size_t M = L.Mmax;
+  size_t o = 0;
+  L.off_rerank = o; o += a256(eagle::rerank_workspace_bytes(L.rpl));
+  L.off_X = o;      o += a256(M * 2 * H * 2);
+  L.off_G = o;      o += a256(M * (size_t)L.maxN * 4);
+  L.off_x = o;      o += a256(M * H * 4);
+  L.off_h = o;      o += a256(M * H * 4);
+  L.off_n = o;      o += a256(M * (size_t)L.maxW * 2);
+  L.off_y = o;      o += a256(M * H * 2);
+  L.off_q = o;      o += a256((size_t)B * R * Hq * D * 2);
+  L.off_att = o;    o += a256((size_t)B * R * Hq * D * 2);
+  L.off_attws = o;  o += a256(L.attn_ws);
+  L.off_stats = o;  o += a256(M * 12);
+  L.off_lm = o;     o += a256(L.lm_ws);
+  L.total = o + 256;
+  return L;
+}
+
+eagle_status_t check_draft_dims(int32_t B, int32_t H, int32_t Hq, int32_t Hkv, int32_t D, int32_t I,
+                                int32_t V, int32_t P, int32_t top_k, int32_t depth, int32_t n_nodes) {
+  if (B < 1 || H < 1 || Hq < 1 || Hkv < 1 || I < 1 || V < 2 || P < 0)
+    return fail(EAGLE_ERR_INVALID_ARG, "need B, H, Hq, Hkv, I >= 1, V >= 2, P >= 0");
+  if (H % 64 || I % 64)
+    return fail(EAGLE_ERR_UNSUPPORTED, "H=%d and I=%d must be multiples of 64", H, I);
+  if (Hq % Hkv) return fail(EAGLE_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (D != 64 && D != 128) return fail(EAGLE_ERR_UNSUPPORTED, "D=%d (supported: 64, 128)", D);
+  eagle_status_t st = check_rerank_dims(B, V, top_k, depth, n_nodes);
+  if (st != EAGLE_OK) return st;
+  const long long R = 1 + (long long)(depth - 1) * top_k;
+  if (R > EAGLE_MAX_TREE)
+    return fail(EAGLE_ERR_UNSUPPORTED, "1 + (depth-1)*top_k = %lld expansion rows > %d", R, EAGLE_MAX_TREE);
+  return EAGLE_OK;
+}
+
+hipError_t draft_gemm(int M, int K, int N, const void* X, const void* W, float* out, char* ws,
+                      const DraftLayout& L, hipStream_t stream) {
+  const eagle::LmPlan pl = eagle::plan_lm_head(M, K, N);
+  float* st = (float*)(ws + L.off_stats);
+  return eagle::launch_lm_head(pl, X, W, st, (int32_t*)(st + L.Mmax), st + 2 * L.Mmax, nullptr, out,
+                               ws + L.off_lm, stream);
+}
+
+}  // namespace
+
+size_t eagle_draft_expand_workspace(int32_t B, int32_t H, int32_t Hq, int32_t Hkv, int32_t D,
+                                    int32_t I, int32_t V, int32_t P, int32_t kv_cap, int32_t top_k,
+                                    int32_t depth) {
+  if (B < 1 || H < 1 || Hq < 1 || Hkv < 1 || I < 1 || V < 2 || P < 0 || top_k < 1 || depth < 1 ||
+      top_k > EAGLE_MAX_TOPK || Hq % Hkv || (D != 64 && D != 128) || kv_cap < P)
+    return 0;
+  return draft_layout(B, H, Hq, Hkv, D, I, V, P, kv_cap, top_k, depth, 1).total;
+}
+
+eagle_status_t eagle_draft_expand(const eagle_draft_head* head, const void* f0,
+                                  const int32_t* root_token, void* k_cache, void* v_cache, int32_t B,
+                                  int32_t H, int32_t Hq, int32_t Hkv, int32_t D, int32_t I, int32_t V,
+                                  int32_t P, int32_t kv_cap, int32_t top_k, int32_t depth,
+                                  int32_t n_nodes, float scale, float eps, int32_t* tokens,
+                                  int32_t* parents, int32_t* depths, float* scores,
+                                  int32_t* draft_row, float* draft_logits, float* draft_lse,
+                                  void* features, int32_t* row_token, int32_t* parent_row,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!head || !head->embed || !head->w_fc || !head->w_qkv || !head->w_o || !head->w_gate_up ||
+      !head->w_down || !head->w_lm || !head->g1 || !head->g2)
+    return fail(EAGLE_ERR_NULL, "every draft-head pointer must be non-NULL");
+  if (!f0 || !root_token || !k_cache || !v_cache || !tokens || !parents || !depths || !scores ||
+      !draft_row || !draft_logits || !draft_lse || !features || !row_token || !parent_row)
+    return fail(EAGLE_ERR_NULL, "all pointers must be non-NULL");
+  eagle_status_t st = check_draft_dims(B, H, Hq, Hkv, D, I, V, P, top_k, depth, n_nodes);
+  if (st != EAGLE_OK) return st;
+  const int R = 1 + (depth - 1) * top_k;
+  if (kv_cap < P + R)
+    return fail(EAGLE_ERR_INVALID_ARG, "kv_cap=%d < P + expansion rows = %d", kv_cap, P + R);
+  const void* const must_align[] = {head->embed, head->w_fc,  head->w_qkv, head->w_o,
+                                    head->w_gate_up, head->w_down, head->w_lm, f0,
+                                    features,    k_cache,     v_cache,     draft_logits};
+  for (const void* p : must_align)
+    if (!aligned16(p)) return fail(EAGLE_ERR_INVALID_ARG, "weights, f0, caches, features and draft_logits must be 16-byte aligned");
+  const DraftLayout L = draft_layout(B, H, Hq, Hkv, D, I, V, P, kv_cap, top_k, depth, n_nodes);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(EAGLE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, L.total);
+  if (!aligned16(workspace)) return fail(EAGLE_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+
+  char* ws = (char*)workspace;
+  void* X = ws + L.off_X;
+  float* G = (float*)(ws + L.off_G);
+  float* xres = (float*)(ws + L.off_x);
+  float* hres = (float*)(ws + L.off_h);
+  void* nb = ws + L.off_n;
+  void* yb = ws + L.off_y;
+  void* qbuf = ws + L.off_q;
+  void* att = ws + L.off_att;
+  void* rws = ws + L.off_rerank;
+  const eagle::DraftDims& dd = L.dd;
+  const int qkvn = (Hq + 2 * Hkv) * D;
+  eagle::AttnPlan apl = eagle::plan_tree_attn(B, R, Hq, Hkv, D, P, kv_cap);
+#define DRAFT_TRY(expr, what)                                   \
+  do {                                                          \
+    const hipError_t e_ = (expr);                               \
+    if (e_ != hipSuccess) return hip_status(e_, what);          \
+  } while (0)
+  DRAFT_TRY(eagle::launch_draft_init_rows(B, R, root_token, row_token, parent_row, stream), "draft init");
+  for (int d = 0; d < depth; ++d) {
+    const int row0 = d == 0 ? 0 : 1 + (d - 1) * top_k;
+    const int nr = d == 0 ? 1 : top_k;
+    const int M = B * nr;
+    if (d > 0)
+      DRAFT_TRY(eagle::launch_draft_frontier(L.rpl, d, draft_lse, rws, row_token, parent_row, stream),
+                "draft frontier");
+    DRAFT_TRY(eagle::launch_draft_gather_input(dd, row0, nr, f0, root_token, head->embed, features,
+                                               row_token, parent_row, X, stream), "draft gather");
+    DRAFT_TRY(draft_gemm(M, 2 * H, H, X, head->w_fc, G, ws, L, stream), "draft fc");
+    DRAFT_TRY(eagle::launch_draft_rms(M, H, eps, G, H, nullptr, head->g1, xres, nb, stream), "draft norm 1");
+    DRAFT_TRY(draft_gemm(M, H, qkvn, nb, head->w_qkv, G, ws, L, stream), "draft qkv");
+    DRAFT_TRY(eagle::launch_draft_qkv_scatter(dd, row0, nr, G, qbuf, k_cache, v_cache, stream), "draft scatter");
+    DRAFT_TRY(eagle::launch_tree_attn(apl, scale, qbuf, k_cache, v_cache, parent_row, att, nullptr,
+                                      ws + L.off_attws, stream), "draft attention");
+    DRAFT_TRY(eagle::launch_draft_gather_rows(dd, row0, nr, Hq * D, att, nb, stream), "draft gather rows");
+    DRAFT_TRY(draft_gemm(M, Hq * D, H, nb, head->w_o, G, ws, L, stream), "draft o");
+    DRAFT_TRY(eagle::launch_draft_rms(M, H, eps, G, H, xres, head->g2, hres, nb, stream), "draft norm 2");
+    DRAFT_TRY(draft_gemm(M, H, 2 * I, nb, head->w_gate_up, G, ws, L, stream), "draft gate/up");
+    DRAFT_TRY(eagle::launch_draft_silu_mul(M, I, G, nb, stream), "draft silu");
+    DRAFT_TRY(draft_gemm(M, I, H, nb, head->w_down, G, ws, L, stream), "draft down");
+    DRAFT_TRY(eagle::launch_draft_output(dd, row0, nr, G, hres, yb, features, stream), "draft output");
+    DRAFT_TRY(draft_gemm(M, H, V, yb, head->w_lm, G, ws, L, stream), "draft lm head");
+    DRAFT_TRY(eagle::launch_draft_place_logits(dd, row0, nr, G, draft_logits, stream), "draft place");
+    eagle::RerankPlan rp = L.rpl;
+    rp.row0 = row0;
+    rp.nrows = nr;
+    DRAFT_TRY(eagle::launch_rerank_rows(rp, draft_logits, draft_lse, rws, stream), "draft rows");
+  }
+  DRAFT_TRY(eagle::launch_rerank_tree(L.rpl, root_token, draft_lse, rws, tokens, parents, depths,
+                                      scores, draft_row, stream), "draft tree");
+#undef DRAFT_TRY
+  return ok();
+}
+
 // ---------------------------------------------------------------- KV commit
 eagle_status_t eagle_kv_commit(void* k_cache, void* v_cache, const int32_t* accept_len,
                                const int32_t* accept_path, int32_t L, int32_t B, int32_t Hkv,

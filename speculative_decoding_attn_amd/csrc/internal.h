@@ -86,6 +86,7 @@ struct RerankPlan {
   int B, V, k, depth, R, n_nodes;
   int chunks;     // vocabulary chunks per row for the top-k / log-sum-exp pass
   int chunk_len;  // vocabulary entries per chunk
+  int row0, nrows;   // rows row0 .. row0+nrows-1 of every sequence take the row pass
 };
 RerankPlan plan_rerank(int B, int V, int top_k, int depth, int n_nodes);
 size_t rerank_workspace_bytes(const RerankPlan& pl);
@@ -103,6 +104,40 @@ hipError_t launch_kv_commit(void* k_cache, void* v_cache, const int32_t* accept_
 
 namespace eagle {
 int rerank_max_candidates();
+// per-depth draft expansion: the row pass over rows [row0, row0 + nrows) of every
+// sequence (plan with those fields set), and the frontier of depth d (d >= 1): for
+// slot j, row r = 1 + (d-1)*k + j gets the token of the j-th best depth-d candidate
+// and the row of the node that proposed it (0 for the root)
+hipError_t launch_rerank_rows(const RerankPlan& pl, const float* draft_logits, float* draft_lse,
+                              void* workspace, hipStream_t stream);
+hipError_t launch_rerank_tree(const RerankPlan& pl, const int32_t* root_token, const float* draft_lse,
+                              void* workspace, int32_t* tokens, int32_t* parents, int32_t* depths,
+                              float* scores, int32_t* draft_row, hipStream_t stream);
+hipError_t launch_draft_frontier(const RerankPlan& pl, int d, const float* draft_lse, void* workspace,
+                                 int32_t* row_token, int32_t* parent_row, hipStream_t stream);
 int rerank_max_row_list();   // R * top_k limit (also caps R at 512 and chunks * top_k at 1024)
 
+// per-depth draft expansion (draft.hip): sizes shared by the glue kernels
+struct DraftDims {
+  int B, H, Hq, Hkv, D, I, V, P, kv_cap, R;
+};
+hipError_t launch_draft_gather_input(const DraftDims& dd, int row0, int nr, const void* f0,
+                                     const int32_t* root_token, const void* embed, const void* feats,
+                                     const int32_t* row_token, const int32_t* parent_row, void* X,
+                                     hipStream_t s);
+hipError_t launch_draft_rms(int M, int H, float eps, const float* a, int lda, const float* res,
+                            const float* gain, float* res_out, void* norm_out, hipStream_t s);
+hipError_t launch_draft_qkv_scatter(const DraftDims& dd, int row0, int nr, const float* qkv, void* qbuf,
+                                    void* k_cache, void* v_cache, hipStream_t s);
+hipError_t launch_draft_gather_rows(const DraftDims& dd, int row0, int nr, int width, const void* src,
+                                    void* dst, hipStream_t s);
+hipError_t launch_draft_silu_mul(int M, int I, const float* gu, void* z, hipStream_t s);
+hipError_t launch_draft_output(const DraftDims& dd, int row0, int nr, const float* d, const float* h,
+                               void* y, void* feats, hipStream_t s);
+hipError_t launch_draft_place_logits(const DraftDims& dd, int row0, int nr, const float* src,
+                                     float* draft_logits, hipStream_t s);
+hipError_t launch_draft_init_rows(int B, int R, const int32_t* root_token, int32_t* row_token,
+                                  int32_t* parent_row, hipStream_t s);
+
 }  // namespace eagle
+

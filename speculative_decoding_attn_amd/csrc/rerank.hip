@@ -127,7 +127,8 @@ rerank_rows(const float* __restrict__ logits, RerankPlan pl, void* ws) {
   __shared__ VI red[kRowThreads / 64];
   RrWs w = rr_ws(ws, pl);
   const int chunk = blockIdx.x % pl.chunks;
-  const size_t row = blockIdx.x / pl.chunks;
+  const int rr = blockIdx.x / pl.chunks;   // rr-th processed row: sequence rr / nrows
+  const size_t row = (size_t)(rr / pl.nrows) * pl.R + pl.row0 + rr % pl.nrows;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int V = pl.V;
   const int x0 = chunk * pl.chunk_len;
@@ -189,10 +190,10 @@ rerank_rows(const float* __restrict__ logits, RerankPlan pl, void* ws) {
   if (tid == 0) {
     float zt = 0.f;
     for (int i = 0; i < kRowThreads / 64; ++i) zt += redf[i];
-    w.chunk_mz[blockIdx.x] = make_float2(mx, zt);
+    w.chunk_mz[row * pl.chunks + chunk] = make_float2(mx, zt);
   }
-  float* out_v = w.chunk_v + (size_t)blockIdx.x * k;
-  int* out_i = w.chunk_i + (size_t)blockIdx.x * k;
+  float* out_v = w.chunk_v + (row * pl.chunks + chunk) * k;
+  int* out_i = w.chunk_i + (row * pl.chunks + chunk) * k;
   if (ncand <= kCandCap) {
     int pos = off + pre;
 #pragma unroll
@@ -263,8 +264,9 @@ rerank_merge(RerankPlan pl, void* ws, float* __restrict__ draft_lse) {
   __shared__ uint64_t keys[4][1024];
   RrWs w = rr_ws(ws, pl);
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int row = blockIdx.x * 4 + wid;
-  if (row >= pl.B * pl.R) return;
+  const int rr = blockIdx.x * 4 + wid;
+  if (rr >= pl.B * pl.nrows) return;
+  const int row = (rr / pl.nrows) * pl.R + pl.row0 + rr % pl.nrows;
   const int k = pl.k, chunks = pl.chunks;
   float mx = -INFINITY;
   for (int c = lane; c < chunks; c += 64) mx = fmaxf(mx, w.chunk_mz[(size_t)row * chunks + c].x);
@@ -329,64 +331,69 @@ __device__ __forceinline__ int rank_in(const uint64_t* keys, int lb, int n, uint
   return rank;
 }
 
-__global__ void __launch_bounds__(kTreeThreads)
-rerank_tree(RerankPlan pl, const int32_t* __restrict__ root_token, const float* __restrict__ draft_lse,
-            void* ws, int32_t* __restrict__ tokens, int32_t* __restrict__ parents,
-            int32_t* __restrict__ depths, float* __restrict__ scores, int32_t* __restrict__ draft_row) {
-  __shared__ float c_score[kMaxCand];
-  __shared__ uint64_t c_key[kMaxCand];
-  __shared__ int c_tok[kMaxCand];
-  __shared__ short c_par[kMaxCand];
-  __shared__ short c_row[kMaxCand];
-  __shared__ short c_pos[kMaxCand];
+// Candidate arrays of one sequence in LDS, and the candidates of levels 1..L: level
+// 1 = the root's proposals; level d+1 = the proposals of the frontier of level d (its
+// best k candidates, which take rows 1 + (d-1)k .. in rank order).  Needs the row
+// lists and normalisers of rows 0 .. 1 + (L-2)k + k-1.
+struct TreeLds {
+  float c_score[kMaxCand];
+  uint64_t c_key[kMaxCand];
+  int c_tok[kMaxCand];
+  short c_par[kMaxCand];
+  short c_row[kMaxCand];
+  short c_pos[kMaxCand];
+  float s_rv[kMaxRowList];
+  int s_ri[kMaxRowList];
+  float s_lse[kMaxRows];
+};
 
-  __shared__ float s_rv[kMaxRowList];
-  __shared__ int s_ri[kMaxRowList];
-  __shared__ float s_lse[kMaxRows];
-
-  RrWs w = rr_ws(ws, pl);
-  const int b = blockIdx.x;
-  const int tid = threadIdx.x;
+// stages the sequence's row lists (rows 0..nrows-1) and normalisers
+__device__ void stage_rows(const RerankPlan& pl, const RrWs& w, const float* draft_lse, int b,
+                           int nrows, TreeLds& t) {
   const int k = pl.k, R = pl.R;
-  const int total = k + (pl.depth - 1) * k * k;
-  // the sequence's row lists and normalisers, staged once in LDS
-  for (int e = tid; e < R * k; e += kTreeThreads) {
-    s_rv[e] = w.row_v[(size_t)b * R * k + e];
-    s_ri[e] = w.row_i[(size_t)b * R * k + e];
+  for (int e = threadIdx.x; e < nrows * k; e += kTreeThreads) {
+    t.s_rv[e] = w.row_v[(size_t)b * R * k + e];
+    t.s_ri[e] = w.row_i[(size_t)b * R * k + e];
   }
-  for (int r = tid; r < R; r += kTreeThreads) s_lse[r] = draft_lse[(size_t)b * R + r];
+  for (int r = threadIdx.x; r < nrows; r += kTreeThreads) t.s_lse[r] = draft_lse[(size_t)b * R + r];
   __syncthreads();
-  const float* rv = s_rv;
-  const int* ri = s_ri;
-  const float* lse = s_lse;
+}
 
-  for (int c = tid; c < total; c += kTreeThreads) c_row[c] = -1;
-  // depth 1: the root's proposals
+// candidates of levels 1..L (ids: level 1 = [0, k), level d+1 = [k + (d-1)k^2, k + d k^2))
+// and the frontier rows of levels 1..L-1 (c_row, -1 elsewhere)
+__device__ void grow_levels(const RerankPlan& pl, int L, TreeLds& t) {
+  const int tid = threadIdx.x;
+  const int k = pl.k;
+  const int total = k + (L - 1) * k * k;
+  const float* rv = t.s_rv;
+  const int* ri = t.s_ri;
+  const float* lse = t.s_lse;
+  for (int c = tid; c < total; c += kTreeThreads) t.c_row[c] = -1;
   for (int r = tid; r < k; r += kTreeThreads) {
-    c_score[r] = rv[r] - lse[0];
-    c_tok[r] = ri[r];
-    c_par[r] = -1;
+    t.c_score[r] = rv[r] - lse[0];
+    t.c_tok[r] = ri[r];
+    t.c_par[r] = -1;
   }
   __syncthreads();
   int lb = 0, ln = k, base = k;
-  for (int d = 1; d < pl.depth; ++d) {
+  for (int d = 1; d < L; ++d) {
     // frontier: rank within the level
-    for (int c = lb + tid; c < lb + ln; c += kTreeThreads) c_key[c] = vi_key(c_score[c], c);
+    for (int c = lb + tid; c < lb + ln; c += kTreeThreads) t.c_key[c] = vi_key(t.c_score[c], c);
     __syncthreads();
     for (int c = lb + tid; c < lb + ln; c += kTreeThreads) {
-      const int rank = rank_in(c_key, lb, ln, c_key[c]);
-      if (rank < k) c_row[c] = (short)(1 + (d - 1) * k + rank);
+      const int rank = rank_in(t.c_key, lb, ln, t.c_key[c]);
+      if (rank < k) t.c_row[c] = (short)(1 + (d - 1) * k + rank);
     }
     __syncthreads();
     for (int c = lb + tid; c < lb + ln; c += kTreeThreads) {
-      const int row = c_row[c];
+      const int row = t.c_row[c];
       if (row < 0) continue;
       const int slot = row - (1 + (d - 1) * k);
       for (int r = 0; r < k; ++r) {
         const int id = base + slot * k + r;
-        c_score[id] = c_score[c] + (rv[(size_t)row * k + r] - lse[row]);
-        c_tok[id] = ri[(size_t)row * k + r];
-        c_par[id] = (short)c;
+        t.c_score[id] = t.c_score[c] + (rv[(size_t)row * k + r] - lse[row]);
+        t.c_tok[id] = ri[(size_t)row * k + r];
+        t.c_par[id] = (short)c;
       }
     }
     __syncthreads();
@@ -394,13 +401,27 @@ rerank_tree(RerankPlan pl, const int32_t* __restrict__ root_token, const float* 
     ln = k * k;
     base += k * k;
   }
+}
+
+__global__ void __launch_bounds__(kTreeThreads)
+rerank_tree(RerankPlan pl, const int32_t* __restrict__ root_token, const float* __restrict__ draft_lse,
+            void* ws, int32_t* __restrict__ tokens, int32_t* __restrict__ parents,
+            int32_t* __restrict__ depths, float* __restrict__ scores, int32_t* __restrict__ draft_row) {
+  __shared__ TreeLds t;
+  RrWs w = rr_ws(ws, pl);
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int k = pl.k;
+  const int total = k + (pl.depth - 1) * k * k;
+  stage_rows(pl, w, draft_lse, b, pl.R, t);
+  grow_levels(pl, pl.depth, t);
   // final selection by overall rank, then breadth-first positions
   const int keep = pl.n_nodes - 1;
-  for (int c = tid; c < total; c += kTreeThreads) c_key[c] = vi_key(c_score[c], c);
+  for (int c = tid; c < total; c += kTreeThreads) t.c_key[c] = vi_key(t.c_score[c], c);
   __syncthreads();
   for (int c = tid; c < total; c += kTreeThreads) {
-    const int rank = rank_in(c_key, 0, total, c_key[c]);
-    c_pos[c] = (short)(rank < keep ? 1 : 0);
+    const int rank = rank_in(t.c_key, 0, total, t.c_key[c]);
+    t.c_pos[c] = (short)(rank < keep ? 1 : 0);
   }
   __syncthreads();
   // breadth-first positions: 1 + number of selected candidates with a smaller id
@@ -408,9 +429,9 @@ rerank_tree(RerankPlan pl, const int32_t* __restrict__ root_token, const float* 
     int run = 0;
     for (int base = 0; base < total; base += 64) {
       const int c = base + tid;
-      const bool sel = c < total && c_pos[c] != 0;
+      const bool sel = c < total && t.c_pos[c] != 0;
       const uint64_t m = __ballot(sel);
-      if (sel) c_pos[c] = (short)(1 + run + __popcll(m & ((1ull << tid) - 1ull)));
+      if (sel) t.c_pos[c] = (short)(1 + run + __popcll(m & ((1ull << tid) - 1ull)));
       run += __popcll(m);
     }
   }
@@ -423,17 +444,44 @@ rerank_tree(RerankPlan pl, const int32_t* __restrict__ root_token, const float* 
     scores[ob] = 0.f;
     draft_row[ob] = 0;
   }
-  // depth of a candidate from its id: level 1 = [0, k), level d+1 = [k + (d-1)k^2, k + d k^2)
   for (int c = tid; c < total; c += kTreeThreads) {
-    const int pos = c_pos[c];
+    const int pos = t.c_pos[c];
     if (pos == 0) continue;
     const int dep = c < k ? 1 : 2 + (c - k) / (k * k);
-    const int pc = c_par[c];
-    tokens[ob + pos] = c_tok[c];
-    parents[ob + pos] = pc < 0 ? 0 : c_pos[pc];
+    const int pc = t.c_par[c];
+    tokens[ob + pos] = t.c_tok[c];
+    parents[ob + pos] = pc < 0 ? 0 : t.c_pos[pc];
     depths[ob + pos] = dep;
-    scores[ob + pos] = c_score[c];
-    draft_row[ob + pos] = c_row[c];
+    scores[ob + pos] = t.c_score[c];
+    draft_row[ob + pos] = t.c_row[c];
+  }
+}
+
+// Frontier of depth d (1 <= d < depth) for the per-depth draft expansion: the best k
+// candidates of level d, in rank order, become rows 1 + (d-1)k + j; each row gets its
+// candidate's token and the row of the node that proposed it.  Needs the row lists
+// of rows 0 .. (d-1)k.
+__global__ void __launch_bounds__(kTreeThreads)
+draft_frontier(RerankPlan pl, int d, const float* __restrict__ draft_lse, void* ws,
+               int32_t* __restrict__ row_token, int32_t* __restrict__ parent_row) {
+  __shared__ TreeLds t;
+  RrWs w = rr_ws(ws, pl);
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int k = pl.k;
+  stage_rows(pl, w, draft_lse, b, 1 + (d - 1) * k, t);
+  grow_levels(pl, d, t);
+  const int lb = d == 1 ? 0 : k + (d - 2) * k * k;
+  const int ln = d == 1 ? k : k * k;
+  for (int c = lb + tid; c < lb + ln; c += kTreeThreads) t.c_key[c] = vi_key(t.c_score[c], c);
+  __syncthreads();
+  for (int c = lb + tid; c < lb + ln; c += kTreeThreads) {
+    const int rank = rank_in(t.c_key, lb, ln, t.c_key[c]);
+    if (rank >= k) continue;
+    const size_t row = (size_t)b * pl.R + 1 + (d - 1) * k + rank;
+    const int pc = t.c_par[c];
+    row_token[row] = t.c_tok[c];
+    parent_row[row] = pc < 0 ? 0 : t.c_row[pc];
   }
 }
 
@@ -449,6 +497,8 @@ RerankPlan plan_rerank(int B, int V, int top_k, int depth, int n_nodes) {
   pl.n_nodes = n_nodes;
   pl.chunk_len = kChunk;
   pl.chunks = (V + kChunk - 1) / kChunk;
+  pl.row0 = 0;
+  pl.nrows = pl.R;
   return pl;
 }
 
@@ -463,21 +513,40 @@ size_t rerank_workspace_bytes(const RerankPlan& pl) {
 int rerank_max_candidates() { return kMaxCand; }
 int rerank_max_row_list() { return kMaxRowList; }
 
-hipError_t launch_rerank(const RerankPlan& pl, const float* draft_logits, const int32_t* root_token,
-                         int32_t* tokens, int32_t* parents, int32_t* depths, float* scores,
-                         int32_t* draft_row, float* draft_lse, void* workspace, hipStream_t stream) {
-  const int rows = pl.B * pl.R;
+hipError_t launch_rerank_rows(const RerankPlan& pl, const float* draft_logits, float* draft_lse,
+                              void* workspace, hipStream_t stream) {
+  const int rows = pl.B * pl.nrows;
   hipLaunchKernelGGL(rerank_rows, dim3(rows * pl.chunks), dim3(kRowThreads), 0, stream, draft_logits,
                      pl, workspace);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(rerank_merge, dim3((rows + 3) / 4), dim3(256), 0, stream, pl, workspace,
                      draft_lse);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_rerank_tree(const RerankPlan& pl, const int32_t* root_token, const float* draft_lse,
+                              void* workspace, int32_t* tokens, int32_t* parents, int32_t* depths,
+                              float* scores, int32_t* draft_row, hipStream_t stream) {
   hipLaunchKernelGGL(rerank_tree, dim3(pl.B), dim3(kTreeThreads), 0, stream, pl, root_token,
                      draft_lse, workspace, tokens, parents, depths, scores, draft_row);
   return hipGetLastError();
+}
+
+hipError_t launch_draft_frontier(const RerankPlan& pl, int d, const float* draft_lse, void* workspace,
+                                 int32_t* row_token, int32_t* parent_row, hipStream_t stream) {
+  hipLaunchKernelGGL(draft_frontier, dim3(pl.B), dim3(kTreeThreads), 0, stream, pl, d, draft_lse,
+                     workspace, row_token, parent_row);
+  return hipGetLastError();
+}
+
+hipError_t launch_rerank(const RerankPlan& pl, const float* draft_logits, const int32_t* root_token,
+                         int32_t* tokens, int32_t* parents, int32_t* depths, float* scores,
+                         int32_t* draft_row, float* draft_lse, void* workspace, hipStream_t stream) {
+  const hipError_t e = launch_rerank_rows(pl, draft_logits, draft_lse, workspace, stream);
+  if (e != hipSuccess) return e;
+  return launch_rerank_tree(pl, root_token, draft_lse, workspace, tokens, parents, depths, scores,
+                            draft_row, stream);
 }
 
 }  // namespace eagle

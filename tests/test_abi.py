@@ -191,3 +191,33 @@ def test_paged_argument_errors(lib):
     # with one-row pages the plan splits a long prefix finely enough for the on-chip
     # slice of the block table, which then needs a split-KV workspace
     assert lib.eagle_tree_verify_attn_paged_workspace(1, 10, 2, 1, 64, 30000, 1) > 0
+
+
+def test_draft_expand_argument_errors(lib):
+    buf = ctypes.create_string_buffer(256)   # host memory: only its address is used
+    base = (ctypes.addressof(buf) + 15) // 16 * 16
+    head = sda.DraftHead(*([base] * 9))
+    f = lib.eagle_draft_expand
+
+    def dx(h=head, B=1, H=256, Hq=4, Hkv=2, D=64, I=512, V=1000, P=10, cap=40, k=4, depth=4, n=12,
+           f0=base, ws=None, wsb=0):
+        p = ctypes.byref(h) if h is not None else None
+        return f(p, f0, base, base, base, B, H, Hq, Hkv, D, I, V, P, cap, k, depth, n, 0.125, 1e-5,
+                 *([base] * 10), ws, wsb, None)
+
+    assert dx(h=None) == 1
+    assert dx(h=sda.DraftHead(*([base] * 8 + [0]))) == 1   # g2 NULL
+    assert dx(f0=None) == 1
+    assert dx(H=200) == 3          # H not a multiple of 64
+    assert dx(I=100) == 3
+    assert dx(D=96) == 3
+    assert dx(Hq=3) == 2           # Hq % Hkv
+    assert dx(k=10, depth=8, cap=200) == 3   # 71 expansion rows > 64
+    assert dx(cap=20) == 2         # kv_cap < P + 13
+    assert dx(f0=base + 8) == 2    # misaligned
+    assert dx() == 4               # no workspace
+    need = lib.eagle_draft_expand_workspace(1, 256, 4, 2, 64, 512, 1000, 10, 40, 4, 4)
+    assert need > 0
+    assert dx(ws=base, wsb=need - 1) == 4
+    assert lib.eagle_draft_expand_workspace(1, 256, 4, 2, 96, 512, 1000, 10, 40, 4, 4) == 0
+    assert lib.eagle_draft_expand_workspace(1, 256, 4, 2, 64, 512, 1000, 10, 5, 4, 4) == 0
