@@ -449,7 +449,9 @@ def summarize_profiles(root):
         f.write("\n".join(lines) + "\n")
     dpath = os.path.join(root, "prof_draft", "run_kernel_stats.csv")
     if os.path.exists(dpath):
-        dstats = _read_csv(dpath)
+        # the library's kernels only (torch's weight initialisation is left out)
+        ours = ("lm_head_", "tree_attn_", "draft_", "rerank_")
+        dstats = [r for r in _read_csv(dpath) if r["Name"].startswith(ours)]
         dtotal = sum(float(r["TotalDurationNs"]) for r in dstats)
         B_, H_, Hq_, Hkv_, D_, I_, V_, P_ = DRAFT_SHAPES["C5"]
         dl = ["# rocprofv3 kernel trace: per-depth draft expansion, C5 shapes", "",
@@ -457,7 +459,8 @@ def summarize_profiles(root):
               f"Workload: eagle_draft_expand with a one-layer draft head (B={B_}, H={H_}, Hq={Hq_}, "
               f"Hkv={Hkv_}, D={D_}, MLP {I_}, V={V_}, draft prefix {P_}), top-k 10, depth 6, 60 nodes; "
               "4 expansions (1 warmup + 3 timed).  lm_head_gemm runs every projection and the LM head "
-              "(6 GEMMs per depth).", "",
+              "(6 GEMMs per depth); the library's kernels only (torch's weight initialisation is left "
+              "out).", "",
               "| kernel | calls | avg us | total ms | share % |", "|---|---|---|---|---|"]
         for r in sorted(dstats, key=lambda r: -float(r["TotalDurationNs"])):
             dl.append(f"| {r['Name']} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
