@@ -334,7 +334,7 @@ static eagle_status_t check_rerank_dims(int32_t B, int32_t V, int32_t top_k, int
     return fail(EAGLE_ERR_UNSUPPORTED, "top_k + (depth-1)*top_k^2 = %lld candidates > %d", cand,
                 eagle::rerank_max_candidates());
   const long long rows = 1 + (long long)(depth - 1) * top_k;
-  const long long chunks = (V + 4095) / 4096;
+  const long long chunks = (V + eagle::rerank_chunk_len() - 1) / eagle::rerank_chunk_len();
   if (rows * top_k > eagle::rerank_max_row_list() || rows > 512 || chunks * top_k > 1024)
     return fail(EAGLE_ERR_UNSUPPORTED, "rerank sizes past the kernel limits (rows*top_k=%lld, rows=%lld, "
                 "chunks*top_k=%lld)", rows * top_k, rows, chunks * top_k);
@@ -375,8 +375,8 @@ struct DraftLayout {
   eagle::DraftDims dd;
   eagle::RerankPlan rpl;
   int Mmax, maxN, maxW;
-  size_t off_rerank, off_X, off_G, off_x, off_h, off_n, off_y, off_q, off_att, off_attws, off_stats,
-      off_lm, total;
+  size_t off_rerank, off_X, off_G, off_x, off_h, off_n, off_y, off_q, off_att, off_attws, off_lm,
+      total;
   size_t attn_ws, lm_ws;
 };
 
@@ -397,15 +397,12 @@ DraftLayout draft_layout(int B, int H, int Hq, int Hkv, int D, int I, int V, int
   // the attention runs over all R rows of the expansion at every depth
   L.attn_ws = eagle::tree_attn_workspace_bytes(eagle::plan_tree_attn(B, R, Hq, Hkv, D, P, kv_cap));
   L.lm_ws = 0;
-  const int shapes[5][2] = {{2 * H, H}, {H, qkvn}, {Hq * D, H}, {H, 2 * I}, {I, H}};
-  for (int m : {B, L.Mmax}) {
+  const int shapes[6][2] = {{2 * H, H}, {H, qkvn}, {Hq * D, H}, {H, 2 * I}, {I, H}, {H, V}};
+  for (int m : {B, L.Mmax})
     for (auto& kn : shapes) {
-      const size_t w = eagle::lm_head_workspace_bytes(eagle::plan_lm_head(m, kn[0], kn[1]));
+      const size_t w = eagle::gemm_f32_workspace_bytes(m, kn[0], kn[1]);
       L.lm_ws = w > L.lm_ws ? w : L.lm_ws;
     }
-    const size_t w = eagle::lm_head_workspace_bytes(eagle::plan_lm_head(m, H, V));
-    L.lm_ws = w > L.lm_ws ? w : L.lm_ws;
-  }
   const size_t M = L.Mmax;
   size_t o = 0;
   L.off_rerank = o; o += a256(eagle::rerank_workspace_bytes(L.rpl));
@@ -418,7 +415,6 @@ DraftLayout draft_layout(int B, int H, int Hq, int Hkv, int D, int I, int V, int
   L.off_q = o;      o += a256((size_t)B * R * Hq * D * 2);
   L.off_att = o;    o += a256((size_t)B * R * Hq * D * 2);
   L.off_attws = o;  o += a256(L.attn_ws);
-  L.off_stats = o;  o += a256(M * 12);
   L.off_lm = o;     o += a256(L.lm_ws);
   L.total = o + 256;
   return L;
@@ -442,10 +438,7 @@ eagle_status_t check_draft_dims(int32_t B, int32_t H, int32_t Hq, int32_t Hkv, i
 
 hipError_t draft_gemm(int M, int K, int N, const void* X, const void* W, float* out, char* ws,
                       const DraftLayout& L, hipStream_t stream) {
-  const eagle::LmPlan pl = eagle::plan_lm_head(M, K, N);
-  float* st = (float*)(ws + L.off_stats);
-  return eagle::launch_lm_head(pl, X, W, st, (int32_t*)(st + L.Mmax), st + 2 * L.Mmax, nullptr, out,
-                               ws + L.off_lm, stream);
+  return eagle::launch_gemm_f32(M, K, N, X, W, out, ws + L.off_lm, stream);
 }
 
 }  // namespace

@@ -56,10 +56,17 @@ struct LmPlan {
   int vrows;      // vocabulary rows per workgroup
   int nvt;        // vocabulary tiles
   int nmb;        // hidden-row blocks
+  int ksplit;     // split-K factor (1: whole rows, with the fused row statistics)
+  int kb_per;     // 64-column blocks per split
 };
 
 LmPlan plan_lm_head(int M, int H, int V);
 size_t lm_head_workspace_bytes(const LmPlan& pl);
+// Plain GEMM out[M][N] = X[M][K] W[N][K]^T in fp32 on the LM-head kernel, with split-K
+// (fp32 partials summed by a second kernel) when the N tiles alone leave most CUs idle.
+size_t gemm_f32_workspace_bytes(int M, int K, int N);
+hipError_t launch_gemm_f32(int M, int K, int N, const void* X, const void* W, float* out,
+                           void* workspace, hipStream_t stream);
 hipError_t launch_lm_head(const LmPlan& pl, const void* hidden, const void* W, float* out_max,
                           int32_t* out_argmax, float* out_lse, float* out_second, float* out_logits,
                           void* workspace, hipStream_t stream);
@@ -104,6 +111,7 @@ hipError_t launch_kv_commit(void* k_cache, void* v_cache, const int32_t* accept_
 
 namespace eagle {
 int rerank_max_candidates();
+int rerank_chunk_len();      // vocabulary entries per chunk of the row pass
 // per-depth draft expansion: the row pass over rows [row0, row0 + nrows) of every
 // sequence (plan with those fields set), and the frontier of depth d (d >= 1): for
 // slot j, row r = 1 + (d-1)*k + j gets the token of the j-th best depth-d candidate

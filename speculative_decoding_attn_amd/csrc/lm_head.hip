@@ -99,8 +99,10 @@ lm_head_gemm(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W
   const int nwg = gridDim.x;
   const int w = blockIdx.x;
   const int logical = (nwg % 8 == 0) ? (w % 8) * (nwg / 8) + (w / 8) : w;
-  const int mb = logical % pl.nmb;
-  const int vt = logical / pl.nmb;
+  const int tiles = pl.nmb * pl.nvt;
+  const int ks = logical / tiles;            // split-K slice
+  const int mb = (logical % tiles) % pl.nmb;
+  const int vt = (logical % tiles) / pl.nmb;
   const int M = pl.M, H = pl.H, V = pl.V;
   const int m0 = mb * MROWS;
   const int v0 = vt * VROWS + wvv * VT * 32;   // this wave's first vocabulary row
@@ -111,19 +113,22 @@ lm_head_gemm(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W
   // chunk that position holds.  Rows past V / M re-read the last row; those outputs
   // are never written.
   const uint32_t base = lds_addr(smem);
+  // this split's 64-column blocks kb0 .. kb0 + nhb - 1
+  const int kb0 = ks * pl.kb_per;
+  const int nhb = min(pl.kb_per, H / 64 - kb0);
   const uint8_t* wsrc[W_DMA];
 #pragma unroll
   for (int t = 0; t < W_DMA; ++t) {
     const int r = 8 * (wv * W_DMA + t) + (lane >> 3);          // row within the W tile
     const int row = min(vt * VROWS + r, V - 1);
-    wsrc[t] = (const uint8_t*)(W + (size_t)row * H) + 16 * swz(r, lane & 7);
+    wsrc[t] = (const uint8_t*)(W + (size_t)row * H + (size_t)kb0 * 64) + 16 * swz(r, lane & 7);
   }
   const uint8_t* hsrc[H_DMA];
 #pragma unroll
   for (int t = 0; t < H_DMA; ++t) {
     const int r = 8 * (wv * H_DMA + t) + (lane >> 3);          // row within the hidden tile
     const int row = min(m0 + r, M - 1);
-    hsrc[t] = (const uint8_t*)(hidden + (size_t)row * H) + 16 * swz(r, lane & 7);
+    hsrc[t] = (const uint8_t*)(hidden + (size_t)row * H + (size_t)kb0 * 64) + 16 * swz(r, lane & 7);
   }
   // one DMA instruction t (8 rows) of W / hidden block blk into stage st; hidden
   // groups wholly past M are skipped (their rows are never written out)
@@ -171,7 +176,6 @@ lm_head_gemm(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W
   static_assert(NG % (LA + 1) == 0, "the hidden fragment ring continues across blocks");
   static_assert(LA <= MT, "the barrier falls in step 3, after step 2 last used wf[0]");
   constexpr int NGI = NG - LA;
-  const int nhb = H / 64;
 #pragma unroll
   for (int t = 0; t < W_DMA; ++t) issue_w(0, 0, t);
 #pragma unroll
@@ -267,7 +271,7 @@ lm_head_gemm(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int vocab = v0 + 32 * j + 8 * q4 + 4 * half;
-          float* dst = logits + (size_t)m * V + vocab;
+          float* dst = logits + ((size_t)ks * M + m) * V + vocab;   // split-K: slice ks
           if (vocab + 3 < V && (V & 3) == 0) {
             *(f32x4*)dst = f32x4{acc[j][i][4 * q4], acc[j][i][4 * q4 + 1], acc[j][i][4 * q4 + 2],
                                  acc[j][i][4 * q4 + 3]};
@@ -282,6 +286,7 @@ lm_head_gemm(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W
     if (half == 0) red[wvv * MROWS + mloc] = f32x4{t.mx, t.sec, t.z, __int_as_float(t.idx)};
   }
   __syncthreads();
+  if (pl.ksplit > 1) return;   // partial sums: no row statistics
   for (int mloc = tid; mloc < MROWS; mloc += THREADS) {
     const int m = m0 + mloc;
     if (m >= M) continue;
@@ -319,6 +324,24 @@ lm_head_merge(LmPlan pl, const f32x4* __restrict__ part, float* __restrict__ out
   }
 }
 
+// out[i] = sum over the split-K slices of part[s][i] (n = M*N entries)
+__global__ void __launch_bounds__(256)
+gemm_splitk_sum(size_t n, int S, const float* __restrict__ part, float* __restrict__ out) {
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  if (i + 3 < n) {
+    f32x4 a = *(const f32x4*)(part + i);
+    for (int s = 1; s < S; ++s) a += *(const f32x4*)(part + (size_t)s * n + i);
+    *(f32x4*)(out + i) = a;
+  } else {
+    for (size_t e = i; e < n; ++e) {
+      float a = 0.f;
+      for (int s = 0; s < S; ++s) a += part[(size_t)s * n + e];
+      out[e] = a;
+    }
+  }
+}
+
 template <int MT, int VT, int WVV, int WVM, int LA>
 hipError_t launch_gemm(const LmPlan& pl, const void* hidden, const void* W, f32x4* part,
                        float* logits, hipStream_t stream) {
@@ -332,7 +355,7 @@ hipError_t launch_gemm(const LmPlan& pl, const void* hidden, const void* W, f32x
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((lm_head_gemm<MT, VT, WVV, WVM, LA>), dim3(pl.nvt * pl.nmb),
+  hipLaunchKernelGGL((lm_head_gemm<MT, VT, WVV, WVM, LA>), dim3(pl.nvt * pl.nmb * pl.ksplit),
                      dim3(WVV * WVM * 64), bytes, stream, (const uint16_t*)hidden,
                      (const uint16_t*)W, pl, part, logits);
   return hipGetLastError();
@@ -366,7 +389,55 @@ LmPlan plan_lm_head(int M, int H, int V) {
   }
   pl.nvt = (V + pl.vrows - 1) / pl.vrows;
   pl.nmb = (M + pl.mrows - 1) / pl.mrows;
+  pl.ksplit = 1;
+  pl.kb_per = H / 64;
   return pl;
+}
+
+namespace {
+
+// split-K for plain GEMMs: enough slices to give every CU about two workgroups, each
+// slice at least 16 blocks of 64 columns long
+LmPlan plan_gemm_f32(int M, int K, int N) {
+  LmPlan pl = plan_lm_head(M, K, N);
+  const int nhb = K / 64;
+  const int tiles = pl.nvt * pl.nmb;
+  int S = 1;
+  while (S * 2 * tiles <= 2 * kNumCUs && nhb / (S * 2) >= 16) S *= 2;
+  pl.ksplit = S;
+  pl.kb_per = (nhb + S - 1) / S;
+  pl.ksplit = (nhb + pl.kb_per - 1) / pl.kb_per;
+  return pl;
+}
+
+}  // namespace
+
+size_t gemm_f32_workspace_bytes(int M, int K, int N) {
+  const LmPlan pl = plan_gemm_f32(M, K, N);
+  size_t b = lm_head_workspace_bytes(pl);
+  if (pl.ksplit > 1) b += (size_t)pl.ksplit * M * N * sizeof(float) + 256;
+  return b;
+}
+
+hipError_t launch_gemm_f32(int M, int K, int N, const void* X, const void* W, float* out,
+                           void* workspace, hipStream_t stream) {
+  const LmPlan pl = plan_gemm_f32(M, K, N);
+  f32x4* part = (f32x4*)workspace;
+  float* dst = out;
+  if (pl.ksplit > 1)
+    dst = (float*)((char*)workspace + (lm_head_workspace_bytes(pl) + 255) / 256 * 256);
+  hipError_t e;
+  switch (pl.variant) {
+    case 3: e = launch_gemm<4, 2, 4, 2, 3>(pl, X, W, part, dst, stream); break;
+    case 2: e = launch_gemm<4, 2, 4, 1, 3>(pl, X, W, part, dst, stream); break;
+    case 1: e = launch_gemm<2, 2, 4, 1, 1>(pl, X, W, part, dst, stream); break;
+    default: e = launch_gemm<1, 1, 4, 1, 1>(pl, X, W, part, dst, stream); break;
+  }
+  if (e != hipSuccess || pl.ksplit == 1) return e;
+  const size_t n = (size_t)M * N;
+  hipLaunchKernelGGL(gemm_splitk_sum, dim3((unsigned)((n + 1023) / 1024)), dim3(256), 0, stream, n,
+                     pl.ksplit, dst, out);
+  return hipGetLastError();
 }
 
 size_t lm_head_workspace_bytes(const LmPlan& pl) {

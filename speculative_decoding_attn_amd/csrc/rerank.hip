@@ -26,7 +26,10 @@ namespace eagle {
 namespace {
 
 constexpr int kRowThreads = 256;
-constexpr int kRowPer = 16;                        // elements per thread in rerank_rows
+#ifndef EAGLE_RERANK_ROW_PER
+#define EAGLE_RERANK_ROW_PER 32
+#endif
+constexpr int kRowPer = EAGLE_RERANK_ROW_PER;      // elements per thread in rerank_rows
 constexpr int kChunk = kRowThreads * kRowPer;      // vocabulary entries per chunk
 constexpr int kTreeThreads = 1024;
 constexpr int kMaxCand = 2048;                     // candidates per sequence in rerank_tree
@@ -110,7 +113,7 @@ __device__ __forceinline__ float wave_sort_desc(float v) {
   return v;
 }
 
-// One workgroup per (row, vocabulary chunk of 4096).  Max and exp-sum of the chunk,
+// One workgroup per (row, vocabulary chunk of kChunk entries).  Max and exp-sum of the chunk,
 // and its top-k: every wave keeps the elements not below the k-th largest of its
 // 64 lane maxima (at least k of its elements are that large, so its top-k is among
 // them) and appends them to a short LDS list; one wave then extracts the chunk's k
@@ -136,14 +139,16 @@ rerank_rows(const float* __restrict__ logits, RerankPlan pl, void* ws) {
 
   // element e of thread tid is x0 + e*256 + tid: every load instruction is coalesced
   float val[kRowPer];
-  int idx[kRowPer];
 #pragma unroll
   for (int e = 0; e < kRowPer; ++e) {
     const int x = x0 + e * kRowThreads + tid;
-    const bool ok = x < V;
-    val[e] = ok ? src[x] : -INFINITY;
-    idx[e] = ok ? x : 0x7fffffff;
+    val[e] = x < V ? src[x] : -INFINITY;
   }
+  // index of element e (past the row: the largest index, below every real one)
+  auto idx_of = [&](int e) {
+    const int x = x0 + e * kRowThreads + tid;
+    return x < V ? x : 0x7fffffff;
+  };
   float lmax = val[0];
 #pragma unroll
   for (int e = 1; e < kRowPer; ++e) lmax = fmaxf(lmax, val[e]);
@@ -200,7 +205,7 @@ rerank_rows(const float* __restrict__ logits, RerankPlan pl, void* ws) {
     for (int e = 0; e < kRowPer; ++e)
       if (val[e] >= thr) {
         cand_v[pos] = val[e];
-        cand_i[pos] = idx[e];
+        cand_i[pos] = idx_of(e);
         ++pos;
       }
     __syncthreads();
@@ -232,8 +237,9 @@ rerank_rows(const float* __restrict__ logits, RerankPlan pl, void* ws) {
     VI best{-INFINITY, 0x7fffffff};
 #pragma unroll
     for (int e = 0; e < kRowPer; ++e) {
-      const bool after = val[e] < pv || (val[e] == pv && idx[e] > pi);
-      if (after && better(val[e], idx[e], best.v, best.i)) best = VI{val[e], idx[e]};
+      const int ie = idx_of(e);
+      const bool after = val[e] < pv || (val[e] == pv && ie > pi);
+      if (after && better(val[e], ie, best.v, best.i)) best = VI{val[e], ie};
     }
     best = wave_best(best);
     __syncthreads();
@@ -511,6 +517,7 @@ size_t rerank_workspace_bytes(const RerankPlan& pl) {
 }
 
 int rerank_max_candidates() { return kMaxCand; }
+int rerank_chunk_len() { return kChunk; }
 int rerank_max_row_list() { return kMaxRowList; }
 
 hipError_t launch_rerank_rows(const RerankPlan& pl, const float* draft_logits, float* draft_lse,
