@@ -394,8 +394,14 @@ DraftLayout draft_layout(int B, int H, int Hq, int Hkv, int D, int I, int V, int
   for (int n : {H, qkvn, 2 * I}) L.maxN = n > L.maxN ? n : L.maxN;
   L.maxW = H;
   for (int w : {Hq * D, I}) L.maxW = w > L.maxW ? w : L.maxW;
-  // the attention runs over all R rows of the expansion at every depth
-  L.attn_ws = eagle::tree_attn_workspace_bytes(eagle::plan_tree_attn(B, R, Hq, Hkv, D, P, kv_cap));
+  // the attention of depth d computes that depth's rows (queries) over the R-row tree
+  L.attn_ws = 0;
+  for (int d = 0; d < depth; ++d) {
+    const int row0 = d == 0 ? 0 : 1 + (d - 1) * top_k, nr = d == 0 ? 1 : top_k;
+    const size_t w = eagle::tree_attn_workspace_bytes(
+        eagle::plan_tree_attn_rows(B, R, row0, nr, Hq, Hkv, D, P, kv_cap));
+    L.attn_ws = w > L.attn_ws ? w : L.attn_ws;
+  }
   L.lm_ws = 0;
   const int shapes[6][2] = {{2 * H, H}, {H, qkvn}, {Hq * D, H}, {H, 2 * I}, {I, H}, {H, V}};
   for (int m : {B, L.Mmax})
@@ -494,7 +500,6 @@ eagle_status_t eagle_draft_expand(const eagle_draft_head* head, const void* f0,
   void* rws = ws + L.off_rerank;
   const eagle::DraftDims& dd = L.dd;
   const int qkvn = (Hq + 2 * Hkv) * D;
-  eagle::AttnPlan apl = eagle::plan_tree_attn(B, R, Hq, Hkv, D, P, kv_cap);
 #define DRAFT_TRY(expr, what)                                   \
   do {                                                          \
     const hipError_t e_ = (expr);                               \
@@ -514,6 +519,7 @@ eagle_status_t eagle_draft_expand(const eagle_draft_head* head, const void* f0,
     DRAFT_TRY(eagle::launch_draft_rms(M, H, eps, G, H, nullptr, head->g1, xres, nb, stream), "draft norm 1");
     DRAFT_TRY(draft_gemm(M, H, qkvn, nb, head->w_qkv, G, ws, L, stream), "draft qkv");
     DRAFT_TRY(eagle::launch_draft_qkv_scatter(dd, row0, nr, G, qbuf, k_cache, v_cache, stream), "draft scatter");
+    const eagle::AttnPlan apl = eagle::plan_tree_attn_rows(B, R, row0, nr, Hq, Hkv, D, P, kv_cap);
     DRAFT_TRY(eagle::launch_tree_attn(apl, scale, qbuf, k_cache, v_cache, parent_row, att, nullptr,
                                       ws + L.off_attws, stream), "draft attention");
     DRAFT_TRY(eagle::launch_draft_gather_rows(dd, row0, nr, Hq * D, att, nb, stream), "draft gather rows");

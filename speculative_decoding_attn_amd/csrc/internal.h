@@ -37,6 +37,9 @@ struct AttnPlan {
   int page_shift;   // log2(page_size)
   int max_pages;    // row stride of block_table
   int num_blocks;
+  // query subset (nq > 0): only nodes node0 .. node0+nq-1 of the N-node tree are
+  // computed (the draft expansion's newest rows); masks and keys cover the whole tree
+  int node0, nq;
 };
 
 // paged KV: a split's slice of the block table is staged in LDS
@@ -44,6 +47,8 @@ constexpr int kMaxSplitPages = 1024;
 AttnPlan plan_tree_attn_paged(int B, int N, int Hq, int Hkv, int D, int P, int page_shift);
 
 AttnPlan plan_tree_attn(int B, int N, int Hq, int Hkv, int D, int P, int kv_cap);
+AttnPlan plan_tree_attn_rows(int B, int N, int node0, int nq, int Hq, int Hkv, int D, int P,
+                             int kv_cap);
 size_t tree_attn_workspace_bytes(const AttnPlan& pl);
 hipError_t launch_tree_attn(const AttnPlan& pl, float scale, const void* q, const void* k,
                             const void* v, const int32_t* parents, void* out, float* lse,

@@ -98,7 +98,8 @@ tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   // so every access stays inside the layouts the plan was sized for)
   const int P = pl.prefix_len ? min(max(pl.prefix_len[b], 0), pl.P) : pl.P;
   const int N = pl.tree_len ? min(max(pl.tree_len[b], 1), pl.N) : pl.N;
-  const int R = N * G;   // this sequence's query rows; rows past R are padding
+  // this sequence's query rows (rows past R are padding): its N nodes, or the subset
+  const int R = (pl.nq > 0 ? pl.nq : N) * G;
   // split s covers prefix keys [s*len, (s+1)*len) below P (possibly none); the last
   // split also takes the tree keys P .. P+N-1
   const int key_begin = (split == pl.S - 1) ? min(split * pl.split_len, P) : split * pl.split_len;
@@ -128,8 +129,9 @@ tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   for (int t = 0; t < ROWT; ++t) {
     const int r = rowbase + 32 * t + l32;
     if (r < R) {
-      const int i = r / G;
-      const int h = g * G + (r - i * G);
+      const int il = r / G;
+      const int i = pl.node0 + il;
+      const int h = g * G + (r - il * G);
       const uint16_t* qp = q + ((size_t)(b * pl.N + i) * pl.Hq + h) * D + 8 * half;
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) qf[t][s] = as_bf16x8(*(const u32x4*)(qp + 16 * s));
@@ -344,8 +346,9 @@ tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     if (r >= R) continue;
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     const float lse = (mc[t] + log2f(ltot)) * kLn2;
-    const int i = r / G;
-    const int h = g * G + (r - i * G);
+    const int il = r / G;
+    const int i = pl.node0 + il;
+    const int h = g * G + (r - il * G);
     if (pl.S == 1) {
       uint16_t* op = out + ((size_t)(b * pl.N + i) * pl.Hq + h) * D;
 #pragma unroll
@@ -407,8 +410,9 @@ tree_attn_merge(AttnPlan pl, const float* __restrict__ part_o, const float* __re
     for (int e = 0; e < PER; ++e) acc[e] += wgt * op[e];
   }
   const float inv = 1.f / wsum;
-  const int i = r / pl.G;
-  const int h = g * pl.G + (r - i * pl.G);
+  const int il = r / pl.G;
+  const int i = pl.node0 + il;
+  const int h = g * pl.G + (r - il * pl.G);
   uint16_t* o = out + ((size_t)(b * pl.N + i) * pl.Hq + h) * D + lane * PER;
   if (PER == 2) {
     *(uint32_t*)o = pack_bf16x2(acc[0] * inv, acc[PER - 1] * inv);
@@ -484,7 +488,7 @@ tree_attn_pingpong(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   const int G = pl.G;
   const int P = pl.prefix_len ? min(max(pl.prefix_len[b], 0), pl.P) : pl.P;
   const int N = pl.tree_len ? min(max(pl.tree_len[b], 1), pl.N) : pl.N;
-  const int R = N * G;
+  const int R = (pl.nq > 0 ? pl.nq : N) * G;   // query rows (all nodes, or the subset)
   const bool last = split == pl.S - 1;
   const int key_begin = last ? min(split * pl.split_len, P) : split * pl.split_len;
   const int key_end = last ? P + N : min(P, (split + 1) * pl.split_len);
@@ -512,8 +516,9 @@ tree_attn_pingpong(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   bf16x8 qf[KSTEPS];
   uint64_t anc;
   if (r_row < R) {
-    const int i = r_row / G;
-    const int h = g * G + (r_row - i * G);
+    const int il = r_row / G;
+    const int i = pl.node0 + il;
+    const int h = g * G + (r_row - il * G);
     const uint16_t* qp = q + ((size_t)(b * pl.N + i) * pl.Hq + h) * D + 8 * half;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) qf[s] = as_bf16x8(*(const u32x4*)(qp + 16 * s));
@@ -726,8 +731,9 @@ tree_attn_pingpong(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   if (r_row >= R) return;
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
   const float lse = (mc + log2f(ltot)) * kLn2;
-  const int i = r_row / G;
-  const int h = g * G + (r_row - i * G);
+  const int il = r_row / G;
+  const int i = pl.node0 + il;
+  const int h = g * G + (r_row - il * G);
   if (pl.S == 1) {
     uint16_t* op = out + ((size_t)(b * pl.N + i) * pl.Hq + h) * D;
 #pragma unroll
@@ -815,6 +821,13 @@ hipError_t launch_fwd_d(const AttnPlan& pl, const void* q, const void* k, const 
 }  // namespace
 
 AttnPlan plan_tree_attn(int B, int N, int Hq, int Hkv, int D, int P, int kv_cap) {
+  return plan_tree_attn_rows(B, N, 0, 0, Hq, Hkv, D, P, kv_cap);
+}
+
+// Nodes node0 .. node0+nq-1 of an N-node tree (nq = 0: all N); the rows, row blocks and
+// splits follow the queried rows.
+AttnPlan plan_tree_attn_rows(int B, int N, int node0, int nq, int Hq, int Hkv, int D, int P,
+                             int kv_cap) {
   AttnPlan pl{};
   pl.B = B;
   pl.N = N;
@@ -824,7 +837,9 @@ AttnPlan plan_tree_attn(int B, int N, int Hq, int Hkv, int D, int P, int kv_cap)
   pl.D = D;
   pl.P = P;
   pl.kv_cap = kv_cap;
-  pl.R = N * pl.G;
+  pl.node0 = nq > 0 ? node0 : 0;
+  pl.nq = nq > 0 ? nq : 0;
+  pl.R = (nq > 0 ? nq : N) * pl.G;
   // rows per wave: 32 (one MFMA row tile, 2 waves per SIMD) or 64 (two row tiles, 1 wave
   // per SIMD: half the LDS reads per MFMA)
   pl.rowt = kAttnRowTiles;
