@@ -337,11 +337,29 @@ __device__ __forceinline__ int rank_in(const uint64_t* keys, int lb, int n, uint
   return rank;
 }
 
+// Ranks (as rank_in) of candidates lb .. lb+n-1 into rank[lb ..], with up to 8 threads
+// per candidate, each counting a share of the keys (LDS adds); ends with a barrier.
+__device__ void rank_all(const uint64_t* keys, int lb, int n, int* rank) {
+  int T = kTreeThreads / n;
+  T = T < 1 ? 1 : (T > 8 ? 8 : T);
+  const int per = (n + T - 1) / T;
+  for (int c = lb + threadIdx.x; c < lb + n; c += kTreeThreads) rank[c] = 0;
+  __syncthreads();
+  for (int job = threadIdx.x; job < n * T; job += kTreeThreads) {
+    const int c = lb + job % n, part = job / n;
+    const int lo = part * per;
+    const int cnt = min(per, n - lo);
+    if (cnt > 0) atomicAdd(&rank[c], rank_in(keys, lb + lo, cnt, keys[c]));
+  }
+  __syncthreads();
+}
+
 // Candidate arrays of one sequence in LDS, and the candidates of levels 1..L: level
 // 1 = the root's proposals; level d+1 = the proposals of the frontier of level d (its
 // best k candidates, which take rows 1 + (d-1)k .. in rank order).  Needs the row
 // lists and normalisers of rows 0 .. 1 + (L-2)k + k-1.
 struct TreeLds {
+  int c_rank[kMaxCand];
   float c_score[kMaxCand];
   uint64_t c_key[kMaxCand];
   int c_tok[kMaxCand];
@@ -386,21 +404,24 @@ __device__ void grow_levels(const RerankPlan& pl, int L, TreeLds& t) {
     // frontier: rank within the level
     for (int c = lb + tid; c < lb + ln; c += kTreeThreads) t.c_key[c] = vi_key(t.c_score[c], c);
     __syncthreads();
+    rank_all(t.c_key, lb, ln, t.c_rank);
     for (int c = lb + tid; c < lb + ln; c += kTreeThreads) {
-      const int rank = rank_in(t.c_key, lb, ln, t.c_key[c]);
-      if (rank < k) t.c_row[c] = (short)(1 + (d - 1) * k + rank);
+      const int rank = t.c_rank[c];
+      if (rank < k) {
+        t.c_row[c] = (short)(1 + (d - 1) * k + rank);
+        t.c_pos[rank] = (short)c;   // frontier slot -> candidate
+      }
     }
     __syncthreads();
-    for (int c = lb + tid; c < lb + ln; c += kTreeThreads) {
-      const int row = t.c_row[c];
-      if (row < 0) continue;
-      const int slot = row - (1 + (d - 1) * k);
-      for (int r = 0; r < k; ++r) {
-        const int id = base + slot * k + r;
-        t.c_score[id] = t.c_score[c] + (rv[(size_t)row * k + r] - lse[row]);
-        t.c_tok[id] = ri[(size_t)row * k + r];
-        t.c_par[id] = (short)c;
-      }
+    // the k proposals of every frontier slot, one thread each
+    for (int e = tid; e < k * k; e += kTreeThreads) {
+      const int slot = e / k, r = e % k;
+      const int c = t.c_pos[slot];
+      const int row = 1 + (d - 1) * k + slot;
+      const int id = base + e;
+      t.c_score[id] = t.c_score[c] + (rv[(size_t)row * k + r] - lse[row]);
+      t.c_tok[id] = ri[(size_t)row * k + r];
+      t.c_par[id] = (short)c;
     }
     __syncthreads();
     lb = base;
@@ -425,10 +446,8 @@ rerank_tree(RerankPlan pl, const int32_t* __restrict__ root_token, const float* 
   const int keep = pl.n_nodes - 1;
   for (int c = tid; c < total; c += kTreeThreads) t.c_key[c] = vi_key(t.c_score[c], c);
   __syncthreads();
-  for (int c = tid; c < total; c += kTreeThreads) {
-    const int rank = rank_in(t.c_key, 0, total, t.c_key[c]);
-    t.c_pos[c] = (short)(rank < keep ? 1 : 0);
-  }
+  rank_all(t.c_key, 0, total, t.c_rank);
+  for (int c = tid; c < total; c += kTreeThreads) t.c_pos[c] = (short)(t.c_rank[c] < keep ? 1 : 0);
   __syncthreads();
   // breadth-first positions: 1 + number of selected candidates with a smaller id
   if (tid < 64) {
@@ -481,8 +500,9 @@ draft_frontier(RerankPlan pl, int d, const float* __restrict__ draft_lse, void* 
   const int ln = d == 1 ? k : k * k;
   for (int c = lb + tid; c < lb + ln; c += kTreeThreads) t.c_key[c] = vi_key(t.c_score[c], c);
   __syncthreads();
+  rank_all(t.c_key, lb, ln, t.c_rank);
   for (int c = lb + tid; c < lb + ln; c += kTreeThreads) {
-    const int rank = rank_in(t.c_key, lb, ln, t.c_key[c]);
+    const int rank = t.c_rank[c];
     if (rank >= k) continue;
     const size_t row = (size_t)b * pl.R + 1 + (d - 1) * k + rank;
     const int pc = t.c_par[c];
