@@ -10,14 +10,15 @@
 //
 // Kernels:
 //   rerank_rows   one workgroup per (row, vocabulary chunk): the chunk's max and
-//                 exp-sum, and its top-k by k rounds of "best element strictly after
-//                 the previous pick" in (logit desc, token asc) order.  Streams the
-//                 fp32 draft logits once (the HBM-bound part).
+//                 exp-sum, and its top-k in (logit desc, token asc) order, ranked
+//                 in parallel over a short candidate list.  Streams the fp32 draft
+//                 logits once (the HBM-bound part).
 //   rerank_merge  one wave per row: merges the chunk results into the row's lse and
-//                 top-k (same extraction order).
+//                 top-k (same order).
 //   rerank_tree   one workgroup per sequence: candidate scores depth by depth,
-//                 frontier = best k of each depth, final = best n_nodes-1 overall,
-//                 all by counting ranks; output breadth first.
+//                 frontier = best k of each depth (ranks counted within the depth),
+//                 final = best n_nodes-1 overall (rank within the depth plus binary
+//                 searches in the other depths' sorted keys); output breadth first.
 #include "common.h"
 #include "internal.h"
 
@@ -113,19 +114,38 @@ __device__ __forceinline__ float wave_sort_desc(float v) {
   return v;
 }
 
+// Rank of key among keys lb .. lb+n-1 of an LDS list: how many come first (larger
+// keys first).  Independent LDS reads, unrolled, so the loop is not bound by one
+// read's latency per comparison.
+__device__ __forceinline__ int rank_in(const uint64_t* keys, int lb, int n, uint64_t key) {
+  int rank = 0;
+  int o = lb;
+  const int end = lb + n;
+  for (; o + 8 <= end; o += 8) {
+    uint64_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = keys[o + e];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rank += v[e] > key ? 1 : 0;
+  }
+  for (; o < end; ++o) rank += keys[o] > key ? 1 : 0;
+  return rank;
+}
+
 // One workgroup per (row, vocabulary chunk of kChunk entries).  Max and exp-sum of the chunk,
-// and its top-k: every wave keeps the elements not below the k-th largest of its
-// 64 lane maxima (at least k of its elements are that large, so its top-k is among
-// them) and appends them to a short LDS list; one wave then extracts the chunk's k
-// best from that list in (logit desc, token asc) order.  If ties make the list
-// overflow, the whole chunk is searched instead (same order, same result).
+// and its top-k: every wave keeps the valid elements not below the k-th largest of
+// its 64 lane maxima (at least k of its elements are that large, so its top-k is
+// among them) and appends them to a short LDS list as (logit desc, token asc) keys;
+// each listed key's rank in the list is counted, in parallel over the list, and
+// ranks below k are written in rank order (padding past a chunk with fewer than k
+// valid entries).  If ties make the list overflow, the whole chunk is searched by k
+// rounds instead (same order, same result).
 constexpr int kCandCap = 512;
 
 __global__ void __launch_bounds__(kRowThreads)
 rerank_rows(const float* __restrict__ logits, RerankPlan pl, void* ws) {
   __shared__ float redf[kRowThreads / 64];
-  __shared__ float cand_v[kCandCap];
-  __shared__ int cand_i[kCandCap];
+  __shared__ uint64_t cand_key[kCandCap];
   __shared__ int wave_cnt[kRowThreads / 64];
   __shared__ VI red[kRowThreads / 64];
   RrWs w = rr_ws(ws, pl);
@@ -175,7 +195,7 @@ rerank_rows(const float* __restrict__ logits, RerankPlan pl, void* ws) {
   const float thr = k >= 64 ? -INFINITY : __shfl(sorted, k - 1);
   int mine = 0;
 #pragma unroll
-  for (int e = 0; e < kRowPer; ++e) mine += val[e] >= thr ? 1 : 0;
+  for (int e = 0; e < kRowPer; ++e) mine += (val[e] >= thr && idx_of(e) < V) ? 1 : 0;
   int pre = mine;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -203,43 +223,35 @@ rerank_rows(const float* __restrict__ logits, RerankPlan pl, void* ws) {
     int pos = off + pre;
 #pragma unroll
     for (int e = 0; e < kRowPer; ++e)
-      if (val[e] >= thr) {
-        cand_v[pos] = val[e];
-        cand_i[pos] = idx_of(e);
-        ++pos;
-      }
+      if (val[e] >= thr && idx_of(e) < V) cand_key[pos++] = vi_key(val[e], idx_of(e));
     __syncthreads();
-    if (wid != 0) return;
-    float pv = INFINITY;
-    int pi = -1;
-    for (int r = 0; r < k; ++r) {
-      VI best{-INFINITY, 0x7fffffff};
-      for (int c = lane; c < ncand; c += 64) {
-        const float v = cand_v[c];
-        const int i = cand_i[c];
-        const bool after = v < pv || (v == pv && i > pi);
-        if (after && better(v, i, best.v, best.i)) best = VI{v, i};
+    for (int c = tid; c < ncand; c += kRowThreads) {
+      const uint64_t key = cand_key[c];
+      const int rank = rank_in(cand_key, 0, ncand, key);
+      if (rank < k) {
+        out_v[rank] = key_value(key);
+        out_i[rank] = key_index(key);
       }
-      best = wave_best(best);
-      if (lane == 0) {
-        out_v[r] = best.v;
-        out_i[r] = best.i;
-      }
-      pv = best.v;
-      pi = best.i;
+    }
+    for (int r = ncand + tid; r < k; r += kRowThreads) {
+      out_v[r] = -INFINITY;
+      out_i[r] = 0x7fffffff;
     }
     return;
   }
-  // many ties: k rounds over the whole chunk
+  // many ties: k rounds over the whole chunk, re-read from memory (a rare path; the
+  // registers of the main path stay free)
   float pv = INFINITY;
   int pi = -1;
   for (int r = 0; r < k; ++r) {
     VI best{-INFINITY, 0x7fffffff};
-#pragma unroll
+#pragma unroll 1
     for (int e = 0; e < kRowPer; ++e) {
-      const int ie = idx_of(e);
-      const bool after = val[e] < pv || (val[e] == pv && ie > pi);
-      if (after && better(val[e], ie, best.v, best.i)) best = VI{val[e], ie};
+      const int x = x0 + e * kRowThreads + tid;
+      const float v = x < V ? src[x] : -INFINITY;
+      const int ie = x < V ? x : 0x7fffffff;
+      const bool after = v < pv || (v == pv && ie > pi);
+      if (after && better(v, ie, best.v, best.i)) best = VI{v, ie};
     }
     best = wave_best(best);
     __syncthreads();
@@ -319,49 +331,32 @@ rerank_merge(RerankPlan pl, void* ws, float* __restrict__ draft_lse) {
   }
 }
 
-// Rank of candidate (s, c) among candidates lb .. lb+n-1 of the LDS score list: how
-// many come first in (score desc, id asc) order.  Independent LDS reads, unrolled,
-// so the loop is not bound by one read's latency per comparison.
-__device__ __forceinline__ int rank_in(const uint64_t* keys, int lb, int n, uint64_t key) {
-  int rank = 0;
-  int o = lb;
-  const int end = lb + n;
-  for (; o + 8 <= end; o += 8) {
-    uint64_t v[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = keys[o + e];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) rank += v[e] > key ? 1 : 0;
-  }
-  for (; o < end; ++o) rank += keys[o] > key ? 1 : 0;
-  return rank;
+// Adds to rank[c] (c in lb .. lb+n-1) how many of the candidates lb .. lb+n-1 come
+// first (LDS adds; rank[] must start at zero).  Each candidate's count is split over
+// P = 8, 4, 2 or 1 threads (n <= 128, 256, 512 or more): thread tid takes candidate
+// tid % (1024/P) and part tid / (1024/P).  No barrier.
+__device__ void rank_level(const uint64_t* keys, int lb, int n, int* rank) {
+  static_assert(kTreeThreads == 1024, "the thread split below assumes 1024 threads");
+  const int tid = threadIdx.x;
+  const int lg = n <= 128 ? 7 : (n <= 256 ? 8 : (n <= 512 ? 9 : 10));   // log2(1024/P)
+  const int P = kTreeThreads >> lg;
+  const int per = (n + P - 1) >> (10 - lg);   // ceil(n / P)
+  const int part = tid >> lg;
+  const int lo = part * per;
+  const int cnt = min(per, n - lo);
+  for (int c = tid & ((1 << lg) - 1); c < n; c += 1 << lg)
+    if (cnt > 0) atomicAdd(&rank[lb + c], rank_in(keys, lb + lo, cnt, keys[lb + c]));
 }
 
-// Ranks (as rank_in) of candidates lb .. lb+n-1 into rank[lb ..], with up to 8 threads
-// per candidate, each counting a share of the keys (LDS adds); ends with a barrier.
-__device__ void rank_all(const uint64_t* keys, int lb, int n, int* rank) {
-  int T = kTreeThreads / n;
-  T = T < 1 ? 1 : (T > 8 ? 8 : T);
-  const int per = (n + T - 1) / T;
-  for (int c = lb + threadIdx.x; c < lb + n; c += kTreeThreads) rank[c] = 0;
-  __syncthreads();
-  for (int job = threadIdx.x; job < n * T; job += kTreeThreads) {
-    const int c = lb + job % n, part = job / n;
-    const int lo = part * per;
-    const int cnt = min(per, n - lo);
-    if (cnt > 0) atomicAdd(&rank[c], rank_in(keys, lb + lo, cnt, keys[c]));
-  }
-  __syncthreads();
-}
-
-// Candidate arrays of one sequence in LDS, and the candidates of levels 1..L: level
-// 1 = the root's proposals; level d+1 = the proposals of the frontier of level d (its
-// best k candidates, which take rows 1 + (d-1)k .. in rank order).  Needs the row
-// lists and normalisers of rows 0 .. 1 + (L-2)k + k-1.
+// Candidate arrays of one sequence in LDS.  Level 1 = the root's proposals; level
+// d+1 = the proposals of the frontier of level d (its best k candidates, which take
+// rows 1 + (d-1)k .. in rank order).  Ids: level 1 = [0, k), level d+1 =
+// [k + (d-1)k^2, k + d k^2).  c_rank = rank within the candidate's level.
 struct TreeLds {
   int c_rank[kMaxCand];
   float c_score[kMaxCand];
   uint64_t c_key[kMaxCand];
+  uint64_t c_sorted[kMaxCand];   // each level's keys in rank order (final selection)
   int c_tok[kMaxCand];
   short c_par[kMaxCand];
   short c_row[kMaxCand];
@@ -370,6 +365,9 @@ struct TreeLds {
   int s_ri[kMaxRowList];
   float s_lse[kMaxRows];
 };
+
+__device__ __forceinline__ int level_base(int d, int k) { return d == 1 ? 0 : k + (d - 2) * k * k; }
+__device__ __forceinline__ int level_size(int d, int k) { return d == 1 ? k : k * k; }
 
 // stages the sequence's row lists (rows 0..nrows-1) and normalisers
 __device__ void stage_rows(const RerankPlan& pl, const RrWs& w, const float* draft_lse, int b,
@@ -383,8 +381,8 @@ __device__ void stage_rows(const RerankPlan& pl, const RrWs& w, const float* dra
   __syncthreads();
 }
 
-// candidates of levels 1..L (ids: level 1 = [0, k), level d+1 = [k + (d-1)k^2, k + d k^2))
-// and the frontier rows of levels 1..L-1 (c_row, -1 elsewhere)
+// candidates (score, token, parent, key) and within-level ranks of levels 1..L, and
+// the frontier rows of levels 1..L-1 (c_row, -1 elsewhere); ends with a barrier
 __device__ void grow_levels(const RerankPlan& pl, int L, TreeLds& t) {
   const int tid = threadIdx.x;
   const int k = pl.k;
@@ -392,19 +390,24 @@ __device__ void grow_levels(const RerankPlan& pl, int L, TreeLds& t) {
   const float* rv = t.s_rv;
   const int* ri = t.s_ri;
   const float* lse = t.s_lse;
-  for (int c = tid; c < total; c += kTreeThreads) t.c_row[c] = -1;
+  for (int c = tid; c < total; c += kTreeThreads) {
+    t.c_row[c] = -1;
+    t.c_rank[c] = 0;
+  }
   for (int r = tid; r < k; r += kTreeThreads) {
-    t.c_score[r] = rv[r] - lse[0];
+    const float sc = rv[r] - lse[0];
+    t.c_score[r] = sc;
+    t.c_key[r] = vi_key(sc, r);
     t.c_tok[r] = ri[r];
     t.c_par[r] = -1;
   }
   __syncthreads();
-  int lb = 0, ln = k, base = k;
-  for (int d = 1; d < L; ++d) {
-    // frontier: rank within the level
-    for (int c = lb + tid; c < lb + ln; c += kTreeThreads) t.c_key[c] = vi_key(t.c_score[c], c);
+  for (int d = 1; d <= L; ++d) {
+    const int lb = level_base(d, k), ln = level_size(d, k);
+    rank_level(t.c_key, lb, ln, t.c_rank);
     __syncthreads();
-    rank_all(t.c_key, lb, ln, t.c_rank);
+    if (d == L) break;
+    // frontier: the level's best k take rows 1 + (d-1)k + rank
     for (int c = lb + tid; c < lb + ln; c += kTreeThreads) {
       const int rank = t.c_rank[c];
       if (rank < k) {
@@ -413,21 +416,62 @@ __device__ void grow_levels(const RerankPlan& pl, int L, TreeLds& t) {
       }
     }
     __syncthreads();
-    // the k proposals of every frontier slot, one thread each
-    for (int e = tid; e < k * k; e += kTreeThreads) {
-      const int slot = e / k, r = e % k;
+    // the k proposals of every frontier slot, one thread each (slot = e / 64,
+    // proposal r = e % 64 < k)
+    const int base = lb + ln;
+    for (int e = tid; e < k * 64; e += kTreeThreads) {
+      const int slot = e >> 6, r = e & 63;
+      if (r >= k) continue;
       const int c = t.c_pos[slot];
       const int row = 1 + (d - 1) * k + slot;
-      const int id = base + e;
-      t.c_score[id] = t.c_score[c] + (rv[(size_t)row * k + r] - lse[row]);
+      const int id = base + slot * k + r;
+      const float sc = t.c_score[c] + (rv[(size_t)row * k + r] - lse[row]);
+      t.c_score[id] = sc;
+      t.c_key[id] = vi_key(sc, id);
       t.c_tok[id] = ri[(size_t)row * k + r];
       t.c_par[id] = (short)c;
     }
     __syncthreads();
-    lb = base;
-    ln = k * k;
-    base += k * k;
   }
+}
+
+// Depth (level) of candidate c, from the level bases (no division).
+__device__ __forceinline__ int level_of(int c, int k, int L) {
+  int d = 1;
+  for (int e = 2; e <= L; ++e) d += c >= level_base(e, k) ? 1 : 0;
+  return d;
+}
+
+// For every level d in d0 .. d0+7 (<= L, != skip): adds how many keys of level d
+// (descending in sorted) are larger than key.  Binary searches over the largest power
+// of two not above the largest level, the levels in step, with clamped reads issued
+// together: one LDS round trip per step.
+__device__ __forceinline__ int count_larger8(const uint64_t* sorted, int d0, int L, int skip, int k,
+                                             uint64_t key) {
+  int lo[8], n[8], base[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int d = d0 + j;
+    const bool on = d <= L && d != skip;
+    n[j] = on ? level_size(d, k) : 0;
+    base[j] = on ? level_base(d, k) : 0;
+    lo[j] = 0;
+  }
+  const int nmax = k * k;
+  int step = 1;
+  while (step * 2 <= nmax) step *= 2;
+  for (; step > 0; step >>= 1) {
+    uint64_t v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = sorted[base[j] + min(lo[j] + step, max(n[j], 1)) - 1];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (lo[j] + step <= n[j] && v[j] > key) lo[j] += step;
+  }
+  int sum = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) sum += lo[j];
+  return sum;
 }
 
 __global__ void __launch_bounds__(kTreeThreads)
@@ -439,26 +483,44 @@ rerank_tree(RerankPlan pl, const int32_t* __restrict__ root_token, const float* 
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int k = pl.k;
-  const int total = k + (pl.depth - 1) * k * k;
+  const int L = pl.depth;
+  const int total = k + (L - 1) * k * k;
   stage_rows(pl, w, draft_lse, b, pl.R, t);
-  grow_levels(pl, pl.depth, t);
-  // final selection by overall rank, then breadth-first positions
+  grow_levels(pl, L, t);
+  // Final selection: the best n_nodes-1 candidates overall.  A candidate's overall
+  // rank is its rank within its level plus, for every other level, how many of that
+  // level's keys are larger (a binary search in the level's keys in rank order).
   const int keep = pl.n_nodes - 1;
-  for (int c = tid; c < total; c += kTreeThreads) t.c_key[c] = vi_key(t.c_score[c], c);
+  for (int c = tid; c < total; c += kTreeThreads)
+    t.c_sorted[level_base(level_of(c, k, L), k) + t.c_rank[c]] = t.c_key[c];
   __syncthreads();
-  rank_all(t.c_key, 0, total, t.c_rank);
-  for (int c = tid; c < total; c += kTreeThreads) t.c_pos[c] = (short)(t.c_rank[c] < keep ? 1 : 0);
+  for (int c = tid; c < total; c += kTreeThreads) {
+    const int dc = level_of(c, k, L);
+    const uint64_t key = t.c_key[c];
+    int rank = t.c_rank[c];
+    for (int d0 = 1; d0 <= L; d0 += 8) rank += count_larger8(t.c_sorted, d0, L, dc, k, key);
+    t.c_pos[c] = (short)(rank < keep ? 1 : 0);
+  }
   __syncthreads();
-  // breadth-first positions: 1 + number of selected candidates with a smaller id
-  if (tid < 64) {
+  // breadth-first positions: 1 + number of selected candidates with a smaller id.
+  // Selected counts per 64-candidate group, then each candidate adds the counts of
+  // the groups before its own.
+  const int lane = tid & 63, wv = tid >> 6;
+  const int ngroups = (total + 63) >> 6;   // <= kMaxCand / 64 = 32
+  __shared__ int group_cnt[kMaxCand / 64];
+  for (int g = wv; g < ngroups; g += kTreeThreads / 64) {
+    const int c = (g << 6) + lane;
+    const uint64_t m = __ballot(c < total && t.c_pos[c] != 0);
+    if (lane == 0) group_cnt[g] = __popcll(m);
+  }
+  __syncthreads();
+  for (int g = wv; g < ngroups; g += kTreeThreads / 64) {
+    const int c = (g << 6) + lane;
+    const bool sel = c < total && t.c_pos[c] != 0;
+    const uint64_t m = __ballot(sel);
     int run = 0;
-    for (int base = 0; base < total; base += 64) {
-      const int c = base + tid;
-      const bool sel = c < total && t.c_pos[c] != 0;
-      const uint64_t m = __ballot(sel);
-      if (sel) t.c_pos[c] = (short)(1 + run + __popcll(m & ((1ull << tid) - 1ull)));
-      run += __popcll(m);
-    }
+    for (int j = 0; j < g; ++j) run += group_cnt[j];
+    if (sel) t.c_pos[c] = (short)(1 + run + __popcll(m & ((1ull << lane) - 1ull)));
   }
   __syncthreads();
   const size_t ob = (size_t)b * pl.n_nodes;
@@ -472,7 +534,7 @@ rerank_tree(RerankPlan pl, const int32_t* __restrict__ root_token, const float* 
   for (int c = tid; c < total; c += kTreeThreads) {
     const int pos = t.c_pos[c];
     if (pos == 0) continue;
-    const int dep = c < k ? 1 : 2 + (c - k) / (k * k);
+    const int dep = level_of(c, k, L);
     const int pc = t.c_par[c];
     tokens[ob + pos] = t.c_tok[c];
     parents[ob + pos] = pc < 0 ? 0 : t.c_pos[pc];
@@ -496,11 +558,7 @@ draft_frontier(RerankPlan pl, int d, const float* __restrict__ draft_lse, void* 
   const int k = pl.k;
   stage_rows(pl, w, draft_lse, b, 1 + (d - 1) * k, t);
   grow_levels(pl, d, t);
-  const int lb = d == 1 ? 0 : k + (d - 2) * k * k;
-  const int ln = d == 1 ? k : k * k;
-  for (int c = lb + tid; c < lb + ln; c += kTreeThreads) t.c_key[c] = vi_key(t.c_score[c], c);
-  __syncthreads();
-  rank_all(t.c_key, lb, ln, t.c_rank);
+  const int lb = level_base(d, k), ln = level_size(d, k);
   for (int c = lb + tid; c < lb + ln; c += kTreeThreads) {
     const int rank = t.c_rank[c];
     if (rank >= k) continue;
