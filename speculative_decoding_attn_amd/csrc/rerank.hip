@@ -142,6 +142,10 @@ __device__ __forceinline__ int rank_in(const uint64_t* keys, int lb, int n, uint
 // rounds instead (same order, same result).
 constexpr int kCandCap = 512;
 
+// VEC: 16-byte loads (V % 4 == 0 and 16-byte aligned logits), element e of thread tid
+// is x0 + (e/4)*1024 + 4*tid + e%4; otherwise 4-byte loads, element e is
+// x0 + e*256 + tid.  Either way every load instruction is coalesced.
+template <bool VEC>
 __global__ void __launch_bounds__(kRowThreads)
 rerank_rows(const float* __restrict__ logits, RerankPlan pl, void* ws) {
   __shared__ float redf[kRowThreads / 64];
@@ -157,16 +161,29 @@ rerank_rows(const float* __restrict__ logits, RerankPlan pl, void* ws) {
   const int x0 = chunk * pl.chunk_len;
   const float* src = logits + row * (size_t)V;
 
-  // element e of thread tid is x0 + e*256 + tid: every load instruction is coalesced
+  auto pos_of = [&](int e) {
+    return VEC ? x0 + (e >> 2) * (4 * kRowThreads) + 4 * tid + (e & 3) : x0 + e * kRowThreads + tid;
+  };
   float val[kRowPer];
+  if constexpr (VEC) {
+    static_assert(kRowPer % 4 == 0, "whole 16-byte groups per thread");
 #pragma unroll
-  for (int e = 0; e < kRowPer; ++e) {
-    const int x = x0 + e * kRowThreads + tid;
-    val[e] = x < V ? src[x] : -INFINITY;
+    for (int q = 0; q < kRowPer / 4; ++q) {
+      const int x = pos_of(4 * q);   // x % 4 == 0 and V % 4 == 0: x < V covers x + 3
+      const f32x4 v = x < V ? *(const f32x4*)(src + x) : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) val[4 * q + j] = v[j];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kRowPer; ++e) {
+      const int x = pos_of(e);
+      val[e] = x < V ? src[x] : -INFINITY;
+    }
   }
   // index of element e (past the row: the largest index, below every real one)
   auto idx_of = [&](int e) {
-    const int x = x0 + e * kRowThreads + tid;
+    const int x = pos_of(e);
     return x < V ? x : 0x7fffffff;
   };
   float lmax = val[0];
@@ -601,8 +618,12 @@ int rerank_max_row_list() { return kMaxRowList; }
 hipError_t launch_rerank_rows(const RerankPlan& pl, const float* draft_logits, float* draft_lse,
                               void* workspace, hipStream_t stream) {
   const int rows = pl.B * pl.nrows;
-  hipLaunchKernelGGL(rerank_rows, dim3(rows * pl.chunks), dim3(kRowThreads), 0, stream, draft_logits,
-                     pl, workspace);
+  if (pl.V % 4 == 0 && ((uintptr_t)draft_logits & 15) == 0)
+    hipLaunchKernelGGL(rerank_rows<true>, dim3(rows * pl.chunks), dim3(kRowThreads), 0, stream,
+                       draft_logits, pl, workspace);
+  else
+    hipLaunchKernelGGL(rerank_rows<false>, dim3(rows * pl.chunks), dim3(kRowThreads), 0, stream,
+                       draft_logits, pl, workspace);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(rerank_merge, dim3((rows + 3) / 4), dim3(256), 0, stream, pl, workspace,

@@ -38,6 +38,10 @@ CASES = [
     (2, 300, 8, 1, 9),
     (1, 20000, 16, 4, 64),
     (1, 64, 64, 1, 64),
+    # the last 8192-entry vocabulary chunk holds fewer than k entries (16-byte and
+    # 4-byte load paths)
+    (1, 16388, 10, 3, 25),
+    (2, 8195, 6, 3, 15),
 ]
 
 
