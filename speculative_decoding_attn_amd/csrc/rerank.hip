@@ -52,10 +52,10 @@ __device__ __forceinline__ uint32_t ordered_bits(float f) {
   const uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-__device__ __forceinline__ float key_value(uint64_t key) {
-  const uint32_t o = (uint32_t)(key >> 32);
+__device__ __forceinline__ float ordered_float(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
+__device__ __forceinline__ float key_value(uint64_t key) { return ordered_float((uint32_t)(key >> 32)); }
 __device__ __forceinline__ int key_index(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
 __device__ __forceinline__ uint64_t vi_key(float v, int i) {
   return ((uint64_t)ordered_bits(v) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
@@ -99,19 +99,17 @@ __host__ __device__ inline RrWs rr_ws(void* ws, const RerankPlan& pl) {
   return w;
 }
 
-// Descending bitonic sort of one float per lane across the wave.
-__device__ __forceinline__ float wave_sort_desc(float v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int k = 2; k <= 64; k <<= 1)
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const float o = __shfl_xor(v, j);
-      const bool lower = (lane & j) == 0;
-      const bool desc = (lane & k) == 0;
-      v = (lower == desc) ? fmaxf(v, o) : fminf(v, o);
-    }
-  return v;
+// k-th largest (1 <= k <= 64) of the wave's 64 values: the largest t (in the
+// order-preserving unsigned image) with at least k values >= t, found bit by bit
+// with ballots (no cross-lane data movement).
+__device__ __forceinline__ float wave_kth_largest(float v, int k) {
+  const uint32_t u = ordered_bits(v);
+  uint32_t t = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = t | (1u << bit);
+    if (__popcll(__ballot(u >= c)) >= k) t = c;
+  }
+  return ordered_float(t);
 }
 
 // Rank of key among keys lb .. lb+n-1 of an LDS list: how many come first (larger
@@ -150,7 +148,7 @@ __global__ void __launch_bounds__(kRowThreads)
 rerank_rows(const float* __restrict__ logits, RerankPlan pl, void* ws) {
   __shared__ float redf[kRowThreads / 64];
   __shared__ uint64_t cand_key[kCandCap];
-  __shared__ int wave_cnt[kRowThreads / 64];
+  __shared__ int ncand_s;
   __shared__ VI red[kRowThreads / 64];
   RrWs w = rr_ws(ws, pl);
   const int chunk = blockIdx.x % pl.chunks;
@@ -191,6 +189,7 @@ rerank_rows(const float* __restrict__ logits, RerankPlan pl, void* ws) {
   for (int e = 1; e < kRowPer; ++e) lmax = fmaxf(lmax, val[e]);
 
   // chunk max and exp-sum
+  if (tid == 0) ncand_s = 0;
   float mx = wave_max(lmax);
   if (lane == 0) redf[wid] = mx;
   __syncthreads();
@@ -206,29 +205,16 @@ rerank_rows(const float* __restrict__ logits, RerankPlan pl, void* ws) {
   __syncthreads();
   if (lane == 0) redf[wid] = z;
 
-  // candidates of this wave: elements >= the k-th largest lane maximum
+  // candidates of this wave: valid elements >= the k-th largest lane maximum; list
+  // slots by LDS adds (the list's order does not matter: ranks are counted)
   const int k = pl.k;
-  const float sorted = wave_sort_desc(lmax);
-  const float thr = k >= 64 ? -INFINITY : __shfl(sorted, k - 1);
+  const float thr = k >= 64 ? -INFINITY : wave_kth_largest(lmax, k);
   int mine = 0;
 #pragma unroll
   for (int e = 0; e < kRowPer; ++e) mine += (val[e] >= thr && idx_of(e) < V) ? 1 : 0;
-  int pre = mine;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(pre, o);
-    if (lane >= o) pre += t;
-  }
-  const int wtotal = __shfl(pre, 63);
-  pre -= mine;
-  if (lane == 0) wave_cnt[wid] = wtotal;
+  const int pos0 = mine > 0 ? atomicAdd(&ncand_s, mine) : 0;
   __syncthreads();
-  int off = 0, ncand = 0;
-#pragma unroll
-  for (int i = 0; i < kRowThreads / 64; ++i) {
-    if (i < wid) off += wave_cnt[i];
-    ncand += wave_cnt[i];
-  }
+  const int ncand = ncand_s;
   if (tid == 0) {
     float zt = 0.f;
     for (int i = 0; i < kRowThreads / 64; ++i) zt += redf[i];
@@ -237,7 +223,7 @@ rerank_rows(const float* __restrict__ logits, RerankPlan pl, void* ws) {
   float* out_v = w.chunk_v + (row * pl.chunks + chunk) * k;
   int* out_i = w.chunk_i + (row * pl.chunks + chunk) * k;
   if (ncand <= kCandCap) {
-    int pos = off + pre;
+    int pos = pos0;
 #pragma unroll
     for (int e = 0; e < kRowPer; ++e)
       if (val[e] >= thr && idx_of(e) < V) cand_key[pos++] = vi_key(val[e], idx_of(e));
@@ -321,7 +307,7 @@ rerank_merge(RerankPlan pl, void* ws, float* __restrict__ draft_lse) {
   float thr = -INFINITY;
   if (chunks <= 64 && k <= chunks) {
     const float cm = lane < chunks ? cv[(size_t)lane * k] : -INFINITY;
-    thr = __shfl(wave_sort_desc(cm), k - 1);
+    thr = wave_kth_largest(cm, k);
   }
   // keep entries >= thr (lane-major over the chunks * k entries)
   uint64_t* kk = keys[wid];
