@@ -99,6 +99,26 @@ __host__ __device__ inline RrWs rr_ws(void* ws, const RerankPlan& pl) {
   return w;
 }
 
+// Wave-wide max / sum with every lane holding the result, in registers: DPP steps
+// within rows of 16 (lane ^ 1, lane ^ 2, mirror within 8, mirror within 16), then
+// the 16- and 32-lane swaps pair each lane with lane ^ 16 and lane ^ 32.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+template <bool MAX>
+__device__ __forceinline__ float wave_reduce(float x) {
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+  x = op(x, dpp<0xB1>(x));    // quad_perm [1,0,3,2]
+  x = op(x, dpp<0x4E>(x));    // quad_perm [2,3,0,1]
+  x = op(x, dpp<0x141>(x));   // row_half_mirror
+  x = op(x, dpp<0x140>(x));   // row_mirror
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return op(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // k-th largest (1 <= k <= 64) of the wave's 64 values: the largest t (in the
 // order-preserving unsigned image) with at least k values >= t, found bit by bit
 // with ballots (no cross-lane data movement).
@@ -190,7 +210,7 @@ rerank_rows(const float* __restrict__ logits, RerankPlan pl, void* ws) {
 
   // chunk max and exp-sum
   if (tid == 0) ncand_s = 0;
-  float mx = wave_max(lmax);
+  float mx = wave_reduce<true>(lmax);
   if (lane == 0) redf[wid] = mx;
   __syncthreads();
   mx = redf[0];
@@ -201,7 +221,7 @@ rerank_rows(const float* __restrict__ logits, RerankPlan pl, void* ws) {
 #pragma unroll
     for (int e = 0; e < kRowPer; ++e) z += __builtin_amdgcn_exp2f((val[e] - mx) * kLog2e);
   }
-  z = wave_sum(z);
+  z = wave_reduce<false>(z);
   __syncthreads();
   if (lane == 0) redf[wid] = z;
 
@@ -291,13 +311,13 @@ rerank_merge(RerankPlan pl, void* ws, float* __restrict__ draft_lse) {
   const int k = pl.k, chunks = pl.chunks;
   float mx = -INFINITY;
   for (int c = lane; c < chunks; c += 64) mx = fmaxf(mx, w.chunk_mz[(size_t)row * chunks + c].x);
-  mx = wave_max(mx);
+  mx = wave_reduce<true>(mx);
   float z = 0.f;
   for (int c = lane; c < chunks; c += 64) {
     const float2 e = w.chunk_mz[(size_t)row * chunks + c];
     if (e.x > -INFINITY) z += e.y * __builtin_amdgcn_exp2f((e.x - mx) * kLog2e);
   }
-  z = wave_sum(z);
+  z = wave_reduce<false>(z);
   if (lane == 0) draft_lse[row] = mx + logf(z);
 
   const float* cv = w.chunk_v + (size_t)row * chunks * k;
