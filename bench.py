@@ -450,7 +450,7 @@ def summarize_profiles(root):
     dpath = os.path.join(root, "prof_draft", "run_kernel_stats.csv")
     if os.path.exists(dpath):
         # the library's kernels only (torch's weight initialisation is left out)
-        ours = ("lm_head_", "tree_attn_", "draft_", "rerank_")
+        ours = ("lm_head_", "gemm_splitk", "tree_attn_", "draft_", "rerank_")
         dstats = [r for r in _read_csv(dpath) if r["Name"].startswith(ours)]
         dtotal = sum(float(r["TotalDurationNs"]) for r in dstats)
         B_, H_, Hq_, Hkv_, D_, I_, V_, P_ = DRAFT_SHAPES["C5"]
