@@ -28,90 +28,115 @@ __device__ __forceinline__ int seq_row(int m, int nr, int row0, int R, int* b_ou
   return b * R + row0 + (m - b * nr);
 }
 
+// The elementwise kernels take a 2-D grid: blockIdx.y = processed row m, blockIdx.x
+// = a slice of kSlice columns, 8 columns (16-byte pieces) per thread.  Widths are
+// multiples of 8 (H, I multiples of 64; D 64 or 128).
+constexpr int kSlice = kGlueThreads * 8;
+
 // X[m] = [feature ; E[token]] (bf16, 2H): the root reads f0 and the root token, other
-// rows the feature of their parent row and their own token.  16-byte pieces.
+// rows the feature of their parent row and their own token.
 __global__ void __launch_bounds__(kGlueThreads)
 draft_gather_input(DraftDims dd, int row0, int nr, const uint16_t* __restrict__ f0,
                    const int32_t* __restrict__ root_token, const uint16_t* __restrict__ embed,
                    const uint16_t* __restrict__ feats, const int32_t* __restrict__ row_token,
                    const int32_t* __restrict__ parent_row, uint16_t* __restrict__ X) {
-  const int m = blockIdx.x;
+  const int m = blockIdx.y;
+  const int H = dd.H;
+  const int e = (blockIdx.x * kGlueThreads + threadIdx.x) * 8;   // column of [f ; E[t]]
+  if (e >= 2 * H) return;
   int b;
   const int grow = seq_row(m, nr, row0, dd.R, &b);
   const int r = grow - b * dd.R;
-  const int H = dd.H;
-  const uint16_t* fsrc;
-  int tok;
-  if (r == 0) {
-    fsrc = f0 + (size_t)b * H;
-    tok = root_token[b];
+  const uint16_t* src;
+  if (e < H) {
+    const int pr = r == 0 ? -1 : min(max(parent_row[grow], 0), dd.R - 1);
+    src = (r == 0 ? f0 + (size_t)b * H : feats + ((size_t)b * dd.R + pr) * H) + e;
   } else {
-    const int pr = min(max(parent_row[grow], 0), dd.R - 1);
-    fsrc = feats + ((size_t)b * dd.R + pr) * H;
-    tok = row_token[grow];
+    const int tok = min(max(r == 0 ? root_token[b] : row_token[grow], 0), dd.V - 1);
+    src = embed + (size_t)tok * H + (e - H);
   }
-  tok = min(max(tok, 0), dd.V - 1);
-  const uint16_t* esrc = embed + (size_t)tok * H;
-  uint16_t* dst = X + (size_t)m * 2 * H;
-  for (int e = threadIdx.x * 8; e < H; e += kGlueThreads * 8) {
-    *(u32x4*)(dst + e) = *(const u32x4*)(fsrc + e);
-    *(u32x4*)(dst + H + e) = *(const u32x4*)(esrc + e);
-  }
+  *(u32x4*)(X + (size_t)m * 2 * H + e) = *(const u32x4*)src;
 }
 
-__device__ __forceinline__ float block_sum(float v, float* red) {
-  v = wave_sum(v);
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[w] = v;
-  __syncthreads();
-  float t = 0.f;
-#pragma unroll
-  for (int i = 0; i < kGlueThreads / 64; ++i) t += red[i];
-  __syncthreads();
-  return t;
-}
+constexpr int kRmsThreads = 1024;
+constexpr int kRmsRegs = 4;   // float4 pieces per thread kept in registers: H <= 16384
 
-// s = a (+ res); res_out = s (fp32); norm_out = bf16(s / sqrt(mean(s^2) + eps) * gain)
-__global__ void __launch_bounds__(kGlueThreads)
+// s = a (+ res); res_out = s (fp32); norm_out = bf16(s / sqrt(mean(s^2) + eps) * gain).
+// One 1024-thread workgroup per row; for H <= 16384 every thread keeps its pieces of
+// s in registers, beyond that s is re-read from res_out.
+__global__ void __launch_bounds__(kRmsThreads)
 draft_rms(int H, float eps, const float* __restrict__ a, int lda, const float* __restrict__ res,
           const float* __restrict__ gain, float* __restrict__ res_out, uint16_t* __restrict__ norm_out) {
-  __shared__ float red[kGlueThreads / 64];
+  __shared__ float red[kRmsThreads / 64];
   const int m = blockIdx.x;
-  const float* ar = a + (size_t)m * lda;
-  const float* rr = res ? res + (size_t)m * H : nullptr;
+  const int tid = threadIdx.x;
+  const int nq = H / 4;
+  const f32x4* ar = (const f32x4*)(a + (size_t)m * lda);
+  const f32x4* rr = res ? (const f32x4*)(res + (size_t)m * H) : nullptr;
+  f32x4* so = (f32x4*)(res_out + (size_t)m * H);
+  f32x4 sv[kRmsRegs];
   float ss = 0.f;
-  for (int e = threadIdx.x; e < H; e += kGlueThreads) {
-    const float s = ar[e] + (rr ? rr[e] : 0.f);
-    res_out[(size_t)m * H + e] = s;
-    ss += s * s;
+#pragma unroll
+  for (int j = 0; j < kRmsRegs; ++j) {
+    const int q = tid + j * kRmsThreads;
+    if (q < nq) {
+      f32x4 v = ar[q];
+      if (rr) v += rr[q];
+      sv[j] = v;
+      so[q] = v;
+      ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+    }
   }
-  const float inv = rsqrtf(block_sum(ss, red) / (float)H + eps);
-  for (int e = 2 * threadIdx.x; e < H; e += 2 * kGlueThreads) {
-    const float s0 = res_out[(size_t)m * H + e], s1 = res_out[(size_t)m * H + e + 1];
-    *(uint32_t*)(norm_out + (size_t)m * H + e) = pack_bf16x2(s0 * inv * gain[e], s1 * inv * gain[e + 1]);
+  for (int q = tid + kRmsRegs * kRmsThreads; q < nq; q += kRmsThreads) {
+    f32x4 v = ar[q];
+    if (rr) v += rr[q];
+    so[q] = v;
+    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
   }
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int i = 0; i < kRmsThreads / 64; ++i) tot += red[i];
+  const float inv = rsqrtf(tot / (float)H + eps);
+  uint16_t* no = norm_out + (size_t)m * H;
+  auto put = [&](int q, f32x4 v) {
+    const int e = 4 * q;
+    *(uint2*)(no + e) = make_uint2(pack_bf16x2(v[0] * inv * gain[e], v[1] * inv * gain[e + 1]),
+                                   pack_bf16x2(v[2] * inv * gain[e + 2], v[3] * inv * gain[e + 3]));
+  };
+#pragma unroll
+  for (int j = 0; j < kRmsRegs; ++j) {
+    const int q = tid + j * kRmsThreads;
+    if (q < nq) put(q, sv[j]);
+  }
+  for (int q = tid + kRmsRegs * kRmsThreads; q < nq; q += kRmsThreads) put(q, so[q]);
 }
 
-// qkv fp32 [M][(Hq + 2 Hkv) D] -> q bf16 at [b][r][Hq][D]; k, v bf16 at cache row P + r
+// qkv fp32 [M][(Hq + 2 Hkv) D] -> q bf16 at [b][r][Hq][D]; k, v bf16 at cache row P + r.
+// A thread's 8 columns stay inside one head (D and the q / k / v widths are multiples of 8).
 __global__ void __launch_bounds__(kGlueThreads)
 draft_qkv_scatter(DraftDims dd, int row0, int nr, const float* __restrict__ qkv,
                   uint16_t* __restrict__ qbuf, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc) {
-  const int m = blockIdx.x;
+  const int m = blockIdx.y;
+  const int D = dd.D, qn = dd.Hq * D, kn = dd.Hkv * D;
+  const int e = (blockIdx.x * kGlueThreads + threadIdx.x) * 8;
+  if (e >= qn + 2 * kn) return;
   int b;
   const int grow = seq_row(m, nr, row0, dd.R, &b);
   const int r = grow - b * dd.R;
-  const int D = dd.D, qn = dd.Hq * D, kn = dd.Hkv * D;
-  const float* src = qkv + (size_t)m * (qn + 2 * kn);
-  for (int e = 2 * threadIdx.x; e < qn + 2 * kn; e += 2 * kGlueThreads) {
-    const uint32_t pk = pack_bf16x2(src[e], src[e + 1]);
-    if (e < qn) {
-      *(uint32_t*)(qbuf + (size_t)grow * qn + e) = pk;
-    } else {
-      const int f = (e - qn) % kn;
-      const int g = f / D, c = f % D;
-      uint16_t* cache = e < qn + kn ? kc : vc;
-      *(uint32_t*)(cache + (((size_t)b * dd.Hkv + g) * dd.kv_cap + dd.P + r) * D + c) = pk;
-    }
+  const f32x4* src = (const f32x4*)(qkv + (size_t)m * (qn + 2 * kn) + e);
+  const f32x4 v0 = src[0], v1 = src[1];
+  const u32x4 pk = {pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]), pack_bf16x2(v1[0], v1[1]),
+                    pack_bf16x2(v1[2], v1[3])};
+  if (e < qn) {
+    *(u32x4*)(qbuf + (size_t)grow * qn + e) = pk;
+  } else {
+    const int f = (e - qn) % kn;
+    const int g = f / D, c = f % D;
+    uint16_t* cache = e < qn + kn ? kc : vc;
+    *(u32x4*)(cache + (((size_t)b * dd.Hkv + g) * dd.kv_cap + dd.P + r) * D + c) = pk;
   }
 }
 
@@ -119,42 +144,51 @@ draft_qkv_scatter(DraftDims dd, int row0, int nr, const float* __restrict__ qkv,
 __global__ void __launch_bounds__(kGlueThreads)
 draft_gather_rows(DraftDims dd, int row0, int nr, int width, const uint16_t* __restrict__ src,
                   uint16_t* __restrict__ dst) {
-  const int m = blockIdx.x;
+  const int m = blockIdx.y;
+  const int e = (blockIdx.x * kGlueThreads + threadIdx.x) * 8;
+  if (e >= width) return;
   int b;
   const int grow = seq_row(m, nr, row0, dd.R, &b);
-  for (int e = threadIdx.x * 8; e < width; e += kGlueThreads * 8)
-    *(u32x4*)(dst + (size_t)m * width + e) = *(const u32x4*)(src + (size_t)grow * width + e);
+  *(u32x4*)(dst + (size_t)m * width + e) = *(const u32x4*)(src + (size_t)grow * width + e);
 }
 
 // gu fp32 [M][2I] (gate, then up) -> z = bf16(silu(gate) * up) [M][I]
 __global__ void __launch_bounds__(kGlueThreads)
 draft_silu_mul(int I, const float* __restrict__ gu, uint16_t* __restrict__ z) {
-  const int m = blockIdx.x;
-  const float* g = gu + (size_t)m * 2 * I;
-  for (int e = 2 * threadIdx.x; e < I; e += 2 * kGlueThreads) {
-    const float g0 = g[e], g1 = g[e + 1];
-    const float s0 = g0 / (1.f + __expf(-g0)), s1 = g1 / (1.f + __expf(-g1));
-    *(uint32_t*)(z + (size_t)m * I + e) = pack_bf16x2(s0 * g[I + e], s1 * g[I + e + 1]);
-  }
+  const int m = blockIdx.y;
+  const int e = (blockIdx.x * kGlueThreads + threadIdx.x) * 8;
+  if (e >= I) return;
+  const f32x4* g = (const f32x4*)(gu + (size_t)m * 2 * I + e);
+  const f32x4* u = (const f32x4*)(gu + (size_t)m * 2 * I + I + e);
+  const f32x4 g0 = g[0], g1 = g[1], u0 = u[0], u1 = u[1];
+  auto sm = [](float x, float up) { return x / (1.f + __expf(-x)) * up; };
+  *(u32x4*)(z + (size_t)m * I + e) =
+      u32x4{pack_bf16x2(sm(g0[0], u0[0]), sm(g0[1], u0[1])), pack_bf16x2(sm(g0[2], u0[2]), sm(g0[3], u0[3])),
+            pack_bf16x2(sm(g1[0], u1[0]), sm(g1[1], u1[1])), pack_bf16x2(sm(g1[2], u1[2]), sm(g1[3], u1[3]))};
 }
 
 // y = bf16(h + d): dense [M][H] (the LM head input) and the row's feature [b][r][H]
 __global__ void __launch_bounds__(kGlueThreads)
 draft_output(DraftDims dd, int row0, int nr, const float* __restrict__ d, const float* __restrict__ h,
              uint16_t* __restrict__ y, uint16_t* __restrict__ feats) {
-  const int m = blockIdx.x;
+  const int m = blockIdx.y;
+  const int H = dd.H;
+  const int e = (blockIdx.x * kGlueThreads + threadIdx.x) * 8;
+  if (e >= H) return;
   int b;
   const int grow = seq_row(m, nr, row0, dd.R, &b);
-  const int H = dd.H;
-  for (int e = 2 * threadIdx.x; e < H; e += 2 * kGlueThreads) {
-    const size_t i = (size_t)m * H + e;
-    const uint32_t pk = pack_bf16x2(h[i] + d[i], h[i + 1] + d[i + 1]);
-    *(uint32_t*)(y + i) = pk;
-    *(uint32_t*)(feats + (size_t)grow * H + e) = pk;
-  }
+  const size_t i = (size_t)m * H + e;
+  const f32x4 h0 = *(const f32x4*)(h + i), h1 = *(const f32x4*)(h + i + 4);
+  const f32x4 d0 = *(const f32x4*)(d + i), d1 = *(const f32x4*)(d + i + 4);
+  const u32x4 pk = {pack_bf16x2(h0[0] + d0[0], h0[1] + d0[1]), pack_bf16x2(h0[2] + d0[2], h0[3] + d0[3]),
+                    pack_bf16x2(h1[0] + d1[0], h1[1] + d1[1]), pack_bf16x2(h1[2] + d1[2], h1[3] + d1[3])};
+  *(u32x4*)(y + i) = pk;
+  *(u32x4*)(feats + (size_t)grow * H + e) = pk;
 }
 
-// logits [M][V] -> the rows' slots of draft_logits [B][R][V]
+// logits [M][V] -> the rows' slots of draft_logits [B][R][V] (16-byte pieces when
+// V % 4 == 0, which keeps every row 16-byte aligned)
+template <bool VEC>
 __global__ void __launch_bounds__(kGlueThreads)
 draft_place_logits(DraftDims dd, int row0, int nr, const float* __restrict__ src,
                    float* __restrict__ draft_logits) {
@@ -162,8 +196,16 @@ draft_place_logits(DraftDims dd, int row0, int nr, const float* __restrict__ src
   int b;
   const int grow = seq_row(m, nr, row0, dd.R, &b);
   const size_t V = dd.V;
-  for (size_t e = (size_t)blockIdx.x * kGlueThreads + threadIdx.x; e < V; e += (size_t)gridDim.x * kGlueThreads)
-    draft_logits[(size_t)grow * V + e] = src[(size_t)m * V + e];
+  const size_t e = ((size_t)blockIdx.x * kGlueThreads + threadIdx.x) * 8;
+  if (VEC) {
+    if (e >= V) return;
+    const f32x4* s4 = (const f32x4*)(src + (size_t)m * V + e);
+    f32x4* d4 = (f32x4*)(draft_logits + (size_t)grow * V + e);
+    d4[0] = s4[0];
+    if (e + 4 < V) d4[1] = s4[1];
+  } else {
+    for (size_t x = e; x < e + 8 && x < V; ++x) draft_logits[(size_t)grow * V + x] = src[(size_t)m * V + x];
+  }
 }
 
 // every row starts without a parent (the root keeps -1) and with token 0; row 0 of a
@@ -183,7 +225,8 @@ hipError_t launch_draft_gather_input(const DraftDims& dd, int row0, int nr, cons
                                      const int32_t* root_token, const void* embed, const void* feats,
                                      const int32_t* row_token, const int32_t* parent_row, void* X,
                                      hipStream_t s) {
-  hipLaunchKernelGGL(draft_gather_input, dim3(dd.B * nr), dim3(kGlueThreads), 0, s, dd, row0, nr,
+  hipLaunchKernelGGL(draft_gather_input, dim3((2 * dd.H + kSlice - 1) / kSlice, dd.B * nr),
+                     dim3(kGlueThreads), 0, s, dd, row0, nr,
                      (const uint16_t*)f0, root_token, (const uint16_t*)embed, (const uint16_t*)feats,
                      row_token, parent_row, (uint16_t*)X);
   return hipGetLastError();
@@ -191,42 +234,51 @@ hipError_t launch_draft_gather_input(const DraftDims& dd, int row0, int nr, cons
 
 hipError_t launch_draft_rms(int M, int H, float eps, const float* a, int lda, const float* res,
                             const float* gain, float* res_out, void* norm_out, hipStream_t s) {
-  hipLaunchKernelGGL(draft_rms, dim3(M), dim3(kGlueThreads), 0, s, H, eps, a, lda, res, gain, res_out,
+  hipLaunchKernelGGL(draft_rms, dim3(M), dim3(kRmsThreads), 0, s, H, eps, a, lda, res, gain, res_out,
                      (uint16_t*)norm_out);
   return hipGetLastError();
 }
 
 hipError_t launch_draft_qkv_scatter(const DraftDims& dd, int row0, int nr, const float* qkv, void* qbuf,
                                     void* k_cache, void* v_cache, hipStream_t s) {
-  hipLaunchKernelGGL(draft_qkv_scatter, dim3(dd.B * nr), dim3(kGlueThreads), 0, s, dd, row0, nr, qkv,
+  const int width = (dd.Hq + 2 * dd.Hkv) * dd.D;
+  hipLaunchKernelGGL(draft_qkv_scatter, dim3((width + kSlice - 1) / kSlice, dd.B * nr), dim3(kGlueThreads),
+                     0, s, dd, row0, nr, qkv,
                      (uint16_t*)qbuf, (uint16_t*)k_cache, (uint16_t*)v_cache);
   return hipGetLastError();
 }
 
 hipError_t launch_draft_gather_rows(const DraftDims& dd, int row0, int nr, int width, const void* src,
                                     void* dst, hipStream_t s) {
-  hipLaunchKernelGGL(draft_gather_rows, dim3(dd.B * nr), dim3(kGlueThreads), 0, s, dd, row0, nr, width,
+  hipLaunchKernelGGL(draft_gather_rows, dim3((width + kSlice - 1) / kSlice, dd.B * nr), dim3(kGlueThreads),
+                     0, s, dd, row0, nr, width,
                      (const uint16_t*)src, (uint16_t*)dst);
   return hipGetLastError();
 }
 
 hipError_t launch_draft_silu_mul(int M, int I, const float* gu, void* z, hipStream_t s) {
-  hipLaunchKernelGGL(draft_silu_mul, dim3(M), dim3(kGlueThreads), 0, s, I, gu, (uint16_t*)z);
+  hipLaunchKernelGGL(draft_silu_mul, dim3((I + kSlice - 1) / kSlice, M), dim3(kGlueThreads), 0, s, I, gu,
+                     (uint16_t*)z);
   return hipGetLastError();
 }
 
 hipError_t launch_draft_output(const DraftDims& dd, int row0, int nr, const float* d, const float* h,
                                void* y, void* feats, hipStream_t s) {
-  hipLaunchKernelGGL(draft_output, dim3(dd.B * nr), dim3(kGlueThreads), 0, s, dd, row0, nr, d, h,
+  hipLaunchKernelGGL(draft_output, dim3((dd.H + kSlice - 1) / kSlice, dd.B * nr), dim3(kGlueThreads), 0, s,
+                     dd, row0, nr, d, h,
                      (uint16_t*)y, (uint16_t*)feats);
   return hipGetLastError();
 }
 
 hipError_t launch_draft_place_logits(const DraftDims& dd, int row0, int nr, const float* src,
                                      float* draft_logits, hipStream_t s) {
-  const int xblocks = (int)((dd.V + kGlueThreads * 8 - 1) / (kGlueThreads * 8));
-  hipLaunchKernelGGL(draft_place_logits, dim3(xblocks, dd.B * nr), dim3(kGlueThreads), 0, s, dd, row0,
-                     nr, src, draft_logits);
+  const int xblocks = (int)((dd.V + kSlice - 1) / kSlice);
+  if (dd.V % 4 == 0)
+    hipLaunchKernelGGL(draft_place_logits<true>, dim3(xblocks, dd.B * nr), dim3(kGlueThreads), 0, s, dd,
+                       row0, nr, src, draft_logits);
+  else
+    hipLaunchKernelGGL(draft_place_logits<false>, dim3(xblocks, dd.B * nr), dim3(kGlueThreads), 0, s, dd,
+                       row0, nr, src, draft_logits);
   return hipGetLastError();
 }
 
