@@ -849,9 +849,12 @@ AttnPlan plan_tree_attn_rows(int B, int N, int node0, int nq, int Hq, int Hkv, i
   while (pl.waves < max_waves && pl.waves * wave_rows < pl.R) pl.waves *= 2;
   pl.RB = (pl.R + pl.waves * wave_rows - 1) / (pl.waves * wave_rows);
   pl.Rpad = pl.RB * pl.waves * wave_rows;
-  // about one workgroup per CU
+  // About one workgroup per CU; narrow workgroups (one or two waves, one wave per SIMD
+  // at most) get three or two per CU so that every SIMD streams keys (the LDS of
+  // three fits in a CU)
   const long long units = (long long)B * Hkv * pl.RB;
-  int s_target = (int)((kNumCUs + units - 1) / units);
+  const int wg_per_cu = pl.waves == 1 ? 3 : (pl.waves == 2 ? 2 : 1);
+  int s_target = (int)(((long long)kNumCUs * wg_per_cu + units - 1) / units);
   int s_max = P / kMinSplitKeys;
   int S = s_target < s_max ? s_target : s_max;
   if (S < 1) S = 1;
