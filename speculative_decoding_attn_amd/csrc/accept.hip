@@ -95,6 +95,7 @@ accept_greedy_kernel(const int32_t* __restrict__ tokens, const int32_t* __restri
 // timeout the sequence's accept_len is set to -1 and all its workgroups leave.
 // ---------------------------------------------------------------------------
 constexpr int kSpecThreads = 256;
+constexpr int kSpecRegs = 16;   // entries per thread kept in registers (chunks up to 4096)
 constexpr unsigned kSpinLimit = 1u << 24;
 
 struct SpecWs {
@@ -202,7 +203,7 @@ __device__ bool exchange(const SpecWs& w, int b, int chunks, int me, unsigned ge
   return ok;
 }
 
-__global__ void __launch_bounds__(kSpecThreads)
+__global__ void __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)))
 accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict__ parents,
                    const int32_t* __restrict__ draft_row, const float* __restrict__ target_logits,
                    const float* __restrict__ draft_logits, const float* __restrict__ u_accept,
@@ -239,6 +240,8 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
 
   double sample_c = 0.0;   // corrected target for the final draw: max(0, q - c p) / S
   int sample_node = 0;
+  const bool in_regs = x1 - x0 <= kSpecRegs * kSpecThreads;
+  double qr[kSpecRegs], pr[kSpecRegs];   // q, p of the thread's entries when in_regs
 
   for (;;) {
     // children of v in ascending index (none at max_depth)
@@ -253,20 +256,49 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
     int row = draft_row[(size_t)b * N + v];
     const bool has_draft = nk > 0 && row >= 0 && row < pl.R;
 
-    // ---- q and p of node v: chunk max / exp-sum, exchanged, then fp64 values
+    // ---- q and p of node v: chunk max / exp-sum, exchanged, then fp64 values.  A
+    // thread's entries are x0 + tid + i * kSpecThreads; when the chunk fits, they are
+    // loaded once into registers (same order of operations either way).
     const float* tl = target_logits + ((size_t)b * N + v) * V;
     const float* dl = has_draft ? draft_logits + ((size_t)b * pl.R + row) * V : tl;
     double mq = -INFINITY, mp = -INFINITY;
-    for (int x = x0 + tid; x < x1; x += kSpecThreads) {
-      mq = fmax(mq, (double)tl[x]);
-      mp = fmax(mp, (double)dl[x]);
+    float tr[kSpecRegs], dr[kSpecRegs];
+    if (in_regs) {
+#pragma unroll
+      for (int i = 0; i < kSpecRegs; ++i) {
+        const int x = x0 + tid + i * kSpecThreads;
+        tr[i] = x < x1 ? tl[x] : -INFINITY;
+        dr[i] = x < x1 ? dl[x] : -INFINITY;
+      }
+#pragma unroll
+      for (int i = 0; i < kSpecRegs; ++i) {
+        if (x0 + tid + i * kSpecThreads < x1) {
+          mq = fmax(mq, (double)tr[i]);
+          mp = fmax(mp, (double)dr[i]);
+        }
+      }
+    } else {
+      for (int x = x0 + tid; x < x1; x += kSpecThreads) {
+        mq = fmax(mq, (double)tl[x]);
+        mp = fmax(mp, (double)dl[x]);
+      }
     }
     mq = wg_max_d(mq, red);
     mp = wg_max_d(mp, red);
     double zq = 0.0, zp = 0.0;
-    for (int x = x0 + tid; x < x1; x += kSpecThreads) {
-      zq += exp((double)tl[x] - mq);
-      zp += exp((double)dl[x] - mp);
+    if (in_regs) {
+#pragma unroll
+      for (int i = 0; i < kSpecRegs; ++i) {
+        if (x0 + tid + i * kSpecThreads < x1) {
+          zq += exp((double)tr[i] - mq);
+          zp += exp((double)dr[i] - mp);
+        }
+      }
+    } else {
+      for (int x = x0 + tid; x < x1; x += kSpecThreads) {
+        zq += exp((double)tl[x] - mq);
+        zp += exp((double)dl[x] - mp);
+      }
     }
     zq = wg_sum_d(zq, red);
     zp = wg_sum_d(zp, red);
@@ -286,9 +318,22 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
     }
     const double lse_q = Mq + log(Zq);
     const double lse_p = Mp + log(Zp);
-    for (int x = x0 + tid; x < x1; x += kSpecThreads) {
-      qb[x] = exp((double)tl[x] - lse_q);
-      pb[x] = exp((double)dl[x] - lse_p);
+    if (in_regs) {
+#pragma unroll
+      for (int i = 0; i < kSpecRegs; ++i) {
+        const int x = x0 + tid + i * kSpecThreads;
+        qr[i] = x < x1 ? exp((double)tr[i] - lse_q) : 0.0;
+        pr[i] = x < x1 ? exp((double)dr[i] - lse_p) : 0.0;
+        if (x < x1) {
+          qb[x] = qr[i];
+          pb[x] = pr[i];
+        }
+      }
+    } else {
+      for (int x = x0 + tid; x < x1; x += kSpecThreads) {
+        qb[x] = exp((double)tl[x] - lse_q);
+        pb[x] = exp((double)dl[x] - lse_p);
+      }
     }
     __syncthreads();
 
@@ -317,7 +362,13 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
       }
       const double c2 = cst + S;
       double part = 0.0;
-      for (int x = x0 + tid; x < x1; x += kSpecThreads) part += fmax(0.0, qb[x] - c2 * pb[x]);
+      if (in_regs) {
+#pragma unroll
+        for (int i = 0; i < kSpecRegs; ++i)
+          if (x0 + tid + i * kSpecThreads < x1) part += fmax(0.0, qr[i] - c2 * pr[i]);
+      } else {
+        for (int x = x0 + tid; x < x1; x += kSpecThreads) part += fmax(0.0, qb[x] - c2 * pb[x]);
+      }
       part = wg_sum_d(part, red);
       const double mine[4] = {part, 0.0, 0.0, 0.0};
       if (!exchange(w, b, chunks, me, gen++, mine, lds_all, &lds_flag)) { aborted = true; break; }
