@@ -100,6 +100,15 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_byte_addr) {
                : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_byte_addr))
                : "memory", "m0");
 }
+// The same copy with the non-temporal cache policy, for data read exactly once (a
+// weight stream): its lines are not kept in the caches at the expense of operands
+// that are reused, such as the hidden rows every workgroup re-reads from L2.
+__device__ __forceinline__ void dma16_nt(const void* src, uint32_t lds_byte_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+               :
+               : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_byte_addr))
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {

@@ -10,7 +10,8 @@
 // (for the largest M: 8 waves, two per SIMD, so one wave's MFMAs cover the other's
 // waits).  Both operands are staged in LDS, 64 columns (128 bytes per row) at
 // a time, by global->LDS DMA loads that read whole 128-byte lines (8 rows per wave
-// instruction) into XOR-swizzled rows; W is streamed from HBM exactly once and runs
+// instruction) into XOR-swizzled rows; W is streamed from HBM exactly once (non-
+// temporal loads, so it does not evict the hidden rows from L2) and runs
 // two to three blocks ahead, the hidden rows (L2-resident) one to two.  In the output
 // layout every lane holds 16 vocabulary entries of ONE row, so the epilogue reduces
 // in registers, then across lane l ^ 32, then across the waves of the workgroup, and
@@ -133,7 +134,7 @@ lm_head_gemm(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W
   // one DMA instruction t (8 rows) of W / hidden block blk into stage st; hidden
   // groups wholly past M are skipped (their rows are never written out)
   auto issue_w = [&](int blk, int st, int t) {
-    dma16(wsrc[t] + (size_t)blk * RB, base + st * WSTAGE + 8 * (wv * W_DMA + t) * RB);
+    dma16_nt(wsrc[t] + (size_t)blk * RB, base + st * WSTAGE + 8 * (wv * W_DMA + t) * RB);
   };
   auto issue_h = [&](int blk, int st, int t) {
     if (m0 + 8 * (wv * H_DMA + t) < M)
@@ -310,9 +311,20 @@ lm_head_merge(LmPlan pl, const f32x4* __restrict__ part, float* __restrict__ out
   const int m = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
   if (m >= pl.M) return;
   Top2 t{-INFINITY, -INFINITY, 0.f, 0x7fffffff};
-  for (int p = lane; p < pl.nvt; p += 64) {
-    const f32x4 e = part[(size_t)m * pl.nvt + p];
-    t = merge_top2(t, Top2{e[0], e[1], e[2], __float_as_int(e[3])});
+  // up to PB partials per lane are loaded before any of them is merged (one memory
+  // round trip per row for up to 64*PB vocabulary tiles)
+  constexpr int PB = 8;
+  for (int p0 = 0; p0 < pl.nvt; p0 += 64 * PB) {
+    f32x4 e[PB];
+#pragma unroll
+    for (int u = 0; u < PB; ++u) {
+      const int p = p0 + 64 * u + lane;
+      e[u] = p < pl.nvt ? part[(size_t)m * pl.nvt + p] : f32x4{-INFINITY, -INFINITY, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < PB; ++u)
+      if (p0 + 64 * u + lane < pl.nvt)
+        t = merge_top2(t, Top2{e[u][0], e[u][1], e[u][2], __float_as_int(e[u][3])});
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) t = merge_top2(t, shfl_xor_top2(t, o));

@@ -438,7 +438,7 @@ tree_attn_merge(AttnPlan pl, const float* __restrict__ part_o, const float* __re
 // runs the exponentials.
 //
 // K and V chunks reach LDS by global-to-LDS DMA (each lane moves 16 bytes to
-// m0 + 16*lane), four chunks deep.  Rows are stored whole (256 bytes) with their
+// m0 + 16*lane, non-temporal: the cache streams through once), four chunks deep.  Rows are stored whole (256 bytes) with their
 // 16-byte pieces permuted: K piece c of row r sits at c ^ (r & 15), which makes the
 // b128 fragment reads of 16 consecutive rows hit every bank once; V piece c of row r
 // sits at c ^ 4*(r & 3), which does the same for the transposing reads
@@ -559,8 +559,8 @@ tree_attn_pingpong(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       const int row = 8 * wv + 4 * t + (lane >> 4);
       const size_t off = row_off(min(kb + row, key_lim - 1));
       const uint32_t dst = st + (uint32_t)(8 * wv + 4 * t) * XROW;
-      dma16(kbase + off + 8 * ((lane & 15) ^ (row & 15)), dst);
-      dma16(vbase + off + 8 * ((lane & 15) ^ (4 * (row & 3))), dst + XHALF);
+      dma16_nt(kbase + off + 8 * ((lane & 15) ^ (row & 15)), dst);
+      dma16_nt(vbase + off + 8 * ((lane & 15) ^ (4 * (row & 3))), dst + XHALF);
     }
   };
 
