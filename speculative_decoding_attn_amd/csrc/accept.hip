@@ -90,18 +90,20 @@ accept_greedy_kernel(const int32_t* __restrict__ tokens, const int32_t* __restri
 //
 // Parallel layout.  Each sequence gets `chunks` workgroups, each owning a contiguous
 // slice of the vocabulary.  Every workgroup follows the same control flow; the
-// vocabulary reductions are exchanged through the workspace and a per-sequence
-// counter barrier (release/acquire at agent scope).  Every spin is bounded: on
-// timeout the sequence's accept_len is set to -1 and all its workgroups leave.
+// vocabulary reductions are exchanged through the workspace in self-validating
+// words (each 64-bit word carries the exchange's generation next to 32 bits of a
+// partial), so a reader needs no separate arrival counter or ordering wait: it polls
+// the words themselves.  Every spin is bounded: on timeout the sequence's accept_len
+// is set to -1 and all its workgroups leave.
 // ---------------------------------------------------------------------------
 constexpr int kSpecThreads = 256;
 constexpr int kSpecRegs = 16;   // entries per thread kept in registers (chunks up to 4096)
 constexpr unsigned kSpinLimit = 1u << 24;
 
 struct SpecWs {
-  unsigned* counters;   // [B] barrier arrivals
+  unsigned* counters;   // [B] (unused; kept for the layout)
   int* abort_flags;     // [B]
-  double* slots;        // [B][2][chunks][4] exchanged partials
+  unsigned long long* slots;   // [B][2][chunks][8] tagged halves of the exchanged partials
   double* qbuf;         // [B][V] fp64 q of the current node
   double* pbuf;         // [B][V] fp64 p of the current node
 };
@@ -112,8 +114,8 @@ __device__ __forceinline__ SpecWs spec_ws(void* ws, int B, int chunks, int V) {
   w.counters = (unsigned*)base;
   w.abort_flags = (int*)(base + 256 * ((B * 4 + 255) / 256));
   size_t off = 2 * 256 * (size_t)((B * 4 + 255) / 256);
-  w.slots = (double*)(base + off);
-  off += (size_t)B * 2 * chunks * 4 * sizeof(double);
+  w.slots = (unsigned long long*)(base + off);
+  off += (size_t)B * 2 * chunks * 8 * sizeof(unsigned long long);
   off = (off + 255) / 256 * 256;
   w.qbuf = (double*)(base + off);
   off += (size_t)B * V * sizeof(double);
@@ -127,6 +129,10 @@ __global__ void spec_init_kernel(void* ws, int B, int chunks, int V) {
     w.counters[i] = 0u;
     w.abort_flags[i] = 0;
   }
+  // generation tags start at 0: no word left by an earlier call can look current
+  const int nslot = B * 2 * chunks * 8;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < nslot; i += gridDim.x * blockDim.x)
+    w.slots[i] = 0ull;
 }
 
 // Workgroup-wide sum of a double (all threads get the result).
@@ -155,52 +161,60 @@ __device__ __forceinline__ double wg_max_d(double x, double* red) {
   return t;
 }
 
-// Publish this workgroup's 4 partials for generation `gen`, wait for all chunks of
-// the sequence, and return the chunk-ordered partials in lds_all[chunks][4].
-// Returns false on timeout.  The partials and the arrival counter are accessed with
-// relaxed agent-scope atomics, which are coherent across the XCDs' L2 caches without
-// cache-wide write-back or invalidation; the partial stores are complete (s_waitcnt
-// vmcnt(0)) before the counter increment that announces them, and the partial loads
-// are issued only after the counter has been seen complete.
-__device__ bool exchange(const SpecWs& w, int b, int chunks, int me, unsigned gen,
+// Publish this workgroup's first nv partials (of 4) for generation `gen`, wait for
+// every chunk of the sequence, and return the chunk-ordered partials in
+// lds_all[chunks][4] (entries k < nv).  Returns false on timeout.
+//
+// A double is sent as two 64-bit words: generation + 1 in the high 32 bits, one half
+// of the double in the low 32 bits.  64-bit stores and loads are single-copy atomic,
+// so a word whose tag matches holds that half of this generation's value, whatever
+// order the words become visible in: readers poll the words directly (relaxed
+// agent-scope atomics, coherent across the XCDs' L2 caches) and write the halves
+// straight into lds_all, which is the little-endian layout of the doubles.  The two
+// buffers alternate by generation; a workgroup can only write generation g + 2 after
+// every workgroup has written g + 1, i.e. after all of them have read g.
+__device__ bool exchange(const SpecWs& w, int b, int chunks, int me, unsigned gen, int nv,
                          const double (&mine)[4], double* lds_all, int* lds_flag) {
-  unsigned long long* slot =
-      (unsigned long long*)(w.slots + (((size_t)b * 2 + (gen & 1)) * chunks) * 4);
-  if (threadIdx.x < 4)
-    __hip_atomic_store(&slot[me * 4 + threadIdx.x], __double_as_longlong(mine[threadIdx.x]),
+  unsigned long long* slot = w.slots + (((size_t)b * 2 + (gen & 1)) * chunks) * 8;
+  const unsigned tag = gen + 1;
+  const int nw = 2 * nv;
+  if (threadIdx.x < nw) {
+    const int k = threadIdx.x >> 1;
+    const double val = k == 0 ? mine[0] : (k == 1 ? mine[1] : (k == 2 ? mine[2] : mine[3]));
+    const unsigned long long bits = (unsigned long long)__double_as_longlong(val);
+    const unsigned half = (threadIdx.x & 1) ? (unsigned)(bits >> 32) : (unsigned)bits;
+    __hip_atomic_store(&slot[me * 8 + threadIdx.x], ((unsigned long long)tag << 32) | half,
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int ok = 1;
-    if (chunks > 1) {
-      __hip_atomic_fetch_add(&w.counters[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const unsigned target = (gen + 1) * (unsigned)chunks;
-      unsigned spins = 0;
-      while (__hip_atomic_load(&w.counters[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-        if (__hip_atomic_load(&w.abort_flags[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-          ok = 0;
-          break;
-        }
-        if (++spins > kSpinLimit) {
-          __hip_atomic_store(&w.abort_flags[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          ok = 0;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
+  }
+  if (threadIdx.x == 0) *lds_flag = 1;
+  __syncthreads();   // lds_flag set; every thread is done with the previous lds_all
+  bool ok = true;
+  unsigned* words = (unsigned*)lds_all;
+  for (int i = threadIdx.x; i < chunks * nw; i += blockDim.x) {
+    const int c = i / nw, k = i - c * nw;
+    unsigned spins = 0;
+    unsigned long long v;
+    for (;;) {
+      v = __hip_atomic_load(&slot[c * 8 + k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((unsigned)(v >> 32) == tag) break;
+      if ((++spins & 63u) == 0u &&
+          __hip_atomic_load(&w.abort_flags[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+        ok = false;
+        break;
       }
+      if (spins > kSpinLimit) {
+        __hip_atomic_store(&w.abort_flags[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ok = false;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
     }
-    *lds_flag = ok;
+    if (!ok) break;
+    words[c * 8 + k] = (unsigned)v;
   }
+  if (!ok) *lds_flag = 0;
   __syncthreads();
-  const bool ok = *lds_flag != 0;
-  if (ok) {
-    for (int i = threadIdx.x; i < chunks * 4; i += blockDim.x)
-      lds_all[i] = __longlong_as_double(
-          (long long)__hip_atomic_load(&slot[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-  }
-  __syncthreads();
-  return ok;
+  return *lds_flag != 0;
 }
 
 __global__ void __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)))
@@ -214,6 +228,9 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
   __shared__ int lds_flag;
   __shared__ int kids[64];
   __shared__ int nkids_s;
+  // per child (in sibling order): token, its target and draft logits, its uniform
+  __shared__ int kid_tok[64];
+  __shared__ float kid_tl[64], kid_dl[64], kid_u[64];
   __shared__ int path_s[65];
 
   const int chunks = pl.chunks;
@@ -239,6 +256,7 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
   bool aborted = false;
 
   double sample_c = 0.0;   // corrected target for the final draw: max(0, q - c p) / S
+  double fallback_c = 0.0; // the previous c, should the residual at sample_c be empty
   int sample_node = 0;
   const bool in_regs = x1 - x0 <= kSpecRegs * kSpecThreads;
   double qr[kSpecRegs], pr[kSpecRegs];   // q, p of the thread's entries when in_regs
@@ -255,12 +273,23 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
     const int nk = nkids_s;
     int row = draft_row[(size_t)b * N + v];
     const bool has_draft = nk > 0 && row >= 0 && row < pl.R;
+    const float* tl = target_logits + ((size_t)b * N + v) * V;
+    const float* dl = has_draft ? draft_logits + ((size_t)b * pl.R + row) * V : tl;
+    // the children's operands, loaded once here so that their latency overlaps the
+    // softmax below instead of sitting in every rejection round
+    if (tid < nk) {
+      const int kid = kids[tid];
+      const int t = tok[kid];
+      const bool tv = t >= 0 && t < V;
+      kid_tok[tid] = tv ? t : -1;
+      kid_tl[tid] = tv ? tl[t] : 0.f;
+      kid_dl[tid] = tv ? dl[t] : 0.f;
+      kid_u[tid] = u_accept[(size_t)b * N + kid];
+    }
 
     // ---- q and p of node v: chunk max / exp-sum, exchanged, then fp64 values.  A
     // thread's entries are x0 + tid + i * kSpecThreads; when the chunk fits, they are
     // loaded once into registers (same order of operations either way).
-    const float* tl = target_logits + ((size_t)b * N + v) * V;
-    const float* dl = has_draft ? draft_logits + ((size_t)b * pl.R + row) * V : tl;
     double mq = -INFINITY, mp = -INFINITY;
     float tr[kSpecRegs], dr[kSpecRegs];
     if (in_regs) {
@@ -304,7 +333,7 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
     zp = wg_sum_d(zp, red);
     {
       const double mine[4] = {mq, zq, mp, zp};
-      if (!exchange(w, b, chunks, me, gen++, mine, lds_all, &lds_flag)) { aborted = true; break; }
+      if (!exchange(w, b, chunks, me, gen++, 4, mine, lds_all, &lds_flag)) { aborted = true; break; }
     }
     double Mq = -INFINITY, Mp = -INFINITY;
     for (int c = 0; c < chunks; ++c) {
@@ -345,22 +374,28 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
 
     // ---- children in order against the corrected target
     double cst = 0.0, S = 1.0;
+    double last_c = -1.0;
     int accepted = -1;
     for (int j = 0; j < nk; ++j) {
       const int kid = kids[j];
-      const int t = tok[kid];
       double qt = 0.0, pt = 0.0;
-      if (t >= 0 && t < V) {
-        qt = exp((double)tl[t] - lse_q);
-        pt = exp((double)dl[t] - lse_p);
+      if (kid_tok[j] >= 0) {
+        qt = exp((double)kid_tl[j] - lse_q);
+        pt = exp((double)kid_dl[j] - lse_p);
       }
       const double resid = fmax(0.0, qt - cst * pt);
       const double ratio = pt > 0.0 ? fmin(1.0, resid / (S * pt)) : (resid > 0.0 ? 1.0 : 0.0);
-      if ((double)u_accept[(size_t)b * N + kid] < ratio) {
+      if ((double)kid_u[j] < ratio) {
         accepted = kid;
         break;
       }
       const double c2 = cst + S;
+      if (j == nk - 1) {
+        // every child rejected: the residual at c2 is drawn from directly; its mass
+        // comes with the draw's chunk totals (zero exactly when S(c2) is zero)
+        last_c = c2;
+        break;
+      }
       double part = 0.0;
       if (in_regs) {
 #pragma unroll
@@ -371,7 +406,7 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
       }
       part = wg_sum_d(part, red);
       const double mine[4] = {part, 0.0, 0.0, 0.0};
-      if (!exchange(w, b, chunks, me, gen++, mine, lds_all, &lds_flag)) { aborted = true; break; }
+      if (!exchange(w, b, chunks, me, gen++, 1, mine, lds_all, &lds_flag)) { aborted = true; break; }
       double S2 = 0.0;
       for (int c = 0; c < chunks; ++c) S2 += lds_all[4 * c];
       if (S2 > 0.0) {
@@ -381,7 +416,8 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
     }
     if (aborted) break;
     if (accepted < 0) {
-      sample_c = cst;
+      sample_c = last_c >= 0.0 ? last_c : cst;
+      fallback_c = cst;
       sample_node = v;
       break;
     }
@@ -393,39 +429,43 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
 
   const int cap = pl.max_depth + 1;
   if (!aborted) {
-    // ---- inverse-CDF draw from max(0, q - c p) (c = 0: q itself)
-    const double c = sample_c;
-    // contiguous per-thread ranges so that the scan runs in index order
-    const int span = x1 - x0;
-    const int per = (span + kSpecThreads - 1) / kSpecThreads;
-    const int t0 = x0 + tid * per;
-    const int t1 = min(x1, t0 + per);
-    double tsum = 0.0;
-    int tlast = -1;
-    for (int x = t0; x < t1; ++x) {
-      const double m = fmax(0.0, qb[x] - c * pb[x]);
-      tsum += m;
-      if (m > 0.0) tlast = x;
-    }
-    // exclusive scan of thread sums (index order) and the chunk total
-    __shared__ double scan_s[kSpecThreads];
-    __shared__ int last_s[kSpecThreads];
-    scan_s[tid] = tsum;
-    last_s[tid] = tlast;
-    __syncthreads();
-    double chunk_total = 0.0;
-    double before = 0.0;
-    int chunk_last = -1;
-    for (int i = 0; i < kSpecThreads; ++i) {
-      if (i == tid) before = chunk_total;
-      chunk_total += scan_s[i];
-      chunk_last = max(chunk_last, last_s[i]);
-    }
-    __syncthreads();
-    const double mine[4] = {chunk_total, (double)chunk_last, 0.0, 0.0};
-    if (!exchange(w, b, chunks, me, gen++, mine, lds_all, &lds_flag)) {
-      aborted = true;
-    } else {
+    // ---- inverse-CDF draw from max(0, q - c p) (c = 0: q itself); if the residual at
+    // the last c vanished by rounding, the draw falls back to the previous c (the
+    // decision every workgroup takes from the same totals)
+    double c = sample_c;
+    for (;;) {
+      // contiguous per-thread ranges so that the scan runs in index order
+      const int span = x1 - x0;
+      const int per = (span + kSpecThreads - 1) / kSpecThreads;
+      const int t0 = x0 + tid * per;
+      const int t1 = min(x1, t0 + per);
+      double tsum = 0.0;
+      int tlast = -1;
+      for (int x = t0; x < t1; ++x) {
+        const double m = fmax(0.0, qb[x] - c * pb[x]);
+        tsum += m;
+        if (m > 0.0) tlast = x;
+      }
+      // exclusive scan of thread sums (index order) and the chunk total
+      __shared__ double scan_s[kSpecThreads];
+      __shared__ int last_s[kSpecThreads];
+      scan_s[tid] = tsum;
+      last_s[tid] = tlast;
+      __syncthreads();
+      double chunk_total = 0.0;
+      double before = 0.0;
+      int chunk_last = -1;
+      for (int i = 0; i < kSpecThreads; ++i) {
+        if (i == tid) before = chunk_total;
+        chunk_total += scan_s[i];
+        chunk_last = max(chunk_last, last_s[i]);
+      }
+      __syncthreads();
+      const double mine[4] = {chunk_total, (double)chunk_last, 0.0, 0.0};
+      if (!exchange(w, b, chunks, me, gen++, 2, mine, lds_all, &lds_flag)) {
+        aborted = true;
+        break;
+      }
       double total = 0.0, offset = 0.0;
       int glast = -1, glast_owner = 0;
       for (int cc = 0; cc < chunks; ++cc) {
@@ -435,6 +475,10 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
           glast = (int)lds_all[4 * cc + 1];
           glast_owner = cc;
         }
+      }
+      if (!(total > 0.0) && c != fallback_c) {
+        c = fallback_c;
+        continue;
       }
       const double T = (double)u_sample[(size_t)b * N + sample_node] * total;
       __shared__ int found_s;
@@ -459,6 +503,7 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
       }
       __syncthreads();
       if (tid == 0 && found_s >= 0) out_tokens[(size_t)b * cap + alpha] = found_s;
+      break;
     }
   }
 
@@ -510,7 +555,7 @@ SpecPlan plan_accept_spec(int B, int N, int V) {
 
 size_t accept_spec_workspace_bytes(const SpecPlan& pl) {
   size_t off = 2 * 256 * (size_t)((pl.B * 4 + 255) / 256);
-  off += (size_t)pl.B * 2 * pl.chunks * 4 * sizeof(double);
+  off += (size_t)pl.B * 2 * pl.chunks * 8 * sizeof(unsigned long long);
   off = (off + 255) / 256 * 256;
   off += 2 * (size_t)pl.B * pl.V * sizeof(double);
   return off + 256;

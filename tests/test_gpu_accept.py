@@ -164,3 +164,37 @@ def test_spec_full_c4_tree(gpu_lib):
     assert a[0] == alpha and list(p[0, :alpha + 1]) == path
     assert len(trace[0][2]) == 10 and trace[0][3] == -1       # ten rejections at the root
     assert 0 <= o[0, alpha] < V
+
+
+@pytest.mark.parametrize("nk", [1, 2, 3])
+def test_spec_vanishing_residual(gpu_lib, nk):
+    """q = p, supported on one or two tokens, and every child's token outside that
+    support: each child is rejected (ratio 0) and the residual max(0, q - c p) at the
+    next c is exactly zero, so the draw falls back to q itself (the pages' rule keeps the
+    corrected target when the residual has no mass)."""
+    V, N = 16, nk + 1
+    B = 4
+    tl = np.zeros((B, N, V), np.float32)
+    dl = np.zeros((B, 1, V), np.float32)
+    support = [(5,), (2, 11), (0,), (7, 8)]
+    for b, sup in enumerate(support):
+        row = np.full(V, -1000.0, np.float32)   # exp(-1000) is 0 in fp64: exact zeros
+        row[list(sup)] = 0.0
+        tl[b, :] = row
+        dl[b, 0] = row
+    parents = np.tile(np.array([-1] + [0] * nk, np.int32), (B, 1))
+    draft_row = np.tile(np.array([0] + [-1] * nk, np.int32), (B, 1))
+    tokens = np.zeros((B, N), np.int32)
+    for b, sup in enumerate(support):
+        outside = [t for t in range(V) if t not in sup]
+        tokens[b, 1:] = outside[:nk]
+    ua = np.full((B, N), 0.5, np.float32)
+    us = np.array([[0.3] * N, [0.25] * N, [0.9] * N, [0.75] * N], np.float32)
+    print(f"spec vanishing residual nk={nk}", flush=True)
+    a, p, o = _spec_gpu(gpu_lib, tokens, parents, draft_row, tl, dl, ua, us, 5)
+    for b, sup in enumerate(support):
+        alpha, path, out = oracle.accept_spec(tokens[b], parents[b], tl[b], dl[b], draft_row[b],
+                                              ua[b], us[b], 5)
+        expect = sup[0] if len(sup) == 1 or us[b, 0] < 0.5 else sup[1]
+        assert alpha == 0 and path == [0] and out == [expect]
+        assert a[b] == 0 and p[b, 0] == 0 and o[b, 0] == expect
