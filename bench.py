@@ -417,10 +417,17 @@ PROFILE_RUNS = {
                       "--output-format csv -- python -u bench.py --copy-calib",
     "pmc_copy_write": "rocprofv3 --pmc WRITE_SIZE -T -d gpurun_out/pmc_copy_write -o run "
                       "--output-format csv -- python -u bench.py --copy-calib",
+    "pmc_mfma": "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CU_CYCLES "
+                "SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS GRBM_GUI_ACTIVE GRBM_COUNT -T "
+                "-d gpurun_out/pmc_mfma -o run --output-format csv -- python -u bench.py --steps 2 "
+                "--warmup 1 --no-cpu-baseline --no-spec",
 }
 TRACE_MD = "c5_step_kernel_trace.md"
 DRAFT_TRACE_MD = "c5_draft_expand_kernel_trace.md"
 TRAFFIC_MD = "c5_step_hbm_traffic.md"
+MFMA_MD = "c5_step_mfma_counters.md"
+SIMDS = 1024   # 256 CUs x 4 SIMDs
+XCCS = 8
 
 
 def _read_csv(path):
@@ -516,6 +523,54 @@ def summarize_profiles(root):
         with open(os.path.join(PROFILE_DIR, f"{short}_C5_traffic.json"), "w") as f:
             json.dump(rec, f, indent=1)
     print("\n".join(lines + [""] + rows))
+    mpath = os.path.join(root, "pmc_mfma", "run_counter_collection.csv")
+    if os.path.exists(mpath):
+        print(summarize_mfma(mpath))
+
+
+def summarize_mfma(path):
+    """Per-kernel matrix-core and LDS counters of the C5 step (the PROFILE_RUNS
+    "pmc_mfma" run): the clock the kernel ran at (GRBM_GUI_ACTIVE cycles per XCC over
+    the dispatch time), MFMA busy cycles per SIMD over those cycles, bf16 MFMA flops
+    (512 per MOPS unit, padding included) over the dispatch time, LDS activity."""
+    import collections
+    per = collections.defaultdict(dict)
+    span = {}
+    for r in _read_csv(path):
+        key = (int(r["Dispatch_Id"]), r["Kernel_Name"].split("(")[0])
+        per[key][r["Counter_Name"]] = float(r["Counter_Value"])
+        span[key] = (int(r["Start_Timestamp"]), int(r["End_Timestamp"]))
+    agg = collections.defaultdict(list)
+    for key, c in per.items():
+        name = key[1].split("::")[-1].split("<")[0]
+        if name not in ("lm_head_gemm", "tree_attn_pingpong"):
+            continue
+        t0, t1 = span[key]
+        dur_s = (t1 - t0) * 1e-9
+        cycles = c["GRBM_GUI_ACTIVE"] / XCCS
+        agg[name].append({"us": dur_s * 1e6, "mhz": cycles / dur_s / 1e6,
+                          "busy": c["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * SIMDS),
+                          "tflops": c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / dur_s / 1e12,
+                          "lds_active": c["SQ_LDS_IDX_ACTIVE"] / (cycles * SIMDS / 4),
+                          "conflicts": c["SQ_LDS_BANK_CONFLICT"]})
+    lines = ["# rocprofv3 matrix-core and LDS counters: C5 verification step", "",
+             "Command (repository root, one MI355X):", "", "    " + PROFILE_RUNS["pmc_mfma"], "",
+             "Per kernel, the mean over the run's dispatches (3 steps).  clock = GRBM_GUI_ACTIVE / 8 XCCs",
+             "over the dispatch time; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (clock cycles x 1024 SIMDs);",
+             "bf16 MFMA rate = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 flop over the dispatch time (padded",
+             "tiles included); LDS active = SQ_LDS_IDX_ACTIVE / (clock cycles x 256 CUs).  Peak bf16",
+             "MFMA at the measured clock = 1024 flop/clk/SIMD x 1024 SIMDs x clock.", "",
+             "| kernel | dispatches | avg us | clock MHz | MFMA busy % | bf16 MFMA TFLOP/s | peak at clock TFLOP/s | LDS active % | LDS bank conflicts |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for name, v in sorted(agg.items()):
+        m = {k: sum(x[k] for x in v) / len(v) for k in v[0]}
+        lines.append(f"| {name} | {len(v)} | {m['us']:.1f} | {m['mhz']:.0f} | {100 * m['busy']:.1f} | "
+                     f"{m['tflops']:.0f} | {1024 * SIMDS * m['mhz'] * 1e6 / 1e12:.0f} | "
+                     f"{100 * m['lds_active']:.1f} | {m['conflicts']:.0f} |")
+    text = "\n".join(lines) + "\n"
+    with open(os.path.join(PROFILE_DIR, MFMA_MD), "w") as f:
+        f.write(text)
+    return text
 
 
 def main(argv=None):
