@@ -360,13 +360,10 @@ hipError_t launch_gemm(const LmPlan& pl, const void* hidden, const void* W, f32x
   constexpr int bytes = lm_lds_bytes<MT, VT, WVV, WVM>();
   static_assert(bytes <= 160 * 1024, "MI355X LDS is 160 KiB per workgroup");
   static_assert(WVV * WVM * MT * 32 * 16 <= bytes, "the epilogue's partials reuse the staging LDS");
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)lm_head_gemm<MT, VT, WVV, WVM, LA>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // once per process; function-local static initialisation is thread-safe
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)lm_head_gemm<MT, VT, WVV, WVM, LA>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((lm_head_gemm<MT, VT, WVV, WVM, LA>), dim3(pl.nvt * pl.nmb * pl.ksplit),
                      dim3(WVV * WVM * 64), bytes, stream, (const uint16_t*)hidden,
                      (const uint16_t*)W, pl, part, logits);

@@ -767,13 +767,10 @@ template <bool PAGED>
 hipError_t launch_pingpong(const AttnPlan& pl, const void* q, const void* k, const void* v,
                            const int32_t* parents, void* out, float* lse, float* part_o,
                            float* part_lse, hipStream_t stream) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute((const void*)tree_attn_pingpong<PAGED>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, XLDS);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // once per process; function-local static initialisation is thread-safe
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)tree_attn_pingpong<PAGED>, hipFuncAttributeMaxDynamicSharedMemorySize, XLDS);
+  if (attr != hipSuccess) return attr;
   const int nwg = pl.B * pl.Hkv * pl.RB * pl.S;
   hipLaunchKernelGGL(tree_attn_pingpong<PAGED>, dim3(nwg), dim3(512), XLDS, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, parents, pl,
