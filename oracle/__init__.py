@@ -21,7 +21,8 @@ invariants.  No function here is "parity unpinned".
 from .tree import ancestor_sets, children_of, node_depths  # noqa: F401
 from .attention import tree_verify_attention, tree_verify_attention_node  # noqa: F401
 from .lm_head import lm_head_logits, lm_head_row_stats, lm_head  # noqa: F401
-from .accept import accept_greedy, accept_spec, sample_inverse_cdf, spec_node_round  # noqa: F401
+from .accept import (accept_greedy, accept_spec, sample_inverse_cdf, spec_node_round,  # noqa: F401
+                     spec_node_round_point_mass)
 from .rerank import eagle2_rerank, grow_tree  # noqa: F401
 from .draft import bf16_round, draft_expand, draft_layer_row  # noqa: F401
 from .kv_commit import kv_commit  # noqa: F401

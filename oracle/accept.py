@@ -104,8 +104,32 @@ def spec_node_round(q, p, child_tokens, u_accept):
     return -1, q_left, ratios
 
 
+def spec_node_round_point_mass(q, child_tokens, u_accept):
+    """The same multi-round check when the siblings are proposed deterministically
+    (EAGLE-2's expansion keeps the draft's top-k tokens, [P3] section 2): the draft
+    distribution behind child t is then the point mass at t, and the rule of
+    spec_node_round with that p reads: accept t when u < q_left(t); on rejection
+    max(0, q_left - point mass at t) is q_left with t set to zero, renormalised.
+    Returns (j, q_left, ratios) like spec_node_round."""
+    q_left = np.asarray(q, dtype=np.float64).copy()
+    ratios = []
+    for j, t in enumerate(child_tokens):
+        t = int(t)
+        p = np.zeros_like(q_left)
+        p[t] = 1.0
+        ratio = min(1.0, q_left[t] / p[t])
+        ratios.append(ratio)
+        if float(u_accept[j]) < ratio:
+            return j, q_left, ratios
+        resid = np.maximum(0.0, q_left - p)
+        z = resid.sum()
+        if z > 0:
+            q_left = resid / z
+    return -1, q_left, ratios
+
+
 def accept_spec(tokens, parents, target_logits, draft_logits, draft_row, u_accept, u_sample,
-                max_depth: int, trace: list | None = None):
+                max_depth: int, trace: list | None = None, mode: str = "sampled"):
     """One sequence.
 
     tokens, parents, draft_row: [N] ints (draft_row[i] = row of draft_logits holding
@@ -114,9 +138,16 @@ def accept_spec(tokens, parents, target_logits, draft_logits, draft_row, u_accep
     (u_accept[c] is used when child c is tried, u_sample[v] when a token is drawn
     at node v).  Temperature 1: q = softmax(target_logits[v]), p = softmax(draft row).
 
+    mode "sampled" applies the pages' rule with the draft distribution p of the node
+    (siblings drawn from p); mode "point_mass" treats every sibling as proposed
+    deterministically (spec_node_round_point_mass; draft_logits are not read, a node
+    still needs draft_row >= 0 to have its children tried).
+
     Returns (alpha, path, out_tokens) like accept_greedy.  If ``trace`` is a list,
     one (node, child_list, ratios, j) tuple per visited node is appended.
     """
+    if mode not in ("sampled", "point_mass"):
+        raise ValueError(f"unknown mode {mode!r}")
     parents = [int(x) for x in parents]
     depth = node_depths(parents)
     v = 0
@@ -130,9 +161,13 @@ def accept_spec(tokens, parents, target_logits, draft_logits, draft_row, u_accep
                 trace.append((v, [], [], -1))
             x = sample_inverse_cdf(q, u_sample[v])
             break
-        p = _softmax64(draft_logits[row])
-        j, q_left, ratios = spec_node_round(q, p, [tokens[c] for c in kids],
-                                            [u_accept[c] for c in kids])
+        if mode == "point_mass":
+            j, q_left, ratios = spec_node_round_point_mass(q, [tokens[c] for c in kids],
+                                                           [u_accept[c] for c in kids])
+        else:
+            p = _softmax64(draft_logits[row])
+            j, q_left, ratios = spec_node_round(q, p, [tokens[c] for c in kids],
+                                                [u_accept[c] for c in kids])
         if trace is not None:
             trace.append((v, kids, ratios, j))
         if j < 0:

@@ -39,11 +39,12 @@ def accept_greedy_ragged(tokens, parents, target_argmax, tree_len, max_depth: in
 
 
 def accept_spec_ragged(tokens, parents, target_logits, draft_logits, draft_row, u_accept,
-                       u_sample, tree_len, max_depth: int):
+                       u_sample, tree_len, max_depth: int, mode: str = "sampled"):
     """Per sequence: accept_spec on its first tree_len[b] nodes (draft rows as given)."""
     res = []
     for b in range(len(tree_len)):
         n = int(tree_len[b])
         res.append(accept_spec(tokens[b][:n], parents[b][:n], target_logits[b][:n], draft_logits[b],
-                               draft_row[b][:n], u_accept[b][:n], u_sample[b][:n], max_depth))
+                               draft_row[b][:n], u_accept[b][:n], u_sample[b][:n], max_depth,
+                               mode=mode))
     return res

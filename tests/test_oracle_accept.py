@@ -256,3 +256,94 @@ def test_sample_inverse_cdf_edges():
     assert oracle.sample_inverse_cdf(d, 0.25) == 3
     assert oracle.sample_inverse_cdf(d, 0.9999999) == 3
     assert oracle.sample_inverse_cdf(d, 1.0) == 3      # overshoot: last nonzero entry
+
+
+# ---------------------------------------------------------------- deterministic siblings
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4])
+@pytest.mark.parametrize("seed", range(3))
+def test_spec_point_mass_exact_for_every_fixed_sibling_set(k, seed):
+    """Deterministic siblings ([P3] section 2: the expansion keeps the draft's top-k):
+    for EVERY fixed tuple of sibling tokens, duplicates included, the first emitted token
+    of the point-mass rule is distributed exactly as q (sum over the accept/reject
+    branches of the node's rounds)."""
+    rng = np.random.default_rng(100 + seed)
+    V = 8
+    q = _rand_dist(rng, V, 1.5)
+    for tup in itertools.product(range(V), repeat=k):
+        j, q_left, ratios = oracle.spec_node_round_point_mass(q, tup, [1.0] * k)
+        assert j == -1 and len(ratios) == k
+        law = np.zeros(V)
+        reach = 1.0
+        for t, r in zip(tup, ratios):
+            law[t] += reach * r
+            reach *= 1.0 - r
+        law += reach * q_left
+        np.testing.assert_allclose(law, q, rtol=0, atol=1e-12)
+
+
+def test_spec_point_mass_closed_form():
+    """Distinct siblings t1, t2, t3: ratio_j = q(t_j) / (1 - q(t_1) - ... - q(t_{j-1})),
+    and the residual after all three is q without them, renormalised."""
+    rng = np.random.default_rng(7)
+    q = _rand_dist(rng, 8, 1.0)
+    tup = (5, 2, 6)
+    _, q_left, ratios = oracle.spec_node_round_point_mass(q, tup, [1.0] * 3)
+    np.testing.assert_allclose(ratios, [q[5], q[2] / (1 - q[5]), q[6] / (1 - q[5] - q[2])],
+                               rtol=1e-13)
+    want = q.copy()
+    want[list(tup)] = 0.0
+    np.testing.assert_allclose(q_left, want / want.sum(), rtol=1e-13)
+
+
+def test_spec_sampled_rule_is_not_exact_for_fixed_siblings():
+    """Why the point-mass mode exists: with the siblings fixed to the draft's top-2
+    (not drawn from p), the pages' rule with p itself does not reproduce q."""
+    rng = np.random.default_rng(3)
+    V = 8
+    q = _rand_dist(rng, V, 1.5)
+    p = _rand_dist(rng, V, 2.0)
+    tup = tuple(int(t) for t in np.argsort(-p)[:2])
+    _, q_left, ratios = oracle.spec_node_round(q, p, tup, [1.0] * 2)
+    law = np.zeros(V)
+    reach = 1.0
+    for t, r in zip(tup, ratios):
+        law[t] += reach * r
+        reach *= 1.0 - r
+    law += reach * q_left
+    assert np.abs(law - q).max() > 1e-3
+
+
+def test_spec_point_mass_monte_carlo_through_accept_spec():
+    """accept_spec(mode="point_mass") on a depth-2 tree whose siblings are the draft's
+    top-3 at each level: the first and second emitted tokens follow q (chi-square, 7 d.o.f.)."""
+    rng = np.random.default_rng(11)
+    V, T = 8, 20000
+    tl0 = rng.standard_normal(V) * 1.2
+    tl1 = rng.standard_normal(V) * 1.2
+    dl = rng.standard_normal((2, V)) * 2.0
+    q0 = np.exp(tl0 - tl0.max()); q0 /= q0.sum()
+    top0 = [int(t) for t in np.argsort(-dl[0])[:3]]
+    top1 = [int(t) for t in np.argsort(-dl[1])[:3]]
+    # node 1 (first child, token top0[0]) is expanded with top1; nodes 2, 3 are leaves
+    parents = [-1, 0, 0, 0, 1, 1, 1]
+    tokens = [0] + top0 + top1
+    draft_row = [0, 1, -1, -1, -1, -1, -1]
+    target = np.stack([tl0, tl1, tl0, tl0, tl0, tl0, tl0])
+    first = np.zeros(V)
+    second = np.zeros(V)
+    n_second = 0
+    u = rng.random((T, 2, 7))
+    for n in range(T):
+        alpha, path, out = oracle.accept_spec(tokens, parents, target, dl, draft_row, u[n, 0],
+                                              u[n, 1], 5, mode="point_mass")
+        first[out[0]] += 1
+        if alpha >= 1 and path[1] == 1:
+            second[out[1]] += 1
+            n_second += 1
+    from scipy.stats import chi2
+    stat = ((first - T * q0) ** 2 / (T * q0)).sum()
+    assert chi2.sf(stat, V - 1) > 1e-3
+    q1 = np.exp(tl1 - tl1.max()); q1 /= q1.sum()
+    stat2 = ((second - n_second * q1) ** 2 / (n_second * q1)).sum()
+    assert chi2.sf(stat2, V - 1) > 1e-3
