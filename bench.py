@@ -183,9 +183,11 @@ def copy_calibration(torch, dev, nbytes=1 << 30, reps=5):
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}))
 
 
-def spec_latency(torch, sda, dev, iters=20):
+def spec_latency(torch, sda, dev, iters=20, mode="sampled"):
     """eagle_accept_spec at the Llama-3-8B-shaped speculative-sampling workload (C4): a
-    60-node tree from eagle2_rerank, target logits N(0,1) over 128256 tokens."""
+    60-node tree from eagle2_rerank, target logits N(0,1) over 128256 tokens.  mode
+    "sampled" runs the pages' rule with the draft distribution (10 residual rounds at
+    the root), "point_mass" the rule for deterministic top-k siblings."""
     cfg = synth.CONFIGS["C4"]
     dl = torch.from_numpy(synth.normal_f32((1, cfg.rows, cfg.V), cfg.draft_std, 0, cfg.index, 6)).to(dev)
     root = torch.from_numpy(synth.integers((1,), 0, cfg.V, 0, cfg.index, 7)).to(dev)
@@ -197,14 +199,14 @@ def spec_latency(torch, sda, dev, iters=20):
                      device=dev)
     for _ in range(3):
         sda.eagle_accept_spec(tree["tokens"], tree["parents"], tree["draft_row"], tl, dl, ua, us,
-                              cfg.max_depth, workspace=ws)
+                              cfg.max_depth, workspace=ws, mode=mode)
     torch.cuda.synchronize()
     s = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(s)
     for _ in range(iters):
         sda.eagle_accept_spec(tree["tokens"], tree["parents"], tree["draft_row"], tl, dl, ua, us,
-                              cfg.max_depth, workspace=ws)
+                              cfg.max_depth, workspace=ws, mode=mode)
     e1.record(s)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1000.0 / iters
@@ -703,6 +705,7 @@ def main(argv=None):
     }
     if not args.no_spec:
         out["accept_spec_us_C4"] = round(spec_latency(torch, sda, dev), 2)
+        out["accept_spec_point_mass_us_C4"] = round(spec_latency(torch, sda, dev, mode="point_mass"), 2)
         out["kv_commit_80_layers"] = kv_commit_latency(torch, sda, dev, tree["parents"])
         out["ragged_C5"] = ragged_step(torch, sda, dev, x)
         out["paged_attention_C5"] = paged_attention(torch, sda, dev, x, tree["parents"])

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define EAGLE_ABI_VERSION 1
+#define EAGLE_ABI_VERSION 2
 #define EAGLE_MAX_TREE 64   /* nodes per sequence, root included */
 #define EAGLE_MAX_TOPK 64
 
@@ -70,6 +70,12 @@ typedef enum {
   EAGLE_ERR_TREE = 5,          /* eagle_check_tree: parent array breaks the tree rules */
   EAGLE_ERR_HIP = 6            /* a HIP runtime call failed; see eagle_last_error() */
 } eagle_status_t;
+
+/* Sibling model of eagle_accept_spec (see there). */
+typedef enum {
+  EAGLE_SPEC_SAMPLED = 0,
+  EAGLE_SPEC_POINT_MASS = 1
+} eagle_spec_mode_t;
 
 /* Version of this ABI (EAGLE_ABI_VERSION of the built library). */
 int eagle_abi_version(void);
@@ -172,6 +178,18 @@ eagle_status_t eagle_accept_greedy(const int32_t* tokens, const int32_t* parents
  * draft_row < 0, or at depth max_depth, one token is drawn from q.  Draws are
  * inverse-CDF: the smallest x whose cumulative mass exceeds u times the total.
  *
+ * mode selects what the siblings are:
+ *   EAGLE_SPEC_SAMPLED     the children were drawn from the node's draft distribution
+ *                          p (the pages' rule as stated above; exact for such draws);
+ *   EAGLE_SPEC_POINT_MASS  the children are the draft's deterministic proposals, as
+ *                          in EAGLE-2's top-k expansion ([P3] section 2): the draft
+ *                          distribution behind child t is the point mass at t, so t is
+ *                          accepted when u < q'(t), and a rejection sets q'(t) to zero
+ *                          and renormalises (exact for any fixed set of siblings).
+ *                          draft_logits are not read in this mode; a node still needs
+ *                          a valid draft_row to have its children tried.
+ * Any other mode value is EAGLE_ERR_INVALID_ARG.
+ *
  *   tokens, parents, draft_row int32 [B][N] (draft_row[b][i] in [-1, draft_rows))
  *   target_logits fp32 [B][N][V]; draft_logits fp32 [B][draft_rows][V]
  *   u_accept, u_sample fp32 [B][N] in [0, 1)
@@ -183,9 +201,9 @@ eagle_status_t eagle_accept_spec(const int32_t* tokens, const int32_t* parents,
                                  const int32_t* draft_row, const float* target_logits,
                                  const float* draft_logits, int32_t draft_rows,
                                  const float* u_accept, const float* u_sample, int32_t B,
-                                 int32_t N, int32_t V, int32_t max_depth, int32_t* accept_len,
-                                 int32_t* accept_path, int32_t* out_tokens, void* workspace,
-                                 size_t workspace_bytes, hipStream_t stream);
+                                 int32_t N, int32_t V, int32_t max_depth, int32_t mode,
+                                 int32_t* accept_len, int32_t* accept_path, int32_t* out_tokens,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Ragged batches.  [P3] section 4 (batch sizes above one are the method's weak spot)
@@ -220,7 +238,7 @@ eagle_status_t eagle_accept_spec_ragged(const int32_t* tokens, const int32_t* pa
                                         const float* draft_logits, int32_t draft_rows,
                                         const float* u_accept, const float* u_sample,
                                         const int32_t* tree_len, int32_t B, int32_t N, int32_t V,
-                                        int32_t max_depth, int32_t* accept_len,
+                                        int32_t max_depth, int32_t mode, int32_t* accept_len,
                                         int32_t* accept_path, int32_t* out_tokens,
                                         void* workspace, size_t workspace_bytes,
                                         hipStream_t stream);

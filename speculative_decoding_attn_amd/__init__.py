@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libeagle_mi355.so")
 _lib = None
 
 EAGLE_OK = 0
+SPEC_MODES = {"sampled": 0, "point_mass": 1}   # eagle_spec_mode_t
 STATUS_NAMES = {0: "EAGLE_OK", 1: "EAGLE_ERR_NULL", 2: "EAGLE_ERR_INVALID_ARG",
                 3: "EAGLE_ERR_UNSUPPORTED", 4: "EAGLE_ERR_WORKSPACE", 5: "EAGLE_ERR_TREE",
                 6: "EAGLE_ERR_HIP"}
@@ -48,7 +49,7 @@ _SIGNATURES = {
     "eagle_kv_commit": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp],
                         ctypes.c_int),
     "eagle_accept_spec_workspace": ([_i32] * 3, _sz),
-    "eagle_accept_spec": ([_vp] * 5 + [_i32, _vp, _vp, _i32, _i32, _i32, _i32] + [_vp] * 4
+    "eagle_accept_spec": ([_vp] * 5 + [_i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32] + [_vp] * 4
                           + [_sz, _vp], ctypes.c_int),
     "eagle_tree_verify_attn_ragged": ([_vp] * 6 + [_i32] * 7 + [_f32, _vp, _vp, _vp, _sz, _vp],
                                       ctypes.c_int),
@@ -56,7 +57,7 @@ _SIGNATURES = {
     "eagle_tree_verify_attn_paged": ([_vp] * 5 + [_i32] * 9 + [_f32, _vp, _vp, _vp, _sz, _vp],
                                      ctypes.c_int),
     "eagle_accept_greedy_ragged": ([_vp] * 4 + [_i32, _i32, _i32] + [_vp] * 4, ctypes.c_int),
-    "eagle_accept_spec_ragged": ([_vp] * 5 + [_i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32]
+    "eagle_accept_spec_ragged": ([_vp] * 5 + [_i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32]
                                  + [_vp] * 4 + [_sz, _vp], ctypes.c_int),
     "eagle2_rerank_workspace": ([_i32] * 4, _sz),
     "eagle2_rerank": ([_vp, _vp] + [_i32] * 5 + [_vp] * 7 + [_sz, _vp], ctypes.c_int),
@@ -314,11 +315,15 @@ def eagle_accept_spec(tokens: torch.Tensor, parents: torch.Tensor, draft_row: to
                       target_logits: torch.Tensor, draft_logits: torch.Tensor,
                       u_accept: torch.Tensor, u_sample: torch.Tensor, max_depth: int,
                       workspace: Optional[torch.Tensor] = None,
-                      tree_len: Optional[torch.Tensor] = None):
+                      tree_len: Optional[torch.Tensor] = None, mode: str = "sampled"):
     """tokens, parents, draft_row [B][N] int32; target_logits [B][N][V] fp32;
     draft_logits [B][R][V] fp32; u_accept, u_sample [B][N] fp32.  With tree_len
-    (int32 [B]) eagle_accept_spec_ragged is called."""
+    (int32 [B]) eagle_accept_spec_ragged is called.  mode: "sampled" (siblings drawn
+    from the draft distribution) or "point_mass" (deterministic siblings)."""
     lib = load()
+    if mode not in SPEC_MODES:
+        raise ValueError(f"mode must be one of {sorted(SPEC_MODES)}")
+    m = SPEC_MODES[mode]
     dev = tokens.device
     for t, n in ((tokens, "tokens"), (parents, "parents"), (draft_row, "draft_row")):
         _need(t, n, torch.int32, dev)
@@ -338,7 +343,7 @@ def eagle_accept_spec(tokens: torch.Tensor, parents: torch.Tensor, draft_row: to
     if tree_len is None:
         st = lib.eagle_accept_spec(tokens.data_ptr(), parents.data_ptr(), draft_row.data_ptr(),
                                    target_logits.data_ptr(), draft_logits.data_ptr(), R,
-                                   u_accept.data_ptr(), u_sample.data_ptr(), B, N, V, max_depth,
+                                   u_accept.data_ptr(), u_sample.data_ptr(), B, N, V, max_depth, m,
                                    alen.data_ptr(), path.data_ptr(), out.data_ptr(),
                                    workspace.data_ptr(), workspace.numel(), _stream())
         _check(st, "eagle_accept_spec")
@@ -349,7 +354,7 @@ def eagle_accept_spec(tokens: torch.Tensor, parents: torch.Tensor, draft_row: to
     st = lib.eagle_accept_spec_ragged(tokens.data_ptr(), parents.data_ptr(), draft_row.data_ptr(),
                                       target_logits.data_ptr(), draft_logits.data_ptr(), R,
                                       u_accept.data_ptr(), u_sample.data_ptr(), tree_len.data_ptr(),
-                                      B, N, V, max_depth, alen.data_ptr(), path.data_ptr(),
+                                      B, N, V, max_depth, m, alen.data_ptr(), path.data_ptr(),
                                       out.data_ptr(), workspace.data_ptr(), workspace.numel(),
                                       _stream())
     _check(st, "eagle_accept_spec_ragged")
@@ -357,10 +362,11 @@ def eagle_accept_spec(tokens: torch.Tensor, parents: torch.Tensor, draft_row: to
 
 
 def eagle_accept_spec_ragged(tokens, parents, draft_row, target_logits, draft_logits, u_accept,
-                             u_sample, tree_len, max_depth: int, workspace=None):
+                             u_sample, tree_len, max_depth: int, workspace=None,
+                             mode: str = "sampled"):
     """eagle_accept_spec with per-sequence tree sizes tree_len (int32 [B])."""
     return eagle_accept_spec(tokens, parents, draft_row, target_logits, draft_logits, u_accept,
-                             u_sample, max_depth, workspace=workspace, tree_len=tree_len)
+                             u_sample, max_depth, workspace=workspace, tree_len=tree_len, mode=mode)
 
 
 def eagle2_rerank(draft_logits: torch.Tensor, root_token: torch.Tensor, top_k: int, depth: int,

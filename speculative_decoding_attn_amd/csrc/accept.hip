@@ -248,6 +248,7 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
   const int tid = threadIdx.x;
   // ragged batches: nodes past this sequence's tree do not exist
   const int Nb = pl.tree_len ? min(max(pl.tree_len[b], 1), N) : N;
+  const bool pm = pl.mode != 0;   // deterministic siblings (point-mass draft per child)
 
   unsigned gen = 0;
   int v = 0;
@@ -274,7 +275,7 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
     int row = draft_row[(size_t)b * N + v];
     const bool has_draft = nk > 0 && row >= 0 && row < pl.R;
     const float* tl = target_logits + ((size_t)b * N + v) * V;
-    const float* dl = has_draft ? draft_logits + ((size_t)b * pl.R + row) * V : tl;
+    const float* dl = (has_draft && !pm) ? draft_logits + ((size_t)b * pl.R + row) * V : tl;
     // the children's operands, loaded once here so that their latency overlaps the
     // softmax below instead of sitting in every rejection round
     if (tid < nk) {
@@ -376,7 +377,38 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
     double cst = 0.0, S = 1.0;
     double last_c = -1.0;
     int accepted = -1;
-    for (int j = 0; j < nk; ++j) {
+    if (pm) {
+      // Deterministic siblings: the draft distribution behind child t is the point mass
+      // at t, so q'(t) = q(t) / (1 - removed) for a token not rejected yet (0 for one
+      // that was), and a rejection removes q(t).  Every workgroup takes the same
+      // decisions from the same values: no exchange.
+      double removed = 0.0;
+      unsigned long long gone = 0ull;   // children whose token was removed from q'
+      for (int j = 0; j < nk; ++j) {
+        const int t = kid_tok[j];
+        bool dup = false;
+        for (int i = 0; i < j; ++i) dup |= ((gone >> i) & 1ull) && kid_tok[i] == t;
+        const double qt = t >= 0 ? exp((double)kid_tl[j] - lse_q) : 0.0;
+        const double ratio = (t < 0 || dup) ? 0.0 : fmin(1.0, qt / (1.0 - removed));
+        if ((double)kid_u[j] < ratio) {
+          accepted = kids[j];
+          break;
+        }
+        if (t >= 0 && !dup && 1.0 - removed - qt > 0.0) {
+          removed += qt;
+          gone |= 1ull << j;
+        }
+      }
+      if (accepted < 0) {
+        // the draw from q without the removed tokens: zero them in this chunk of q
+        if (tid < nk && ((gone >> tid) & 1ull)) {
+          const int t = kid_tok[tid];
+          if (t >= x0 && t < x1) qb[t] = 0.0;
+        }
+        __syncthreads();
+      }
+    }
+    for (int j = 0; j < (pm ? 0 : nk); ++j) {
       const int kid = kids[j];
       double qt = 0.0, pt = 0.0;
       if (kid_tok[j] >= 0) {
@@ -416,8 +448,8 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
     }
     if (aborted) break;
     if (accepted < 0) {
-      sample_c = last_c >= 0.0 ? last_c : cst;
-      fallback_c = cst;
+      sample_c = pm ? 0.0 : (last_c >= 0.0 ? last_c : cst);
+      fallback_c = pm ? 0.0 : cst;
       sample_node = v;
       break;
     }

@@ -270,9 +270,9 @@ static eagle_status_t spec_impl(const int32_t* tokens, const int32_t* parents,
                                 const float* draft_logits, int32_t draft_rows,
                                 const float* u_accept, const float* u_sample,
                                 const int32_t* tree_len, int32_t B, int32_t N, int32_t V,
-                                int32_t max_depth, int32_t* accept_len, int32_t* accept_path,
-                                int32_t* out_tokens, void* workspace, size_t workspace_bytes,
-                                hipStream_t stream) {
+                                int32_t max_depth, int32_t mode, int32_t* accept_len,
+                                int32_t* accept_path, int32_t* out_tokens, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
   if (!tokens || !parents || !draft_row || !target_logits || !draft_logits || !u_accept ||
       !u_sample || !accept_len || !accept_path || !out_tokens)
     return fail(EAGLE_ERR_NULL, "all pointers must be non-NULL");
@@ -280,7 +280,10 @@ static eagle_status_t spec_impl(const int32_t* tokens, const int32_t* parents,
     return fail(EAGLE_ERR_INVALID_ARG, "need B,N,V,draft_rows >= 1 and max_depth >= 0");
   if (N > EAGLE_MAX_TREE) return fail(EAGLE_ERR_UNSUPPORTED, "N=%d > %d", N, EAGLE_MAX_TREE);
   if (max_depth > EAGLE_MAX_TREE) return fail(EAGLE_ERR_INVALID_ARG, "max_depth=%d > %d", max_depth, EAGLE_MAX_TREE);
+  if (mode != EAGLE_SPEC_SAMPLED && mode != EAGLE_SPEC_POINT_MASS)
+    return fail(EAGLE_ERR_INVALID_ARG, "mode=%d (EAGLE_SPEC_SAMPLED or EAGLE_SPEC_POINT_MASS)", mode);
   eagle::SpecPlan pl = eagle::plan_accept_spec(B, N, V);
+  pl.mode = mode;
   pl.R = draft_rows;
   pl.max_depth = max_depth;
   pl.tree_len = tree_len;
@@ -298,12 +301,12 @@ eagle_status_t eagle_accept_spec(const int32_t* tokens, const int32_t* parents,
                                  const int32_t* draft_row, const float* target_logits,
                                  const float* draft_logits, int32_t draft_rows,
                                  const float* u_accept, const float* u_sample, int32_t B,
-                                 int32_t N, int32_t V, int32_t max_depth, int32_t* accept_len,
-                                 int32_t* accept_path, int32_t* out_tokens, void* workspace,
-                                 size_t workspace_bytes, hipStream_t stream) {
+                                 int32_t N, int32_t V, int32_t max_depth, int32_t mode,
+                                 int32_t* accept_len, int32_t* accept_path, int32_t* out_tokens,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return spec_impl(tokens, parents, draft_row, target_logits, draft_logits, draft_rows, u_accept,
-                   u_sample, nullptr, B, N, V, max_depth, accept_len, accept_path, out_tokens,
-                   workspace, workspace_bytes, stream);
+                   u_sample, nullptr, B, N, V, max_depth, mode, accept_len, accept_path,
+                   out_tokens, workspace, workspace_bytes, stream);
 }
 
 eagle_status_t eagle_accept_spec_ragged(const int32_t* tokens, const int32_t* parents,
@@ -311,14 +314,14 @@ eagle_status_t eagle_accept_spec_ragged(const int32_t* tokens, const int32_t* pa
                                         const float* draft_logits, int32_t draft_rows,
                                         const float* u_accept, const float* u_sample,
                                         const int32_t* tree_len, int32_t B, int32_t N, int32_t V,
-                                        int32_t max_depth, int32_t* accept_len,
+                                        int32_t max_depth, int32_t mode, int32_t* accept_len,
                                         int32_t* accept_path, int32_t* out_tokens,
                                         void* workspace, size_t workspace_bytes,
                                         hipStream_t stream) {
   if (!tree_len) return fail(EAGLE_ERR_NULL, "tree_len is NULL (use eagle_accept_spec)");
   return spec_impl(tokens, parents, draft_row, target_logits, draft_logits, draft_rows, u_accept,
-                   u_sample, tree_len, B, N, V, max_depth, accept_len, accept_path, out_tokens,
-                   workspace, workspace_bytes, stream);
+                   u_sample, tree_len, B, N, V, max_depth, mode, accept_len, accept_path,
+                   out_tokens, workspace, workspace_bytes, stream);
 }
 
 // ---------------------------------------------------------------- rerank

@@ -83,6 +83,7 @@ hipError_t launch_accept_greedy(const int32_t* tokens, const int32_t* parents,
 
 struct SpecPlan {
   int B, N, V, R, max_depth;
+  int mode;       // 0: siblings drawn from the draft distribution; 1: deterministic (point mass)
   int chunks;     // vocabulary chunks (one workgroup each) per sequence
   const int32_t* tree_len;   // ragged batches: per-sequence tree size (<= N), may be null
 };

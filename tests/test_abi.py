@@ -41,7 +41,7 @@ def test_binding_covers_every_symbol():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.eagle_abi_version() == 1
+    assert lib.eagle_abi_version() == 2
     assert lib.eagle_status_string(0) == b"ok"
     assert lib.eagle_status_string(99) == b"unknown status"
 
@@ -126,9 +126,16 @@ def test_accept_and_rerank_argument_errors(lib):
     assert g(FAKE, FAKE, FAKE, 1, 65, 4, FAKE, FAKE, FAKE, None) == 3
     assert g(FAKE, FAKE, FAKE, 1, 5, -1, FAKE, FAKE, FAKE, None) == 2
     s = lib.eagle_accept_spec
-    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, None, 1, 5, 8, 3, FAKE, FAKE, FAKE, FAKE,
+    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, None, 1, 5, 8, 3, 0, FAKE, FAKE, FAKE, FAKE,
              1 << 20, None) == 1
-    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 1, 5, 8, 3, FAKE, FAKE, FAKE, None, 0,
+    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 1, 5, 8, 3, 0, FAKE, FAKE, FAKE, None, 0,
+             None) == 4
+    # sibling model: EAGLE_SPEC_SAMPLED (0) or EAGLE_SPEC_POINT_MASS (1) only
+    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 1, 5, 8, 3, 2, FAKE, FAKE, FAKE, FAKE,
+             1 << 20, None) == 2
+    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 1, 5, 8, 3, -1, FAKE, FAKE, FAKE, FAKE,
+             1 << 20, None) == 2
+    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 1, 5, 8, 3, 1, FAKE, FAKE, FAKE, None, 0,
              None) == 4
     r = lib.eagle2_rerank
 
@@ -172,8 +179,10 @@ def test_ragged_argument_errors(lib):
     assert g(FAKE, FAKE, FAKE, None, 1, 5, 4, FAKE, FAKE, FAKE, None) == 1
     assert g(FAKE, FAKE, FAKE, FAKE, 1, 65, 4, FAKE, FAKE, FAKE, None) == 3
     s = lib.eagle_accept_spec_ragged
-    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, None, 1, 5, 8, 3, FAKE, FAKE, FAKE, FAKE,
+    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, None, 1, 5, 8, 3, 0, FAKE, FAKE, FAKE, FAKE,
              1 << 20, None) == 1
+    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, 1, 5, 8, 3, 7, FAKE, FAKE, FAKE, FAKE,
+             1 << 20, None) == 2
 
 
 def test_paged_argument_errors(lib):

@@ -56,9 +56,9 @@ def test_greedy_random_trees(gpu_lib, seed):
         assert list(o[b]) == _padded(out, cap)
 
 
-def _spec_gpu(lib, tokens, parents, draft_row, tl, dl, ua, us, max_depth):
+def _spec_gpu(lib, tokens, parents, draft_row, tl, dl, ua, us, max_depth, mode="sampled"):
     a, p, o = lib.eagle_accept_spec(to_dev(tokens), to_dev(parents), to_dev(draft_row), to_dev(tl),
-                                    to_dev(dl), to_dev(ua), to_dev(us), max_depth)
+                                    to_dev(dl), to_dev(ua), to_dev(us), max_depth, mode=mode)
     torch.cuda.synchronize()
     return a.cpu().numpy(), p.cpu().numpy(), o.cpu().numpy()
 
@@ -198,3 +198,99 @@ def test_spec_vanishing_residual(gpu_lib, nk):
         expect = sup[0] if len(sup) == 1 or us[b, 0] < 0.5 else sup[1]
         assert alpha == 0 and path == [0] and out == [expect]
         assert a[b] == 0 and p[b, 0] == 0 and o[b, 0] == expect
+
+
+# ---------------------------------------------------------------- deterministic siblings
+
+@pytest.mark.parametrize("seed,B,N,V", [(0, 64, 8, 8), (1, 16, 20, 1000), (2, 4, 60, 5003),
+                                        (3, 2, 64, 40000)])
+def test_spec_point_mass_decisions_match_oracle(gpu_lib, seed, B, N, V):
+    """mode="point_mass": siblings are each node's top tokens of its draft row (ties and
+    repeats included by taking some siblings twice); accept lengths, paths and accepted
+    tokens bit-exact against the oracle's point-mass rule, with the same uniforms."""
+    tokens, parents, draft_row, tl, dl, ua, us = _spec_case(seed, B, N, V, 5, 0, 1.0, 1.5, 0)
+    rng = np.random.default_rng(900 + seed)
+    for b in range(B):
+        for v in range(N):
+            kids = [c for c in range(1, N) if parents[b, c] == v]
+            if not kids or draft_row[b, v] < 0:
+                continue
+            order = np.argsort(-dl[b, draft_row[b, v]], kind="stable")
+            for j, c in enumerate(kids):
+                tokens[b, c] = order[j % 3] if rng.random() < 0.2 else order[j]
+    # plant acceptances: some uniforms small enough to accept a likely child
+    ua = np.where(rng.random(ua.shape) < 0.3, ua * 1e-3, ua).astype(np.float32)
+    max_depth = 64
+    print(f"spec point-mass parity seed={seed} B={B} N={N} V={V}", flush=True)
+    a, p, o = _spec_gpu(gpu_lib, tokens, parents, draft_row, tl, dl, ua, us, max_depth,
+                        mode="point_mass")
+    cap = max_depth + 1
+    near = 0
+    tok_diff = 0
+    accepted_any = 0
+    for b in range(B):
+        trace = []
+        alpha, path, out = oracle.accept_spec(tokens[b], parents[b], tl[b], dl[b], draft_row[b],
+                                              ua[b], us[b], max_depth, trace=trace,
+                                              mode="point_mass")
+        margins = [abs(float(ua[b, kid]) - r) for (_, kids, ratios, _) in trace
+                   for kid, r in zip(kids, ratios)]
+        if margins and min(margins) <= 1e-6:
+            near += 1
+            continue
+        accepted_any += alpha > 0
+        assert a[b] == alpha
+        assert list(p[b]) == _padded(path, cap)
+        assert list(o[b, :alpha]) == out[:alpha]
+        assert 0 <= o[b, alpha] < V
+        tok_diff += int(o[b, alpha] != out[alpha])
+    assert near <= max(1, B // 20)
+    assert tok_diff <= max(1, B // 20)
+    assert accepted_any > 0 or B < 4   # tiny batches over large vocabularies may accept nothing
+
+
+def test_spec_point_mass_chi_square_on_gpu(gpu_lib):
+    """2e5 trials, V = 8, the root's three children fixed to the draft's top-3 (the
+    same tokens in every trial): with the point-mass rule the first emitted token
+    follows q; with the sampled rule it would not (see the oracle's contrast test)."""
+    T, V, N = 200_000, 8, 4
+    tlrow = synth.normal_f32((V,), 1.2, 0, 660, 1)
+    dlrow = synth.normal_f32((V,), 2.0, 0, 660, 2)
+    q = np.exp(tlrow.astype(np.float64) - tlrow.max())
+    q /= q.sum()
+    top3 = np.argsort(-dlrow, kind="stable")[:3].astype(np.int32)
+    parents = np.tile(np.array([-1, 0, 0, 0], np.int32), (T, 1))
+    draft_row = np.tile(np.array([0, -1, -1, -1], np.int32), (T, 1))
+    tokens = np.tile(np.concatenate([[0], top3]).astype(np.int32), (T, 1))
+    tl = np.broadcast_to(tlrow, (T, N, V)).copy()
+    dl = np.broadcast_to(dlrow, (T, 1, V)).copy()
+    ua = synth.uniform_f32((T, N), 0, 660, 4)
+    us = synth.uniform_f32((T, N), 0, 660, 5)
+    a, path, o = _spec_gpu(gpu_lib, tokens, parents, draft_row, tl, dl, ua, us, 5,
+                           mode="point_mass")
+    first = np.bincount(o[:, 0], minlength=V)[:V].astype(np.float64)
+    stat = ((first - T * q) ** 2 / (T * q)).sum()
+    assert chi2.sf(stat, V - 1) > 1e-3, (first / T, q)
+
+
+def test_spec_point_mass_full_c4_tree(gpu_lib):
+    """C4 shapes with the point-mass rule (the rule that is exact for EAGLE-2's top-k
+    siblings): decisions against the oracle on the rerank tree."""
+    cfg = synth.CONFIGS["C4"]
+    V = cfg.V
+    dl = synth.normal_f32((1, cfg.rows, V), cfg.draft_std, 0, cfg.index, 6)
+    root = int(synth.integers((1,), 0, V, 0, cfg.index, 7)[0])
+    tree = oracle.eagle2_rerank(dl[0], root, cfg.top_k, cfg.depth, cfg.N)
+    tl = synth.normal_f32((1, cfg.N, V), 1.0, 0, cfg.index, 10)
+    ua = synth.uniform_f32((1, cfg.N), 0, cfg.index, 8)
+    us = synth.uniform_f32((1, cfg.N), 0, cfg.index, 9)
+    toks = tree["tokens"][None].astype(np.int32)
+    par = tree["parents"][None].astype(np.int32)
+    drow = tree["draft_row"][None].astype(np.int32)
+    a, p, o = _spec_gpu(gpu_lib, toks, par, drow, tl, dl, ua, us, cfg.max_depth, mode="point_mass")
+    trace = []
+    alpha, path, out = oracle.accept_spec(toks[0], par[0], tl[0], dl[0], drow[0], ua[0], us[0],
+                                          cfg.max_depth, trace=trace, mode="point_mass")
+    assert a[0] == alpha and list(p[0, :alpha + 1]) == path
+    assert list(o[0, :alpha]) == out[:alpha]
+    assert 0 <= o[0, alpha] < V

@@ -96,7 +96,8 @@ def test_ragged_greedy(gpu_lib):
         assert list(o[b]) == list(out) + [-1] * (maxd + 1 - len(out))
 
 
-def test_ragged_spec(gpu_lib):
+@pytest.mark.parametrize("mode", ["sampled", "point_mass"])
+def test_ragged_spec(gpu_lib, mode):
     B, Nmax, V, R_per, maxd = 8, 24, 700, 5, 64
     parents = synth.random_parents(B, Nmax, 0, 780, 1)
     tl = synth.normal_f32((B, Nmax, V), 1.0, 0, 780, 2)
@@ -111,7 +112,8 @@ def test_ragged_spec(gpu_lib):
         for v in sorted(set(parents[b, 1:].tolist())):
             draft_row[b, v] = rowpick[b, v]
     a, p, o = gpu_lib.eagle_accept_spec(to_dev(tokens), to_dev(parents), to_dev(draft_row), to_dev(tl),
-                                        to_dev(dl), to_dev(ua), to_dev(us), maxd, tree_len=to_dev(N_arr))
+                                        to_dev(dl), to_dev(ua), to_dev(us), maxd, tree_len=to_dev(N_arr),
+                                        mode=mode)
     torch.cuda.synchronize()
     a, p, o = a.cpu().numpy(), p.cpu().numpy(), o.cpu().numpy()
     checked = 0
@@ -119,7 +121,8 @@ def test_ragged_spec(gpu_lib):
         n = int(N_arr[b])
         trace = []
         alpha, path, out = oracle.accept_spec(tokens[b][:n], parents[b][:n], tl[b][:n], dl[b],
-                                              draft_row[b][:n], ua[b][:n], us[b][:n], maxd, trace=trace)
+                                              draft_row[b][:n], ua[b][:n], us[b][:n], maxd, trace=trace,
+                                              mode=mode)
         margins = [abs(float(ua[b, kid]) - r) for (_, kids, ratios, _) in trace
                    for kid, r in zip(kids, ratios)]
         if margins and min(margins) <= 1e-6:
