@@ -229,6 +229,7 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
   __shared__ int kids[64];
   __shared__ int nkids_s;
   // per child (in sibling order): token, its target and draft logits, its uniform
+  __shared__ double cterm[128];   // per-chunk softmax terms: q in [0, 64), p in [64, 128)
   __shared__ int kid_tok[64];
   __shared__ float kid_tl[64], kid_dl[64], kid_u[64];
   __shared__ int path_s[65];
@@ -298,7 +299,7 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
       for (int i = 0; i < kSpecRegs; ++i) {
         const int x = x0 + tid + i * kSpecThreads;
         tr[i] = x < x1 ? tl[x] : -INFINITY;
-        dr[i] = x < x1 ? dl[x] : -INFINITY;
+        dr[i] = (x < x1 && !pm) ? dl[x] : -INFINITY;
       }
 #pragma unroll
       for (int i = 0; i < kSpecRegs; ++i) {
@@ -313,25 +314,26 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
         mp = fmax(mp, (double)dl[x]);
       }
     }
+    // (point-mass mode never uses the draft distribution: its half is skipped)
     mq = wg_max_d(mq, red);
-    mp = wg_max_d(mp, red);
+    if (!pm) mp = wg_max_d(mp, red);
     double zq = 0.0, zp = 0.0;
     if (in_regs) {
 #pragma unroll
       for (int i = 0; i < kSpecRegs; ++i) {
         if (x0 + tid + i * kSpecThreads < x1) {
           zq += exp((double)tr[i] - mq);
-          zp += exp((double)dr[i] - mp);
+          if (!pm) zp += exp((double)dr[i] - mp);
         }
       }
     } else {
       for (int x = x0 + tid; x < x1; x += kSpecThreads) {
         zq += exp((double)tl[x] - mq);
-        zp += exp((double)dl[x] - mp);
+        if (!pm) zp += exp((double)dl[x] - mp);
       }
     }
     zq = wg_sum_d(zq, red);
-    zp = wg_sum_d(zp, red);
+    if (!pm) zp = wg_sum_d(zp, red);
     {
       const double mine[4] = {mq, zq, mp, zp};
       if (!exchange(w, b, chunks, me, gen++, 4, mine, lds_all, &lds_flag)) { aborted = true; break; }
@@ -341,28 +343,36 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
       Mq = fmax(Mq, lds_all[4 * c]);
       Mp = fmax(Mp, lds_all[4 * c + 2]);
     }
-    double Zq = 0.0, Zp = 0.0;
-    for (int c = 0; c < chunks; ++c) {
-      if (lds_all[4 * c] > -INFINITY) Zq += lds_all[4 * c + 1] * exp(lds_all[4 * c] - Mq);
-      if (lds_all[4 * c + 2] > -INFINITY) Zp += lds_all[4 * c + 3] * exp(lds_all[4 * c + 2] - Mp);
+    // chunk terms: one exponential per lane, then summed in chunk order by every
+    // thread (an empty chunk adds +0.0, which leaves the sum unchanged)
+    if (tid < chunks) {
+      cterm[tid] = lds_all[4 * tid] > -INFINITY ? lds_all[4 * tid + 1] * exp(lds_all[4 * tid] - Mq) : 0.0;
+    } else if (tid >= 64 && tid < 64 + chunks && !pm) {
+      const int c = tid - 64;
+      cterm[tid] = lds_all[4 * c + 2] > -INFINITY ? lds_all[4 * c + 3] * exp(lds_all[4 * c + 2] - Mp) : 0.0;
     }
+    __syncthreads();
+    double Zq = 0.0, Zp = 0.0;
+    for (int c = 0; c < chunks; ++c) Zq += cterm[c];
+    if (!pm)
+      for (int c = 0; c < chunks; ++c) Zp += cterm[64 + c];
     const double lse_q = Mq + log(Zq);
-    const double lse_p = Mp + log(Zp);
+    const double lse_p = pm ? 0.0 : Mp + log(Zp);
     if (in_regs) {
 #pragma unroll
       for (int i = 0; i < kSpecRegs; ++i) {
         const int x = x0 + tid + i * kSpecThreads;
         qr[i] = x < x1 ? exp((double)tr[i] - lse_q) : 0.0;
-        pr[i] = x < x1 ? exp((double)dr[i] - lse_p) : 0.0;
+        pr[i] = (x < x1 && !pm) ? exp((double)dr[i] - lse_p) : 0.0;
         if (x < x1) {
           qb[x] = qr[i];
-          pb[x] = pr[i];
+          if (!pm) pb[x] = pr[i];
         }
       }
     } else {
       for (int x = x0 + tid; x < x1; x += kSpecThreads) {
         qb[x] = exp((double)tl[x] - lse_q);
-        pb[x] = exp((double)dl[x] - lse_p);
+        if (!pm) pb[x] = exp((double)dl[x] - lse_p);
       }
     }
     __syncthreads();
@@ -474,7 +484,7 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
       double tsum = 0.0;
       int tlast = -1;
       for (int x = t0; x < t1; ++x) {
-        const double m = fmax(0.0, qb[x] - c * pb[x]);
+        const double m = pm ? qb[x] : fmax(0.0, qb[x] - c * pb[x]);
         tsum += m;
         if (m > 0.0) tlast = x;
       }
@@ -521,7 +531,7 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
         if (Tl >= before && Tl < before + tsum) {
           double run = before;
           for (int x = t0; x < t1; ++x) {
-            run += fmax(0.0, qb[x] - c * pb[x]);
+            run += pm ? qb[x] : fmax(0.0, qb[x] - c * pb[x]);
             if (run > Tl) {
               found_s = x;
               break;
