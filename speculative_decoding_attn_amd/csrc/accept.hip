@@ -319,12 +319,14 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
     if (!pm) mp = wg_max_d(mp, red);
     double zq = 0.0, zp = 0.0;
     if (in_regs) {
+      // exp(x - chunk max) stays in qr / pr; scaled to q / p once the totals are known
 #pragma unroll
       for (int i = 0; i < kSpecRegs; ++i) {
-        if (x0 + tid + i * kSpecThreads < x1) {
-          zq += exp((double)tr[i] - mq);
-          if (!pm) zp += exp((double)dr[i] - mp);
-        }
+        const bool in = x0 + tid + i * kSpecThreads < x1;
+        qr[i] = in ? exp((double)tr[i] - mq) : 0.0;
+        pr[i] = (in && !pm) ? exp((double)dr[i] - mp) : 0.0;
+        zq += qr[i];
+        zp += pr[i];
       }
     } else {
       for (int x = x0 + tid; x < x1; x += kSpecThreads) {
@@ -359,11 +361,13 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
     const double lse_q = Mq + log(Zq);
     const double lse_p = pm ? 0.0 : Mp + log(Zp);
     if (in_regs) {
+      const double sq = exp(mq - lse_q);
+      const double sp = pm ? 0.0 : exp(mp - lse_p);
 #pragma unroll
       for (int i = 0; i < kSpecRegs; ++i) {
         const int x = x0 + tid + i * kSpecThreads;
-        qr[i] = x < x1 ? exp((double)tr[i] - lse_q) : 0.0;
-        pr[i] = (x < x1 && !pm) ? exp((double)dr[i] - lse_p) : 0.0;
+        qr[i] *= sq;
+        pr[i] *= sp;
         if (x < x1) {
           qb[x] = qr[i];
           if (!pm) pb[x] = pr[i];
