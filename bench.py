@@ -538,15 +538,18 @@ def summarize_mfma(path):
     import collections
     per = collections.defaultdict(dict)
     span = {}
+    import re
     for r in _read_csv(path):
-        key = (int(r["Dispatch_Id"]), r["Kernel_Name"].split("(")[0])
+        # plain ("lm_head_gemm") or demangled ("void eagle::(anonymous namespace)::lm_head_gemm<...>(...)")
+        m = re.search(r"(?<![A-Za-z0-9_])(lm_head_gemm|tree_attn_pingpong)(?![A-Za-z0-9_])", r["Kernel_Name"])
+        if not m:
+            continue
+        key = (int(r["Dispatch_Id"]), m.group(1))
         per[key][r["Counter_Name"]] = float(r["Counter_Value"])
         span[key] = (int(r["Start_Timestamp"]), int(r["End_Timestamp"]))
     agg = collections.defaultdict(list)
     for key, c in per.items():
-        name = key[1].split("::")[-1].split("<")[0]
-        if name not in ("lm_head_gemm", "tree_attn_pingpong"):
-            continue
+        name = key[1]
         t0, t1 = span[key]
         dur_s = (t1 - t0) * 1e-9
         cycles = c["GRBM_GUI_ACTIVE"] / XCCS
