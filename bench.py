@@ -183,7 +183,7 @@ def copy_calibration(torch, dev, nbytes=1 << 30, reps=5):
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}))
 
 
-def spec_latency(torch, sda, dev, iters=20, mode="sampled"):
+def spec_latency(torch, sda, dev, iters=100, mode="sampled"):
     """eagle_accept_spec at the Llama-3-8B-shaped speculative-sampling workload (C4): a
     60-node tree from eagle2_rerank, target logits N(0,1) over 128256 tokens.  mode
     "sampled" runs the pages' rule with the draft distribution (10 residual rounds at
