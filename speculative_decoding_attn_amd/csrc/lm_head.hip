@@ -169,7 +169,7 @@ lm_head_gemm(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W
   // while the last LA groups of block b are multiplied, so the matrix cores do not
   // wait for the barrier.  The DMA instructions are spread over the block instead of
   // issued in bursts (a burst fills the vector L1's miss queue and stalls the wave's
-  // in-order issue, MFMAs included): W block b+2 over groups 0..NG-LA-1 (its stage
+  // in-order issue, MFMAs included): W block b+2 over groups WSTART..NG-LA-1 (its stage
   // was freed at block b-1's barrier), hidden block b+2 over the last LA groups (its
   // stage is block b's, freed at this barrier).  Hidden loads are issued after the W
   // loads of the same block, so at block b's barrier only W block b+2 may be
@@ -177,6 +177,10 @@ lm_head_gemm(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W
   static_assert(NG % (LA + 1) == 0, "the hidden fragment ring continues across blocks");
   static_assert(LA <= MT, "the barrier falls in step 3, after step 2 last used wf[0]");
   constexpr int NGI = NG - LA;
+  // first group that issues W block b+2: with two row halves (the large-M tile) the W
+  // loads go out over the second half of the block only, which keeps fewer of them in
+  // flight and measured faster there; the smaller tiles spread them over the block
+  constexpr int WSTART = WVM > 1 ? NGI / 2 : 0;
 #pragma unroll
   for (int t = 0; t < W_DMA; ++t) issue_w(0, 0, t);
 #pragma unroll
@@ -217,7 +221,7 @@ lm_head_gemm(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W
       }
 #pragma unroll
       for (int t = 0; t < W_DMA; ++t)
-        if ((t * NGI) / W_DMA == g && more) issue_w(b + 2, sw2, t);
+        if (WSTART + (t * (NGI - WSTART)) / W_DMA == g && more) issue_w(b + 2, sw2, t);
       if (g == NGI) {
         if (more) wait_vmcnt<W_DMA>();
         else wait_vmcnt<0>();
