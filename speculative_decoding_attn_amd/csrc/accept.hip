@@ -88,6 +88,12 @@ accept_greedy_kernel(const int32_t* __restrict__ tokens, const int32_t* __restri
 // max(0, q - c p) with the next c, and the acceptance ratio of token t is
 // max(0, q(t) - c p(t)) / (S p(t)).  All of it runs in fp64 on fp64 q and p.
 //
+// Deterministic siblings (point-mass mode, EAGLE-2's top-k expansion): the draft
+// distribution behind child t is the point mass at t, so the same rule accepts t when
+// u < q'(t) = q(t) / (1 - removed mass) and a rejection removes q(t) from q'.  Those
+// decisions need no vocabulary pass; the final draw is from q with the removed tokens
+// zeroed.
+//
 // Parallel layout.  Each sequence gets `chunks` workgroups, each owning a contiguous
 // slice of the vocabulary.  Every workgroup follows the same control flow; the
 // vocabulary reductions are exchanged through the workspace in self-validating
