@@ -380,6 +380,46 @@ tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 }
 
 // One wave per (pair, row): combine the S split partials with their lse weights.
+// D = 128: one (pair, row) per half wave, 4 entries (16 bytes) per lane; the same
+// arithmetic per entry as tree_attn_merge
+__global__ void __launch_bounds__(256)
+tree_attn_merge_hw(AttnPlan pl, const float* __restrict__ part_o, const float* __restrict__ part_lse,
+                   uint16_t* __restrict__ out, float* __restrict__ lse_out) {
+  constexpr int D = 128;
+  const int lane = threadIdx.x & 31;
+  const int gr = blockIdx.x * (blockDim.x / 32) + (threadIdx.x >> 5);
+  const int pairs = pl.B * pl.Hkv;
+  if (gr >= pairs * pl.R) return;
+  const int pair = gr / pl.R;
+  const int r = gr % pl.R;
+  const int b = pair / pl.Hkv;
+  const int g = pair % pl.Hkv;
+  if (pl.tree_len && r >= min(max(pl.tree_len[b], 1), pl.N) * pl.G) return;   // past this tree
+  const size_t base = (size_t)pair * pl.S * pl.Rpad + r;
+  float mx = -INFINITY;
+  for (int s = 0; s < pl.S; ++s) mx = fmaxf(mx, part_lse[base + (size_t)s * pl.Rpad]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  for (int s = 0; s < pl.S; ++s) {
+    const size_t prow = base + (size_t)s * pl.Rpad;
+    const float wgt = expf(part_lse[prow] - mx);
+    wsum += wgt;
+    const f32x4 o = *(const f32x4*)(part_o + prow * D + lane * 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += wgt * o[e];
+  }
+  const float inv = 1.f / wsum;
+  const int il = r / pl.G;
+  const int i = pl.node0 + il;
+  const int h = g * pl.G + (r - il * pl.G);
+  uint16_t* o = out + ((size_t)(b * pl.N + i) * pl.Hq + h) * D + lane * 4;
+  u32x2 pk;
+  pk[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  pk[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  *(u32x2*)o = pk;
+  if (lane == 0 && lse_out) lse_out[(size_t)(b * pl.N + i) * pl.Hq + h] = mx + logf(wsum);
+}
+
 template <int D>
 __global__ void __launch_bounds__(256)
 tree_attn_merge(AttnPlan pl, const float* __restrict__ part_o, const float* __restrict__ part_lse,
@@ -911,8 +951,8 @@ hipError_t launch_tree_attn(const AttnPlan& pl0, float scale, const void* q, con
   const int rows = pl.B * pl.Hkv * pl.R;
   const int blocks = (rows + 3) / 4;
   if (pl.D == 128)
-    hipLaunchKernelGGL(tree_attn_merge<128>, dim3(blocks), dim3(256), 0, stream, pl, part_o, part_lse,
-                       (uint16_t*)out, lse);
+    hipLaunchKernelGGL(tree_attn_merge_hw, dim3((rows + 7) / 8), dim3(256), 0, stream, pl, part_o,
+                       part_lse, (uint16_t*)out, lse);
   else
     hipLaunchKernelGGL(tree_attn_merge<64>, dim3(blocks), dim3(256), 0, stream, pl, part_o, part_lse,
                        (uint16_t*)out, lse);
