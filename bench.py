@@ -105,6 +105,25 @@ def attn_flops(parents_np, cfg) -> float:
     return 4.0 * cfg.D * cfg.Hq * total_keys
 
 
+def _host_info():
+    """The host the CPU baseline ran on: CPU model, cores this process may use, cores
+    in the machine."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
+    return {"cpu_model": model, "usable_cores": usable, "machine_cores": os.cpu_count()}
+
+
 def cpu_baseline(cfg):
     """Time the fp64 oracle on a bounded sample of the C5 step and scale to one step."""
     import oracle
@@ -163,7 +182,7 @@ def cpu_baseline(cfg):
 
     step = t_attn + t_lm + t_rr + t_acc
     return {"value": round(B * N / step, 3), "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "host": _host_info(),
             "sample": (f"fp64 numpy oracle on {n_pairs}/{B * Hkv} attention (sequence, KV head) "
                        f"pairs, {n_slices}/64 LM-head vocabulary slices, {n_rerank}/{B} rerank "
                        f"sequences and all {B} greedy acceptances of the C5 step, each scaled "

@@ -77,3 +77,10 @@ def test_mfma_summary_from_counters(tmp_path, monkeypatch):
     assert cells[6] == str(round(1024 * 1024 * 2.0e9 / 1e12))   # peak at that clock
     assert cells[7] == "25.0"                     # LDS active %
     assert os.path.exists(tmp_path / bench.MFMA_MD)
+
+
+def test_host_info_names_the_cpu():
+    info = bench._host_info()
+    assert set(info) == {"cpu_model", "usable_cores", "machine_cores"}
+    assert 1 <= info["usable_cores"] <= info["machine_cores"]
+    assert isinstance(info["cpu_model"], str) and info["cpu_model"]
