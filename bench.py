@@ -425,22 +425,24 @@ def ragged_step(torch, sda, dev, x, steps=20):
             "breakdown_us": {k: round(v, 2) for k, v in per.items()}}
 
 
+# rocprofv3 runs behind the committed summaries; {out} is the directory they write to
+# (the same directory is then passed to --summarize-profiles)
 PROFILE_RUNS = {
-    "prof": "rocprofv3 --kernel-trace --stats -T -d gpurun_out/prof -o run --output-format csv "
+    "prof": "rocprofv3 --kernel-trace --stats -T -d {out}/prof -o run --output-format csv "
             "-- python -u bench.py --steps 50 --warmup 5 --no-cpu-baseline --no-spec",
-    "prof_draft": "rocprofv3 --kernel-trace --stats -T -d gpurun_out/prof_draft -o run --output-format csv "
+    "prof_draft": "rocprofv3 --kernel-trace --stats -T -d {out}/prof_draft -o run --output-format csv "
                   "-- python -u bench.py --only-draft",
-    "pmc_fetch": "rocprofv3 --pmc FETCH_SIZE -T -d gpurun_out/pmc_fetch -o run --output-format csv "
+    "pmc_fetch": "rocprofv3 --pmc FETCH_SIZE -T -d {out}/pmc_fetch -o run --output-format csv "
                  "-- python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-spec",
-    "pmc_write": "rocprofv3 --pmc WRITE_SIZE -T -d gpurun_out/pmc_write -o run --output-format csv "
+    "pmc_write": "rocprofv3 --pmc WRITE_SIZE -T -d {out}/pmc_write -o run --output-format csv "
                  "-- python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-spec",
-    "pmc_copy_fetch": "rocprofv3 --pmc FETCH_SIZE -T -d gpurun_out/pmc_copy_fetch -o run "
+    "pmc_copy_fetch": "rocprofv3 --pmc FETCH_SIZE -T -d {out}/pmc_copy_fetch -o run "
                       "--output-format csv -- python -u bench.py --copy-calib",
-    "pmc_copy_write": "rocprofv3 --pmc WRITE_SIZE -T -d gpurun_out/pmc_copy_write -o run "
+    "pmc_copy_write": "rocprofv3 --pmc WRITE_SIZE -T -d {out}/pmc_copy_write -o run "
                       "--output-format csv -- python -u bench.py --copy-calib",
     "pmc_mfma": "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CU_CYCLES "
                 "SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS GRBM_GUI_ACTIVE GRBM_COUNT -T "
-                "-d gpurun_out/pmc_mfma -o run --output-format csv -- python -u bench.py --steps 2 "
+                "-d {out}/pmc_mfma -o run --output-format csv -- python -u bench.py --steps 2 "
                 "--warmup 1 --no-cpu-baseline --no-spec",
 }
 TRACE_MD = "c5_step_kernel_trace.md"
@@ -449,6 +451,11 @@ TRAFFIC_MD = "c5_step_hbm_traffic.md"
 MFMA_MD = "c5_step_mfma_counters.md"
 SIMDS = 1024   # 256 CUs x 4 SIMDs
 XCCS = 8
+
+
+def _run_cmd(name, root):
+    """The command of PROFILE_RUNS[name] as run with output directory `root`."""
+    return PROFILE_RUNS[name].replace("{out}", os.path.normpath(root))
 
 
 def _read_csv(path):
@@ -465,7 +472,7 @@ def summarize_profiles(root):
     stats = _read_csv(os.path.join(root, "prof", "run_kernel_stats.csv"))
     total = sum(float(r["TotalDurationNs"]) for r in stats)
     lines = ["# rocprofv3 kernel trace: C5 verification step", "",
-             "Command (repository root, one MI355X):", "", "    " + PROFILE_RUNS["prof"], "",
+             "Command (repository root, one MI355X):", "", "    " + _run_cmd("prof", root), "",
              f"Workload: C5 (B={B}, N={N}, Hq={Hq}, Hkv={Hkv}, D={D}, P={P}, H={H}, V={V}); "
              "55 steps (5 warmup + 50 timed, as bench.py times them), nothing else.", "",
              "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
@@ -483,7 +490,7 @@ def summarize_profiles(root):
         dtotal = sum(float(r["TotalDurationNs"]) for r in dstats)
         B_, H_, Hq_, Hkv_, D_, I_, V_, P_ = DRAFT_SHAPES["C5"]
         dl = ["# rocprofv3 kernel trace: per-depth draft expansion, C5 shapes", "",
-              "Command (repository root, one MI355X):", "", "    " + PROFILE_RUNS["prof_draft"], "",
+              "Command (repository root, one MI355X):", "", "    " + _run_cmd("prof_draft", root), "",
               f"Workload: eagle_draft_expand with a one-layer draft head (B={B_}, H={H_}, Hq={Hq_}, "
               f"Hkv={Hkv_}, D={D_}, MLP {I_}, V={V_}, draft prefix {P_}), top-k 10, depth 6, 60 nodes; "
               "4 expansions (1 warmup + 3 timed).  lm_head_gemm runs every projection and the LM head "
@@ -517,7 +524,7 @@ def summarize_profiles(root):
     attn_name = next(k for k in fetch if k.startswith("tree_attn_") and "merge" not in k)
     algo = {attn_name: 2 * B * Hkv * (P + N) * D * 2 + 2 * B * N * Hq * D * 2 + B * N * Hq * 4,
             "lm_head_gemm": V * H * 2 + B * N * H * 2 + B * N * 16}
-    cmds = [PROFILE_RUNS[k] for k in ("pmc_fetch", "pmc_write", "pmc_copy_fetch", "pmc_copy_write")]
+    cmds = [_run_cmd(k, root) for k in ("pmc_fetch", "pmc_write", "pmc_copy_fetch", "pmc_copy_write")]
     rows = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE), C5 verification step", "",
             "Commands (repository root, one MI355X; each counter in a run of its own):", ""]
     rows += ["    " + c for c in cmds]
@@ -546,15 +553,17 @@ def summarize_profiles(root):
     print("\n".join(lines + [""] + rows))
     mpath = os.path.join(root, "pmc_mfma", "run_counter_collection.csv")
     if os.path.exists(mpath):
-        print(summarize_mfma(mpath))
+        print(summarize_mfma(mpath, root))
 
 
-def summarize_mfma(path):
+def summarize_mfma(path, root=None):
     """Per-kernel matrix-core and LDS counters of the C5 step (the PROFILE_RUNS
     "pmc_mfma" run): the clock the kernel ran at (GRBM_GUI_ACTIVE cycles per XCC over
     the dispatch time), MFMA busy cycles per SIMD over those cycles, bf16 MFMA flops
     (512 per MOPS unit, padding included) over the dispatch time, LDS activity."""
     import collections
+    if root is None:   # <root>/pmc_mfma/run_counter_collection.csv
+        root = os.path.dirname(os.path.dirname(os.path.abspath(path)))
     per = collections.defaultdict(dict)
     span = {}
     import re
@@ -578,7 +587,7 @@ def summarize_mfma(path):
                           "lds_active": c["SQ_LDS_IDX_ACTIVE"] / (cycles * SIMDS / 4),
                           "conflicts": c["SQ_LDS_BANK_CONFLICT"]})
     lines = ["# rocprofv3 matrix-core and LDS counters: C5 verification step", "",
-             "Command (repository root, one MI355X):", "", "    " + PROFILE_RUNS["pmc_mfma"], "",
+             "Command (repository root, one MI355X):", "", "    " + _run_cmd("pmc_mfma", root), "",
              "Per kernel, the mean over the run's dispatches (3 steps).  clock = GRBM_GUI_ACTIVE / 8 XCCs",
              "over the dispatch time; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (clock cycles x 1024 SIMDs);",
              "bf16 MFMA rate = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 flop over the dispatch time (padded",
