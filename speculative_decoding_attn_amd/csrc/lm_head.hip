@@ -383,9 +383,13 @@ LmPlan plan_lm_head(int M, int H, int V) {
   pl.V = V;
   // tile shapes (LDS holds 3 W stages of vrows x 128 B and 2 hidden stages of
   // mrows x 128 B)
-  if (M > 128) {
+  if (M > 192) {
     pl.variant = 3;          // 8 waves (4 vocab x 2 row halves), 2 per SIMD: 256 rows x 256 vocab
     pl.mrows = 256;
+    pl.vrows = 256;
+  } else if (M > 128) {
+    pl.variant = 4;          // the same grid with three row tiles per half: 192 rows x 256 vocab
+    pl.mrows = 192;
     pl.vrows = 256;
   } else if (M > 64) {
     pl.variant = 2;          // 4 waves, MT=4 VT=2: 128 rows x 256 vocab
@@ -442,6 +446,7 @@ hipError_t launch_gemm_f32(int M, int K, int N, const void* X, const void* W, fl
   hipError_t e;
   switch (pl.variant) {
     case 3: e = launch_gemm<4, 2, 4, 2, 3>(pl, X, W, part, dst, stream); break;
+    case 4: e = launch_gemm<3, 2, 4, 2, 3>(pl, X, W, part, dst, stream); break;
     case 2: e = launch_gemm<4, 2, 4, 1, 3>(pl, X, W, part, dst, stream); break;
     case 1: e = launch_gemm<2, 2, 4, 1, 1>(pl, X, W, part, dst, stream); break;
     default: e = launch_gemm<1, 1, 4, 1, 1>(pl, X, W, part, dst, stream); break;
@@ -464,6 +469,7 @@ hipError_t launch_lm_head(const LmPlan& pl, const void* hidden, const void* W, f
   hipError_t e;
   switch (pl.variant) {
     case 3: e = launch_gemm<4, 2, 4, 2, 3>(pl, hidden, W, part, out_logits, stream); break;
+    case 4: e = launch_gemm<3, 2, 4, 2, 3>(pl, hidden, W, part, out_logits, stream); break;
     case 2: e = launch_gemm<4, 2, 4, 1, 3>(pl, hidden, W, part, out_logits, stream); break;
     case 1: e = launch_gemm<2, 2, 4, 1, 1>(pl, hidden, W, part, out_logits, stream); break;
     default: e = launch_gemm<1, 1, 4, 1, 1>(pl, hidden, W, part, out_logits, stream); break;

@@ -22,6 +22,9 @@ CASES = [
     (60, 4096, 5000),
     (64, 192, 640),
     (65, 256, 700),
+    (129, 512, 777),
+    (185, 1024, 2560),
+    (192, 256, 1000),
     (240, 1024, 2560),
     (300, 512, 1337),
 ]
