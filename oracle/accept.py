@@ -37,6 +37,14 @@ def _softmax64(logits):
     return e / e.sum()
 
 
+def _dist(logits, lse):
+    """The distribution of a logit row: softmax in fp64, or, with the normaliser the
+    caller recorded for the row (its log-sum-exp), exp(logit - lse) as given."""
+    if lse is None:
+        return _softmax64(logits)
+    return np.exp(np.asarray(logits, dtype=np.float64) - float(lse))
+
+
 def sample_inverse_cdf(dist, u: float) -> int:
     """Smallest x with sum_{y<=x} dist(y) > u * sum(dist); if rounding leaves none,
     the last x with dist(x) > 0."""
@@ -129,7 +137,8 @@ def spec_node_round_point_mass(q, child_tokens, u_accept):
 
 
 def accept_spec(tokens, parents, target_logits, draft_logits, draft_row, u_accept, u_sample,
-                max_depth: int, trace: list | None = None, mode: str = "sampled"):
+                max_depth: int, trace: list | None = None, mode: str = "sampled",
+                target_lse=None, draft_lse=None):
     """One sequence.
 
     tokens, parents, draft_row: [N] ints (draft_row[i] = row of draft_logits holding
@@ -143,6 +152,11 @@ def accept_spec(tokens, parents, target_logits, draft_logits, draft_row, u_accep
     deterministically (spec_node_round_point_mass; draft_logits are not read, a node
     still needs draft_row >= 0 to have its children tried).
 
+    target_lse [N] / draft_lse [R] (optional): the log-sum-exp recorded for each
+    target / draft row ([P2] multi-round section: the draft keeps each sampled
+    token's probability as it drafts; the target's come with its LM head).  When
+    given, q = exp(target_logits[v] - target_lse[v]) and p likewise, used as they are.
+
     Returns (alpha, path, out_tokens) like accept_greedy.  If ``trace`` is a list,
     one (node, child_list, ratios, j) tuple per visited node is appended.
     """
@@ -154,7 +168,7 @@ def accept_spec(tokens, parents, target_logits, draft_logits, draft_row, u_accep
     path = [0]
     while True:
         kids = children_of(parents, v) if depth[v] < max_depth else []
-        q = _softmax64(target_logits[v])
+        q = _dist(target_logits[v], None if target_lse is None else target_lse[v])
         row = int(draft_row[v])
         if not kids or row < 0:
             if trace is not None:
@@ -165,7 +179,7 @@ def accept_spec(tokens, parents, target_logits, draft_logits, draft_row, u_accep
             j, q_left, ratios = spec_node_round_point_mass(q, [tokens[c] for c in kids],
                                                            [u_accept[c] for c in kids])
         else:
-            p = _softmax64(draft_logits[row])
+            p = _dist(draft_logits[row], None if draft_lse is None else draft_lse[row])
             j, q_left, ratios = spec_node_round(q, p, [tokens[c] for c in kids],
                                                 [u_accept[c] for c in kids])
         if trace is not None:

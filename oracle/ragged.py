@@ -39,12 +39,15 @@ def accept_greedy_ragged(tokens, parents, target_argmax, tree_len, max_depth: in
 
 
 def accept_spec_ragged(tokens, parents, target_logits, draft_logits, draft_row, u_accept,
-                       u_sample, tree_len, max_depth: int, mode: str = "sampled"):
+                       u_sample, tree_len, max_depth: int, mode: str = "sampled",
+                       target_lse=None, draft_lse=None):
     """Per sequence: accept_spec on its first tree_len[b] nodes (draft rows as given)."""
     res = []
     for b in range(len(tree_len)):
         n = int(tree_len[b])
         res.append(accept_spec(tokens[b][:n], parents[b][:n], target_logits[b][:n], draft_logits[b],
                                draft_row[b][:n], u_accept[b][:n], u_sample[b][:n], max_depth,
-                               mode=mode))
+                               mode=mode,
+                               target_lse=None if target_lse is None else target_lse[b][:n],
+                               draft_lse=None if draft_lse is None else draft_lse[b]))
     return res

@@ -10,8 +10,6 @@ from __future__ import annotations
 
 from typing import List, Set
 
-import numpy as np
-
 
 def node_depths(parents) -> List[int]:
     """Depth of every node: the root has depth 0, a child one more than its parent."""
@@ -38,9 +36,3 @@ def children_of(parents, v: int) -> List[int]:
     """Children of node v in ascending node index (sibling order)."""
     return [c for c in range(len(parents)) if int(parents[c]) == v]
 
-
-def check_tree(parents) -> bool:
-    parents = np.asarray(parents)
-    if parents.ndim != 1 or parents.size == 0 or parents[0] != -1:
-        return False
-    return all(0 <= parents[i] < i for i in range(1, parents.size))

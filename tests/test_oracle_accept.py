@@ -347,3 +347,29 @@ def test_spec_point_mass_monte_carlo_through_accept_spec():
     q1 = np.exp(tl1 - tl1.max()); q1 /= q1.sum()
     stat2 = ((second - n_second * q1) ** 2 / (n_second * q1)).sum()
     assert chi2.sf(stat2, V - 1) > 1e-3
+
+
+@pytest.mark.parametrize("mode", ["sampled", "point_mass"])
+def test_spec_given_normalisers_reduce_to_softmax(mode):
+    """accept_spec with the rows' log-sum-exp supplied (scipy's logsumexp) takes the same
+    decisions, with the same acceptance ratios to rounding, and emits the same tokens as
+    with the normalisers formed from the logits: q = exp(l - lse) is softmax(l)."""
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(21)
+    V = 50
+    for trial in range(40):
+        N = int(rng.integers(2, 12))
+        parents = _rand_tree(rng, N)
+        tl = rng.standard_normal((N, V)) * 1.5
+        dl = rng.standard_normal((N, V)) * 2.5
+        draft_row = np.where(rng.random(N) < 0.8, np.arange(N), -1)
+        tokens = rng.integers(0, V, size=N)
+        ua, us = rng.random(N), rng.random(N)
+        t0, t1 = [], []
+        a = oracle.accept_spec(tokens, parents, tl, dl, draft_row, ua, us, 4, trace=t0, mode=mode)
+        b = oracle.accept_spec(tokens, parents, tl, dl, draft_row, ua, us, 4, trace=t1, mode=mode,
+                               target_lse=logsumexp(tl, axis=1), draft_lse=logsumexp(dl, axis=1))
+        assert a == b
+        assert [(v, k, j) for v, k, _, j in t0] == [(v, k, j) for v, k, _, j in t1]
+        for (_, _, r0, _), (_, _, r1, _) in zip(t0, t1):
+            np.testing.assert_allclose(r1, r0, rtol=1e-12, atol=1e-15)
