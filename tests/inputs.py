@@ -86,3 +86,21 @@ def draft_weights_for(vals, b=None):
     """The oracle's weight dict (shared by all sequences)."""
     keys = list(DRAFT_STD) + ["g1", "g2", "Hq", "Hkv", "D"]
     return {k: vals[k] for k in keys}
+
+
+# ---- per-depth draft expansion: the GPU parity cases and their float tolerance.
+# (seed, B, H, Hq, Hkv, D, I, V, P, top_k, depth, n_nodes, whole_tree): seeds chosen
+# with the oracle alone so that deep rows, and in the first two cases whole trees, are
+# decided clearly; V spans one to eight LM-head vocabulary tiles.
+DRAFT_CASES = [
+    (23, 4, 128, 8, 2, 128, 192, 128, 0, 3, 5, 14, True),
+    (26, 3, 192, 2, 1, 64, 320, 96, 37, 5, 3, 16, True),
+    (7, 4, 256, 4, 2, 64, 512, 200, 100, 4, 4, 12, False),
+    (4, 2, 256, 4, 2, 64, 512, 1000, 100, 4, 4, 12, False),
+]
+# Float tolerance (max-abs, logits and bf16 features) of the draft expansion: at least
+# 1.5 x the largest deviation from the fp64 oracle that a CPU model of the kernels'
+# arithmetic (bf16 storage at the oracle's rounding points, fp32 accumulation, softmax
+# weights rounded to bf16 before the value product) shows on DRAFT_CASES;
+# tests/test_oracle_draft.py checks that bound.
+DRAFT_TAU = 0.05

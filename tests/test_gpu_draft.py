@@ -1,12 +1,13 @@
 """Per-depth draft expansion on the GPU against the oracle (oracle/draft.py).
 
 Indices (each row's token and proposing row, the final tree) bit-exact; draft
-logits and features within a float tolerance.  The tolerance is derived from the
-arithmetic: a row's logits are W_lm y with y rounded to bf16 (relative step 2^-8)
-after a chain of seven bf16-rounded GEMM inputs, and the GPU's fp32 values round to
-the neighbouring bf16 value wherever they sit within ~1e-6 of a rounding boundary
-the oracle's fp64 values fall on the other side of; measured, logits of std ~1.3
-differ by up to ~0.03.  So logits and features: max-abs 0.06, relative L2 1e-2.
+logits and features within a float tolerance derived from the arithmetic (not from
+the GPU's output): tests/test_oracle_draft.py recomputes the oracle's rows with the
+kernels' arithmetic modelled on the CPU (fp32 accumulation, bf16 storage at the same
+points, softmax weights rounded to bf16 before the value product) and finds logits
+within 0.027 and features within 0.031 (one bf16 spacing in [4, 8)) of the oracle; so
+logits and features get max-abs DRAFT_TAU = 0.05 (at least 1.5 x that) and relative
+L2 1e-2.
 
 The expansion's decisions compare cumulative log-probabilities, so a decision whose
 margin is below that error may go either way.  What the decisions make unique is
@@ -14,8 +15,8 @@ compared: a node is identified by its token path from the root (its row number a
 output position also depend on the order among the chosen candidates, which may be
 a near-tie without changing which candidates are chosen).  Rows are compared down to
 the last depth whose choices (each proposing row's top-k cut, the frontier's cut)
-all have a margin above 0.06 in the oracle, matched by token path; the tree, as the
-set of token paths with their depths and scores, when every cut including the
+all have a margin above DRAFT_TAU in the oracle, matched by token path; the tree, as
+the set of token paths with their depths and scores, when every cut including the
 final selection's is that clear.
 """
 import numpy as np
@@ -23,16 +24,18 @@ import pytest
 import torch
 
 import synth
-from inputs import draft_case, draft_weights_for, rel_l2, to_dev, to_dev_bf16
+from inputs import (DRAFT_CASES, DRAFT_TAU, draft_case, draft_weights_for, rel_l2, to_dev,
+                    to_dev_bf16)
 from oracle.draft import draft_expand, draft_layer_row
 import speculative_decoding_attn_amd as sda
 
 pytestmark = pytest.mark.gpu
 
-TAU = 0.06
+TAU = DRAFT_TAU
 
 
 def assert_close_draft(got, ref):
+    """Logits and features: max-abs TAU and relative L2 1e-2."""
     got = np.asarray(got, dtype=np.float64)
     err = np.abs(got - ref).max()
     rl = rel_l2(got, ref)
@@ -147,14 +150,7 @@ def run_case(seed, B, H, Hq, Hkv, D, I, V, P, top_k, depth, n_nodes):
     return verified_rows, trees_checked
 
 
-# seeds chosen (with the oracle alone) so that deep rows, and in the first two cases
-# whole trees, are decided clearly; V spans one to eight LM-head vocabulary tiles
-@pytest.mark.parametrize("seed,B,H,Hq,Hkv,D,I,V,P,top_k,depth,n_nodes,whole_tree", [
-    (23, 4, 128, 8, 2, 128, 192, 128, 0, 3, 5, 14, True),
-    (26, 3, 192, 2, 1, 64, 320, 96, 37, 5, 3, 16, True),
-    (7, 4, 256, 4, 2, 64, 512, 200, 100, 4, 4, 12, False),
-    (4, 2, 256, 4, 2, 64, 512, 1000, 100, 4, 4, 12, False),
-])
+@pytest.mark.parametrize("seed,B,H,Hq,Hkv,D,I,V,P,top_k,depth,n_nodes,whole_tree", DRAFT_CASES)
 def test_draft_expand_matches_oracle(gpu_lib, seed, B, H, Hq, Hkv, D, I, V, P, top_k, depth, n_nodes,
                                      whole_tree):
     rows, trees = run_case(seed, B, H, Hq, Hkv, D, I, V, P, top_k, depth, n_nodes)
