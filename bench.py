@@ -87,10 +87,34 @@ def make_inputs(cfg, torch, dev):
     x["v"] = dbf(synth.normal_bf16_bits((B, Hkv, P + N, D), 1.0, 0, cfg.index, 3))
     x["hidden"] = dbf(synth.normal_bf16_bits((B * N, H), 1.0, 0, cfg.index, 4))
     x["W"] = dbf(synth.normal_bf16_bits((V, H), cfg.w_std, 0, cfg.index, 5))
-    x["draft_logits"] = torch.from_numpy(
-        synth.normal_f32((B, cfg.rows, V), cfg.draft_std, 0, cfg.index, 6)).to(dev)
+    if cfg.rows:
+        x["draft_logits"] = torch.from_numpy(
+            synth.normal_f32((B, cfg.rows, V), cfg.draft_std, 0, cfg.index, 6)).to(dev)
     x["root"] = torch.from_numpy(synth.integers((B,), 0, V, 0, cfg.index, 7)).to(dev)
     return x
+
+
+def attn_bytes(cfg) -> int:
+    """Algorithmic HBM bytes of one tree-attention call: K and V of every (sequence, KV
+    head) over prefix + tree once, q and out (bf16), lse (fp32)."""
+    B, N, Hq, Hkv, D, P = cfg.B, cfg.N, cfg.Hq, cfg.Hkv, cfg.D, cfg.P
+    return 2 * B * Hkv * (P + N) * D * 2 + 2 * B * N * Hq * D * 2 + B * N * Hq * 4
+
+
+def lm_bytes(M, H, V, logits=False) -> int:
+    """Algorithmic HBM bytes of one LM-head call: W and the hidden rows once, 16 bytes of
+    row statistics per row, plus the fp32 logits when they are written."""
+    return V * H * 2 + M * H * 2 + M * 16 + (M * V * 4 if logits else 0)
+
+
+def roof(us, nbytes, nflops=None):
+    """HBM and bf16-MFMA fractions of nominal peak for `nbytes` / `nflops` in `us`."""
+    out = {"us": round(us, 2), "hbm_gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+           "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    if nflops is not None:
+        tf = nflops / (us * 1e-6) / 1e12
+        out.update({"mfma_tflops": round(tf, 1), "mfma_frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4)})
+    return out
 
 
 def attn_flops(parents_np, cfg) -> float:
@@ -124,7 +148,7 @@ def _host_info():
     return {"cpu_model": model, "usable_cores": usable, "machine_cores": os.cpu_count()}
 
 
-def cpu_baseline(cfg):
+def cpu_baseline(cfg, n_pairs=6, n_slices=24, n_rerank=2):
     """Time the fp64 oracle on a bounded sample of the C5 step and scale to one step."""
     import oracle
     try:
@@ -135,7 +159,6 @@ def cpu_baseline(cfg):
     B, N, Hq, Hkv, D, P, H, V = cfg.B, cfg.N, cfg.Hq, cfg.Hkv, cfg.D, cfg.P, cfg.H, cfg.V
     G = Hq // Hkv
     f64 = synth.bf16_bits_to_f64
-    n_pairs, n_slices, n_rerank = 6, 24, 2
     slice_rows = (V + 63) // 64
 
     # attention: n_pairs of the B*Hkv (sequence, KV head) pairs, all nodes and heads
@@ -192,21 +215,200 @@ def cpu_baseline(cfg):
                               "rerank": round(t_rr, 3), "accept_greedy": round(t_acc, 4)}}
 
 
+def cpu_baseline_single_thread(cfg):
+    """The same oracle sample, smaller (1 of 32 attention pairs, 4 of 64 LM-head slices,
+    1 rerank sequence), with the BLAS pool limited to one thread."""
+    try:
+        import threadpoolctl
+    except Exception:  # pragma: no cover
+        return None
+    with threadpoolctl.threadpool_limits(limits=1):
+        r = cpu_baseline(cfg, n_pairs=1, n_slices=4, n_rerank=1)
+    r["cores"] = 1
+    return r
+
+
 def copy_calibration(torch, dev, nbytes=1 << 30, reps=5):
-    """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters;
+    also prints the copy's rate (bytes read + written per second)."""
     src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
     for _ in range(reps):
         dst.copy_(src)
+    e1.record(s)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}))
+    sec = e0.elapsed_time(e1) / 1000.0 / reps
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps,
+                      "copy_gbs_read_plus_write": round(2 * nbytes / sec / 1e9, 1)}))
 
 
-def spec_latency(torch, sda, dev, iters=100, mode="sampled"):
+def measured_ceilings(torch, sda, dev, read_bytes=4 << 30, reps=10, mfma_iters=20000):
+    """What this GPU reaches, next to the nominal peaks: a streaming HBM read of a 4 GiB
+    buffer (the library's read probe, 16-byte non-temporal loads), a 1 GiB device copy
+    (torch), and the bf16 matrix-core loop (the library's probe: 8192 waves, four
+    independent 32x32x16 MFMA chains each).  Event-timed on the launch stream."""
+    s = torch.cuda.current_stream()
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(n):
+            fn()
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1000.0 / n
+
+    buf = torch.ones(read_bytes // 2, dtype=torch.bfloat16, device=dev)
+    t_read = timed(lambda: sda.eagle_calib_stream_read(buf), reps)
+    del buf
+    src = torch.ones(1 << 29, dtype=torch.int16, device=dev)
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: dst.copy_(src), reps)
+    del src, dst
+    out = torch.empty(2048 * 256, dtype=torch.float32, device=dev)
+    flops = sda.eagle_calib_mfma_bf16(mfma_iters, out)
+    t_mfma = timed(lambda: sda.eagle_calib_mfma_bf16(mfma_iters, out), 3)
+    torch.cuda.empty_cache()
+    rd = read_bytes / t_read / 1e9
+    cp = 2 * (1 << 30) / t_copy / 1e9
+    mf = flops / t_mfma / 1e12
+    return {"stream_read_gbs": round(rd, 1), "stream_read_frac_of_peak": round(rd / HBM_PEAK_GBS, 4),
+            "copy_gbs_read_plus_write": round(cp, 1),
+            "mfma_bf16_tflops": round(mf, 1), "mfma_bf16_frac_of_peak": round(mf / BF16_MFMA_PEAK_TFLOPS, 4),
+            "how": "4 GiB streaming read (eagle_calib_stream_read), 1 GiB device copy, "
+                   f"{mfma_iters}-step bf16 MFMA loop (eagle_calib_mfma_bf16); mean of {reps} / 3 runs"}
+
+
+def lm_head_back_to_back(torch, sda, dev, x, iters=20):
+    """The C5 LM head alone, launched back to back (nothing in between): W (2.1 GB)
+    streams from HBM on every call, as inside the step."""
+    cfg = synth.CONFIGS["C5"]
+    M, H, V = cfg.B * cfg.N, cfg.H, cfg.V
+    ws = torch.empty(sda.load().eagle_lm_head_workspace(M, H, V), dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        sda.eagle_lm_head_argmax(x["hidden"], x["W"], want_logits=False, workspace=ws)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(iters):
+        sda.eagle_lm_head_argmax(x["hidden"], x["W"], want_logits=False, workspace=ws)
+    e1.record(s)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / iters
+    return dict(roof(us, lm_bytes(M, H, V), 2.0 * M * H * V), calls=iters)
+
+
+def config_step(torch, sda, dev, name, steps=20, warmup=3):
+    """One verification step at another of the five workloads, each call timed with HIP
+    events on the launch stream:
+      C2  static EAGLE-1 tree: attention -> LM head -> greedy acceptance
+      C3  eagle2_rerank -> attention -> LM head -> greedy acceptance
+      C4  eagle2_rerank -> attention -> LM head (fp32 logits written) -> speculative
+          acceptance (sampled siblings) fed the LM head's out_lse and the rerank's
+          draft_lse
+    tokens/s = B*N tree tokens / step time; per kernel the HBM and bf16-MFMA fractions
+    of the nominal peaks (algorithmic bytes and flops)."""
+    cfg = synth.CONFIGS[name]
+    B, N, Hq, Hkv, D, P, H, V = cfg.B, cfg.N, cfg.Hq, cfg.Hkv, cfg.D, cfg.P, cfg.H, cfg.V
+    x = make_inputs(cfg, torch, dev)
+    lib = sda.load()
+    spec = cfg.accept == "spec"
+    ws_attn = torch.empty(max(1, lib.eagle_tree_verify_attn_workspace(B, N, Hq, Hkv, D, P)),
+                          dtype=torch.uint8, device=dev)
+    ws_lm = torch.empty(lib.eagle_lm_head_workspace(B * N, H, V), dtype=torch.uint8, device=dev)
+    attn_out = torch.empty((B, N, Hq, D), dtype=torch.bfloat16, device=dev)
+    attn_lse = torch.empty((B, N, Hq), dtype=torch.float32, device=dev)
+    static = None
+    if cfg.parents is not None:
+        static = {"parents": torch.tensor([cfg.parents] * B, dtype=torch.int32, device=dev),
+                  "tokens": torch.from_numpy(synth.integers((B, N), 0, V, 0, cfg.index, 21)).to(dev)}
+    else:
+        ws_rr = torch.empty(lib.eagle2_rerank_workspace(B, V, cfg.top_k, cfg.depth), dtype=torch.uint8,
+                            device=dev)
+    if spec:
+        ua = torch.from_numpy(synth.uniform_f32((B, N), 0, cfg.index, 8)).to(dev)
+        us = torch.from_numpy(synth.uniform_f32((B, N), 0, cfg.index, 9)).to(dev)
+        ws_sp = torch.empty(lib.eagle_accept_spec_workspace(B, N, V), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    names = (["rerank"] if static is None else []) + ["tree_attn", "lm_head",
+                                                      "accept_spec" if spec else "accept_greedy"]
+
+    def step(ev=None):
+        k = 0
+        if ev:
+            ev[k].record(stream)
+        if static is None:
+            tree = sda.eagle2_rerank(x["draft_logits"], x["root"], cfg.top_k, cfg.depth, N,
+                                     workspace=ws_rr)
+            k += 1
+            if ev:
+                ev[k].record(stream)
+        else:
+            tree = static
+        sda.eagle_tree_verify_attn(x["q"], x["k"], x["v"], tree["parents"], P, D ** -0.5,
+                                   out=attn_out, lse=attn_lse, workspace=ws_attn)
+        k += 1
+        if ev:
+            ev[k].record(stream)
+        res = sda.eagle_lm_head_argmax(x["hidden"], x["W"], want_logits=spec, workspace=ws_lm)
+        k += 1
+        if ev:
+            ev[k].record(stream)
+        if spec:
+            acc = sda.eagle_accept_spec(tree["tokens"], tree["parents"], tree["draft_row"],
+                                        res["logits"].view(B, N, V), x["draft_logits"], ua, us,
+                                        cfg.max_depth, workspace=ws_sp,
+                                        target_lse=res["lse"].view(B, N), draft_lse=tree["draft_lse"])
+        else:
+            acc = sda.eagle_accept_greedy(tree["tokens"], tree["parents"], res["argmax"].view(B, N),
+                                          cfg.max_depth)
+        k += 1
+        if ev:
+            ev[k].record(stream)
+        return tree, acc
+
+    for _ in range(warmup):
+        tree, acc = step()
+    torch.cuda.synchronize()
+    parents_np = tree["parents"].cpu().numpy()
+    alen = acc[0].cpu().numpy()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    ms = evs[0][0].elapsed_time(evs[-1][-1]) / steps
+    per = {n: 1000.0 * sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps
+           for j, n in enumerate(names)}
+    kern = {"tree_attn": roof(per["tree_attn"], attn_bytes(cfg), attn_flops(parents_np, cfg)),
+            "lm_head": roof(per["lm_head"], lm_bytes(B * N, H, V, logits=spec), 2.0 * B * N * H * V)}
+    if static is None:
+        kern["rerank"] = roof(per["rerank"], B * cfg.rows * V * 4)
+    del x
+    torch.cuda.empty_cache()
+    return {"workload": (f"{name}: B={B} Hq={Hq} Hkv={Hkv} D={D} P={P} N={N} H={H} V={V}, "
+                         + ("static EAGLE-1 tree" if static is not None else
+                            f"EAGLE-2 tree (top-k {cfg.top_k}, depth {cfg.depth})")
+                         + (", speculative sampling" if spec else ", greedy")),
+            "tokens_per_s": round(B * N / (ms / 1000.0), 1), "ms_per_step": round(ms, 4),
+            "breakdown_us": {k: round(v, 2) for k, v in per.items()}, "kernels": kern,
+            "accept_len": [int(a) for a in alen]}
+
+
+def spec_latency(torch, sda, dev, iters=100, mode="sampled", with_lse=True):
     """eagle_accept_spec at the Llama-3-8B-shaped speculative-sampling workload (C4): a
     60-node tree from eagle2_rerank, target logits N(0,1) over 128256 tokens.  mode
     "sampled" runs the pages' rule with the draft distribution (10 residual rounds at
-    the root), "point_mass" the rule for deterministic top-k siblings."""
+    the root), "point_mass" the rule for deterministic top-k siblings.  with_lse hands
+    the rows' normalisers over (as the LM head and the rerank produce them); without,
+    the kernel forms them itself."""
     cfg = synth.CONFIGS["C4"]
     dl = torch.from_numpy(synth.normal_f32((1, cfg.rows, cfg.V), cfg.draft_std, 0, cfg.index, 6)).to(dev)
     root = torch.from_numpy(synth.integers((1,), 0, cfg.V, 0, cfg.index, 7)).to(dev)
@@ -216,16 +418,23 @@ def spec_latency(torch, sda, dev, iters=100, mode="sampled"):
     us = torch.from_numpy(synth.uniform_f32((1, cfg.N), 0, cfg.index, 9)).to(dev)
     ws = torch.empty(sda.load().eagle_accept_spec_workspace(1, cfg.N, cfg.V), dtype=torch.uint8,
                      device=dev)
-    for _ in range(3):
+    lse = {}
+    if with_lse:
+        lse = {"target_lse": torch.logsumexp(tl.double(), dim=-1).float().contiguous(),
+               "draft_lse": tree["draft_lse"]}
+
+    def call():
         sda.eagle_accept_spec(tree["tokens"], tree["parents"], tree["draft_row"], tl, dl, ua, us,
-                              cfg.max_depth, workspace=ws, mode=mode)
+                              cfg.max_depth, workspace=ws, mode=mode, **lse)
+
+    for _ in range(3):
+        call()
     torch.cuda.synchronize()
     s = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(s)
     for _ in range(iters):
-        sda.eagle_accept_spec(tree["tokens"], tree["parents"], tree["draft_row"], tl, dl, ua, us,
-                              cfg.max_depth, workspace=ws, mode=mode)
+        call()
     e1.record(s)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1000.0 / iters
@@ -613,8 +822,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-spec", action="store_true",
-                    help="only the C5 step: skip the spec latency, KV commit, ragged, paged and "
-                         "draft-expansion measurements")
+                    help="only the C5 step: skip the other workloads' steps, the measured "
+                         "ceilings, the back-to-back LM head, the spec latency, KV commit, "
+                         "ragged, paged and draft-expansion measurements")
     ap.add_argument("--only-draft", action="store_true",
                     help="only the C5-shaped draft expansion (eagle_draft_expand)")
     ap.add_argument("--copy-calib", action="store_true",
@@ -700,22 +910,24 @@ def main(argv=None):
     value = B * N / (ms_per_step / 1000.0)
 
     # rooflines
-    lm_bytes = V * H * 2 + B * N * H * 2 + B * N * 16
-    lm_gbs = lm_bytes / (per["lm_head"] * 1e-6) / 1e9
-    attn_bytes = 2 * B * Hkv * (P + N) * D * 2 + 2 * B * N * Hq * D * 2 + B * N * Hq * 4
+    lm_b = lm_bytes(B * N, H, V)
+    lm_gbs = lm_b / (per["lm_head"] * 1e-6) / 1e9
+    attn_b = attn_bytes(cfg)
     a_flops = attn_flops(parents_np, cfg)
     attn_tflops = a_flops / (per["tree_attn"] * 1e-6) / 1e12
-    attn_gbs = attn_bytes / (per["tree_attn"] * 1e-6) / 1e9
+    attn_gbs = attn_b / (per["tree_attn"] * 1e-6) / 1e9
     rr_bytes = B * cfg.rows * V * 4
     dominant = max(("lm_head", "tree_attn"), key=lambda n: per[n])
     roof_lm = {"kernel": "lm_head (eagle_lm_head_argmax)", "bound": "hbm",
                "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                "frac": round(lm_gbs / HBM_PEAK_GBS, 4), "traffic": _traffic("lm_head"),
-               "algorithmic_bytes": lm_bytes, "avg_us": round(per["lm_head"], 2)}
+               "algorithmic_bytes": lm_b, "avg_us": round(per["lm_head"], 2),
+               "mfma_frac": round(2.0 * B * N * H * V / (per["lm_head"] * 1e-6) / 1e12
+                                  / BF16_MFMA_PEAK_TFLOPS, 4)}
     roof_attn = {"kernel": "tree_attn (eagle_tree_verify_attn)", "bound": "mfma",
                  "achieved": round(attn_tflops, 1), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                  "frac": round(attn_tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": _traffic("tree_attn"),
-                 "algorithmic_flops": a_flops, "algorithmic_bytes": attn_bytes,
+                 "algorithmic_flops": a_flops, "algorithmic_bytes": attn_b,
                  "hbm_gbs": round(attn_gbs, 1), "hbm_frac": round(attn_gbs / HBM_PEAK_GBS, 4),
                  "avg_us": round(per["tree_attn"], 2)}
     out = {
@@ -735,7 +947,17 @@ def main(argv=None):
         "rerank_hbm_gbs": round(rr_bytes / (per["rerank"] * 1e-6) / 1e9, 1),
     }
     if not args.no_spec:
+        out["lm_head_back_to_back_C5"] = lm_head_back_to_back(torch, sda, dev, x)
+        del x
+        torch.cuda.empty_cache()
+        out["configs"] = {}
+        for name in ("C2", "C3", "C4"):
+            print(f"# {name} step", file=sys.stderr, flush=True)
+            out["configs"][name] = config_step(torch, sda, dev, name)
+        out["measured_ceilings"] = measured_ceilings(torch, sda, dev)
+        x = make_inputs(cfg, torch, dev)
         out["accept_spec_us_C4"] = round(spec_latency(torch, sda, dev), 2)
+        out["accept_spec_no_lse_us_C4"] = round(spec_latency(torch, sda, dev, with_lse=False), 2)
         out["accept_spec_point_mass_us_C4"] = round(spec_latency(torch, sda, dev, mode="point_mass"), 2)
         out["kv_commit_80_layers"] = kv_commit_latency(torch, sda, dev, tree["parents"])
         out["ragged_C5"] = ragged_step(torch, sda, dev, x)
@@ -744,6 +966,8 @@ def main(argv=None):
     if not args.no_cpu_baseline:
         print("# timing the CPU oracle baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg)
+        print("# timing the CPU oracle baseline on one thread", file=sys.stderr, flush=True)
+        out["cpu_baseline"]["single_thread"] = cpu_baseline_single_thread(cfg)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out))

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define EAGLE_ABI_VERSION 2
+#define EAGLE_ABI_VERSION 3
 #define EAGLE_MAX_TREE 64   /* nodes per sequence, root included */
 #define EAGLE_MAX_TOPK 64
 
@@ -71,6 +71,16 @@ typedef enum {
   EAGLE_ERR_HIP = 6            /* a HIP runtime call failed; see eagle_last_error() */
 } eagle_status_t;
 
+/* Element type of the attention and LM-head operands.  EAGLE_BF16 is the one this
+ * library implements; EAGLE_F32 names fp32 operands (an fp32 model such as the
+ * tiny CPU-scale configuration) and is answered with EAGLE_ERR_UNSUPPORTED: such
+ * tensors are rounded to bf16 by the caller.  Any other value is
+ * EAGLE_ERR_INVALID_ARG. */
+typedef enum {
+  EAGLE_BF16 = 0,
+  EAGLE_F32 = 1
+} eagle_dtype_t;
+
 /* Sibling model of eagle_accept_spec (see there). */
 typedef enum {
   EAGLE_SPEC_SAMPLED = 0,
@@ -81,7 +91,7 @@ typedef enum {
 int eagle_abi_version(void);
 
 /* Static text for a status value (never NULL). */
-const char* eagle_status_string(int status);
+const char* eagle_status_string(eagle_status_t status);
 
 /* Detail text of the calling thread's last error (empty string if none). */
 const char* eagle_last_error(void);
@@ -111,6 +121,9 @@ eagle_status_t eagle_check_tree(const int32_t* parents_host, int32_t B, int32_t 
  *   out  bf16 [B][N][Hq][D] (written)
  *   lse  fp32 [B][N][Hq] (written; may be NULL)
  *   scale > 0 (usually 1/sqrt(D)); D in {64, 128}; Hq % Hkv == 0; N <= 64; P >= 0.
+ *   dtype  EAGLE_BF16 (the type of q, k, v and out)
+ *   kv_cap the row capacity of k and v per (sequence, KV head), so that a cache
+ *          allocated once for the longest context can be passed as it is
  * Workspace: eagle_tree_verify_attn_workspace(B, N, Hq, Hkv, D, P) bytes (it holds
  * split-KV partial results; 0 means none is needed and workspace may be NULL).
  */
@@ -119,8 +132,9 @@ size_t eagle_tree_verify_attn_workspace(int32_t B, int32_t N, int32_t Hq, int32_
 eagle_status_t eagle_tree_verify_attn(const void* q, const void* k, const void* v,
                                       const int32_t* parents, int32_t B, int32_t N, int32_t Hq,
                                       int32_t Hkv, int32_t D, int32_t P, int32_t kv_cap,
-                                      float scale, void* out, float* lse, void* workspace,
-                                      size_t workspace_bytes, hipStream_t stream);
+                                      float scale, eagle_dtype_t dtype, void* out, float* lse,
+                                      void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
 
 /*
  * Frozen LM head with fused row statistics.  [P2] paragraphs on the
@@ -134,13 +148,16 @@ eagle_status_t eagle_tree_verify_attn(const void* q, const void* k, const void* 
  *     out_logits    = the fp32 logits [M][V] (may be NULL; needed by eagle_accept_spec)
  *
  *   hidden bf16 [M][H], weight bf16 [V][H] (nn.Linear layout).  H % 64 == 0, V >= 2.
+ *   dtype EAGLE_BF16 (the type of hidden and weight)
+ *   out_max, out_lse, out_second fp32 [M]; out_argmax int32 [M]
  * Workspace: eagle_lm_head_workspace(M, H, V) bytes (never 0).
  */
 size_t eagle_lm_head_workspace(int32_t M, int32_t H, int32_t V);
 eagle_status_t eagle_lm_head_argmax(const void* hidden, const void* weight, int32_t M, int32_t H,
-                                    int32_t V, float* out_max, int32_t* out_argmax,
-                                    float* out_lse, float* out_second, float* out_logits,
-                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+                                    int32_t V, eagle_dtype_t dtype, float* out_max,
+                                    int32_t* out_argmax, float* out_lse, float* out_second,
+                                    float* out_logits, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
 
 /*
  * Greedy acceptance.  [P1] greedy decoding paragraph and the figure paragraph
@@ -167,11 +184,12 @@ eagle_status_t eagle_accept_greedy(const int32_t* tokens, const int32_t* parents
  * the target, p the draft; accept a draft token t when a uniform is below
  * min(1, q(t)/p(t)), otherwise correct the target and retry), [P2] multi-round
  * speculative sampling section (recursive form over the token tree, keeping the
- * target distribution), [P3] section 2, speculative decoding basics.  At the
- * current node v (starting at the root): q = softmax(target_logits[b][v]),
- * p = softmax(draft_logits[b][draft_row[b][v]]); the children of v are tried in
- * ascending node index with u_accept[b][child]: accept when
- * u < min(1, q'(t)/p(t)) where q' is the corrected target (q' = q for the first
+ * target distribution; the draft records each sampled token's probability as it
+ * drafts), [P3] section 2, speculative decoding basics.  At the current node v
+ * (starting at the root): q = exp(target_logits[b][v] - target_lse[b][v]),
+ * p = exp(draft_logits[b][r] - draft_lse[b][r]) with r = draft_row[b][v]; the
+ * children of v are tried in ascending node index with u_accept[b][child]: accept
+ * when u < min(1, q'(t)/p(t)) where q' is the corrected target (q' = q for the first
  * child); a rejection replaces q' by the normalised positive part of (q' - p).  An
  * accepted child becomes the current node.  When every child is rejected, one
  * token is drawn from q' with u_sample[b][v]; at a node with no children, with
@@ -186,24 +204,34 @@ eagle_status_t eagle_accept_greedy(const int32_t* tokens, const int32_t* parents
  *                          distribution behind child t is the point mass at t, so t is
  *                          accepted when u < q'(t), and a rejection sets q'(t) to zero
  *                          and renormalises (exact for any fixed set of siblings).
- *                          draft_logits are not read in this mode; a node still needs
- *                          a valid draft_row to have its children tried.
+ *                          draft_logits and draft_lse are not read in this mode; a node
+ *                          still needs a valid draft_row to have its children tried.
  * Any other mode value is EAGLE_ERR_INVALID_ARG.
  *
- *   tokens, parents, draft_row int32 [B][N] (draft_row[b][i] in [-1, draft_rows))
- *   target_logits fp32 [B][N][V]; draft_logits fp32 [B][draft_rows][V]
+ *   tokens, parents int32 [B][N]; max_depth >= 0
+ *   target_logits fp32 [B][N][V]; target_lse fp32 [B][N] (log-sum-exp of each target
+ *     row, as eagle_lm_head_argmax writes it to out_lse) or NULL
+ *   draft_logits fp32 [B][draft_rows][V]; draft_lse fp32 [B][draft_rows] (as
+ *     eagle2_rerank writes it) or NULL
+ *   draft_row int32 [B][N] (in [-1, draft_rows)); draft_rows >= 1
  *   u_accept, u_sample fp32 [B][N] in [0, 1)
- *   outputs as eagle_accept_greedy.
+ *   outputs as eagle_accept_greedy; on a spin timeout inside the kernel (a GPU that
+ *     does not run the sequence's workgroups together) every output of that
+ *     sequence is -1, accept_len included.
+ * When a normaliser is NULL the kernel forms it from the logits itself (one more
+ * cross-workgroup exchange per visited node); given ones are used as they are.
  * Workspace: eagle_accept_spec_workspace(B, N, V) bytes.
  */
 size_t eagle_accept_spec_workspace(int32_t B, int32_t N, int32_t V);
-eagle_status_t eagle_accept_spec(const int32_t* tokens, const int32_t* parents,
-                                 const int32_t* draft_row, const float* target_logits,
-                                 const float* draft_logits, int32_t draft_rows,
-                                 const float* u_accept, const float* u_sample, int32_t B,
-                                 int32_t N, int32_t V, int32_t max_depth, int32_t mode,
-                                 int32_t* accept_len, int32_t* accept_path, int32_t* out_tokens,
-                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+eagle_status_t eagle_accept_spec(const int32_t* tokens, const int32_t* parents, int32_t B,
+                                 int32_t N, int32_t V, int32_t max_depth,
+                                 const float* target_logits, const float* target_lse,
+                                 const float* draft_logits, const float* draft_lse,
+                                 const int32_t* draft_row, int32_t draft_rows,
+                                 const float* u_accept, const float* u_sample,
+                                 eagle_spec_mode_t mode, int32_t* accept_len,
+                                 int32_t* accept_path, int32_t* out_tokens, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Ragged batches.  [P3] section 4 (batch sizes above one are the method's weak spot)
@@ -225,23 +253,24 @@ eagle_status_t eagle_tree_verify_attn_ragged(const void* q, const void* k, const
                                              const int32_t* parents, const int32_t* prefix_len,
                                              const int32_t* tree_len, int32_t B, int32_t N,
                                              int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
-                                             int32_t kv_cap, float scale, void* out, float* lse,
-                                             void* workspace, size_t workspace_bytes,
-                                             hipStream_t stream);
+                                             int32_t kv_cap, float scale, eagle_dtype_t dtype,
+                                             void* out, float* lse, void* workspace,
+                                             size_t workspace_bytes, hipStream_t stream);
 eagle_status_t eagle_accept_greedy_ragged(const int32_t* tokens, const int32_t* parents,
                                           const int32_t* target_argmax, const int32_t* tree_len,
                                           int32_t B, int32_t N, int32_t max_depth,
                                           int32_t* accept_len, int32_t* accept_path,
                                           int32_t* out_tokens, hipStream_t stream);
 eagle_status_t eagle_accept_spec_ragged(const int32_t* tokens, const int32_t* parents,
-                                        const int32_t* draft_row, const float* target_logits,
-                                        const float* draft_logits, int32_t draft_rows,
-                                        const float* u_accept, const float* u_sample,
                                         const int32_t* tree_len, int32_t B, int32_t N, int32_t V,
-                                        int32_t max_depth, int32_t mode, int32_t* accept_len,
-                                        int32_t* accept_path, int32_t* out_tokens,
-                                        void* workspace, size_t workspace_bytes,
-                                        hipStream_t stream);
+                                        int32_t max_depth, const float* target_logits,
+                                        const float* target_lse, const float* draft_logits,
+                                        const float* draft_lse, const int32_t* draft_row,
+                                        int32_t draft_rows, const float* u_accept,
+                                        const float* u_sample, eagle_spec_mode_t mode,
+                                        int32_t* accept_len, int32_t* accept_path,
+                                        int32_t* out_tokens, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Paged KV cache.  [P3] section 4 (limitations: dynamic draft trees strain paged
@@ -265,8 +294,9 @@ eagle_status_t eagle_tree_verify_attn_paged(const void* q, const void* k_pool, c
                                             int32_t B, int32_t N, int32_t Hq, int32_t Hkv,
                                             int32_t D, int32_t P, int32_t page_size,
                                             int32_t max_pages, int32_t num_blocks, float scale,
-                                            void* out, float* lse, void* workspace,
-                                            size_t workspace_bytes, hipStream_t stream);
+                                            eagle_dtype_t dtype, void* out, float* lse,
+                                            void* workspace, size_t workspace_bytes,
+                                            hipStream_t stream);
 
 /*
  * EAGLE-2 dynamic draft tree.  [P3] section 2 (dynamic draft tree: confidence
@@ -384,6 +414,27 @@ eagle_status_t eagle_kv_commit(void* k_cache, void* v_cache, const int32_t* acce
                                const int32_t* accept_path, int32_t L, int32_t B, int32_t Hkv,
                                int32_t D, int32_t P, int32_t kv_cap, int32_t path_len,
                                hipStream_t stream);
+
+/*
+ * Measurement probes (not part of the verification step).  They measure, on the GPU
+ * they run on, the two ceilings the kernels above are judged against: the HBM read
+ * bandwidth a streaming kernel reaches and the rate the bf16 matrix cores sustain.
+ *
+ * eagle_calib_stream_read: reads `bytes` (a positive multiple of 16) from the device
+ *   buffer `src` (16-byte aligned) once, in 16-byte non-temporal loads spread over
+ *   4096 workgroups; `sink` is a device buffer of at least 4096 uint32 that is
+ *   written only in a case that cannot occur (it keeps the loads from being dropped).
+ * eagle_calib_mfma_bf16: 2048 workgroups of four waves, each wave running four
+ *   independent chains of `iters` v_mfma_f32_32x32x16_bf16 on register operands;
+ *   `out` (device, at least 2048 * 256 floats) receives one value per lane.
+ *   eagle_calib_mfma_bf16_flops(iters) is the number of flops one call performs
+ *   (0 for iters < 1).
+ */
+eagle_status_t eagle_calib_stream_read(const void* src, size_t bytes, void* sink,
+                                       hipStream_t stream);
+double eagle_calib_mfma_bf16_flops(int32_t iters);
+eagle_status_t eagle_calib_mfma_bf16(int32_t iters, float* out, size_t out_floats,
+                                     hipStream_t stream);
 
 #ifdef __cplusplus
 }

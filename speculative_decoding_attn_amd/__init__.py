@@ -22,6 +22,7 @@ _lib = None
 
 EAGLE_OK = 0
 SPEC_MODES = {"sampled": 0, "point_mass": 1}   # eagle_spec_mode_t
+EAGLE_BF16 = 0                                 # eagle_dtype_t of bf16 operands
 STATUS_NAMES = {0: "EAGLE_OK", 1: "EAGLE_ERR_NULL", 2: "EAGLE_ERR_INVALID_ARG",
                 3: "EAGLE_ERR_UNSUPPORTED", 4: "EAGLE_ERR_WORKSPACE", 5: "EAGLE_ERR_TREE",
                 6: "EAGLE_ERR_HIP"}
@@ -41,29 +42,32 @@ _SIGNATURES = {
     "eagle_last_error": ([], ctypes.c_char_p),
     "eagle_check_tree": ([_vp, _i32, _i32], ctypes.c_int),
     "eagle_tree_verify_attn_workspace": ([_i32] * 6, _sz),
-    "eagle_tree_verify_attn": ([_vp, _vp, _vp, _vp] + [_i32] * 7 + [_f32, _vp, _vp, _vp, _sz, _vp],
-                               ctypes.c_int),
+    "eagle_tree_verify_attn": ([_vp, _vp, _vp, _vp] + [_i32] * 7 + [_f32, _i32, _vp, _vp, _vp, _sz,
+                                                                    _vp], ctypes.c_int),
     "eagle_lm_head_workspace": ([_i32] * 3, _sz),
-    "eagle_lm_head_argmax": ([_vp, _vp, _i32, _i32, _i32] + [_vp] * 6 + [_sz, _vp], ctypes.c_int),
+    "eagle_lm_head_argmax": ([_vp, _vp, _i32, _i32, _i32, _i32] + [_vp] * 6 + [_sz, _vp], ctypes.c_int),
     "eagle_accept_greedy": ([_vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
     "eagle_kv_commit": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp],
                         ctypes.c_int),
     "eagle_accept_spec_workspace": ([_i32] * 3, _sz),
-    "eagle_accept_spec": ([_vp] * 5 + [_i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32] + [_vp] * 4
-                          + [_sz, _vp], ctypes.c_int),
-    "eagle_tree_verify_attn_ragged": ([_vp] * 6 + [_i32] * 7 + [_f32, _vp, _vp, _vp, _sz, _vp],
+    "eagle_accept_spec": ([_vp, _vp, _i32, _i32, _i32, _i32] + [_vp] * 5 + [_i32, _vp, _vp, _i32]
+                          + [_vp] * 4 + [_sz, _vp], ctypes.c_int),
+    "eagle_tree_verify_attn_ragged": ([_vp] * 6 + [_i32] * 7 + [_f32, _i32, _vp, _vp, _vp, _sz, _vp],
                                       ctypes.c_int),
     "eagle_tree_verify_attn_paged_workspace": ([_i32] * 7, _sz),
-    "eagle_tree_verify_attn_paged": ([_vp] * 5 + [_i32] * 9 + [_f32, _vp, _vp, _vp, _sz, _vp],
+    "eagle_tree_verify_attn_paged": ([_vp] * 5 + [_i32] * 9 + [_f32, _i32, _vp, _vp, _vp, _sz, _vp],
                                      ctypes.c_int),
     "eagle_accept_greedy_ragged": ([_vp] * 4 + [_i32, _i32, _i32] + [_vp] * 4, ctypes.c_int),
-    "eagle_accept_spec_ragged": ([_vp] * 5 + [_i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32]
-                                 + [_vp] * 4 + [_sz, _vp], ctypes.c_int),
+    "eagle_accept_spec_ragged": ([_vp, _vp, _vp, _i32, _i32, _i32, _i32] + [_vp] * 5
+                                 + [_i32, _vp, _vp, _i32] + [_vp] * 4 + [_sz, _vp], ctypes.c_int),
     "eagle2_rerank_workspace": ([_i32] * 4, _sz),
     "eagle2_rerank": ([_vp, _vp] + [_i32] * 5 + [_vp] * 7 + [_sz, _vp], ctypes.c_int),
     "eagle_draft_expand_workspace": ([_i32] * 11, _sz),
     "eagle_draft_expand": ([_vp] * 5 + [_i32] * 12 + [_f32, _f32] + [_vp] * 11 + [_sz, _vp],
                            ctypes.c_int),
+    "eagle_calib_stream_read": ([_vp, _sz, _vp, _vp], ctypes.c_int),
+    "eagle_calib_mfma_bf16_flops": ([_i32], ctypes.c_double),
+    "eagle_calib_mfma_bf16": ([_i32, _vp, _sz, _vp], ctypes.c_int),
 }
 
 
@@ -165,8 +169,8 @@ def eagle_tree_verify_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pa
     wsb = 0 if workspace is None else workspace.numel()
     if prefix_len is None and tree_len is None:
         st = lib.eagle_tree_verify_attn(q.data_ptr(), k.data_ptr(), v.data_ptr(), parents.data_ptr(),
-                                        B, N, Hq, Hkv, D, P, kv_cap, float(scale), out.data_ptr(),
-                                        _ptr(lse), _ptr(workspace), wsb, _stream())
+                                        B, N, Hq, Hkv, D, P, kv_cap, float(scale), EAGLE_BF16,
+                                        out.data_ptr(), _ptr(lse), _ptr(workspace), wsb, _stream())
         _check(st, "eagle_tree_verify_attn")
         return out, lse
     for t, n in ((prefix_len, "prefix_len"), (tree_len, "tree_len")):
@@ -176,7 +180,7 @@ def eagle_tree_verify_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, pa
                 raise ValueError(f"{n} must be [B]")
     st = lib.eagle_tree_verify_attn_ragged(q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                            parents.data_ptr(), _ptr(prefix_len), _ptr(tree_len),
-                                           B, N, Hq, Hkv, D, P, kv_cap, float(scale),
+                                           B, N, Hq, Hkv, D, P, kv_cap, float(scale), EAGLE_BF16,
                                            out.data_ptr(), _ptr(lse), _ptr(workspace), wsb,
                                            _stream())
     _check(st, "eagle_tree_verify_attn_ragged")
@@ -212,7 +216,7 @@ def eagle_tree_verify_attn_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: 
     st = lib.eagle_tree_verify_attn_paged(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
                                           block_table.data_ptr(), parents.data_ptr(), B, N, Hq, Hkv,
                                           D, P, ps, block_table.shape[1], nblk, float(scale),
-                                          out.data_ptr(), _ptr(lse), _ptr(workspace),
+                                          EAGLE_BF16, out.data_ptr(), _ptr(lse), _ptr(workspace),
                                           0 if workspace is None else workspace.numel(), _stream())
     _check(st, "eagle_tree_verify_attn_paged")
     return out, lse
@@ -244,7 +248,7 @@ def eagle_lm_head_argmax(hidden: torch.Tensor, weight: torch.Tensor, want_logits
            "logits": torch.empty((M, V), dtype=torch.float32, **f) if want_logits else None}
     if workspace is None:
         workspace = _workspace(lib.eagle_lm_head_workspace(M, H, V), dev)
-    st = lib.eagle_lm_head_argmax(hidden.data_ptr(), weight.data_ptr(), M, H, V,
+    st = lib.eagle_lm_head_argmax(hidden.data_ptr(), weight.data_ptr(), M, H, V, EAGLE_BF16,
                                   res["max"].data_ptr(), res["argmax"].data_ptr(),
                                   res["lse"].data_ptr(), _ptr(res["second"]), _ptr(res["logits"]),
                                   workspace.data_ptr(), workspace.numel(), _stream())
@@ -315,11 +319,15 @@ def eagle_accept_spec(tokens: torch.Tensor, parents: torch.Tensor, draft_row: to
                       target_logits: torch.Tensor, draft_logits: torch.Tensor,
                       u_accept: torch.Tensor, u_sample: torch.Tensor, max_depth: int,
                       workspace: Optional[torch.Tensor] = None,
-                      tree_len: Optional[torch.Tensor] = None, mode: str = "sampled"):
+                      tree_len: Optional[torch.Tensor] = None, mode: str = "sampled",
+                      target_lse: Optional[torch.Tensor] = None,
+                      draft_lse: Optional[torch.Tensor] = None):
     """tokens, parents, draft_row [B][N] int32; target_logits [B][N][V] fp32;
-    draft_logits [B][R][V] fp32; u_accept, u_sample [B][N] fp32.  With tree_len
-    (int32 [B]) eagle_accept_spec_ragged is called.  mode: "sampled" (siblings drawn
-    from the draft distribution) or "point_mass" (deterministic siblings)."""
+    draft_logits [B][R][V] fp32; u_accept, u_sample [B][N] fp32; optional normalisers
+    target_lse [B][N] and draft_lse [B][R] fp32 (the LM head's out_lse and the rerank's
+    draft_lse).  With tree_len (int32 [B]) eagle_accept_spec_ragged is called.  mode:
+    "sampled" (siblings drawn from the draft distribution) or "point_mass"
+    (deterministic siblings)."""
     lib = load()
     if mode not in SPEC_MODES:
         raise ValueError(f"mode must be one of {sorted(SPEC_MODES)}")
@@ -335,38 +343,40 @@ def eagle_accept_spec(tokens: torch.Tensor, parents: torch.Tensor, draft_row: to
     R = draft_logits.shape[1]
     if tuple(target_logits.shape) != (B, N, V) or tuple(draft_logits.shape) != (B, R, V):
         raise ValueError("inconsistent logits shapes")
+    for t, n, shape in ((target_lse, "target_lse", (B, N)), (draft_lse, "draft_lse", (B, R))):
+        if t is not None:
+            _need(t, n, torch.float32, dev)
+            if tuple(t.shape) != shape:
+                raise ValueError(f"{n} must be {list(shape)}")
     alen = torch.empty(B, dtype=torch.int32, device=dev)
     path = torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev)
     out = torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev)
     if workspace is None:
         workspace = _workspace(lib.eagle_accept_spec_workspace(B, N, V), dev)
+    tail = (_ptr(target_logits), _ptr(target_lse), _ptr(draft_logits), _ptr(draft_lse),
+            draft_row.data_ptr(), R, u_accept.data_ptr(), u_sample.data_ptr(), m,
+            alen.data_ptr(), path.data_ptr(), out.data_ptr(), workspace.data_ptr(),
+            workspace.numel(), _stream())
     if tree_len is None:
-        st = lib.eagle_accept_spec(tokens.data_ptr(), parents.data_ptr(), draft_row.data_ptr(),
-                                   target_logits.data_ptr(), draft_logits.data_ptr(), R,
-                                   u_accept.data_ptr(), u_sample.data_ptr(), B, N, V, max_depth, m,
-                                   alen.data_ptr(), path.data_ptr(), out.data_ptr(),
-                                   workspace.data_ptr(), workspace.numel(), _stream())
+        st = lib.eagle_accept_spec(tokens.data_ptr(), parents.data_ptr(), B, N, V, max_depth, *tail)
         _check(st, "eagle_accept_spec")
         return alen, path, out
     _need(tree_len, "tree_len", torch.int32, dev)
     if tuple(tree_len.shape) != (B,):
         raise ValueError("tree_len must be [B]")
-    st = lib.eagle_accept_spec_ragged(tokens.data_ptr(), parents.data_ptr(), draft_row.data_ptr(),
-                                      target_logits.data_ptr(), draft_logits.data_ptr(), R,
-                                      u_accept.data_ptr(), u_sample.data_ptr(), tree_len.data_ptr(),
-                                      B, N, V, max_depth, m, alen.data_ptr(), path.data_ptr(),
-                                      out.data_ptr(), workspace.data_ptr(), workspace.numel(),
-                                      _stream())
+    st = lib.eagle_accept_spec_ragged(tokens.data_ptr(), parents.data_ptr(), tree_len.data_ptr(),
+                                      B, N, V, max_depth, *tail)
     _check(st, "eagle_accept_spec_ragged")
     return alen, path, out
 
 
 def eagle_accept_spec_ragged(tokens, parents, draft_row, target_logits, draft_logits, u_accept,
                              u_sample, tree_len, max_depth: int, workspace=None,
-                             mode: str = "sampled"):
+                             mode: str = "sampled", target_lse=None, draft_lse=None):
     """eagle_accept_spec with per-sequence tree sizes tree_len (int32 [B])."""
     return eagle_accept_spec(tokens, parents, draft_row, target_logits, draft_logits, u_accept,
-                             u_sample, max_depth, workspace=workspace, tree_len=tree_len, mode=mode)
+                             u_sample, max_depth, workspace=workspace, tree_len=tree_len, mode=mode,
+                             target_lse=target_lse, draft_lse=draft_lse)
 
 
 def eagle2_rerank(draft_logits: torch.Tensor, root_token: torch.Tensor, top_k: int, depth: int,
@@ -459,3 +469,24 @@ def eagle_draft_expand(head: dict, f0: torch.Tensor, root_token: torch.Tensor, k
                                 workspace.numel(), _stream())
     _check(st, "eagle_draft_expand")
     return res
+
+
+def eagle_calib_stream_read(src: torch.Tensor) -> None:
+    """Read the device tensor `src` once (streaming-read bandwidth probe)."""
+    lib = load()
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous device tensor")
+    sink = torch.empty(4096, dtype=torch.int32, device=src.device)
+    nbytes = src.numel() * src.element_size() // 16 * 16
+    _check(lib.eagle_calib_stream_read(src.data_ptr(), nbytes, sink.data_ptr(), _stream()),
+           "eagle_calib_stream_read")
+
+
+def eagle_calib_mfma_bf16(iters: int, out: Optional[torch.Tensor] = None) -> float:
+    """Run the bf16 matrix-core loop once; returns its flop count."""
+    lib = load()
+    if out is None:
+        out = torch.empty(2048 * 256, dtype=torch.float32, device="cuda")
+    _check(lib.eagle_calib_mfma_bf16(iters, out.data_ptr(), out.numel(), _stream()),
+           "eagle_calib_mfma_bf16")
+    return lib.eagle_calib_mfma_bf16_flops(iters)

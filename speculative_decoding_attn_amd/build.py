@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libeagle_mi355.so")
 SOURCES = ["api.hip", "tree_attn.hip", "lm_head.hip", "accept.hip", "rerank.hip", "kv_commit.hip",
-           "draft.hip"]
+           "draft.hip", "calib.hip"]
 ARCH = "gfx950"
 
 

@@ -100,24 +100,29 @@ accept_greedy_kernel(const int32_t* __restrict__ tokens, const int32_t* __restri
 // words (each 64-bit word carries the exchange's generation next to 32 bits of a
 // partial), so a reader needs no separate arrival counter or ordering wait: it polls
 // the words themselves.  Every spin is bounded: on timeout the sequence's accept_len
-// is set to -1 and all its workgroups leave.
+// is set to -1 and all its workgroups leave; the last workgroup of a sequence to
+// leave writes its outputs (an exit counter in the workspace).
 // ---------------------------------------------------------------------------
 constexpr int kSpecThreads = 256;
 constexpr int kSpecRegs = 16;   // entries per thread kept in registers (chunks up to 4096)
 constexpr unsigned kSpinLimit = 1u << 24;
 
 struct SpecWs {
-  unsigned* counters;   // [B] (unused; kept for the layout)
+  unsigned* exits;      // [B] workgroups of the sequence that have finished (+ abort bit)
   int* abort_flags;     // [B]
   unsigned long long* slots;   // [B][2][chunks][8] tagged halves of the exchanged partials
   double* qbuf;         // [B][V] fp64 q of the current node
   double* pbuf;         // [B][V] fp64 p of the current node
 };
 
+// exits[b]: low 16 bits count the workgroups of sequence b that are done, bit 16 is set
+// by any workgroup that gave up on a spin
+constexpr unsigned kExitAbortBit = 1u << 16;
+
 __device__ __forceinline__ SpecWs spec_ws(void* ws, int B, int chunks, int V) {
   SpecWs w;
   char* base = (char*)ws;
-  w.counters = (unsigned*)base;
+  w.exits = (unsigned*)base;
   w.abort_flags = (int*)(base + 256 * ((B * 4 + 255) / 256));
   size_t off = 2 * 256 * (size_t)((B * 4 + 255) / 256);
   w.slots = (unsigned long long*)(base + off);
@@ -129,16 +134,18 @@ __device__ __forceinline__ SpecWs spec_ws(void* ws, int B, int chunks, int V) {
   return w;
 }
 
-__global__ void spec_init_kernel(void* ws, int B, int chunks, int V) {
+// Clears the exit counters, abort flags and exchange tags of every sequence; a grid of
+// enough workgroups that each thread clears a few words.
+__global__ void __launch_bounds__(256) spec_init_kernel(void* ws, int B, int chunks, int V) {
   SpecWs w = spec_ws(ws, B, chunks, V);
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < B; i += gridDim.x * blockDim.x) {
-    w.counters[i] = 0u;
+  const int stride = gridDim.x * blockDim.x;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < B; i += stride) {
+    w.exits[i] = 0u;
     w.abort_flags[i] = 0;
   }
   // generation tags start at 0: no word left by an earlier call can look current
   const int nslot = B * 2 * chunks * 8;
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < nslot; i += gridDim.x * blockDim.x)
-    w.slots[i] = 0ull;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < nslot; i += stride) w.slots[i] = 0ull;
 }
 
 // Workgroup-wide sum of a double (all threads get the result).
@@ -295,94 +302,123 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
       kid_u[tid] = u_accept[(size_t)b * N + kid];
     }
 
-    // ---- q and p of node v: chunk max / exp-sum, exchanged, then fp64 values.  A
-    // thread's entries are x0 + tid + i * kSpecThreads; when the chunk fits, they are
-    // loaded once into registers (same order of operations either way).
-    double mq = -INFINITY, mp = -INFINITY;
-    float tr[kSpecRegs], dr[kSpecRegs];
-    if (in_regs) {
+    // ---- q and p of node v.  A thread's entries are x0 + tid + i * kSpecThreads; when
+    // the chunk fits, they are kept in registers (same order of operations either way).
+    // With the caller's normalisers (target_lse, and draft_lse when the children are
+    // tried against the draft distribution) every value is exp(logit - lse) at once;
+    // otherwise the chunk max and exp-sum are exchanged first and the normalisers
+    // formed from them.
+    const bool need_p = has_draft && !pm;
+    const bool given = pl.target_lse != nullptr && (!need_p || pl.draft_lse != nullptr);
+    double lse_q = 0.0, lse_p = 0.0;
+    if (given) {
+      lse_q = (double)pl.target_lse[(size_t)b * N + v];
+      if (need_p) lse_p = (double)pl.draft_lse[(size_t)b * pl.R + row];
+      if (in_regs) {
 #pragma unroll
-      for (int i = 0; i < kSpecRegs; ++i) {
-        const int x = x0 + tid + i * kSpecThreads;
-        tr[i] = x < x1 ? tl[x] : -INFINITY;
-        dr[i] = (x < x1 && !pm) ? dl[x] : -INFINITY;
-      }
-#pragma unroll
-      for (int i = 0; i < kSpecRegs; ++i) {
-        if (x0 + tid + i * kSpecThreads < x1) {
-          mq = fmax(mq, (double)tr[i]);
-          mp = fmax(mp, (double)dr[i]);
+        for (int i = 0; i < kSpecRegs; ++i) {
+          const int x = x0 + tid + i * kSpecThreads;
+          const bool in = x < x1;
+          qr[i] = in ? exp((double)tl[x] - lse_q) : 0.0;
+          pr[i] = (in && need_p) ? exp((double)dl[x] - lse_p) : 0.0;
+          if (in) {
+            qb[x] = qr[i];
+            if (!pm) pb[x] = pr[i];
+          }
+        }
+      } else {
+        for (int x = x0 + tid; x < x1; x += kSpecThreads) {
+          qb[x] = exp((double)tl[x] - lse_q);
+          if (!pm) pb[x] = need_p ? exp((double)dl[x] - lse_p) : 0.0;
         }
       }
     } else {
-      for (int x = x0 + tid; x < x1; x += kSpecThreads) {
-        mq = fmax(mq, (double)tl[x]);
-        mp = fmax(mp, (double)dl[x]);
-      }
-    }
-    // (point-mass mode never uses the draft distribution: its half is skipped)
-    mq = wg_max_d(mq, red);
-    if (!pm) mp = wg_max_d(mp, red);
-    double zq = 0.0, zp = 0.0;
-    if (in_regs) {
-      // exp(x - chunk max) stays in qr / pr; scaled to q / p once the totals are known
+      double mq = -INFINITY, mp = -INFINITY;
+      float tr[kSpecRegs], dr[kSpecRegs];
+      if (in_regs) {
 #pragma unroll
-      for (int i = 0; i < kSpecRegs; ++i) {
-        const bool in = x0 + tid + i * kSpecThreads < x1;
-        qr[i] = in ? exp((double)tr[i] - mq) : 0.0;
-        pr[i] = (in && !pm) ? exp((double)dr[i] - mp) : 0.0;
-        zq += qr[i];
-        zp += pr[i];
-      }
-    } else {
-      for (int x = x0 + tid; x < x1; x += kSpecThreads) {
-        zq += exp((double)tl[x] - mq);
-        if (!pm) zp += exp((double)dl[x] - mp);
-      }
-    }
-    zq = wg_sum_d(zq, red);
-    if (!pm) zp = wg_sum_d(zp, red);
-    {
-      const double mine[4] = {mq, zq, mp, zp};
-      if (!exchange(w, b, chunks, me, gen++, 4, mine, lds_all, &lds_flag)) { aborted = true; break; }
-    }
-    double Mq = -INFINITY, Mp = -INFINITY;
-    for (int c = 0; c < chunks; ++c) {
-      Mq = fmax(Mq, lds_all[4 * c]);
-      Mp = fmax(Mp, lds_all[4 * c + 2]);
-    }
-    // chunk terms: one exponential per lane, then summed in chunk order by every
-    // thread (an empty chunk adds +0.0, which leaves the sum unchanged)
-    if (tid < chunks) {
-      cterm[tid] = lds_all[4 * tid] > -INFINITY ? lds_all[4 * tid + 1] * exp(lds_all[4 * tid] - Mq) : 0.0;
-    } else if (tid >= 64 && tid < 64 + chunks && !pm) {
-      const int c = tid - 64;
-      cterm[tid] = lds_all[4 * c + 2] > -INFINITY ? lds_all[4 * c + 3] * exp(lds_all[4 * c + 2] - Mp) : 0.0;
-    }
-    __syncthreads();
-    double Zq = 0.0, Zp = 0.0;
-    for (int c = 0; c < chunks; ++c) Zq += cterm[c];
-    if (!pm)
-      for (int c = 0; c < chunks; ++c) Zp += cterm[64 + c];
-    const double lse_q = Mq + log(Zq);
-    const double lse_p = pm ? 0.0 : Mp + log(Zp);
-    if (in_regs) {
-      const double sq = exp(mq - lse_q);
-      const double sp = pm ? 0.0 : exp(mp - lse_p);
+        for (int i = 0; i < kSpecRegs; ++i) {
+          const int x = x0 + tid + i * kSpecThreads;
+          tr[i] = x < x1 ? tl[x] : -INFINITY;
+          dr[i] = (x < x1 && !pm) ? dl[x] : -INFINITY;
+        }
 #pragma unroll
-      for (int i = 0; i < kSpecRegs; ++i) {
-        const int x = x0 + tid + i * kSpecThreads;
-        qr[i] *= sq;
-        pr[i] *= sp;
-        if (x < x1) {
-          qb[x] = qr[i];
-          if (!pm) pb[x] = pr[i];
+        for (int i = 0; i < kSpecRegs; ++i) {
+          if (x0 + tid + i * kSpecThreads < x1) {
+            mq = fmax(mq, (double)tr[i]);
+            mp = fmax(mp, (double)dr[i]);
+          }
+        }
+      } else {
+        for (int x = x0 + tid; x < x1; x += kSpecThreads) {
+          mq = fmax(mq, (double)tl[x]);
+          mp = fmax(mp, (double)dl[x]);
         }
       }
-    } else {
-      for (int x = x0 + tid; x < x1; x += kSpecThreads) {
-        qb[x] = exp((double)tl[x] - lse_q);
-        if (!pm) pb[x] = exp((double)dl[x] - lse_p);
+      // (point-mass mode never uses the draft distribution: its half is skipped)
+      mq = wg_max_d(mq, red);
+      if (!pm) mp = wg_max_d(mp, red);
+      double zq = 0.0, zp = 0.0;
+      if (in_regs) {
+        // exp(x - chunk max) stays in qr / pr; scaled to q / p once the totals are known
+#pragma unroll
+        for (int i = 0; i < kSpecRegs; ++i) {
+          const bool in = x0 + tid + i * kSpecThreads < x1;
+          qr[i] = in ? exp((double)tr[i] - mq) : 0.0;
+          pr[i] = (in && !pm) ? exp((double)dr[i] - mp) : 0.0;
+          zq += qr[i];
+          zp += pr[i];
+        }
+      } else {
+        for (int x = x0 + tid; x < x1; x += kSpecThreads) {
+          zq += exp((double)tl[x] - mq);
+          if (!pm) zp += exp((double)dl[x] - mp);
+        }
+      }
+      zq = wg_sum_d(zq, red);
+      if (!pm) zp = wg_sum_d(zp, red);
+      {
+        const double mine[4] = {mq, zq, mp, zp};
+        if (!exchange(w, b, chunks, me, gen++, 4, mine, lds_all, &lds_flag)) { aborted = true; break; }
+      }
+      double Mq = -INFINITY, Mp = -INFINITY;
+      for (int c = 0; c < chunks; ++c) {
+        Mq = fmax(Mq, lds_all[4 * c]);
+        Mp = fmax(Mp, lds_all[4 * c + 2]);
+      }
+      // chunk terms: one exponential per lane, then summed in chunk order by every
+      // thread (an empty chunk adds +0.0, which leaves the sum unchanged)
+      if (tid < chunks) {
+        cterm[tid] = lds_all[4 * tid] > -INFINITY ? lds_all[4 * tid + 1] * exp(lds_all[4 * tid] - Mq) : 0.0;
+      } else if (tid >= 64 && tid < 64 + chunks && !pm) {
+        const int c = tid - 64;
+        cterm[tid] = lds_all[4 * c + 2] > -INFINITY ? lds_all[4 * c + 3] * exp(lds_all[4 * c + 2] - Mp) : 0.0;
+      }
+      __syncthreads();
+      double Zq = 0.0, Zp = 0.0;
+      for (int c = 0; c < chunks; ++c) Zq += cterm[c];
+      if (!pm)
+        for (int c = 0; c < chunks; ++c) Zp += cterm[64 + c];
+      lse_q = Mq + log(Zq);
+      lse_p = pm ? 0.0 : Mp + log(Zp);
+      if (in_regs) {
+        const double sq = exp(mq - lse_q);
+        const double sp = pm ? 0.0 : exp(mp - lse_p);
+#pragma unroll
+        for (int i = 0; i < kSpecRegs; ++i) {
+          const int x = x0 + tid + i * kSpecThreads;
+          qr[i] *= sq;
+          pr[i] *= sp;
+          if (x < x1) {
+            qb[x] = qr[i];
+            if (!pm) pb[x] = pr[i];
+          }
+        }
+      } else {
+        for (int x = x0 + tid; x < x1; x += kSpecThreads) {
+          qb[x] = exp((double)tl[x] - lse_q);
+          if (!pm) pb[x] = exp((double)dl[x] - lse_p);
+        }
       }
     }
     __syncthreads();
@@ -559,8 +595,20 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
     }
   }
 
-  if (me == 0 && tid < 64) {
-    const bool bad = aborted;
+  // ---- exit.  The last workgroup of the sequence to finish writes the path, the
+  // accepted drafts' tokens and the padding, or -1 everywhere (accept_len too) if any
+  // workgroup of the sequence gave up on a spin.  The drawn token was stored by thread
+  // 0 of the workgroup that found it before that workgroup's release below, so the
+  // last workgroup's acquire orders its -1 after it.
+  __shared__ unsigned exit_old;
+  __syncthreads();
+  if (tid == 0)
+    exit_old = __hip_atomic_fetch_add(&w.exits[b], 1u + (aborted ? kExitAbortBit : 0u),
+                                      __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const unsigned prior = exit_old;
+  if ((prior & 0xFFFFu) == (unsigned)(chunks - 1) && tid < 64) {
+    const bool bad = aborted || (prior & kExitAbortBit) != 0u;
     for (int j = tid; j < cap; j += 64) {
       if (bad) {
         accept_path[(size_t)b * cap + j] = -1;
@@ -618,8 +666,11 @@ hipError_t launch_accept_spec(const SpecPlan& pl, const int32_t* tokens, const i
                               const float* draft_logits, const float* u_accept,
                               const float* u_sample, int32_t* accept_len, int32_t* accept_path,
                               int32_t* out_tokens, void* workspace, hipStream_t stream) {
-  hipLaunchKernelGGL(spec_init_kernel, dim3(1), dim3(256), 0, stream, workspace, pl.B, pl.chunks,
-                     pl.V);
+  const int words = pl.B * 2 * pl.chunks * 8;
+  int init_blocks = (words + 4 * 256 - 1) / (4 * 256);   // about four words per thread
+  init_blocks = init_blocks < 1 ? 1 : (init_blocks > 1024 ? 1024 : init_blocks);
+  hipLaunchKernelGGL(spec_init_kernel, dim3(init_blocks), dim3(256), 0, stream, workspace, pl.B,
+                     pl.chunks, pl.V);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(accept_spec_kernel, dim3(pl.B * pl.chunks), dim3(kSpecThreads), 0, stream,

@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+
 #include "../../include/eagle_mi355.h"
 #include "internal.h"
 
@@ -33,13 +34,22 @@ eagle_status_t hip_status(hipError_t e, const char* what) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// The element type of the attention and LM-head operands: bf16 is the one
+// implemented; fp32 operands are a valid request this library does not serve.
+eagle_status_t check_dtype(eagle_dtype_t dtype) {
+  if (dtype == EAGLE_BF16) return EAGLE_OK;
+  if (dtype == EAGLE_F32)
+    return fail(EAGLE_ERR_UNSUPPORTED, "dtype EAGLE_F32: only bf16 operands are implemented (round fp32 inputs to bf16)");
+  return fail(EAGLE_ERR_INVALID_ARG, "dtype=%d is not an eagle_dtype_t value", (int)dtype);
+}
+
 }  // namespace
 
 extern "C" {
 
 int eagle_abi_version(void) { return EAGLE_ABI_VERSION; }
 
-const char* eagle_status_string(int status) {
+const char* eagle_status_string(eagle_status_t status) {
   switch (status) {
     case EAGLE_OK: return "ok";
     case EAGLE_ERR_NULL: return "null pointer";
@@ -90,11 +100,13 @@ static eagle_status_t attn_impl(const void* q, const void* k, const void* v,
                                 const int32_t* parents, const int32_t* prefix_len,
                                 const int32_t* tree_len, int32_t B, int32_t N, int32_t Hq,
                                 int32_t Hkv, int32_t D, int32_t P, int32_t kv_cap, float scale,
-                                void* out, float* lse, void* workspace, size_t workspace_bytes,
-                                hipStream_t stream, const char* name) {
+                                eagle_dtype_t dtype, void* out, float* lse, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream, const char* name) {
   if (!q || !k || !v || !parents || !out)
     return fail(EAGLE_ERR_NULL, "q, k, v, parents and out must be non-NULL");
-  eagle_status_t st = check_attn_dims(B, N, Hq, Hkv, D, P);
+  eagle_status_t st = check_dtype(dtype);
+  if (st != EAGLE_OK) return st;
+  st = check_attn_dims(B, N, Hq, Hkv, D, P);
   if (st != EAGLE_OK) return st;
   if (kv_cap < P + N) return fail(EAGLE_ERR_INVALID_ARG, "kv_cap=%d < P+N=%d", kv_cap, P + N);
   if (!(scale > 0.f) || scale != scale || scale > 1e30f)
@@ -117,10 +129,11 @@ static eagle_status_t attn_impl(const void* q, const void* k, const void* v,
 eagle_status_t eagle_tree_verify_attn(const void* q, const void* k, const void* v,
                                       const int32_t* parents, int32_t B, int32_t N, int32_t Hq,
                                       int32_t Hkv, int32_t D, int32_t P, int32_t kv_cap,
-                                      float scale, void* out, float* lse, void* workspace,
-                                      size_t workspace_bytes, hipStream_t stream) {
-  return attn_impl(q, k, v, parents, nullptr, nullptr, B, N, Hq, Hkv, D, P, kv_cap, scale, out, lse,
-                   workspace, workspace_bytes, stream, "eagle_tree_verify_attn");
+                                      float scale, eagle_dtype_t dtype, void* out, float* lse,
+                                      void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+  return attn_impl(q, k, v, parents, nullptr, nullptr, B, N, Hq, Hkv, D, P, kv_cap, scale, dtype,
+                   out, lse, workspace, workspace_bytes, stream, "eagle_tree_verify_attn");
 }
 
 static int page_shift_of(int32_t page_size) {
@@ -142,11 +155,14 @@ eagle_status_t eagle_tree_verify_attn_paged(const void* q, const void* k_pool, c
                                             int32_t B, int32_t N, int32_t Hq, int32_t Hkv,
                                             int32_t D, int32_t P, int32_t page_size,
                                             int32_t max_pages, int32_t num_blocks, float scale,
-                                            void* out, float* lse, void* workspace,
-                                            size_t workspace_bytes, hipStream_t stream) {
+                                            eagle_dtype_t dtype, void* out, float* lse,
+                                            void* workspace, size_t workspace_bytes,
+                                            hipStream_t stream) {
   if (!q || !k_pool || !v_pool || !block_table || !parents || !out)
     return fail(EAGLE_ERR_NULL, "q, k_pool, v_pool, block_table, parents and out must be non-NULL");
-  eagle_status_t st = check_attn_dims(B, N, Hq, Hkv, D, P);
+  eagle_status_t st = check_dtype(dtype);
+  if (st != EAGLE_OK) return st;
+  st = check_attn_dims(B, N, Hq, Hkv, D, P);
   if (st != EAGLE_OK) return st;
   const int shift = page_shift_of(page_size);
   if (shift < 0) return fail(EAGLE_ERR_UNSUPPORTED, "page_size=%d (a power of two up to 4096)", page_size);
@@ -183,13 +199,14 @@ eagle_status_t eagle_tree_verify_attn_ragged(const void* q, const void* k, const
                                              const int32_t* parents, const int32_t* prefix_len,
                                              const int32_t* tree_len, int32_t B, int32_t N,
                                              int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
-                                             int32_t kv_cap, float scale, void* out, float* lse,
-                                             void* workspace, size_t workspace_bytes,
-                                             hipStream_t stream) {
+                                             int32_t kv_cap, float scale, eagle_dtype_t dtype,
+                                             void* out, float* lse, void* workspace,
+                                             size_t workspace_bytes, hipStream_t stream) {
   if (!prefix_len && !tree_len)
     return fail(EAGLE_ERR_NULL, "prefix_len and tree_len are both NULL (use eagle_tree_verify_attn)");
-  return attn_impl(q, k, v, parents, prefix_len, tree_len, B, N, Hq, Hkv, D, P, kv_cap, scale, out,
-                   lse, workspace, workspace_bytes, stream, "eagle_tree_verify_attn_ragged");
+  return attn_impl(q, k, v, parents, prefix_len, tree_len, B, N, Hq, Hkv, D, P, kv_cap, scale,
+                   dtype, out, lse, workspace, workspace_bytes, stream,
+                   "eagle_tree_verify_attn_ragged");
 }
 
 // ---------------------------------------------------------------- LM head
@@ -206,12 +223,15 @@ size_t eagle_lm_head_workspace(int32_t M, int32_t H, int32_t V) {
 }
 
 eagle_status_t eagle_lm_head_argmax(const void* hidden, const void* weight, int32_t M, int32_t H,
-                                    int32_t V, float* out_max, int32_t* out_argmax,
-                                    float* out_lse, float* out_second, float* out_logits,
-                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                                    int32_t V, eagle_dtype_t dtype, float* out_max,
+                                    int32_t* out_argmax, float* out_lse, float* out_second,
+                                    float* out_logits, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
   if (!hidden || !weight || !out_max || !out_argmax || !out_lse)
     return fail(EAGLE_ERR_NULL, "hidden, weight, out_max, out_argmax and out_lse must be non-NULL");
-  eagle_status_t st = check_lm_dims(M, H, V);
+  eagle_status_t st = check_dtype(dtype);
+  if (st != EAGLE_OK) return st;
+  st = check_lm_dims(M, H, V);
   if (st != EAGLE_OK) return st;
   if (!aligned16(hidden) || !aligned16(weight) || (out_logits && !aligned16(out_logits)))
     return fail(EAGLE_ERR_INVALID_ARG, "hidden, weight and out_logits must be 16-byte aligned");
@@ -266,62 +286,72 @@ size_t eagle_accept_spec_workspace(int32_t B, int32_t N, int32_t V) {
 }
 
 static eagle_status_t spec_impl(const int32_t* tokens, const int32_t* parents,
-                                const int32_t* draft_row, const float* target_logits,
-                                const float* draft_logits, int32_t draft_rows,
-                                const float* u_accept, const float* u_sample,
                                 const int32_t* tree_len, int32_t B, int32_t N, int32_t V,
-                                int32_t max_depth, int32_t mode, int32_t* accept_len,
-                                int32_t* accept_path, int32_t* out_tokens, void* workspace,
-                                size_t workspace_bytes, hipStream_t stream) {
+                                int32_t max_depth, const float* target_logits,
+                                const float* target_lse, const float* draft_logits,
+                                const float* draft_lse, const int32_t* draft_row,
+                                int32_t draft_rows, const float* u_accept, const float* u_sample,
+                                eagle_spec_mode_t mode, int32_t* accept_len, int32_t* accept_path,
+                                int32_t* out_tokens, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream, const char* name) {
   if (!tokens || !parents || !draft_row || !target_logits || !draft_logits || !u_accept ||
       !u_sample || !accept_len || !accept_path || !out_tokens)
-    return fail(EAGLE_ERR_NULL, "all pointers must be non-NULL");
+    return fail(EAGLE_ERR_NULL, "every pointer except target_lse and draft_lse must be non-NULL");
   if (B < 1 || N < 1 || V < 1 || draft_rows < 1 || max_depth < 0)
     return fail(EAGLE_ERR_INVALID_ARG, "need B,N,V,draft_rows >= 1 and max_depth >= 0");
   if (N > EAGLE_MAX_TREE) return fail(EAGLE_ERR_UNSUPPORTED, "N=%d > %d", N, EAGLE_MAX_TREE);
   if (max_depth > EAGLE_MAX_TREE) return fail(EAGLE_ERR_INVALID_ARG, "max_depth=%d > %d", max_depth, EAGLE_MAX_TREE);
   if (mode != EAGLE_SPEC_SAMPLED && mode != EAGLE_SPEC_POINT_MASS)
-    return fail(EAGLE_ERR_INVALID_ARG, "mode=%d (EAGLE_SPEC_SAMPLED or EAGLE_SPEC_POINT_MASS)", mode);
+    return fail(EAGLE_ERR_INVALID_ARG, "mode=%d (EAGLE_SPEC_SAMPLED or EAGLE_SPEC_POINT_MASS)", (int)mode);
   eagle::SpecPlan pl = eagle::plan_accept_spec(B, N, V);
   pl.mode = mode;
   pl.R = draft_rows;
   pl.max_depth = max_depth;
   pl.tree_len = tree_len;
+  pl.target_lse = target_lse;
+  pl.draft_lse = draft_lse;
   const size_t need = eagle::accept_spec_workspace_bytes(pl);
   if (!workspace || workspace_bytes < need)
     return fail(EAGLE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
   if (!aligned16(workspace)) return fail(EAGLE_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  char what[64];
+  snprintf(what, sizeof(what), "%s launch", name);
   return hip_status(eagle::launch_accept_spec(pl, tokens, parents, draft_row, target_logits,
                                               draft_logits, u_accept, u_sample, accept_len,
                                               accept_path, out_tokens, workspace, stream),
-                    "eagle_accept_spec launch");
+                    what);
 }
 
-eagle_status_t eagle_accept_spec(const int32_t* tokens, const int32_t* parents,
-                                 const int32_t* draft_row, const float* target_logits,
-                                 const float* draft_logits, int32_t draft_rows,
-                                 const float* u_accept, const float* u_sample, int32_t B,
-                                 int32_t N, int32_t V, int32_t max_depth, int32_t mode,
-                                 int32_t* accept_len, int32_t* accept_path, int32_t* out_tokens,
-                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return spec_impl(tokens, parents, draft_row, target_logits, draft_logits, draft_rows, u_accept,
-                   u_sample, nullptr, B, N, V, max_depth, mode, accept_len, accept_path,
-                   out_tokens, workspace, workspace_bytes, stream);
+eagle_status_t eagle_accept_spec(const int32_t* tokens, const int32_t* parents, int32_t B,
+                                 int32_t N, int32_t V, int32_t max_depth,
+                                 const float* target_logits, const float* target_lse,
+                                 const float* draft_logits, const float* draft_lse,
+                                 const int32_t* draft_row, int32_t draft_rows,
+                                 const float* u_accept, const float* u_sample,
+                                 eagle_spec_mode_t mode, int32_t* accept_len,
+                                 int32_t* accept_path, int32_t* out_tokens, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  return spec_impl(tokens, parents, nullptr, B, N, V, max_depth, target_logits, target_lse,
+                   draft_logits, draft_lse, draft_row, draft_rows, u_accept, u_sample, mode,
+                   accept_len, accept_path, out_tokens, workspace, workspace_bytes, stream,
+                   "eagle_accept_spec");
 }
 
 eagle_status_t eagle_accept_spec_ragged(const int32_t* tokens, const int32_t* parents,
-                                        const int32_t* draft_row, const float* target_logits,
-                                        const float* draft_logits, int32_t draft_rows,
-                                        const float* u_accept, const float* u_sample,
                                         const int32_t* tree_len, int32_t B, int32_t N, int32_t V,
-                                        int32_t max_depth, int32_t mode, int32_t* accept_len,
-                                        int32_t* accept_path, int32_t* out_tokens,
-                                        void* workspace, size_t workspace_bytes,
-                                        hipStream_t stream) {
+                                        int32_t max_depth, const float* target_logits,
+                                        const float* target_lse, const float* draft_logits,
+                                        const float* draft_lse, const int32_t* draft_row,
+                                        int32_t draft_rows, const float* u_accept,
+                                        const float* u_sample, eagle_spec_mode_t mode,
+                                        int32_t* accept_len, int32_t* accept_path,
+                                        int32_t* out_tokens, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream) {
   if (!tree_len) return fail(EAGLE_ERR_NULL, "tree_len is NULL (use eagle_accept_spec)");
-  return spec_impl(tokens, parents, draft_row, target_logits, draft_logits, draft_rows, u_accept,
-                   u_sample, tree_len, B, N, V, max_depth, mode, accept_len, accept_path,
-                   out_tokens, workspace, workspace_bytes, stream);
+  return spec_impl(tokens, parents, tree_len, B, N, V, max_depth, target_logits, target_lse,
+                   draft_logits, draft_lse, draft_row, draft_rows, u_accept, u_sample, mode,
+                   accept_len, accept_path, out_tokens, workspace, workspace_bytes, stream,
+                   "eagle_accept_spec_ragged");
 }
 
 // ---------------------------------------------------------------- rerank
@@ -568,6 +598,32 @@ eagle_status_t eagle_kv_commit(void* k_cache, void* v_cache, const int32_t* acce
   return hip_status(eagle::launch_kv_commit(k_cache, v_cache, accept_len, accept_path, L, B, Hkv,
                                             D, P, kv_cap, path_len, stream),
                     "eagle_kv_commit launch");
+}
+
+// ---------------------------------------------------------------- measurement probes
+eagle_status_t eagle_calib_stream_read(const void* src, size_t bytes, void* sink,
+                                       hipStream_t stream) {
+  if (!src || !sink) return fail(EAGLE_ERR_NULL, "src and sink must be non-NULL");
+  if (bytes < 16 || bytes % 16) return fail(EAGLE_ERR_INVALID_ARG, "bytes=%zu: a positive multiple of 16", bytes);
+  if (!aligned16(src)) return fail(EAGLE_ERR_INVALID_ARG, "src must be 16-byte aligned");
+  return hip_status(eagle::launch_calib_stream_read(src, bytes, sink, stream),
+                    "eagle_calib_stream_read launch");
+}
+
+double eagle_calib_mfma_bf16_flops(int32_t iters) {
+  if (iters < 1) return 0.0;
+  // workgroups x 4 waves x 4 chains x iters x 32*32*16*2 flop
+  return (double)eagle::kCalibMfmaBlocks * 4.0 * 4.0 * (double)iters * 32768.0;
+}
+
+eagle_status_t eagle_calib_mfma_bf16(int32_t iters, float* out, size_t out_floats,
+                                     hipStream_t stream) {
+  if (!out) return fail(EAGLE_ERR_NULL, "out must be non-NULL");
+  if (iters < 1) return fail(EAGLE_ERR_INVALID_ARG, "iters=%d must be >= 1", iters);
+  if (out_floats < (size_t)eagle::kCalibMfmaBlocks * 256)
+    return fail(EAGLE_ERR_WORKSPACE, "out holds %zu floats, need %d", out_floats,
+                eagle::kCalibMfmaBlocks * 256);
+  return hip_status(eagle::launch_calib_mfma_bf16(iters, out, stream), "eagle_calib_mfma_bf16 launch");
 }
 
 }  // extern "C"

@@ -12,18 +12,13 @@ namespace eagle {
 // MI355X: 256 CUs.  Split-KV aims at about one attention workgroup per CU.
 constexpr int kNumCUs = 256;
 constexpr int kMinSplitKeys = 256;
-#ifndef EAGLE_ATTN_ROW_TILES
-#define EAGLE_ATTN_ROW_TILES 1
-#endif
-constexpr int kAttnRowTiles = EAGLE_ATTN_ROW_TILES;   // 32-row MFMA tiles per wave
 
 struct AttnPlan {
   int B, N, Hq, Hkv, G, D, P, kv_cap;
   int R;          // query rows per (sequence, KV head) = N * G
-  int rowt;       // 32-row tiles per wave (1 or 2)
   int waves;      // waves per workgroup
   int RB;         // row blocks per pair
-  int Rpad;       // RB * waves * rowt * 32
+  int Rpad;       // RB * waves * 32
   int S;          // key splits
   int split_len;  // keys per split (multiple of 32); the last split also takes the tree
   float c;        // scale * log2(e)
@@ -86,6 +81,10 @@ struct SpecPlan {
   int mode;       // 0: siblings drawn from the draft distribution; 1: deterministic (point mass)
   int chunks;     // vocabulary chunks (one workgroup each) per sequence
   const int32_t* tree_len;   // ragged batches: per-sequence tree size (<= N), may be null
+  // the callers' log-sum-exp of every target row [B][N] and draft row [B][R] (may be
+  // null: the kernel then forms the normalisers itself)
+  const float* target_lse;
+  const float* draft_lse;
 };
 SpecPlan plan_accept_spec(int B, int N, int V);
 size_t accept_spec_workspace_bytes(const SpecPlan& pl);
@@ -106,6 +105,12 @@ size_t rerank_workspace_bytes(const RerankPlan& pl);
 hipError_t launch_rerank(const RerankPlan& pl, const float* draft_logits, const int32_t* root_token,
                          int32_t* tokens, int32_t* parents, int32_t* depths, float* scores,
                          int32_t* draft_row, float* draft_lse, void* workspace, hipStream_t stream);
+
+// measurement probes (calib.hip): grid sizes and launchers
+constexpr int kCalibReadBlocks = 4096;   // 256-thread workgroups of the streaming read
+constexpr int kCalibMfmaBlocks = 2048;   // 256-thread workgroups of the MFMA loop
+hipError_t launch_calib_stream_read(const void* src, size_t bytes, void* sink, hipStream_t stream);
+hipError_t launch_calib_mfma_bf16(int iters, float* out, hipStream_t stream);
 
 // KV commit: at most max_depth + 1 <= 65 accepted rows per (layer, sequence, head)
 constexpr int kMaxCommitRows = 65;

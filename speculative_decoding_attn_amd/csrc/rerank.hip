@@ -27,10 +27,7 @@ namespace eagle {
 namespace {
 
 constexpr int kRowThreads = 256;
-#ifndef EAGLE_RERANK_ROW_PER
-#define EAGLE_RERANK_ROW_PER 32
-#endif
-constexpr int kRowPer = EAGLE_RERANK_ROW_PER;      // elements per thread in rerank_rows
+constexpr int kRowPer = 32;                        // elements per thread in rerank_rows
 constexpr int kChunk = kRowThreads * kRowPer;      // vocabulary entries per chunk
 constexpr int kTreeThreads = 1024;
 constexpr int kMaxCand = 2048;                     // candidates per sequence in rerank_tree
@@ -47,9 +44,12 @@ struct VI {
   int i;
 };
 
-// (value desc, index asc) as one unsigned 64-bit key: larger key = better.
+// (value desc, index asc) as one unsigned 64-bit key: larger key = better.  -0.0 is
+// mapped to +0.0 first, so the two zeros rank as equal values (ties then go to the
+// lower index), as the (value, index) comparison `better` has them.
 __device__ __forceinline__ uint32_t ordered_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 __device__ __forceinline__ float ordered_float(uint32_t o) {

@@ -8,7 +8,7 @@
 // (row r = node r/G, head g*G + r%G) share every K/V row, so a workgroup takes a
 // block of WAVES*64 rows of one pair and one contiguous range of keys ("split"):
 // K and V tiles of 32 keys are staged once in LDS and read by all of its waves.
-// Each wave owns 64 rows as two 32-row MFMA tiles.
+// Each wave owns 32 rows (one 32-row MFMA tile).
 //
 // Orientation.  Scores are formed transposed, S^T = K * Q^T, with the 32x32x16 bf16
 // MFMA: lane l then holds 16 keys of ONE query row (l % 32), so the row max, the
@@ -54,7 +54,7 @@ __device__ __forceinline__ int vt_pos(int key) {
   return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
 }
 
-template <int D, int WAVES, int ROWT, bool PAGED>
+template <int D, int WAVES, bool PAGED>
 __global__ void __launch_bounds__(WAVES * 64, 1)
 tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
               const uint16_t* __restrict__ v, const int32_t* __restrict__ parents,
@@ -121,40 +121,31 @@ tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     }
   };
 
-  // ---- Q^T operands (B side of S^T = K Q^T) and ancestor masks, per row tile
-  const int rowbase = rb * (WAVES * ROWT * 32) + wid * ROWT * 32;
-  bf16x8 qf[ROWT][KSTEPS];
-  uint64_t anc[ROWT];
+  // ---- Q^T operand (B side of S^T = K Q^T) and ancestor mask of this wave's rows
+  const int r_row = rb * (WAVES * 32) + wid * 32 + l32;
+  bf16x8 qf[KSTEPS];
+  uint64_t anc;
+  if (r_row < R) {
+    const int il = r_row / G;
+    const int i = pl.node0 + il;
+    const int h = g * G + (r_row - il * G);
+    const uint16_t* qp = q + ((size_t)(b * pl.N + i) * pl.Hq + h) * D + 8 * half;
 #pragma unroll
-  for (int t = 0; t < ROWT; ++t) {
-    const int r = rowbase + 32 * t + l32;
-    if (r < R) {
-      const int il = r / G;
-      const int i = pl.node0 + il;
-      const int h = g * G + (r - il * G);
-      const uint16_t* qp = q + ((size_t)(b * pl.N + i) * pl.Hq + h) * D + 8 * half;
+    for (int s = 0; s < KSTEPS; ++s) qf[s] = as_bf16x8(*(const u32x4*)(qp + 16 * s));
+    anc = ancestor_mask(par, i, N);
+  } else {
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) qf[t][s] = as_bf16x8(*(const u32x4*)(qp + 16 * s));
-      anc[t] = ancestor_mask(par, i, N);
-    } else {
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) qf[t][s] = as_bf16x8(u32x4{0, 0, 0, 0});
-      anc[t] = 1;
-    }
+    for (int s = 0; s < KSTEPS; ++s) qf[s] = as_bf16x8(u32x4{0, 0, 0, 0});
+    anc = 1;
   }
 
-  f32x16 oacc[ROWT][DBLK];
-  float mc[ROWT];     // running max of scale*log2e*s
-  float lsum[ROWT];   // this lane's half of the row sum
+  f32x16 oacc[DBLK];
 #pragma unroll
-  for (int t = 0; t < ROWT; ++t) {
+  for (int db = 0; db < DBLK; ++db)
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[t][db][r] = 0.f;
-    mc[t] = -INFINITY;
-    lsum[t] = 0.f;
-  }
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  float mc = -INFINITY;   // running max of scale*log2e*s
+  float lsum = 0.f;       // this lane's half of the row sum
 
   const float c = pl.c;
   const uint64_t node_mask = N >= 64 ? ~0ull : ((1ull << N) - 1ull);
@@ -248,77 +239,68 @@ tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       const uint16_t* Ks = lds + st * L::STAGE;
       const uint16_t* Vs = Ks + L::KELEMS;
 
-      // S^T tile for 32 keys x ROWT row tiles
-      f32x16 sacc[ROWT];
+      // S^T tile for 32 keys
+      f32x16 sacc;
 #pragma unroll
-      for (int t = 0; t < ROWT; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
+      for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
         const bf16x8 kf = *(const bf16x8*)(Ks + l32 * L::KSTR + 16 * s + 8 * half);
-#pragma unroll
-        for (int t = 0; t < ROWT; ++t) sacc[t] = mfma32(kf, qf[t][s], sacc[t]);
+        sacc = mfma32(kf, qf[s], sacc);
       }
 
       // scores of this lane's 16 keys; chunks that reach into the tree (or past it) get
       // the ancestor mask: bit j of `allowed` says whether key kb + j is visible
-      float sv[ROWT][16];
+      float sv[16];
 #pragma unroll
-      for (int t = 0; t < ROWT; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sv[t][r] = sacc[t][r];
+      for (int r = 0; r < 16; ++r) sv[r] = sacc[r];
       if (kb + KC > P) {
         const int off = kb - P;   // >= -31
+        // only the last split owns the tree keys: in a ragged batch an earlier split
+        // can end inside a chunk at this sequence's prefix end
+        const uint64_t tm = (split == pl.S - 1) ? (anc & node_mask) : 0ull;
+        const uint32_t tree_bits = off >= 0 ? (off < 64 ? (uint32_t)(tm >> off) : 0u)
+                                            : (uint32_t)(tm << (-off));
+        const uint32_t prefix_bits = off < 0 ? ((1u << (-off)) - 1u) : 0u;
+        const uint32_t allowed = (tree_bits | prefix_bits) >> (4 * half);
 #pragma unroll
-        for (int t = 0; t < ROWT; ++t) {
-          // only the last split owns the tree keys: in a ragged batch an earlier split
-          // can end inside a chunk at this sequence's prefix end
-          const uint64_t tm = (split == pl.S - 1) ? (anc[t] & node_mask) : 0ull;
-          const uint32_t tree_bits = off >= 0 ? (off < 64 ? (uint32_t)(tm >> off) : 0u)
-                                              : (uint32_t)(tm << (-off));
-          const uint32_t prefix_bits = off < 0 ? ((1u << (-off)) - 1u) : 0u;
-          const uint32_t allowed = (tree_bits | prefix_bits) >> (4 * half);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int bit = 8 * (r >> 2) + (r & 3);
-            sv[t][r] = ((allowed >> bit) & 1u) ? sv[t][r] : -INFINITY;
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int bit = 8 * (r >> 2) + (r & 3);
+          sv[r] = ((allowed >> bit) & 1u) ? sv[r] : -INFINITY;
         }
       }
 
-      bf16x8 pf[ROWT][2];
+      bf16x8 pf[2];
+      {
+        float mx = sv[0];
 #pragma unroll
-      for (int t = 0; t < ROWT; ++t) {
-        float mx = sv[t][0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sv[t][r]);
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sv[r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float mxc = mx * c;
-        const bool need = mxc > mc[t] + kLazy;
+        const bool need = mxc > mc + kLazy;
         if (__ballot(need)) {
-          const float mnew = need ? mxc : mc[t];
-          const float alpha = need ? exp2f(mc[t] - mnew) : 1.f;
-          lsum[t] *= alpha;
+          const float mnew = need ? mxc : mc;
+          const float alpha = need ? exp2f(mc - mnew) : 1.f;
+          lsum *= alpha;
 #pragma unroll
           for (int db = 0; db < DBLK; ++db)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[t][db][r] *= alpha;
-          mc[t] = mnew;
+            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+          mc = mnew;
         }
-        const float mcu = (mc[t] == -INFINITY) ? 0.f : mc[t];
+        const float mcu = (mc == -INFINITY) ? 0.f : mc;
         float pr[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          pr[r] = __builtin_amdgcn_exp2f(fmaf(sv[t][r], c, -mcu));
-          lsum[t] += pr[r];
+          pr[r] = __builtin_amdgcn_exp2f(fmaf(sv[r], c, -mcu));
+          lsum += pr[r];
         }
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
           u32x4 pk;
 #pragma unroll
           for (int e = 0; e < 4; ++e) pk[e] = pack_bf16x2(pr[8 * cc + 2 * e], pr[8 * cc + 2 * e + 1]);
-          pf[t][cc] = as_bf16x8(pk);
+          pf[cc] = as_bf16x8(pk);
         }
       }
 
@@ -328,8 +310,7 @@ tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
           const bf16x8 vf = *(const bf16x8*)(Vs + (32 * db + l32) * L::VSTR + 16 * cc + 8 * half);
-#pragma unroll
-          for (int t = 0; t < ROWT; ++t) oacc[t][db] = mfma32(vf, pf[t][cc], oacc[t][db]);
+          oacc[db] = mfma32(vf, pf[cc], oacc[db]);
         }
 
       // chunk ch+1 (loaded during iteration ch-1) -> LDS stage st^1, while chunk ch+2's
@@ -339,43 +320,39 @@ tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     }
   }
   // ---- epilogue
+  const float ltot = lsum + __shfl_xor(lsum, 32);
+  if (r_row >= R) return;
+  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+  const float lse = (mc + log2f(ltot)) * kLn2;
+  const int il = r_row / G;
+  const int i = pl.node0 + il;
+  const int h = g * G + (r_row - il * G);
+  if (pl.S == 1) {
+    uint16_t* op = out + ((size_t)(b * pl.N + i) * pl.Hq + h) * D;
 #pragma unroll
-  for (int t = 0; t < ROWT; ++t) {
-    const int r = rowbase + 32 * t + l32;
-    const float ltot = lsum[t] + __shfl_xor(lsum[t], 32);
-    if (r >= R) continue;
-    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-    const float lse = (mc[t] + log2f(ltot)) * kLn2;
-    const int il = r / G;
-    const int i = pl.node0 + il;
-    const int h = g * G + (r - il * G);
-    if (pl.S == 1) {
-      uint16_t* op = out + ((size_t)(b * pl.N + i) * pl.Hq + h) * D;
+    for (int db = 0; db < DBLK; ++db)
 #pragma unroll
-      for (int db = 0; db < DBLK; ++db)
+      for (int j = 0; j < 4; ++j) {
+        const int d0 = 32 * db + 8 * j + 4 * half;
+        u32x2 pk;
+        pk[0] = pack_bf16x2(oacc[db][4 * j] * inv, oacc[db][4 * j + 1] * inv);
+        pk[1] = pack_bf16x2(oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv);
+        *(u32x2*)(op + d0) = pk;
+      }
+    if (half == 0 && lse_out) lse_out[(size_t)(b * pl.N + i) * pl.Hq + h] = lse;
+  } else {
+    const size_t prow = ((size_t)pair * pl.S + split) * pl.Rpad + r_row;
+    float* op = part_o + prow * D;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int d0 = 32 * db + 8 * j + 4 * half;
-          u32x2 pk;
-          pk[0] = pack_bf16x2(oacc[t][db][4 * j] * inv, oacc[t][db][4 * j + 1] * inv);
-          pk[1] = pack_bf16x2(oacc[t][db][4 * j + 2] * inv, oacc[t][db][4 * j + 3] * inv);
-          *(u32x2*)(op + d0) = pk;
-        }
-      if (half == 0 && lse_out) lse_out[(size_t)(b * pl.N + i) * pl.Hq + h] = lse;
-    } else {
-      const size_t prow = ((size_t)pair * pl.S + split) * pl.Rpad + r;
-      float* op = part_o + prow * D;
+    for (int db = 0; db < DBLK; ++db)
 #pragma unroll
-      for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int d0 = 32 * db + 8 * j + 4 * half;
-          f32x4 vv = {oacc[t][db][4 * j] * inv, oacc[t][db][4 * j + 1] * inv,
-                      oacc[t][db][4 * j + 2] * inv, oacc[t][db][4 * j + 3] * inv};
-          *(f32x4*)(op + d0) = vv;
-        }
-      if (half == 0) part_lse[prow] = lse;
-    }
+      for (int j = 0; j < 4; ++j) {
+        const int d0 = 32 * db + 8 * j + 4 * half;
+        f32x4 vv = {oacc[db][4 * j] * inv, oacc[db][4 * j + 1] * inv,
+                    oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv};
+        *(f32x4*)(op + d0) = vv;
+      }
+    if (half == 0) part_lse[prow] = lse;
   }
 }
 
@@ -818,17 +795,17 @@ hipError_t launch_pingpong(const AttnPlan& pl, const void* q, const void* k, con
   return hipGetLastError();
 }
 
-template <int D, int WAVES, int ROWT>
+template <int D, int WAVES>
 hipError_t launch_fwd(const AttnPlan& pl, const void* q, const void* k, const void* v,
                       const int32_t* parents, void* out, float* lse, float* part_o,
                       float* part_lse, hipStream_t stream) {
   const int nwg = pl.B * pl.Hkv * pl.RB * pl.S;
   if (pl.block_table)
-    hipLaunchKernelGGL((tree_attn_fwd<D, WAVES, ROWT, true>), dim3(nwg), dim3(WAVES * 64), 0,
+    hipLaunchKernelGGL((tree_attn_fwd<D, WAVES, true>), dim3(nwg), dim3(WAVES * 64), 0,
                        stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, parents,
                        pl, (uint16_t*)out, lse, part_o, part_lse);
   else
-    hipLaunchKernelGGL((tree_attn_fwd<D, WAVES, ROWT, false>), dim3(nwg), dim3(WAVES * 64), 0,
+    hipLaunchKernelGGL((tree_attn_fwd<D, WAVES, false>), dim3(nwg), dim3(WAVES * 64), 0,
                        stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, parents,
                        pl, (uint16_t*)out, lse, part_o, part_lse);
   return hipGetLastError();
@@ -838,11 +815,6 @@ template <int D>
 hipError_t launch_fwd_d(const AttnPlan& pl, const void* q, const void* k, const void* v,
                         const int32_t* parents, void* out, float* lse, float* part_o,
                         float* part_lse, hipStream_t stream) {
-  if (pl.rowt == 2) {
-    if (pl.waves == 4) return launch_fwd<D, 4, 2>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
-    if (pl.waves == 2) return launch_fwd<D, 2, 2>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
-    return launch_fwd<D, 1, 2>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
-  }
   if constexpr (D == 128) {   // D=64 uses at most 4 waves (chunk staging must divide evenly)
     if (pl.waves == 8) {
       if (pl.block_table)
@@ -850,9 +822,9 @@ hipError_t launch_fwd_d(const AttnPlan& pl, const void* q, const void* k, const 
       return launch_pingpong<false>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
     }
   }
-  if (pl.waves == 4) return launch_fwd<D, 4, 1>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
-  if (pl.waves == 2) return launch_fwd<D, 2, 1>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
-  return launch_fwd<D, 1, 1>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
+  if (pl.waves == 4) return launch_fwd<D, 4>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
+  if (pl.waves == 2) return launch_fwd<D, 2>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
+  return launch_fwd<D, 1>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
 }
 
 }  // namespace
@@ -877,11 +849,10 @@ AttnPlan plan_tree_attn_rows(int B, int N, int node0, int nq, int Hq, int Hkv, i
   pl.node0 = nq > 0 ? node0 : 0;
   pl.nq = nq > 0 ? nq : 0;
   pl.R = (nq > 0 ? nq : N) * pl.G;
-  // rows per wave: 32 (one MFMA row tile, 2 waves per SIMD) or 64 (two row tiles, 1 wave
-  // per SIMD: half the LDS reads per MFMA)
-  pl.rowt = kAttnRowTiles;
-  const int wave_rows = 32 * pl.rowt;
-  const int max_waves = (pl.rowt == 2 || D == 64) ? 4 : 8;
+  // 32 rows per wave (one MFMA row tile); D = 64 uses at most 4 waves (its chunk
+  // staging must divide evenly over the threads)
+  const int wave_rows = 32;
+  const int max_waves = D == 64 ? 4 : 8;
   pl.waves = 1;
   while (pl.waves < max_waves && pl.waves * wave_rows < pl.R) pl.waves *= 2;
   pl.RB = (pl.R + pl.waves * wave_rows - 1) / (pl.waves * wave_rows);

@@ -41,7 +41,7 @@ def test_binding_covers_every_symbol():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.eagle_abi_version() == 2
+    assert lib.eagle_abi_version() == 3
     assert lib.eagle_status_string(0) == b"ok"
     assert lib.eagle_status_string(99) == b"unknown status"
 
@@ -73,10 +73,14 @@ def test_attention_argument_errors(lib):
     ok = dict(B=1, N=10, Hq=2, Hkv=1, D=64, P=128, cap=138, scale=0.125)
 
     def call(q=FAKE, parents=FAKE, out=FAKE, B=1, N=10, Hq=2, Hkv=1, D=64, P=128, cap=138,
-             scale=0.125, ws=None, wsb=0):
-        return f(q, FAKE, FAKE, parents, B, N, Hq, Hkv, D, P, cap, scale, out, None, ws, wsb, None)
+             scale=0.125, dtype=0, ws=None, wsb=0):
+        return f(q, FAKE, FAKE, parents, B, N, Hq, Hkv, D, P, cap, scale, dtype, out, None, ws, wsb,
+                 None)
 
     assert call(q=None) == 1
+    assert call(dtype=1) == 3                  # EAGLE_F32: not implemented
+    assert b"EAGLE_F32" in lib.eagle_last_error()
+    assert call(dtype=7) == 2                  # not an eagle_dtype_t
     assert call(out=None) == 1
     assert call(B=0) == 2
     assert call(Hq=3, Hkv=2) == 2
@@ -108,10 +112,12 @@ def test_workspace_queries_are_pure_and_consistent(lib):
 def test_lm_head_argument_errors(lib):
     f = lib.eagle_lm_head_argmax
 
-    def call(hidden=FAKE, M=4, H=64, V=100, out=FAKE, ws=FAKE, wsb=1 << 20):
-        return f(hidden, FAKE, M, H, V, out, FAKE, FAKE, None, None, ws, wsb, None)
+    def call(hidden=FAKE, M=4, H=64, V=100, dtype=0, out=FAKE, ws=FAKE, wsb=1 << 20):
+        return f(hidden, FAKE, M, H, V, dtype, out, FAKE, FAKE, None, None, ws, wsb, None)
 
     assert call(hidden=None) == 1
+    assert call(dtype=1) == 3
+    assert call(dtype=-1) == 2
     assert call(out=None) == 1
     assert call(M=0) == 2
     assert call(V=1) == 2
@@ -126,17 +132,25 @@ def test_accept_and_rerank_argument_errors(lib):
     assert g(FAKE, FAKE, FAKE, 1, 65, 4, FAKE, FAKE, FAKE, None) == 3
     assert g(FAKE, FAKE, FAKE, 1, 5, -1, FAKE, FAKE, FAKE, None) == 2
     s = lib.eagle_accept_spec
-    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, None, 1, 5, 8, 3, 0, FAKE, FAKE, FAKE, FAKE,
-             1 << 20, None) == 1
-    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 1, 5, 8, 3, 0, FAKE, FAKE, FAKE, None, 0,
-             None) == 4
+
+    def sp(tokens=FAKE, tl=FAKE, tlse=None, dl=FAKE, dlse=None, mode=0, ws=FAKE, wsb=1 << 20,
+           B=1, N=5, V=8, max_depth=3, R=4):
+        # tokens, parents, B, N, V, max_depth, target_logits, target_lse, draft_logits,
+        # draft_lse, draft_row, draft_rows, u_accept, u_sample, mode, outputs, workspace
+        return s(tokens, FAKE, B, N, V, max_depth, tl, tlse, dl, dlse, FAKE, R, FAKE, FAKE, mode,
+                 FAKE, FAKE, FAKE, ws, wsb, None)
+
+    assert sp(tokens=None) == 1
+    assert sp(tl=None) == 1
+    assert sp(dl=None, dlse=FAKE) == 1
+    assert b"target_lse" in lib.eagle_last_error()   # the message names the nullable ones
+    assert sp(ws=None, wsb=0) == 4
     # sibling model: EAGLE_SPEC_SAMPLED (0) or EAGLE_SPEC_POINT_MASS (1) only
-    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 1, 5, 8, 3, 2, FAKE, FAKE, FAKE, FAKE,
-             1 << 20, None) == 2
-    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 1, 5, 8, 3, -1, FAKE, FAKE, FAKE, FAKE,
-             1 << 20, None) == 2
-    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 1, 5, 8, 3, 1, FAKE, FAKE, FAKE, None, 0,
-             None) == 4
+    assert sp(mode=2) == 2
+    assert sp(mode=-1) == 2
+    assert sp(mode=1, ws=None, wsb=0) == 4
+    assert sp(R=0) == 2
+    assert sp(N=65) == 3
     r = lib.eagle2_rerank
 
     def rr(B=1, V=100, k=10, depth=3, n=20, ws=FAKE, wsb=1 << 24):
@@ -170,27 +184,31 @@ def test_kv_commit_argument_errors(lib):
 def test_ragged_argument_errors(lib):
     a = lib.eagle_tree_verify_attn_ragged
     # both per-sequence arrays NULL: the uniform call is the right one
-    assert a(FAKE, FAKE, FAKE, FAKE, None, None, 1, 4, 2, 1, 64, 16, 64, 0.1, FAKE, None, None, 0,
+    assert a(FAKE, FAKE, FAKE, FAKE, None, None, 1, 4, 2, 1, 64, 16, 64, 0.1, 0, FAKE, None, None, 0,
              None) == 1
     # layouts must hold the maxima
-    assert a(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 2, 1, 64, 16, 19, 0.1, FAKE, None, None, 0,
+    assert a(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 2, 1, 64, 16, 19, 0.1, 0, FAKE, None, None, 0,
              None) == 2
+    assert a(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 2, 1, 64, 16, 64, 0.1, 1, FAKE, None, None, 0,
+             None) == 3
     g = lib.eagle_accept_greedy_ragged
     assert g(FAKE, FAKE, FAKE, None, 1, 5, 4, FAKE, FAKE, FAKE, None) == 1
     assert g(FAKE, FAKE, FAKE, FAKE, 1, 65, 4, FAKE, FAKE, FAKE, None) == 3
     s = lib.eagle_accept_spec_ragged
-    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, None, 1, 5, 8, 3, 0, FAKE, FAKE, FAKE, FAKE,
-             1 << 20, None) == 1
-    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, 1, 5, 8, 3, 7, FAKE, FAKE, FAKE, FAKE,
-             1 << 20, None) == 2
+    # tokens, parents, tree_len, B, N, V, max_depth, target_logits, target_lse, draft_logits,
+    # draft_lse, draft_row, draft_rows, u_accept, u_sample, mode, outputs, workspace
+    assert s(FAKE, FAKE, None, 1, 5, 8, 3, FAKE, None, FAKE, None, FAKE, 4, FAKE, FAKE, 0, FAKE,
+             FAKE, FAKE, FAKE, 1 << 20, None) == 1
+    assert s(FAKE, FAKE, FAKE, 1, 5, 8, 3, FAKE, None, FAKE, None, FAKE, 4, FAKE, FAKE, 7, FAKE,
+             FAKE, FAKE, FAKE, 1 << 20, None) == 2
 
 
 def test_paged_argument_errors(lib):
     a = lib.eagle_tree_verify_attn_paged
 
     def pg(ps=16, max_pages=8, nblk=100, P=100, N=10, k=FAKE):
-        return a(FAKE, k, FAKE, FAKE, FAKE, 1, N, 2, 1, 64, P, ps, max_pages, nblk, 0.1, FAKE, None,
-                 FAKE, 1 << 30, None)
+        return a(FAKE, k, FAKE, FAKE, FAKE, 1, N, 2, 1, 64, P, ps, max_pages, nblk, 0.1, 0, FAKE,
+                 None, FAKE, 1 << 30, None)
 
     assert pg(k=None) == 1
     assert pg(ps=24) == 3                  # not a power of two

@@ -96,8 +96,9 @@ def test_ragged_greedy(gpu_lib):
         assert list(o[b]) == list(out) + [-1] * (maxd + 1 - len(out))
 
 
+@pytest.mark.parametrize("with_lse", [False, True])
 @pytest.mark.parametrize("mode", ["sampled", "point_mass"])
-def test_ragged_spec(gpu_lib, mode):
+def test_ragged_spec(gpu_lib, mode, with_lse):
     B, Nmax, V, R_per, maxd = 8, 24, 700, 5, 64
     parents = synth.random_parents(B, Nmax, 0, 780, 1)
     tl = synth.normal_f32((B, Nmax, V), 1.0, 0, 780, 2)
@@ -111,9 +112,15 @@ def test_ragged_spec(gpu_lib, mode):
     for b in range(B):
         for v in sorted(set(parents[b, 1:].tolist())):
             draft_row[b, v] = rowpick[b, v]
+    tlse = dlse = None
+    if with_lse:   # the rows' normalisers as a caller hands them over: fp32, from the CPU
+        from scipy.special import logsumexp
+        tlse = logsumexp(tl.astype(np.float64), axis=-1).astype(np.float32)
+        dlse = logsumexp(dl.astype(np.float64), axis=-1).astype(np.float32)
     a, p, o = gpu_lib.eagle_accept_spec(to_dev(tokens), to_dev(parents), to_dev(draft_row), to_dev(tl),
                                         to_dev(dl), to_dev(ua), to_dev(us), maxd, tree_len=to_dev(N_arr),
-                                        mode=mode)
+                                        mode=mode, target_lse=None if tlse is None else to_dev(tlse),
+                                        draft_lse=None if dlse is None else to_dev(dlse))
     torch.cuda.synchronize()
     a, p, o = a.cpu().numpy(), p.cpu().numpy(), o.cpu().numpy()
     checked = 0
@@ -122,7 +129,9 @@ def test_ragged_spec(gpu_lib, mode):
         trace = []
         alpha, path, out = oracle.accept_spec(tokens[b][:n], parents[b][:n], tl[b][:n], dl[b],
                                               draft_row[b][:n], ua[b][:n], us[b][:n], maxd, trace=trace,
-                                              mode=mode)
+                                              mode=mode,
+                                              target_lse=None if tlse is None else tlse[b][:n],
+                                              draft_lse=None if dlse is None else dlse[b])
         margins = [abs(float(ua[b, kid]) - r) for (_, kids, ratios, _) in trace
                    for kid, r in zip(kids, ratios)]
         if margins and min(margins) <= 1e-6:

@@ -86,3 +86,21 @@ def test_rerank_constant_rows_take_lowest_tokens(gpu_lib):
     logits[1, 1:, 4096:] = 7.0     # a constant tail across chunks in sequence 1
     roots = np.array([1, 2], np.int32)
     _compare(_gpu(gpu_lib, logits, roots, k, depth, n), logits, roots, k, depth, n)
+
+
+def test_rerank_signed_zeros_tie(gpu_lib):
+    """Rows whose top-k cut falls among logits of +0.0 and -0.0 (equal values): the two
+    zeros rank as one value, so the lower token ids win whatever the sign, on both
+    sides; across vocabulary chunks too.  Depth 2 takes the zero ties into the frontier
+    rows as well; 16 nodes = the root, the 6 depth-1 nodes and the 9 depth-2 children
+    of the three clear winners, a cut 2.0 clear of the next candidates."""
+    V, k, depth, n = 9000, 6, 2, 16
+    R = 1 + (depth - 1) * k
+    base = synth.normal_f32((2, R, V), 1.0, 0, 780, 6)
+    logits = np.where(base > 0, -np.abs(base) - 1.0, 0.0).astype(np.float32)   # <= 0 everywhere
+    sign = synth.uniform_f32((2, R, V), 0, 780, 7) < 0.5
+    logits = np.where((logits == 0.0) & sign, np.float32(-0.0), logits).astype(np.float32)
+    logits[:, :, [7, 4100, 8999]] = 2.0          # three clear winners, then the zero ties
+    assert np.signbit(logits[logits == 0.0]).any() and (~np.signbit(logits[logits == 0.0])).any()
+    roots = np.array([5, 6], np.int32)
+    _compare(_gpu(gpu_lib, logits, roots, k, depth, n), logits, roots, k, depth, n)
