@@ -160,6 +160,26 @@ eagle_status_t eagle_lm_head_argmax(const void* hidden, const void* weight, int3
                                     hipStream_t stream);
 
 /*
+ * eagle_lm_head_argmax without allocation, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * it).  Same arguments and results as eagle_lm_head_argmax minus the workspace: the
+ * scratch (the per-vocabulary-tile row partials) lives in a static device array of
+ * EAGLE_LM_HEAD_NOALLOC_SCRATCH_BYTES inside the library, one copy per GPU, held until
+ * the process ends; its address on a device is looked up on the first call made with
+ * that device current.  Sizes whose eagle_lm_head_workspace(M, H, V) exceeds the array
+ * return EAGLE_ERR_UNSUPPORTED (at V = 128256 that is M > 1046).  The call allocates
+ * nothing.  Every call on one GPU uses the same array: calls that overlap on a GPU (two
+ * streams, or two host threads) race and their results are undefined; calls ordered
+ * on one stream are safe (nothing in the array needs clearing between them).
+ */
+#define EAGLE_LM_HEAD_NOALLOC_SCRATCH_BYTES (8 << 20)
+eagle_status_t eagle_lm_head_argmax_noalloc(const void* hidden, const void* weight, int32_t M,
+                                            int32_t H, int32_t V, eagle_dtype_t dtype,
+                                            float* out_max, int32_t* out_argmax, float* out_lse,
+                                            float* out_second, float* out_logits,
+                                            hipStream_t stream);
+
+/*
  * Greedy acceptance.  [P1] greedy decoding paragraph and the figure paragraph
  * after it; [P2] speculative sampling paragraph.  Node i (i > 0) survives when it
  * and every node above it matches: tokens[i] == target_argmax[parents[i]] and its

@@ -46,6 +46,7 @@ _SIGNATURES = {
                                                                     _vp], ctypes.c_int),
     "eagle_lm_head_workspace": ([_i32] * 3, _sz),
     "eagle_lm_head_argmax": ([_vp, _vp, _i32, _i32, _i32, _i32] + [_vp] * 6 + [_sz, _vp], ctypes.c_int),
+    "eagle_lm_head_argmax_noalloc": ([_vp, _vp, _i32, _i32, _i32, _i32] + [_vp] * 6, ctypes.c_int),
     "eagle_accept_greedy": ([_vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp], ctypes.c_int),
     "eagle_kv_commit": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp],
                         ctypes.c_int),

@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 
 #include "../../include/eagle_mi355.h"
 #include "internal.h"
@@ -243,6 +244,68 @@ eagle_status_t eagle_lm_head_argmax(const void* hidden, const void* weight, int3
   return hip_status(eagle::launch_lm_head(pl, hidden, weight, out_max, out_argmax, out_lse,
                                           out_second, out_logits, workspace, stream),
                     "eagle_lm_head_argmax launch");
+}
+
+// ---------------------------------------------------------------- LM head without allocation
+// The scratch of eagle_lm_head_argmax_noalloc: a file-scope device array, one copy per
+// GPU, held until the process ends.  Host code never uses its name as an address: the
+// device address of each GPU's copy comes from hipGetSymbolAddress, once per device
+// (with that device current), and is kept here.
+}  // extern "C"
+
+static __device__ __align__(256) unsigned char scratch[EAGLE_LM_HEAD_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// this device's address of `scratch` (looked up on the device's first call)
+eagle_status_t scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(EAGLE_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(EAGLE_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return EAGLE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+eagle_status_t eagle_lm_head_argmax_noalloc(const void* hidden, const void* weight, int32_t M,
+                                            int32_t H, int32_t V, eagle_dtype_t dtype,
+                                            float* out_max, int32_t* out_argmax, float* out_lse,
+                                            float* out_second, float* out_logits,
+                                            hipStream_t stream) {
+  if (!hidden || !weight || !out_max || !out_argmax || !out_lse)
+    return fail(EAGLE_ERR_NULL, "hidden, weight, out_max, out_argmax and out_lse must be non-NULL");
+  eagle_status_t st = check_dtype(dtype);
+  if (st != EAGLE_OK) return st;
+  st = check_lm_dims(M, H, V);
+  if (st != EAGLE_OK) return st;
+  if (!aligned16(hidden) || !aligned16(weight) || (out_logits && !aligned16(out_logits)))
+    return fail(EAGLE_ERR_INVALID_ARG, "hidden, weight and out_logits must be 16-byte aligned");
+  const eagle::LmPlan pl = eagle::plan_lm_head(M, H, V);
+  const size_t need = eagle::lm_head_workspace_bytes(pl);
+  if (need > (size_t)EAGLE_LM_HEAD_NOALLOC_SCRATCH_BYTES)
+    return fail(EAGLE_ERR_UNSUPPORTED,
+                "M=%d, V=%d need %zu bytes of scratch, more than the %d bytes of the static "
+                "scratch (use eagle_lm_head_argmax with a workspace)",
+                M, V, need, EAGLE_LM_HEAD_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  st = scratch_on_current_device(&ws);
+  if (st != EAGLE_OK) return st;
+  return hip_status(eagle::launch_lm_head(pl, hidden, weight, out_max, out_argmax, out_lse,
+                                          out_second, out_logits, ws, stream),
+                    "eagle_lm_head_argmax_noalloc launch");
 }
 
 // ---------------------------------------------------------------- acceptance
