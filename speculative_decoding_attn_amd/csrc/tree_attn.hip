@@ -39,6 +39,9 @@ namespace {
 
 constexpr int KC = 32;            // keys per chunk
 constexpr float kLazy = 8.0f;     // log2 headroom before the running max is raised
+constexpr float kSumLimit = 256.0f;   // 2^kLazy: a chunk's weight sum at or below it keeps the max
+// (1, 1) in bf16: a dot product with it sums a packed pair
+constexpr bf16x2 kOnesBf16x2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 template <int D>
 struct AttnLds {
@@ -661,41 +664,54 @@ tree_attn_pingpong(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
           sv[t][r] = ((allowed >> bit) & 1ull) ? sv[t][r] : -INFINITY;
         }
     }
-    float mx = sv[0][0];
+    // Exponentials against the running max as it stands (no max of this chunk first):
+    // the chunk's sum of the bf16 weights, taken with dot products against (1, 1),
+    // bounds every weight, so a chunk whose sum stays at or below 2^kLazy has no
+    // weight above it and is kept.  Otherwise (or while the row has no max yet) the
+    // wave takes the exact chunk max, raises the running max to it where it is higher
+    // (rescaling O and the sum), and recomputes the weights.  The row sum is the sum of
+    // the same bf16 weights that multiply V.
+    float csum = 0.f;
+    auto weigh = [&]() {
+      const float mcu = (mc == -INFINITY) ? 0.f : mc;
+      float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int cc = 0; cc < 4; ++cc) {
+        u32x4 pk;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv[t][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mxc = mx * c;
-    const bool need = mxc > mc + kLazy;
-    if (__ballot(need)) {
-      const float mnew = need ? mxc : mc;
-      const float alpha = need ? exp2f(mc - mnew) : 1.f;
-      lsum *= alpha;
-#pragma unroll
-      for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      mc = mnew;
-    }
-    const float mcu = (mc == -INFINITY) ? 0.f : mc;
-    float pr[2][16];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        pr[t][r] = __builtin_amdgcn_exp2f(fmaf(sv[t][r], c, -mcu));
-        lsum += pr[t][r];
+        for (int e = 0; e < 4; ++e) {
+          const int t = cc >> 1, r = 8 * (cc & 1) + 2 * e;
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[t][r], c, -mcu));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[t][r + 1], c, -mcu));
+          pk[e] = pack_bf16x2(p0, p1);
+          part[e] += p0 + p1;
+        }
+        pf[cc] = as_bf16x8(pk);
       }
+      csum = (part[0] + part[1]) + (part[2] + part[3]);
+    };
+    weigh();
+    const bool need = (mc == -INFINITY) || !(csum <= kSumLimit);
+    if (__ballot(need)) {
+      float mx = sv[0][0];
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      u32x4 pk;
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        pk[e] = pack_bf16x2(pr[cc >> 1][8 * (cc & 1) + 2 * e], pr[cc >> 1][8 * (cc & 1) + 2 * e + 1]);
-      pf[cc] = as_bf16x8(pk);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv[t][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));   // both lanes of a row take the same max
+      const float mxc = mx * c;
+      if (mxc > mc) {
+        const float alpha = exp2f(mc - mxc);
+        lsum *= alpha;
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        mc = mxc;
+      }
+      weigh();
     }
+    lsum += csum;
   };
 
   // ---- prologue: chunks 0..2 in flight, 0 and 1 landed; scores and P of chunk 0
