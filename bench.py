@@ -827,6 +827,8 @@ def main(argv=None):
                          "ragged, paged and draft-expansion measurements")
     ap.add_argument("--only-draft", action="store_true",
                     help="only the C5-shaped draft expansion (eagle_draft_expand)")
+    ap.add_argument("--only-ragged", action="store_true",
+                    help="only the ragged C5 step (attention, LM head, greedy acceptance)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--summarize-profiles", metavar="DIR",
@@ -854,6 +856,10 @@ def main(argv=None):
         return 0
     if args.only_draft:
         print(json.dumps({"draft_expand_C5": draft_expansion(torch, sda, dev, "C5")}))
+        return 0
+    if args.only_ragged:
+        x = make_inputs(synth.CONFIGS["C5"], torch, dev)
+        print(json.dumps({"ragged_C5": ragged_step(torch, sda, dev, x)}))
         return 0
 
     cfg = synth.CONFIGS["C5"]

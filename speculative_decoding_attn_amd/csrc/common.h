@@ -64,6 +64,12 @@ __device__ __forceinline__ double wave_sum_d(double x) {
   return x;
 }
 
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
 __device__ __forceinline__ int wave_min_i(int x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x = min(x, __shfl_xor(x, o));

@@ -35,6 +35,11 @@ struct AttnPlan {
   // query subset (nq > 0): only nodes node0 .. node0+nq-1 of the N-node tree are
   // computed (the draft expansion's newest rows); masks and keys cover the whole tree
   int node0, nq;
+  // ragged batches with split keys (device memory in the workspace, filled by a plan
+  // kernel from prefix_len): [0] split length, [1] number of (sequence, split) items,
+  // [2, 2+B) first item of each sequence, [2+B, 2+2B) its number of splits,
+  // [2+2B, 2+2B+B*S) the sequence of each item.  Null otherwise.
+  int* dplan;
 };
 
 // paged KV: a split's slice of the block table is staged in LDS

@@ -57,6 +57,98 @@ __device__ __forceinline__ int vt_pos(int key) {
   return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
 }
 
+// The (sequence, KV head, row block, key split) a workgroup computes.  Uniform batches:
+// every (sequence, KV head) pair is cut into pl.S splits of pl.split_len keys.  Ragged
+// batches with a device plan: sequence b is cut into its own number of splits of one
+// common length, chosen on the device from the real prefix lengths (tree_attn_plan),
+// and blocks past the plan's items have nothing to do.  `slot` indexes the split
+// partials: uniform pair * S + split, planned item * Hkv + KV head.
+struct AttnItem {
+  bool valid;
+  int b, g, rb, split, nsplit, len, slot;
+};
+
+__device__ __forceinline__ AttnItem attn_item(const AttnPlan& pl, int logical) {
+  AttnItem it;
+  it.rb = logical % pl.RB;
+  if (!pl.dplan) {
+    it.split = (logical / pl.RB) % pl.S;
+    const int pair = logical / (pl.RB * pl.S);
+    it.b = pair / pl.Hkv;
+    it.g = pair % pl.Hkv;
+    it.nsplit = pl.S;
+    it.len = pl.split_len;
+    it.slot = pair * pl.S + it.split;
+    it.valid = true;
+    return it;
+  }
+  it.g = (logical / pl.RB) % pl.Hkv;
+  const int t = logical / (pl.RB * pl.Hkv);
+  it.valid = t < pl.dplan[1];
+  const int tt = it.valid ? t : 0;
+  it.b = min(max(pl.dplan[2 + 2 * pl.B + tt], 0), pl.B - 1);
+  it.split = tt - pl.dplan[2 + it.b];
+  it.nsplit = pl.dplan[2 + pl.B + it.b];
+  it.len = pl.dplan[0];
+  it.slot = tt * pl.Hkv + it.g;
+  return it;
+}
+
+// Partial slot of split s of (sequence b, KV head g) (see attn_item).
+__device__ __forceinline__ int attn_slot(const AttnPlan& pl, int b, int g, int s) {
+  return pl.dplan ? (pl.dplan[2 + b] + s) * pl.Hkv + g : (b * pl.Hkv + g) * pl.S + s;
+}
+__device__ __forceinline__ int attn_nsplit(const AttnPlan& pl, int b) {
+  return pl.dplan ? pl.dplan[2 + pl.B + b] : pl.S;
+}
+
+// Ragged batches: choose the split length from the real prefix lengths so that the
+// (sequence, split) items, each sequence cut into ceil(prefix / length) splits (at
+// least one, its tree keys), number at most the B * S items of the uniform plan: the
+// smallest multiple of 32 keys (and at least kMinSplitKeys) that does so.  One
+// workgroup; thread 0 then lays out the item table.
+__global__ void __launch_bounds__(256) tree_attn_plan(AttnPlan pl, int* __restrict__ dplan) {
+  __shared__ int best;
+  const int B = pl.B, cap = pl.B * pl.S;
+  // lengths in whole 32-key chunks, as in the uniform plan: with every prefix at the
+  // maximum the smallest feasible length is the uniform plan's split length (the same
+  // splits).  Each thread tries its own candidates in increasing order, all at once.
+  const int lo = kMinSplitKeys / KC, hi = max(lo, (pl.P + KC - 1) / KC);   // hi: B items
+  if (threadIdx.x == 0) best = hi;
+  __syncthreads();
+  int mine = hi;
+  for (int u = lo + (int)threadIdx.x; u < hi; u += 256) {
+    const int len = u * KC;
+    int c = 0;
+    for (int b = 0; b < B && c <= cap; ++b) {
+      const int P = min(max(pl.prefix_len[b], 0), pl.P);
+      c += max(1, (P + len - 1) / len);
+    }
+    if (c <= cap) {
+      mine = u;
+      break;
+    }
+  }
+  mine = wave_min_i(mine);
+  if ((threadIdx.x & 63) == 0) atomicMin(&best, mine);
+  __syncthreads();
+  const int lo_best = best;
+  if (threadIdx.x == 0) {
+    const int len = lo_best * KC;
+    int t = 0;
+    for (int b = 0; b < B; ++b) {
+      const int P = min(max(pl.prefix_len[b], 0), pl.P);
+      const int nb = min(max(1, (P + len - 1) / len), cap - t - (B - 1 - b));
+      dplan[2 + b] = t;
+      dplan[2 + B + b] = nb;
+      for (int s = 0; s < nb; ++s) dplan[2 + 2 * B + t + s] = b;
+      t += nb;
+    }
+    dplan[0] = len;
+    dplan[1] = t;
+  }
+}
+
 template <int D, int WAVES, bool PAGED>
 __global__ void __launch_bounds__(WAVES * 64, 1)
 tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -91,11 +183,13 @@ tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int nwg = gridDim.x;
   const int w = blockIdx.x;
   const int logical = (nwg % 8 == 0) ? (w % 8) * (nwg / 8) + (w / 8) : w;
-  const int rb = logical % pl.RB;
-  const int split = (logical / pl.RB) % pl.S;
-  const int pair = logical / (pl.RB * pl.S);
-  const int b = pair / pl.Hkv;
-  const int g = pair % pl.Hkv;
+  const AttnItem item = attn_item(pl, logical);
+  if (!item.valid) return;   // a planned ragged batch with fewer items than blocks
+  const int rb = item.rb;
+  const int split = item.split;
+  const int b = item.b;
+  const int g = item.g;
+  const int pair = b * pl.Hkv + g;
   const int G = pl.G;
   // this sequence's prefix and tree (ragged batches: clamped to the plan's maxima,
   // so every access stays inside the layouts the plan was sized for)
@@ -105,8 +199,8 @@ tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int R = (pl.nq > 0 ? pl.nq : N) * G;
   // split s covers prefix keys [s*len, (s+1)*len) below P (possibly none); the last
   // split also takes the tree keys P .. P+N-1
-  const int key_begin = (split == pl.S - 1) ? min(split * pl.split_len, P) : split * pl.split_len;
-  const int key_end = (split == pl.S - 1) ? P + N : min(P, (split + 1) * pl.split_len);
+  const int key_begin = (split == item.nsplit - 1) ? min(split * item.len, P) : split * item.len;
+  const int key_end = (split == item.nsplit - 1) ? P + N : min(P, (split + 1) * item.len);
   const int key_lim = P + N;
 
   const uint16_t* kbase = PAGED ? k : k + (size_t)pair * pl.kv_cap * D;
@@ -261,7 +355,7 @@ tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         const int off = kb - P;   // >= -31
         // only the last split owns the tree keys: in a ragged batch an earlier split
         // can end inside a chunk at this sequence's prefix end
-        const uint64_t tm = (split == pl.S - 1) ? (anc & node_mask) : 0ull;
+        const uint64_t tm = (split == item.nsplit - 1) ? (anc & node_mask) : 0ull;
         const uint32_t tree_bits = off >= 0 ? (off < 64 ? (uint32_t)(tm >> off) : 0u)
                                             : (uint32_t)(tm << (-off));
         const uint32_t prefix_bits = off < 0 ? ((1u << (-off)) - 1u) : 0u;
@@ -330,7 +424,7 @@ tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int il = r_row / G;
   const int i = pl.node0 + il;
   const int h = g * G + (r_row - il * G);
-  if (pl.S == 1) {
+  if (pl.S == 1 && !pl.dplan) {
     uint16_t* op = out + ((size_t)(b * pl.N + i) * pl.Hq + h) * D;
 #pragma unroll
     for (int db = 0; db < DBLK; ++db)
@@ -344,7 +438,7 @@ tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       }
     if (half == 0 && lse_out) lse_out[(size_t)(b * pl.N + i) * pl.Hq + h] = lse;
   } else {
-    const size_t prow = ((size_t)pair * pl.S + split) * pl.Rpad + r_row;
+    const size_t prow = (size_t)item.slot * pl.Rpad + r_row;
     float* op = part_o + prow * D;
 #pragma unroll
     for (int db = 0; db < DBLK; ++db)
@@ -375,13 +469,13 @@ tree_attn_merge_hw(AttnPlan pl, const float* __restrict__ part_o, const float* _
   const int b = pair / pl.Hkv;
   const int g = pair % pl.Hkv;
   if (pl.tree_len && r >= min(max(pl.tree_len[b], 1), pl.N) * pl.G) return;   // past this tree
-  const size_t base = (size_t)pair * pl.S * pl.Rpad + r;
+  const int ns = attn_nsplit(pl, b);
   float mx = -INFINITY;
-  for (int s = 0; s < pl.S; ++s) mx = fmaxf(mx, part_lse[base + (size_t)s * pl.Rpad]);
+  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, part_lse[(size_t)attn_slot(pl, b, g, s) * pl.Rpad + r]);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
-  for (int s = 0; s < pl.S; ++s) {
-    const size_t prow = base + (size_t)s * pl.Rpad;
+  for (int s = 0; s < ns; ++s) {
+    const size_t prow = (size_t)attn_slot(pl, b, g, s) * pl.Rpad + r;
     const float wgt = expf(part_lse[prow] - mx);
     wsum += wgt;
     const f32x4 o = *(const f32x4*)(part_o + prow * D + lane * 4);
@@ -414,15 +508,15 @@ tree_attn_merge(AttnPlan pl, const float* __restrict__ part_o, const float* __re
   const int b = pair / pl.Hkv;
   const int g = pair % pl.Hkv;
   if (pl.tree_len && r >= min(max(pl.tree_len[b], 1), pl.N) * pl.G) return;   // past this tree
-  const size_t base = (size_t)pair * pl.S * pl.Rpad + r;
+  const int ns = attn_nsplit(pl, b);
   float mx = -INFINITY;
-  for (int s = 0; s < pl.S; ++s) mx = fmaxf(mx, part_lse[base + (size_t)s * pl.Rpad]);
+  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, part_lse[(size_t)attn_slot(pl, b, g, s) * pl.Rpad + r]);
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
   float wsum = 0.f;
-  for (int s = 0; s < pl.S; ++s) {
-    const size_t prow = base + (size_t)s * pl.Rpad;
+  for (int s = 0; s < ns; ++s) {
+    const size_t prow = (size_t)attn_slot(pl, b, g, s) * pl.Rpad + r;
     const float wgt = expf(part_lse[prow] - mx);
     wsum += wgt;
     const float* op = part_o + prow * D + lane * PER;
@@ -500,18 +594,20 @@ tree_attn_pingpong(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   const int nwg = gridDim.x;
   const int w = blockIdx.x;
   const int logical = (nwg % 8 == 0) ? (w % 8) * (nwg / 8) + (w / 8) : w;
-  const int rb = logical % pl.RB;
-  const int split = (logical / pl.RB) % pl.S;
-  const int pair = logical / (pl.RB * pl.S);
-  const int b = pair / pl.Hkv;
-  const int g = pair % pl.Hkv;
+  const AttnItem item = attn_item(pl, logical);
+  if (!item.valid) return;   // a planned ragged batch with fewer items than blocks
+  const int rb = item.rb;
+  const int split = item.split;
+  const int b = item.b;
+  const int g = item.g;
+  const int pair = b * pl.Hkv + g;
   const int G = pl.G;
   const int P = pl.prefix_len ? min(max(pl.prefix_len[b], 0), pl.P) : pl.P;
   const int N = pl.tree_len ? min(max(pl.tree_len[b], 1), pl.N) : pl.N;
   const int R = (pl.nq > 0 ? pl.nq : N) * G;   // query rows (all nodes, or the subset)
-  const bool last = split == pl.S - 1;
-  const int key_begin = last ? min(split * pl.split_len, P) : split * pl.split_len;
-  const int key_end = last ? P + N : min(P, (split + 1) * pl.split_len);
+  const bool last = split == item.nsplit - 1;
+  const int key_begin = last ? min(split * item.len, P) : split * item.len;
+  const int key_end = last ? P + N : min(P, (split + 1) * item.len);
   const int key_lim = P + N;
   // keys at or past mask_from are masked: the tree part of the last split, and the
   // tail of a chunk that runs past the end of an earlier split
@@ -767,7 +863,7 @@ tree_attn_pingpong(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   const int il = r_row / G;
   const int i = pl.node0 + il;
   const int h = g * G + (r_row - il * G);
-  if (pl.S == 1) {
+  if (pl.S == 1 && !pl.dplan) {
     uint16_t* op = out + ((size_t)(b * pl.N + i) * pl.Hq + h) * D;
 #pragma unroll
     for (int db = 0; db < DBLK; ++db)
@@ -781,7 +877,7 @@ tree_attn_pingpong(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       }
     if (half == 0 && lse_out) lse_out[(size_t)(b * pl.N + i) * pl.Hq + h] = lse;
   } else {
-    const size_t prow = ((size_t)pair * pl.S + split) * pl.Rpad + r_row;
+    const size_t prow = (size_t)item.slot * pl.Rpad + r_row;
     float* op = part_o + prow * D;
 #pragma unroll
     for (int db = 0; db < DBLK; ++db)
@@ -913,10 +1009,15 @@ AttnPlan plan_tree_attn_paged(int B, int N, int Hq, int Hkv, int D, int P, int p
   return pl;
 }
 
+// split partials (fp32 O rows and lse) and, after them, the ragged batches' item table
+static size_t plan_table_offset(const AttnPlan& pl) {
+  const size_t rows = (size_t)pl.B * pl.Hkv * pl.S * pl.Rpad;
+  return (rows * (size_t)pl.D * sizeof(float) + rows * sizeof(float) + 255) / 256 * 256;
+}
+
 size_t tree_attn_workspace_bytes(const AttnPlan& pl) {
   if (pl.S <= 1) return 0;
-  const size_t rows = (size_t)pl.B * pl.Hkv * pl.S * pl.Rpad;
-  return rows * (size_t)pl.D * sizeof(float) + rows * sizeof(float) + 256;
+  return plan_table_offset(pl) + (size_t)(2 + 2 * pl.B + pl.B * pl.S) * sizeof(int) + 256;
 }
 
 hipError_t launch_tree_attn(const AttnPlan& pl0, float scale, const void* q, const void* k,
@@ -930,6 +1031,13 @@ hipError_t launch_tree_attn(const AttnPlan& pl0, float scale, const void* q, con
     const size_t rows = (size_t)pl.B * pl.Hkv * pl.S * pl.Rpad;
     part_o = (float*)workspace;
     part_lse = part_o + rows * pl.D;
+    // ragged prefixes: split lengths from the real prefix lengths (device plan)
+    if (pl.prefix_len && !pl.block_table && pl.nq == 0) {
+      pl.dplan = (int*)((char*)workspace + plan_table_offset(pl));
+      hipLaunchKernelGGL(tree_attn_plan, dim3(1), dim3(256), 0, stream, pl, pl.dplan);
+      const hipError_t e0 = hipGetLastError();
+      if (e0 != hipSuccess) return e0;
+    }
   }
   const hipError_t e =
       pl.D == 128 ? launch_fwd_d<128>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream)
