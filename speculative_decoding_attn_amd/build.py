@@ -22,6 +22,10 @@ LIB = os.path.join(PKG, "libeagle_mi355.so")
 SOURCES = ["api.hip", "tree_attn.hip", "lm_head.hip", "accept.hip", "rerank.hip", "kv_commit.hip",
            "draft.hip", "calib.hip"]
 ARCH = "gfx950"
+# Per-source options.  Tree attention: MFMA results in VGPRs (the four-wave kernel's
+# vector work reads its scores and rescales its output in place; with accumulators in
+# AGPRs the register allocator spills the loop state).
+EXTRA = {"tree_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc() -> str:
@@ -43,7 +47,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
 
     def compile_one(src: str) -> str:
         obj = os.path.join(OBJDIR, src.replace(".hip", ".o"))
-        cmd = [hipcc, *flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc, *flags(), *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if verbose or r.returncode:
             out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()

@@ -5,6 +5,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace eagle {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -80,6 +83,18 @@ __device__ __forceinline__ int wave_max_i(int x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x = max(x, __shfl_xor(x, o));
   return x;
+}
+
+// f(std::integral_constant<int, 0>{}), ..., f(std::integral_constant<int, N-1>{}):
+// a loop whose index is a compile-time constant in every iteration (register arrays
+// indexed with it stay in registers, whatever the size of the body).
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // Waits until at most N vector-memory operations of this wave are outstanding

@@ -6,7 +6,7 @@
 //
 // Work decomposition.  For one (sequence b, KV head g) pair the R = N*G query rows
 // (row r = node r/G, head g*G + r%G) share every K/V row, so a workgroup takes a
-// block of WAVES*64 rows of one pair and one contiguous range of keys ("split"):
+// block of WAVES*32 rows of one pair and one contiguous range of keys ("split"):
 // K and V tiles of 32 keys are staged once in LDS and read by all of its waves.
 // Each wave owns 32 rows (one 32-row MFMA tile).
 //
@@ -21,10 +21,11 @@
 // Mask.  The ancestor-or-self set of each lane's node is a 64-bit mask in
 // registers; only the key chunks that reach past the prefix are masked.
 //
-// Softmax.  Online max/sum in base 2 with scale*log2(e) folded into one FMA.  The
-// running max is only raised when a chunk exceeds it by more than 2^8 (values then
-// stay below 256), so O is rescaled rarely; the branch is taken per wave when any
-// lane needs it.
+// Softmax.  Base 2 with scale*log2(e) folded into one FMA.  The general kernel keeps
+// an online max that is only raised when a chunk exceeds it by more than 2^8
+// (values then stay below 256), so O is rescaled rarely; the branch is taken per
+// wave when any lane needs it.  The D = 128 eight-wave kernel takes every weight of
+// a split against one reference max per row (its section below).
 //
 // Splits.  The prefix is cut into S ranges of whole 32-key chunks; the last range
 // also covers the tree keys.  With S > 1 every workgroup writes its normalised
@@ -39,9 +40,6 @@ namespace {
 
 constexpr int KC = 32;            // keys per chunk
 constexpr float kLazy = 8.0f;     // log2 headroom before the running max is raised
-constexpr float kSumLimit = 256.0f;   // 2^kLazy: a chunk's weight sum at or below it keeps the max
-// (1, 1) in bf16: a dot product with it sums a packed pair
-constexpr bf16x2 kOnesBf16x2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 template <int D>
 struct AttnLds {
@@ -541,53 +539,68 @@ tree_attn_merge(AttnPlan pl, const float* __restrict__ part_o, const float* __re
 }
 
 // ---------------------------------------------------------------------------
-// D = 128 with eight waves: the two halves of the workgroup in ping-pong.
+// D = 128: eight waves of 32 query rows (two per SIMD), one 256-row block per
+// workgroup, each wave running its own software pipeline over the split.
 //
-// Each wave owns 32 query rows and walks the split in chunks of 64 keys.  Per chunk
-// a wave has a matrix phase (the scores of the next chunk, S^T = K Q^T, and the
-// output update of this one, O^T += V^T P^T: 32 MFMAs) and a vector phase (mask,
-// online max and sum, exponentials and bf16 packing of those scores).  Waves 0-3
-// and 4-7 (one of each per SIMD) run these phases half a chunk apart, separated by
-// workgroup barriers, so on every SIMD one wave issues MFMAs while the other one
-// runs the exponentials.
+// Staging.  K and V reach LDS by global-to-LDS DMA (each lane moves 16 bytes to
+// m0 + 16*lane, non-temporal: the cache streams them through once), in chunks of 32
+// keys, eight stages deep, one workgroup barrier per chunk.  Rows are stored whole
+// (256 bytes) with their 16-byte pieces permuted: K piece c of row r sits at
+// c ^ (r & 15), which makes the b128 fragment reads of 16 consecutive rows hit every
+// bank once; V piece c of row r sits at c ^ 4*(r & 3), which does the same for the
+// transposing reads (ds_read_b64_tr_b16) that hand each lane 4 keys of one V column,
+// the V^T operand of the output MFMA, without a transpose in registers.  Past the end
+// of the split the DMA repeats the split's last row into a stage that is not read
+// again, so every iteration issues and waits alike.
 //
-// K and V chunks reach LDS by global-to-LDS DMA (each lane moves 16 bytes to
-// m0 + 16*lane, non-temporal: the cache streams through once), four chunks deep.  Rows are stored whole (256 bytes) with their
-// 16-byte pieces permuted: K piece c of row r sits at c ^ (r & 15), which makes the
-// b128 fragment reads of 16 consecutive rows hit every bank once; V piece c of row r
-// sits at c ^ 4*(r & 3), which does the same for the transposing reads
-// (ds_read_b64_tr_b16) that hand each lane 4 keys of one V column, the V^T operand
-// of the output MFMA, without a transpose in registers.
-constexpr int XC = 64;               // keys per chunk
-constexpr int XNB = 4;               // LDS stages
+// Reference max.  A row's weights are taken against one value for the whole split:
+// the exact max of the row's scores in the split's first chunk (every row sees a key
+// there: a prefix key, or the root of its tree).  Weights above 1 are exact in fp32
+// and bf16 alike, so nothing is rescaled along the way.  A row whose weights sum past
+// 2^64 (a later score far above the first chunk's) has the whole workgroup redo the
+// split: one walk for the exact row max (scores only), then the walk again with it,
+// where no weight exceeds 1.
+//
+// Pipeline of a wave, iteration j, in a fixed order with no branch:
+//   region 1, 8 MFMA slots: scores of chunk j+1 (S^T = K Q^T, slot s: K fragment s)
+//     and the weights of keys 16-31 of chunk j;
+//   region 2, 8 MFMA slots: output of chunk j (O^T += V^T P^T, slot s: V^T fragment
+//     s) and the weights of keys 0-15 of chunk j+1.
+// A weight pair goes through three steps (scale and shift, exponentials, bf16 pack
+// and row sum) in consecutive slots, so each slot holds independent vector
+// instructions beside its MFMA; the other wave of the SIMD fills the gaps.  LDS
+// fragments are read four ahead of their MFMAs.
 constexpr int XROW = 256;            // bytes per K or V row
-constexpr int XHALF = XC * XROW;     // one chunk of K (or of V): 16 KB
-constexpr int XSTAGE = 2 * XHALF;
-constexpr int XLDS = XNB * XSTAGE;   // 128 KB of dynamic LDS
+constexpr int WC = 32;               // keys per chunk
+constexpr int WNB = 8;               // LDS stages
+constexpr int WHALF = WC * XROW;     // one chunk of K (or of V): 8 KB
+constexpr int WSTAGE = 2 * WHALF;
+constexpr int WLDS = WNB * WSTAGE;   // 128 KB of dynamic LDS
+constexpr float kRowSumLimit = 18446744073709551616.0f;   // 2^64
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
-
 
 __device__ __forceinline__ v4i16 lds_read_tr(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p);
 }
 
 template <bool PAGED>
-__global__ void __launch_bounds__(512, 1)
-tree_attn_pingpong(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                   const uint16_t* __restrict__ v, const int32_t* __restrict__ parents,
-                   AttnPlan pl, uint16_t* __restrict__ out, float* __restrict__ lse_out,
-                   float* __restrict__ part_o, float* __restrict__ part_lse) {
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+tree_attn_d128(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+               const uint16_t* __restrict__ v, const int32_t* __restrict__ parents,
+               AttnPlan pl, uint16_t* __restrict__ out, float* __restrict__ lse_out,
+               float* __restrict__ part_o, float* __restrict__ part_lse) {
   constexpr int D = 128;
   constexpr int KSTEPS = D / 16;
   constexpr int DBLK = D / 32;
   extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
   __shared__ int32_t ptab[PAGED ? kMaxSplitPages : 1];
+  __shared__ int32_t spar[64];   // a tree has at most 64 nodes (64-bit masks)
+  __shared__ int32_t redo;       // some row's weights outgrew the reference max
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wv >> 2;
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
@@ -604,7 +617,7 @@ tree_attn_pingpong(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   const int G = pl.G;
   const int P = pl.prefix_len ? min(max(pl.prefix_len[b], 0), pl.P) : pl.P;
   const int N = pl.tree_len ? min(max(pl.tree_len[b], 1), pl.N) : pl.N;
-  const int R = (pl.nq > 0 ? pl.nq : N) * G;   // query rows (all nodes, or the subset)
+  const int R = (pl.nq > 0 ? pl.nq : N) * G;
   const bool last = split == item.nsplit - 1;
   const int key_begin = last ? min(split * item.len, P) : split * item.len;
   const int key_end = last ? P + N : min(P, (split + 1) * item.len);
@@ -612,10 +625,12 @@ tree_attn_pingpong(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   // keys at or past mask_from are masked: the tree part of the last split, and the
   // tail of a chunk that runs past the end of an earlier split
   const int mask_from = last ? P : key_end;
+  const int n = key_end > key_begin ? (key_end - key_begin + WC - 1) / WC : 0;
+  // last key any load of this split reads (the DMA past the end repeats it)
+  const int kmax = max(0, min(key_lim - 1, key_begin + n * WC - 1));
 
   const uint16_t* kbase = PAGED ? k : k + (size_t)pair * pl.kv_cap * D;
   const uint16_t* vbase = PAGED ? v : v + (size_t)pair * pl.kv_cap * D;
-  const int32_t* par = parents + (size_t)b * pl.N;
   const int first_page = PAGED ? (key_begin >> pl.page_shift) : 0;
   auto row_off = [&](int key) -> size_t {
     if constexpr (PAGED) {
@@ -627,239 +642,292 @@ tree_attn_pingpong(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     }
   };
 
-  // ---- Q^T operand and ancestor mask of this wave's 32 rows
-  const int r_row = rb * 256 + wv * 32 + l32;
-  bf16x8 qf[KSTEPS];
-  uint64_t anc;
-  if (r_row < R) {
-    const int il = r_row / G;
-    const int i = pl.node0 + il;
-    const int h = g * G + (r_row - il * G);
-    const uint16_t* qp = q + ((size_t)(b * pl.N + i) * pl.Hq + h) * D + 8 * half;
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) qf[s] = as_bf16x8(*(const u32x4*)(qp + 16 * s));
-    anc = ancestor_mask(par, i, N);
-  } else {
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) qf[s] = as_bf16x8(u32x4{0, 0, 0, 0});
-    anc = 1;
-  }
-  const uint64_t tmask = last ? (anc & (N >= 64 ? ~0ull : ((1ull << N) - 1ull))) : 0ull;
-
-  f32x16 oacc[DBLK];
-#pragma unroll
-  for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float mc = -INFINITY;   // running max of scale*log2e*s
-  float lsum = 0.f;       // this lane's half of the row sum
-  const float c = pl.c;
-
-  const int n = key_end > key_begin ? (key_end - key_begin + XC - 1) / XC : 0;
+  // the tree's parent links and (paged) this split's slice of the block table to LDS
+  if (tid < pl.N) spar[tid] = parents[(size_t)b * pl.N + tid];
   if constexpr (PAGED) {
-    const int lastkey = min(key_lim - 1, key_begin + n * XC - 1);
-    const int npages = min((lastkey >> pl.page_shift) - first_page + 1, kMaxSplitPages);
+    const int npages = min((kmax >> pl.page_shift) - first_page + 1, kMaxSplitPages);
     const int32_t* bt = pl.block_table + (size_t)b * pl.max_pages + first_page;
     for (int j = tid; j < npages; j += 512) ptab[j] = min(max(bt[j], 0), pl.num_blocks - 1);
-    __syncthreads();
   }
+  if (tid == 0) redo = 0;
+  __syncthreads();
 
   const uint32_t xbase = lds_addr(xs);
-  // chunk cidx -> LDS stage cidx % XNB; wave wv moves rows 8wv .. 8wv+7 of K and V,
-  // rows past the last key are clamped (their scores are masked)
+  // chunk cidx -> LDS stage cidx % WNB; wave wv moves rows 4wv .. 4wv+3 of K and V
   auto issue = [&](int cidx) {
-    const int kb = key_begin + cidx * XC;
-    const uint32_t st = xbase + (uint32_t)(cidx % XNB) * XSTAGE;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int row = 8 * wv + 4 * t + (lane >> 4);
-      const size_t off = row_off(min(kb + row, key_lim - 1));
-      const uint32_t dst = st + (uint32_t)(8 * wv + 4 * t) * XROW;
-      dma16_nt(kbase + off + 8 * ((lane & 15) ^ (row & 15)), dst);
-      dma16_nt(vbase + off + 8 * ((lane & 15) ^ (4 * (row & 3))), dst + XHALF);
-    }
+    const int kb = key_begin + cidx * WC;
+    const uint32_t st = xbase + (uint32_t)(cidx % WNB) * WSTAGE;
+    const int row = 4 * wv + (lane >> 4);
+    const size_t off = row_off(min(kb + row, kmax));
+    const uint32_t dst = st + (uint32_t)(4 * wv) * XROW;
+    dma16_nt(kbase + off + 8 * ((lane & 15) ^ (row & 15)), dst);
+    dma16_nt(vbase + off + 8 * ((lane & 15) ^ (4 * (row & 3))), dst + WHALF);
   };
-
-  f32x16 sacc[2];   // S^T of one chunk: keys 32t .. 32t+31 in tile t
-  bf16x8 pf[4];     // P^T of one chunk, 16 keys per operand
-  // Matrix phase of chunk cidx: O^T += V^T P^T for chunk cidx (16 MFMAs) and the scores
-  // of chunk cidx+1 (16 MFMAs).  The LDS operand of MFMA i is fetched LA MFMAs ahead
-  // (a ring of LA fragments, indexed with compile-time constants), and the scheduler
-  // is told to keep that order, so the reads of later MFMAs overlap the earlier ones.
-  auto matrix_phase = [&](int cidx) {
-    const uint8_t* Vs = xs + (cidx % XNB) * XSTAGE + XHALF;
-    const uint8_t* Ks = xs + ((cidx + 1) % XNB) * XSTAGE;
-    const int m = lane & 15;
-    const int vrow = 4 * half + (m >> 2);
-    const int vcol = 2 * ((lane >> 4) & 1) + ((m & 3) >> 1);
-    const uint8_t* vp = Vs + vrow * XROW + 8 * (m & 1);
-    const int vx = 4 * (m >> 2);
-    const uint8_t* kp = Ks + l32 * XROW;
-    const int kx = l32 & 15;
-    auto fetch = [&](int i) -> bf16x8 {
-      if (i < 16) {   // V^T operand of (cc, db)
-        const int cc = i >> 2, db = i & 3;
-        const uint8_t* p0 = vp + 16 * cc * XROW + 16 * ((4 * db + vcol) ^ vx);
-        const v4i16 both[2] = {lds_read_tr(p0), lds_read_tr(p0 + 8 * XROW)};
-        return __builtin_bit_cast(bf16x8, both);
-      }
-      const int s = (i - 16) >> 1, t = (i - 16) & 1;   // K operand of (s, t)
-      return *(const bf16x8*)(kp + 32 * t * XROW + 16 * ((2 * s + half) ^ kx));
-    };
-    constexpr int LA = 4;
-    bf16x8 ring[LA];
-#pragma unroll
-    for (int i = 0; i < LA; ++i) ring[i] = fetch(i);
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const bf16x8 a = ring[i % LA];
-      if (i + LA < 32) ring[i % LA] = fetch(i + LA);
-      if (i < 16) {
-        oacc[i & 3] = mfma32(a, pf[i >> 2], oacc[i & 3]);
-      } else {
-        const int s = (i - 16) >> 1, t = (i - 16) & 1;
-        sacc[t] = mfma32(a, qf[s], sacc[t]);
-      }
-    }
-    // LA operands' reads first, then per MFMA: the MFMA and the reads LA ahead
-    __builtin_amdgcn_sched_group_barrier(0x100, LA <= 16 ? 2 * LA : 32 + (LA - 16), 0);
-#pragma unroll
-    for (int i = 0; i < 16 - LA; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < LA; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-  };
-  auto softmax = [&](int cidx) {
-    const int kb = key_begin + cidx * XC;
-    float sv[2][16];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sv[t][r] = sacc[t][r];
-    if (kb + XC > mask_from) {
-      const int npre = mask_from - kb;   // < 64
-      uint64_t allowed = npre <= 0 ? 0ull : ((1ull << npre) - 1ull);
-      const int off = kb - P;
-      allowed |= off >= 0 ? (off < 64 ? tmask >> off : 0ull) : (-off < 64 ? tmask << (-off) : 0ull);
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int bit = 32 * t + 8 * (r >> 2) + 4 * half + (r & 3);
-          sv[t][r] = ((allowed >> bit) & 1ull) ? sv[t][r] : -INFINITY;
-        }
-    }
-    // Exponentials against the running max as it stands (no max of this chunk first):
-    // the chunk's sum of the bf16 weights, taken with dot products against (1, 1),
-    // bounds every weight, so a chunk whose sum stays at or below 2^kLazy has no
-    // weight above it and is kept.  Otherwise (or while the row has no max yet) the
-    // wave takes the exact chunk max, raises the running max to it where it is higher
-    // (rescaling O and the sum), and recomputes the weights.  The row sum is the sum of
-    // the same bf16 weights that multiply V.
-    float csum = 0.f;
-    auto weigh = [&]() {
-      const float mcu = (mc == -INFINITY) ? 0.f : mc;
-      float part[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        u32x4 pk;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = cc >> 1, r = 8 * (cc & 1) + 2 * e;
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[t][r], c, -mcu));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[t][r + 1], c, -mcu));
-          pk[e] = pack_bf16x2(p0, p1);
-          part[e] += p0 + p1;
-        }
-        pf[cc] = as_bf16x8(pk);
-      }
-      csum = (part[0] + part[1]) + (part[2] + part[3]);
-    };
-    weigh();
-    const bool need = (mc == -INFINITY) || !(csum <= kSumLimit);
-    if (__ballot(need)) {
-      float mx = sv[0][0];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sv[t][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));   // both lanes of a row take the same max
-      const float mxc = mx * c;
-      if (mxc > mc) {
-        const float alpha = exp2f(mc - mxc);
-        lsum *= alpha;
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-        mc = mxc;
-      }
-      weigh();
-    }
-    lsum += csum;
-  };
-
-  // ---- prologue: chunks 0..2 in flight, 0 and 1 landed; scores and P of chunk 0
-  if (n > 0) issue(0);
-  if (n > 1) issue(1);
-  if (n > 2) {
+  if (n > 0) {
+    issue(0);
+    issue(1);
     issue(2);
-    wait_vmcnt<4>();
-  } else {
-    wait_vmcnt<0>();
   }
+
+  // ---- Q^T operand and ancestor mask of this wave's 32 rows
+  bf16x8 qf[KSTEPS];
+  uint64_t tmask;
+  const int r_row = rb * 256 + wv * 32 + l32;
+  {
+    uint64_t anc = 1;
+    if (r_row < R) {
+      const int il = r_row / G;
+      const int i = pl.node0 + il;
+      const int h = g * G + (r_row - il * G);
+      const uint16_t* qp = q + ((size_t)(b * pl.N + i) * pl.Hq + h) * D + 8 * half;
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) qf[s] = as_bf16x8(*(const u32x4*)(qp + 16 * s));
+      anc = 0;
+      int nn = i;
+      for (int step = 0; step < 64; ++step) {   // root path, bounded
+        if (nn < 0 || nn >= N) break;
+        anc |= 1ull << nn;
+        const int p = spar[nn];
+        if (p >= nn) break;
+        nn = p;
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) qf[s] = as_bf16x8(u32x4{0, 0, 0, 0});
+    }
+    tmask = last ? (anc & (N >= 64 ? ~0ull : ((1ull << N) - 1ull))) : 0ull;
+  }
+  // the Q loads and chunks 0-2 have landed (a wait the compiler sees, so it puts no
+  // wait of its own for the Q loads inside the pipeline); the barrier publishes them
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
   if (n > 0) {
-    const uint8_t* Ks = xs;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int c = 3; c < WNB - 1; ++c) issue(c);
+  }
+
+  f32x16 oacc[DBLK];   // O^T of the wave's rows, 32 dims per tile
+  float mref;          // reference max (scale*log2e units), same in both lanes of a row
+  float part[4];       // partial row sums (this lane's half of the row)
+  f32x16 sacc;         // S^T of the newest chunk, matrix-core output
+  float scp[8];        // scores 8..15 (keys 16-31) of the previous chunk: sacc is reused
+  u32x4 pk[2];         // bf16 weights being formed (P^T operands, 16 keys each)
+  bf16x8 pf[2];        // weights of the chunk whose output is being updated
+  const float c = pl.c;
+  const int kx = l32 & 15;   // K piece permutation of this lane's row
+
+  // keys of chunk cidx this lane's row may see: the prefix part below mask_from and
+  // the tree part on the row's root path (bit = key within the chunk)
+
+  auto mask_bits = [&](int cidx) -> uint32_t {
+    const int kb = key_begin + cidx * WC;
+    const int npre = mask_from - kb;
+    const int off = kb - P;
+    uint64_t a = npre <= 0 ? 0ull : (npre >= 64 ? ~0ull : ((1ull << npre) - 1ull));
+    a |= off >= 0 ? (off < 64 ? tmask >> off : 0ull) : (-off < 64 ? tmask << (-off) : 0ull);
+    return (uint32_t)a;
+  };
+  // value x of score r (key 8*(r/4) + 4*half + r%4), or -inf where alw excludes it
+  auto masked = [&](float x, int r, uint32_t alw, auto MK) -> float {
+    if constexpr (decltype(MK)::value) {
+      const int bit = 8 * (r >> 2) + 4 * half + (r & 3);
+      return ((alw >> bit) & 1u) ? x : -INFINITY;
+    }
+    return x;
+  };
+  // score r of the chunk being weighed: 0-7 from the matrix-core output, 8-15 from
+  // the copy
+  auto score = [&](int r, uint32_t alw, auto MK) -> float {
+    return masked(r >= 8 ? scp[r - 8] : sacc[r], r, alw, MK);
+  };
+  auto copy_hi = [&]() {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
+    for (int r = 0; r < 8; ++r) scp[r] = sacc[8 + r];
+  };
+  // S^T of the chunk in LDS stage `stage` into sacc (no overlap)
+  auto scores_of = [&](int stage) {
+    const uint8_t* Ks = xs + stage * WSTAGE + l32 * XROW;
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s)
+    for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const bf16x8 kf =
-            *(const bf16x8*)(Ks + (32 * t + l32) * XROW + 16 * ((2 * s + half) ^ (l32 & 15)));
-        sacc[t] = mfma32(kf, qf[s], sacc[t]);
+    for (int f = 0; f < KSTEPS; ++f)
+      sacc = mfma32(*(const bf16x8*)(Ks + 16 * ((2 * f + half) ^ kx)), qf[f], sacc);
+  };
+  // row max (scale*log2e units, both lanes of a row) of chunk cidx's scores in sacc
+  auto chunk_max = [&](int cidx) -> float {
+    const uint32_t alw = mask_bits(cidx);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, masked(sacc[r], r, alw, std::true_type{}));
+    return fmaxf(mx, __shfl_xor(mx, 32)) * c;
+  };
+
+  // One pipeline iteration (regions 1 and 2 above).  MK: chunk j or j+1 reaches past
+  // mask_from; LAST: j = n-1, no chunk j+1.  Fragments 0-7 are K of chunk j+1, 8-15
+  // V^T of chunk j (16 keys x 32 dims each).
+  auto iteration = [&](int j, auto MK, auto LASTT) __attribute__((always_inline)) {
+    constexpr bool LAST = decltype(LASTT)::value;
+    constexpr bool MASK = decltype(MK)::value;
+    const uint8_t* Ks = xs + ((j + 1) % WNB) * WSTAGE + l32 * XROW;
+    const int m = lane & 15;
+    const uint8_t* vp = xs + (j % WNB) * WSTAGE + WHALF + (4 * half + (m >> 2)) * XROW + 8 * (m & 1);
+    const int vcol = 2 * ((lane >> 4) & 1) + ((m & 3) >> 1);
+    const int vx = 4 * (m >> 2);
+    auto frag = [&](int f) -> bf16x8 {
+      if (f < 8) return *(const bf16x8*)(Ks + 16 * ((2 * f + half) ^ kx));
+      const int cc = (f - 8) >> 2, db = (f - 8) & 3;
+      const uint8_t* p0 = vp + 16 * cc * XROW + 16 * ((4 * db + vcol) ^ vx);
+      const v4i16 both[2] = {lds_read_tr(p0), lds_read_tr(p0 + 8 * XROW)};
+      return __builtin_bit_cast(bf16x8, both);
+    };
+    const uint32_t alw_j = MASK ? mask_bits(j) : ~0u;
+    const uint32_t alw_n = (MASK && !LAST) ? mask_bits(j + 1) : ~0u;
+    constexpr int F0 = LAST ? 8 : 0;
+    constexpr int LA = 4;
+    bf16x8 ring[LA];
+    static_for<LA>([&](auto I) { ring[(F0 + I) % LA] = frag(F0 + I); });
+    float xa[8][2], ex[8][2];
+    // pair p (scores 2p, 2p+1): A scale and shift, B exponentials, C bf16 pack and
+    // row sum
+    auto stepA = [&](int p, uint32_t alw) {
+      xa[p][0] = fmaf(score(2 * p, alw, MK), c, -mref);
+      xa[p][1] = fmaf(score(2 * p + 1, alw, MK), c, -mref);
+    };
+    auto stepB = [&](int p) {
+      ex[p][0] = __builtin_amdgcn_exp2f(xa[p][0]);
+      ex[p][1] = __builtin_amdgcn_exp2f(xa[p][1]);
+    };
+    auto stepC = [&](int p) {
+      pk[p >> 2][p & 3] = pack_bf16x2(ex[p][0], ex[p][1]);
+      part[p & 3] += ex[p][0] + ex[p][1];
+    };
+    // slot s of a region (8 slots) for pairs p0 .. p0+3: A of pair s/2 (even s), B of
+    // pair (s-1)/2 (odd s), C of pair s/2-1 (even s >= 2); C of the last pair follows
+    auto steps = [&](auto S, int p0, uint32_t alw) {
+      constexpr int s = S;
+      if constexpr (s % 2 == 0) stepA(p0 + s / 2, alw);
+      if constexpr (s % 2 == 1) stepB(p0 + (s - 1) / 2);
+      if constexpr (s % 2 == 0 && s >= 2) stepC(p0 + s / 2 - 1);
+    };
+    // region 1: scores of chunk j+1, pairs 4-7 of chunk j
+    static_for<8>([&](auto S) {
+      constexpr int s = S;
+      if constexpr (!LAST) {
+        if constexpr (s == 0) {   // keys 0-15 of chunk j were weighed, 16-31 copied
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+        }
+        sacc = mfma32(ring[s % LA], qf[s], sacc);
+        ring[s % LA] = frag(s + LA);
       }
-    softmax(0);
-  }
-  // waves 4-7 start half a chunk behind waves 0-3
-  if (grp == 1) __builtin_amdgcn_s_barrier();
+      steps(S, 4, alw_j);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    stepC(7);
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) pf[cc] = as_bf16x8(pk[cc]);
+    if constexpr (!LAST) copy_hi();
+    // region 2: output of chunk j, pairs 0-3 of chunk j+1
+    static_for<8>([&](auto S) {
+      constexpr int s = S;
+      constexpr int f = 8 + s;
+      constexpr int cc = s >> 2, db = s & 3;
+      oacc[db] = mfma32(ring[f % LA], pf[cc], oacc[db]);
+      if constexpr (f + LA < 16) ring[f % LA] = frag(f + LA);
+      if constexpr (!LAST) steps(S, 0, alw_n);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if constexpr (!LAST) stepC(3);
+  };
 
-  for (int j = 0; j < n; ++j) {
-    // matrix phase: chunk j+3 to stage (j-1)%4 (read by both halves before the last
-    // barrier), scores of chunk j+1 (unused after the last chunk), output of chunk j
-    const bool more = j + 3 < n;
-    if (more) issue(j + 3);
-    matrix_phase(j);
-    // chunk j+2 must have landed before the next matrix phase of either half
-    if (more) wait_vmcnt<4>();
-    else wait_vmcnt<0>();
-    __syncthreads();
-    // vector phase
-    if (j + 1 < n) softmax(j + 1);
-    __syncthreads();
-  }
-  if (grp == 0) __builtin_amdgcn_s_barrier();
+  // One walk over the split with the reference max fixed (EXACT: mref already holds
+  // the exact row max; else it is taken from chunk 0).  On entry chunks 0 .. WNB-2
+  // are issued and chunks 0, 1 visible to all waves; on exit no DMA is in flight.
+  auto walk = [&](auto EXACT) __attribute__((always_inline)) {
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) part[e] = 0.f;
+    // prologue: scores of chunk 0, the reference max, the weights of its keys 0-15
+    scores_of(0);
+    if constexpr (!decltype(EXACT)::value) mref = chunk_max(0);
+    copy_hi();
+    {
+      const uint32_t alw0 = mask_bits(0);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(score(2 * p, alw0, std::true_type{}), c, -mref));
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(score(2 * p + 1, alw0, std::true_type{}), c, -mref));
+        pk[0][p] = pack_bf16x2(e0, e1);
+        part[p] += e0 + e1;
+      }
+    }
+    // iteration j: chunks up to j+WNB-2 are issued; chunk j+1 must have landed (all
+    // waves); the DMA of chunk j+WNB-1 goes to stage (j-1) % WNB, last read in
+    // iteration j-1.  Iterations whose chunks j, j+1 need no mask come first: chunk
+    // c needs none when key_begin + (c+1)*WC <= mask_from.
+    constexpr int kAhead = 2 * (WNB - 3);   // DMAs per thread of chunks j+2 .. j+WNB-2
+    const int jm = min(max((mask_from - key_begin) / WC - 1, 0), n - 1);
+    int j = 0;
+    for (; j < jm; ++j) {
+      wait_vmcnt<kAhead>();
+      __syncthreads();
+      issue(j + WNB - 1);
+      iteration(j, std::false_type{}, std::false_type{});
+    }
+    for (; j < n - 1; ++j) {
+      wait_vmcnt<kAhead>();
+      __syncthreads();
+      issue(j + WNB - 1);
+      iteration(j, std::true_type{}, std::false_type{});
+    }
+    iteration(n - 1, std::true_type{}, std::true_type{});
+    wait_vmcnt<0>();   // no DMA may still write this workgroup's LDS past this point
+  };
 
-  // ---- epilogue
+  float lsum = 0.f;
+  if (n > 0) {
+    walk(std::false_type{});
+    lsum = (part[0] + part[1]) + (part[2] + part[3]);
+    const bool big = !((lsum + __shfl_xor(lsum, 32)) <= kRowSumLimit);
+    if (__ballot(big) && lane == 0) atomicOr(&redo, 1);
+    __syncthreads();   // every wave is past its last LDS read, and redo is final
+    if (redo) {
+      // exact row max over the split (scores only, one chunk in flight ahead), then
+      // the walk again with it
+      mref = -INFINITY;
+      issue(0);
+      for (int cidx = 0; cidx < n; ++cidx) {
+        issue(cidx + 1);
+        wait_vmcnt<2>();
+        __syncthreads();
+        scores_of(cidx % WNB);
+        mref = fmaxf(mref, chunk_max(cidx));
+        __syncthreads();
+      }
+      wait_vmcnt<0>();
+      __syncthreads();
+#pragma unroll
+      for (int cidx = 0; cidx < WNB - 1; ++cidx) issue(cidx);
+      wait_vmcnt<2 * (WNB - 3)>();
+      __syncthreads();
+      walk(std::true_type{});
+      lsum = (part[0] + part[1]) + (part[2] + part[3]);
+    }
+  } else {
+    mref = -INFINITY;
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  }
+
   const float ltot = lsum + __shfl_xor(lsum, 32);
   if (r_row >= R) return;
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-  const float lse = (mc + log2f(ltot)) * kLn2;
+  const float lse = (mref + log2f(ltot)) * kLn2;
   const int il = r_row / G;
   const int i = pl.node0 + il;
   const int h = g * G + (r_row - il * G);
@@ -870,10 +938,10 @@ tree_attn_pingpong(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int d0 = 32 * db + 8 * jj + 4 * half;
-        u32x2 pk;
-        pk[0] = pack_bf16x2(oacc[db][4 * jj] * inv, oacc[db][4 * jj + 1] * inv);
-        pk[1] = pack_bf16x2(oacc[db][4 * jj + 2] * inv, oacc[db][4 * jj + 3] * inv);
-        *(u32x2*)(op + d0) = pk;
+        u32x2 pk2;
+        pk2[0] = pack_bf16x2(oacc[db][4 * jj] * inv, oacc[db][4 * jj + 1] * inv);
+        pk2[1] = pack_bf16x2(oacc[db][4 * jj + 2] * inv, oacc[db][4 * jj + 3] * inv);
+        *(u32x2*)(op + d0) = pk2;
       }
     if (half == 0 && lse_out) lse_out[(size_t)(b * pl.N + i) * pl.Hq + h] = lse;
   } else {
@@ -893,15 +961,15 @@ tree_attn_pingpong(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 }
 
 template <bool PAGED>
-hipError_t launch_pingpong(const AttnPlan& pl, const void* q, const void* k, const void* v,
-                           const int32_t* parents, void* out, float* lse, float* part_o,
-                           float* part_lse, hipStream_t stream) {
+hipError_t launch_d128(const AttnPlan& pl, const void* q, const void* k, const void* v,
+                       const int32_t* parents, void* out, float* lse, float* part_o,
+                       float* part_lse, hipStream_t stream) {
   // once per process; function-local static initialisation is thread-safe
   static const hipError_t attr = hipFuncSetAttribute(
-      (const void*)tree_attn_pingpong<PAGED>, hipFuncAttributeMaxDynamicSharedMemorySize, XLDS);
+      (const void*)tree_attn_d128<PAGED>, hipFuncAttributeMaxDynamicSharedMemorySize, WLDS);
   if (attr != hipSuccess) return attr;
   const int nwg = pl.B * pl.Hkv * pl.RB * pl.S;
-  hipLaunchKernelGGL(tree_attn_pingpong<PAGED>, dim3(nwg), dim3(512), XLDS, stream,
+  hipLaunchKernelGGL(tree_attn_d128<PAGED>, dim3(nwg), dim3(512), WLDS, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, parents, pl,
                      (uint16_t*)out, lse, part_o, part_lse);
   return hipGetLastError();
@@ -930,8 +998,8 @@ hipError_t launch_fwd_d(const AttnPlan& pl, const void* q, const void* k, const 
   if constexpr (D == 128) {   // D=64 uses at most 4 waves (chunk staging must divide evenly)
     if (pl.waves == 8) {
       if (pl.block_table)
-        return launch_pingpong<true>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
-      return launch_pingpong<false>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
+        return launch_d128<true>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
+      return launch_d128<false>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
     }
   }
   if (pl.waves == 4) return launch_fwd<D, 4>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);

@@ -114,3 +114,25 @@ def test_attention_full_size_sampled(gpu_lib, name):
         assert_close_attn(got[b, i, g * G:(g + 1) * G], ref)
         np.testing.assert_allclose(lse[b, i, g * G:(g + 1) * G], ref_lse, atol=2e-3)
     assert np.isfinite(got).all() and np.isfinite(lse).all()
+
+
+def test_late_dominant_key(gpu_lib):
+    """Keys far past the start of their split whose scores exceed everything before
+    them by more than 2^64 in weight: the weights taken against the first chunk's max
+    would overflow, so the kernel must walk the split again with the exact row max.
+    A wrong result here is inf/NaN, not a small error."""
+    B, N, Hq, Hkv, D, P = 1, 20, 8, 1, 128, 3000
+    parents = synth.random_parents(B, N, 0, 260, 9)
+    bits, vals, parents = _case(261, B, N, Hq, Hkv, D, P, parents)
+    qb, kb, vb = bits
+    q, k, v = vals
+    # every dim 60.0 (exact in bf16): score = 60 * sum(q) ~ 680 * N(0, 1), so about
+    # half of the rows see a key ~87 (log2 units) above the rest
+    for key in (P // 2 + 40, P - 100):
+        kb[:, :, key] = 0x4270   # bf16 bits of 60.0
+        k[:, :, key] = 60.0
+    got, lse = _run(gpu_lib, (qb, kb, vb), parents, P, D ** -0.5)
+    assert np.isfinite(got).all() and np.isfinite(lse).all()
+    ref, ref_lse = oracle.tree_verify_attention(q, k, v, parents, P, D ** -0.5)
+    assert_close_attn(got, ref)
+    np.testing.assert_allclose(lse, ref_lse, atol=2e-3, rtol=1e-6)
