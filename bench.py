@@ -729,7 +729,7 @@ def summarize_profiles(root):
     w_fac = copy_bytes / 1024.0 / cw[copy_name]
     fetch = per_kernel("pmc_fetch", "FETCH_SIZE")
     write = per_kernel("pmc_write", "WRITE_SIZE")
-    # the C5 attention kernel (the eight-wave ping-pong kernel at these shapes)
+    # the C5 attention kernel (the D = 128 eight-wave kernel at these shapes)
     attn_name = next(k for k in fetch if k.startswith("tree_attn_") and "merge" not in k)
     algo = {attn_name: 2 * B * Hkv * (P + N) * D * 2 + 2 * B * N * Hq * D * 2 + B * N * Hq * 4,
             "lm_head_gemm": V * H * 2 + B * N * H * 2 + B * N * 16}
@@ -778,7 +778,7 @@ def summarize_mfma(path, root=None):
     import re
     for r in _read_csv(path):
         # plain ("lm_head_gemm") or demangled ("void eagle::(anonymous namespace)::lm_head_gemm<...>(...)")
-        m = re.search(r"(?<![A-Za-z0-9_])(lm_head_gemm|tree_attn_pingpong)(?![A-Za-z0-9_])", r["Kernel_Name"])
+        m = re.search(r"(?<![A-Za-z0-9_])(lm_head_gemm|tree_attn_d128)(?![A-Za-z0-9_])", r["Kernel_Name"])
         if not m:
             continue
         key = (int(r["Dispatch_Id"]), m.group(1))
