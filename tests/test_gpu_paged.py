@@ -14,13 +14,15 @@ from inputs import assert_close_attn, to_dev, to_dev_bf16
 pytestmark = pytest.mark.gpu
 
 
-def _paged_case(cfg, B, N, Hq, Hkv, D, P, ps, spare=7):
+def _paged_case(cfg, B, N, Hq, Hkv, D, P, ps, spare=7, plant=()):
     L = P + N
     pages = (L + ps - 1) // ps
     nblk = B * pages + spare
     perm = np.random.default_rng(cfg).permutation(nblk)   # block placement only
     kc = synth.normal_bf16_bits((B, Hkv, pages * ps, D), 1.0, 0, cfg, 2)
     vc = synth.normal_bf16_bits((B, Hkv, pages * ps, D), 1.0, 0, cfg, 3)
+    for row in plant:   # key rows with every dim 60.0 (bf16 bits 0x4270)
+        kc[:, :, row] = 0x4270
     kp = np.full((nblk, Hkv, ps, D), 0x7FC0, np.uint16)
     vp = np.full((nblk, Hkv, ps, D), 0x7FC0, np.uint16)
     table = np.full((B, pages + 3), 123456789, np.int32)   # past the rows: garbage
@@ -72,3 +74,21 @@ def test_paged_matches_contiguous_bitwise(gpu_lib):
                                            to_dev(parents), P)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), c.view(torch.int16)) and torch.equal(la, lc)
+
+
+def test_paged_late_dominant_key(gpu_lib):
+    """Keys far into their split whose scores exceed the split's first chunk by more than
+    2^64 in weight: the paged kernel must redo the split with the exact row max (wrong
+    results would be inf/NaN)."""
+    B, N, Hq, Hkv, D, P, ps = 2, 60, 16, 2, 128, 3000, 16
+    qb, kp, vp, table, parents = _paged_case(861, B, N, Hq, Hkv, D, P, ps, plant=(P // 2 + 40, 700))
+    out, lse = gpu_lib.eagle_tree_verify_attn_paged(to_dev_bf16(qb), to_dev_bf16(kp), to_dev_bf16(vp),
+                                                    to_dev(table), to_dev(parents), P)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    ref, ref_lse = oracle.tree_verify_attention_paged(
+        synth.bf16_bits_to_f64(qb), synth.bf16_bits_to_f64(kp), synth.bf16_bits_to_f64(vp), table,
+        parents, P, ps, D ** -0.5)
+    assert np.isfinite(got).all() and np.isfinite(lse.cpu().numpy()).all()
+    assert_close_attn(got, ref)
+    np.testing.assert_allclose(lse.cpu().numpy(), ref_lse, atol=2e-3, rtol=1e-6)

@@ -16,12 +16,14 @@ pytestmark = pytest.mark.gpu
 SENTINEL = 0x7F7F   # a bf16 pattern the kernel never produces for these inputs
 
 
-def _ragged_attention_case(cfg, B, Nmax, Hq, Hkv, D, P_list, N_list):
+def _ragged_attention_case(cfg, B, Nmax, Hq, Hkv, D, P_list, N_list, plant=()):
     P_list, N_list = np.array(P_list, np.int32), np.array(N_list, np.int32)
     cap = int(P_list.max()) + Nmax + 5   # the layouts are sized for the maxima
     qb = synth.normal_bf16_bits((B, Nmax, Hq, D), 1.0, 0, cfg, 1)
     kb = synth.normal_bf16_bits((B, Hkv, cap, D), 1.0, 0, cfg, 2)
     vb = synth.normal_bf16_bits((B, Hkv, cap, D), 1.0, 0, cfg, 3)
+    for b, row in plant:   # key rows with every dim 60.0 (bf16 bits 0x4270)
+        kb[b, :, row] = 0x4270
     for b in range(B):   # rows past this sequence's prefix + tree: NaN, never read
         kb[b, :, P_list[b] + N_list[b]:] = 0x7FC0
         vb[b, :, P_list[b] + N_list[b]:] = 0x7FC0
@@ -30,16 +32,19 @@ def _ragged_attention_case(cfg, B, Nmax, Hq, Hkv, D, P_list, N_list):
 
 
 @pytest.mark.parametrize("shape", [
-    # B, Nmax, Hq, Hkv, D, prefix lengths, tree sizes
-    (4, 60, 16, 2, 128, [2048, 300, 0, 1111], [60, 17, 40, 1]),
-    (3, 33, 4, 4, 64, [64, 4000, 513], [33, 2, 30]),
-    (2, 26, 8, 1, 128, [9000, 31], [26, 26]),
+    # B, Nmax, Hq, Hkv, D, prefix lengths, tree sizes, planted dominant keys (sequence, row)
+    (4, 60, 16, 2, 128, [2048, 300, 0, 1111], [60, 17, 40, 1], ()),
+    (3, 33, 4, 4, 64, [64, 4000, 513], [33, 2, 30], ()),
+    (2, 26, 8, 1, 128, [9000, 31], [26, 26], ()),
+    # keys whose weights overflow the first chunk's reference max: the split is redone
+    (4, 60, 16, 2, 128, [6000, 300, 0, 1111], [60, 17, 40, 1], ((0, 3040), (3, 700))),
 ])
 def test_ragged_attention(gpu_lib, shape):
-    B, Nmax, Hq, Hkv, D, P_list, N_list = shape
-    print(f"ragged attention B={B} Nmax={Nmax} Hq={Hq} Hkv={Hkv} D={D} P={P_list} N={N_list}", flush=True)
+    B, Nmax, Hq, Hkv, D, P_list, N_list, plant = shape
+    print(f"ragged attention B={B} Nmax={Nmax} Hq={Hq} Hkv={Hkv} D={D} P={P_list} N={N_list} "
+          f"planted={plant}", flush=True)
     qb, kb, vb, parents, P_arr, N_arr = _ragged_attention_case(700 + D + B, B, Nmax, Hq, Hkv, D,
-                                                               P_list, N_list)
+                                                               P_list, N_list, plant)
     Pmax = int(P_arr.max())
     dev = torch.device("cuda:0")
     out = torch.full((B, Nmax, Hq, D), 0, dtype=torch.int16, device=dev)
