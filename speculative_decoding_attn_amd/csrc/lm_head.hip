@@ -133,12 +133,14 @@ lm_head_gemm(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W
   }
   // one DMA instruction t (8 rows) of W / hidden block blk into stage st; hidden
   // groups wholly past M are skipped (their rows are never written out)
-  // Pipeline block blk reads column block (blk + rot) mod nhb: the workgroups start
-  // their K walks at different columns, so the W rows streamed at one moment spread
-  // over the HBM channels instead of sharing one column offset (3-5% at 60-185 rows,
-  // neutral at 240).  The sum order per workgroup is fixed, so results are
-  // deterministic.
-  const int rot = (vt * 37) % nhb;
+  // Small row tiles (<= 64 hidden rows): pipeline block blk reads column block
+  // (blk + rot) mod nhb, so the workgroups start their K walks at different columns
+  // and the W rows streamed at one moment spread over the HBM channels instead of
+  // sharing one column offset (60 rows: 331 -> 316 us).  Larger tiles walk in order:
+  // there the hidden block every workgroup reads at one moment is shared in L2, and
+  // scattered walks cost 35% more HBM traffic for no gain.  The sum order per
+  // workgroup is fixed, so results are deterministic.
+  const int rot = MROWS <= 64 ? (vt * 37) % nhb : 0;
   auto phys = [&](int blk) {
     const int x = blk + rot;
     return x >= nhb ? x - nhb : x;
