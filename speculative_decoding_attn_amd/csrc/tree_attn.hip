@@ -718,7 +718,6 @@ tree_attn_d128(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 
   // keys of chunk cidx this lane's row may see: the prefix part below mask_from and
   // the tree part on the row's root path (bit = key within the chunk)
-
   auto mask_bits = [&](int cidx) -> uint32_t {
     const int kb = key_begin + cidx * WC;
     const int npre = mask_from - kb;
