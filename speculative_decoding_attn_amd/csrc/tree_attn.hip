@@ -543,8 +543,8 @@ tree_attn_merge(AttnPlan pl, const float* __restrict__ part_o, const float* __re
 // workgroup, each wave running its own software pipeline over the split.
 //
 // Staging.  K and V reach LDS by global-to-LDS DMA (each lane moves 16 bytes to
-// m0 + 16*lane, non-temporal: the cache streams them through once), in chunks of 32
-// keys, eight stages deep, one workgroup barrier per chunk.  Rows are stored whole
+// m0 + 16*lane, non-temporal: the cache streams them through once), in chunks of 64
+// keys, four stages deep, one workgroup barrier per chunk.  Rows are stored whole
 // (256 bytes) with their 16-byte pieces permuted: K piece c of row r sits at
 // c ^ (r & 15), which makes the b128 fragment reads of 16 consecutive rows hit every
 // bank once; V piece c of row r sits at c ^ 4*(r & 3), which does the same for the
@@ -561,19 +561,21 @@ tree_attn_merge(AttnPlan pl, const float* __restrict__ part_o, const float* __re
 // split: one walk for the exact row max (scores only), then the walk again with it,
 // where no weight exceeds 1.
 //
-// Pipeline of a wave, iteration j, in a fixed order with no branch:
-//   region 1, 8 MFMA slots: scores of chunk j+1 (S^T = K Q^T, slot s: K fragment s)
-//     and the weights of keys 16-31 of chunk j;
-//   region 2, 8 MFMA slots: output of chunk j (O^T += V^T P^T, slot s: V^T fragment
-//     s) and the weights of keys 0-15 of chunk j+1.
+// Pipeline of a wave, iteration j, in a fixed order with no branch.  A chunk's scores
+// are two 32-key tiles, each its own MFMA accumulation chain; the two chains
+// alternate, so no score MFMA waits on the one before it.
+//   region 1, 16 MFMA slots: scores of chunk j+1 (S^T = K Q^T) and the weights of
+//     tile 1 (keys 32-63) of chunk j;
+//   region 2, 16 MFMA slots: output of chunk j (O^T += V^T P^T) and the weights of
+//     tile 0 (keys 0-31) of chunk j+1.
 // A weight pair goes through three steps (scale and shift, exponentials, bf16 pack
 // and row sum) in consecutive slots, so each slot holds independent vector
 // instructions beside its MFMA; the other wave of the SIMD fills the gaps.  LDS
 // fragments are read four ahead of their MFMAs.
 constexpr int XROW = 256;            // bytes per K or V row
-constexpr int WC = 32;               // keys per chunk
-constexpr int WNB = 8;               // LDS stages
-constexpr int WHALF = WC * XROW;     // one chunk of K (or of V): 8 KB
+constexpr int WC = 64;               // keys per chunk (two 32-key score tiles)
+constexpr int WNB = 4;               // LDS stages
+constexpr int WHALF = WC * XROW;     // one chunk of K (or of V): 16 KB
 constexpr int WSTAGE = 2 * WHALF;
 constexpr int WLDS = WNB * WSTAGE;   // 128 KB of dynamic LDS
 constexpr float kRowSumLimit = 18446744073709551616.0f;   // 2^64
@@ -653,15 +655,18 @@ tree_attn_d128(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   __syncthreads();
 
   const uint32_t xbase = lds_addr(xs);
-  // chunk cidx -> LDS stage cidx % WNB; wave wv moves rows 4wv .. 4wv+3 of K and V
+  // chunk cidx -> LDS stage cidx % WNB; wave wv moves rows 8wv .. 8wv+7 of K and V
   auto issue = [&](int cidx) {
     const int kb = key_begin + cidx * WC;
     const uint32_t st = xbase + (uint32_t)(cidx % WNB) * WSTAGE;
-    const int row = 4 * wv + (lane >> 4);
-    const size_t off = row_off(min(kb + row, kmax));
-    const uint32_t dst = st + (uint32_t)(4 * wv) * XROW;
-    dma16_nt(kbase + off + 8 * ((lane & 15) ^ (row & 15)), dst);
-    dma16_nt(vbase + off + 8 * ((lane & 15) ^ (4 * (row & 3))), dst + WHALF);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int row = 8 * wv + 4 * t + (lane >> 4);
+      const size_t off = row_off(min(kb + row, kmax));
+      const uint32_t dst = st + (uint32_t)(8 * wv + 4 * t) * XROW;
+      dma16_nt(kbase + off + 8 * ((lane & 15) ^ (row & 15)), dst);
+      dma16_nt(vbase + off + 8 * ((lane & 15) ^ (4 * (row & 3))), dst + WHALF);
+    }
   };
   if (n > 0) {
     issue(0);
@@ -709,61 +714,70 @@ tree_attn_d128(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   f32x16 oacc[DBLK];   // O^T of the wave's rows, 32 dims per tile
   float mref;          // reference max (scale*log2e units), same in both lanes of a row
   float part[4];       // partial row sums (this lane's half of the row)
-  f32x16 sacc;         // S^T of the newest chunk, matrix-core output
-  float scp[8];        // scores 8..15 (keys 16-31) of the previous chunk: sacc is reused
-  u32x4 pk[2];         // bf16 weights being formed (P^T operands, 16 keys each)
-  bf16x8 pf[2];        // weights of the chunk whose output is being updated
+  f32x16 sacc[2];      // S^T of the newest chunk, keys 32t .. 32t+31 in tile t
+  float scp[16];       // tile 1 (keys 32-63) of the previous chunk: sacc is reused
+  u32x4 pk[4];         // bf16 weights being formed (P^T operands, 16 keys each)
+  bf16x8 pf[4];        // weights of the chunk whose output is being updated
   const float c = pl.c;
   const int kx = l32 & 15;   // K piece permutation of this lane's row
 
   // keys of chunk cidx this lane's row may see: the prefix part below mask_from and
   // the tree part on the row's root path (bit = key within the chunk)
-  auto mask_bits = [&](int cidx) -> uint32_t {
+  auto mask_bits = [&](int cidx) -> uint64_t {
     const int kb = key_begin + cidx * WC;
     const int npre = mask_from - kb;
     const int off = kb - P;
     uint64_t a = npre <= 0 ? 0ull : (npre >= 64 ? ~0ull : ((1ull << npre) - 1ull));
     a |= off >= 0 ? (off < 64 ? tmask >> off : 0ull) : (-off < 64 ? tmask << (-off) : 0ull);
-    return (uint32_t)a;
+    return a;
   };
-  // value x of score r (key 8*(r/4) + 4*half + r%4), or -inf where alw excludes it
-  auto masked = [&](float x, int r, uint32_t alw, auto MK) -> float {
+  // value x of score r of tile t (key 32t + 8*(r/4) + 4*half + r%4), or -inf where
+  // alw excludes it
+  auto masked = [&](float x, int t, int r, uint64_t alw, auto MK) -> float {
     if constexpr (decltype(MK)::value) {
-      const int bit = 8 * (r >> 2) + 4 * half + (r & 3);
-      return ((alw >> bit) & 1u) ? x : -INFINITY;
+      const int bit = 32 * t + 8 * (r >> 2) + 4 * half + (r & 3);
+      return ((alw >> bit) & 1ull) ? x : -INFINITY;
     }
     return x;
   };
-  // score r of the chunk being weighed: 0-7 from the matrix-core output, 8-15 from
-  // the copy
-  auto score = [&](int r, uint32_t alw, auto MK) -> float {
-    return masked(r >= 8 ? scp[r - 8] : sacc[r], r, alw, MK);
+  // score r of tile t of the chunk being weighed: tile 0 from the matrix-core output,
+  // tile 1 from the copy
+  auto score = [&](int t, int r, uint64_t alw, auto MK) -> float {
+    return masked(t ? scp[r] : sacc[0][r], t, r, alw, MK);
   };
   auto copy_hi = [&]() {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) scp[r] = sacc[8 + r];
+    for (int r = 0; r < 16; ++r) scp[r] = sacc[1][r];
   };
   // S^T of the chunk in LDS stage `stage` into sacc (no overlap)
   auto scores_of = [&](int stage) {
     const uint8_t* Ks = xs + stage * WSTAGE + l32 * XROW;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
 #pragma unroll
     for (int f = 0; f < KSTEPS; ++f)
-      sacc = mfma32(*(const bf16x8*)(Ks + 16 * ((2 * f + half) ^ kx)), qf[f], sacc);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        sacc[t] = mfma32(*(const bf16x8*)(Ks + 32 * t * XROW + 16 * ((2 * f + half) ^ kx)), qf[f],
+                         sacc[t]);
   };
   // row max (scale*log2e units, both lanes of a row) of chunk cidx's scores in sacc
   auto chunk_max = [&](int cidx) -> float {
-    const uint32_t alw = mask_bits(cidx);
+    const uint64_t alw = mask_bits(cidx);
     float mx = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, masked(sacc[r], r, alw, std::true_type{}));
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, masked(sacc[t][r], t, r, alw, std::true_type{}));
     return fmaxf(mx, __shfl_xor(mx, 32)) * c;
   };
 
-  // One pipeline iteration (regions 1 and 2 above).  MK: chunk j or j+1 reaches past
-  // mask_from; LAST: j = n-1, no chunk j+1.  Fragments 0-7 are K of chunk j+1, 8-15
-  // V^T of chunk j (16 keys x 32 dims each).
+  // One pipeline iteration.  MK: chunk j or j+1 reaches past mask_from; LAST: j =
+  // n-1, no chunk j+1.  Fragments 0-15 are K of chunk j+1 (tile f%2, k-step f/2: the
+  // two tiles' accumulation chains alternate), 16-31 V^T of chunk j (16-key step
+  // (f-16)/4, dim tile (f-16)%4).
   auto iteration = [&](int j, auto MK, auto LASTT) __attribute__((always_inline)) {
     constexpr bool LAST = decltype(LASTT)::value;
     constexpr bool MASK = decltype(MK)::value;
@@ -773,70 +787,76 @@ tree_attn_d128(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const int vcol = 2 * ((lane >> 4) & 1) + ((m & 3) >> 1);
     const int vx = 4 * (m >> 2);
     auto frag = [&](int f) -> bf16x8 {
-      if (f < 8) return *(const bf16x8*)(Ks + 16 * ((2 * f + half) ^ kx));
-      const int cc = (f - 8) >> 2, db = (f - 8) & 3;
+      if (f < 16) {
+        const int t = f & 1, sk = f >> 1;
+        return *(const bf16x8*)(Ks + 32 * t * XROW + 16 * ((2 * sk + half) ^ kx));
+      }
+      const int cc = (f - 16) >> 2, db = (f - 16) & 3;
       const uint8_t* p0 = vp + 16 * cc * XROW + 16 * ((4 * db + vcol) ^ vx);
       const v4i16 both[2] = {lds_read_tr(p0), lds_read_tr(p0 + 8 * XROW)};
       return __builtin_bit_cast(bf16x8, both);
     };
-    const uint32_t alw_j = MASK ? mask_bits(j) : ~0u;
-    const uint32_t alw_n = (MASK && !LAST) ? mask_bits(j + 1) : ~0u;
-    constexpr int F0 = LAST ? 8 : 0;
+    const uint64_t alw_j = MASK ? mask_bits(j) : ~0ull;
+    const uint64_t alw_n = (MASK && !LAST) ? mask_bits(j + 1) : ~0ull;
+    constexpr int F0 = LAST ? 16 : 0;
     constexpr int LA = 4;
     bf16x8 ring[LA];
     static_for<LA>([&](auto I) { ring[(F0 + I) % LA] = frag(F0 + I); });
     float xa[8][2], ex[8][2];
-    // pair p (scores 2p, 2p+1): A scale and shift, B exponentials, C bf16 pack and
-    // row sum
-    auto stepA = [&](int p, uint32_t alw) {
-      xa[p][0] = fmaf(score(2 * p, alw, MK), c, -mref);
-      xa[p][1] = fmaf(score(2 * p + 1, alw, MK), c, -mref);
+    // pair p (scores 2p, 2p+1 of tile t): A scale and shift, B exponentials, C bf16
+    // pack (into the P^T operand of 16-key step 2t + p/4) and row sum
+    auto stepA = [&](int t, int p, uint64_t alw) {
+      xa[p][0] = fmaf(score(t, 2 * p, alw, MK), c, -mref);
+      xa[p][1] = fmaf(score(t, 2 * p + 1, alw, MK), c, -mref);
     };
     auto stepB = [&](int p) {
       ex[p][0] = __builtin_amdgcn_exp2f(xa[p][0]);
       ex[p][1] = __builtin_amdgcn_exp2f(xa[p][1]);
     };
-    auto stepC = [&](int p) {
-      pk[p >> 2][p & 3] = pack_bf16x2(ex[p][0], ex[p][1]);
+    auto stepC = [&](int t, int p) {
+      pk[2 * t + (p >> 2)][p & 3] = pack_bf16x2(ex[p][0], ex[p][1]);
       part[p & 3] += ex[p][0] + ex[p][1];
     };
-    // slot s of a region (8 slots) for pairs p0 .. p0+3: A of pair s/2 (even s), B of
-    // pair (s-1)/2 (odd s), C of pair s/2-1 (even s >= 2); C of the last pair follows
-    auto steps = [&](auto S, int p0, uint32_t alw) {
+    // slot s of a region (16 slots) for the 8 pairs of tile t: A of pair s/2 (even s),
+    // B of pair (s-1)/2 (odd s), C of pair s/2-1 (even s >= 2); C of pair 7 follows
+    auto steps = [&](auto S, int t, uint64_t alw) {
       constexpr int s = S;
-      if constexpr (s % 2 == 0) stepA(p0 + s / 2, alw);
-      if constexpr (s % 2 == 1) stepB(p0 + (s - 1) / 2);
-      if constexpr (s % 2 == 0 && s >= 2) stepC(p0 + s / 2 - 1);
+      if constexpr (s % 2 == 0) stepA(t, s / 2, alw);
+      if constexpr (s % 2 == 1) stepB((s - 1) / 2);
+      if constexpr (s % 2 == 0 && s >= 2) stepC(t, s / 2 - 1);
     };
-    // region 1: scores of chunk j+1, pairs 4-7 of chunk j
-    static_for<8>([&](auto S) {
+    // region 1: scores of chunk j+1, tile 1 of chunk j
+    static_for<16>([&](auto S) {
       constexpr int s = S;
       if constexpr (!LAST) {
-        if constexpr (s == 0) {   // keys 0-15 of chunk j were weighed, 16-31 copied
+        constexpr int t = s & 1, sk = s >> 1;
+        if constexpr (s == 0) {   // tile 0 of chunk j was weighed, tile 1 copied
 #pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[tt][r] = 0.f;
         }
-        sacc = mfma32(ring[s % LA], qf[s], sacc);
+        sacc[t] = mfma32(ring[s % LA], qf[sk], sacc[t]);
         ring[s % LA] = frag(s + LA);
       }
-      steps(S, 4, alw_j);
+      steps(S, 1, alw_j);
       __builtin_amdgcn_sched_barrier(0);
     });
-    stepC(7);
+    stepC(1, 7);
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc) pf[cc] = as_bf16x8(pk[cc]);
+    for (int cc = 0; cc < 4; ++cc) pf[cc] = as_bf16x8(pk[cc]);
     if constexpr (!LAST) copy_hi();
-    // region 2: output of chunk j, pairs 0-3 of chunk j+1
-    static_for<8>([&](auto S) {
+    // region 2: output of chunk j, tile 0 of chunk j+1
+    static_for<16>([&](auto S) {
       constexpr int s = S;
-      constexpr int f = 8 + s;
+      constexpr int f = 16 + s;
       constexpr int cc = s >> 2, db = s & 3;
       oacc[db] = mfma32(ring[f % LA], pf[cc], oacc[db]);
-      if constexpr (f + LA < 16) ring[f % LA] = frag(f + LA);
+      if constexpr (f + LA < 32) ring[f % LA] = frag(f + LA);
       if constexpr (!LAST) steps(S, 0, alw_n);
       __builtin_amdgcn_sched_barrier(0);
     });
-    if constexpr (!LAST) stepC(3);
+    if constexpr (!LAST) stepC(0, 7);
   };
 
   // One walk over the split with the reference max fixed (EXACT: mref already holds
@@ -849,25 +869,26 @@ tree_attn_d128(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) part[e] = 0.f;
-    // prologue: scores of chunk 0, the reference max, the weights of its keys 0-15
+    // prologue: scores of chunk 0, the reference max, the weights of its tile 0
     scores_of(0);
     if constexpr (!decltype(EXACT)::value) mref = chunk_max(0);
     copy_hi();
     {
-      const uint32_t alw0 = mask_bits(0);
+      const uint64_t alw0 = mask_bits(0);
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const float e0 = __builtin_amdgcn_exp2f(fmaf(score(2 * p, alw0, std::true_type{}), c, -mref));
-        const float e1 = __builtin_amdgcn_exp2f(fmaf(score(2 * p + 1, alw0, std::true_type{}), c, -mref));
-        pk[0][p] = pack_bf16x2(e0, e1);
-        part[p] += e0 + e1;
+      for (int p = 0; p < 8; ++p) {
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(score(0, 2 * p, alw0, std::true_type{}), c, -mref));
+        const float e1 =
+            __builtin_amdgcn_exp2f(fmaf(score(0, 2 * p + 1, alw0, std::true_type{}), c, -mref));
+        pk[p >> 2][p & 3] = pack_bf16x2(e0, e1);
+        part[p & 3] += e0 + e1;
       }
     }
     // iteration j: chunks up to j+WNB-2 are issued; chunk j+1 must have landed (all
     // waves); the DMA of chunk j+WNB-1 goes to stage (j-1) % WNB, last read in
     // iteration j-1.  Iterations whose chunks j, j+1 need no mask come first: chunk
     // c needs none when key_begin + (c+1)*WC <= mask_from.
-    constexpr int kAhead = 2 * (WNB - 3);   // DMAs per thread of chunks j+2 .. j+WNB-2
+    constexpr int kAhead = 4 * (WNB - 3);   // DMAs per thread of chunks j+2 .. j+WNB-2
     const int jm = min(max((mask_from - key_begin) / WC - 1, 0), n - 1);
     int j = 0;
     for (; j < jm; ++j) {
@@ -900,7 +921,7 @@ tree_attn_d128(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       issue(0);
       for (int cidx = 0; cidx < n; ++cidx) {
         issue(cidx + 1);
-        wait_vmcnt<2>();
+        wait_vmcnt<4>();
         __syncthreads();
         scores_of(cidx % WNB);
         mref = fmaxf(mref, chunk_max(cidx));
@@ -910,7 +931,7 @@ tree_attn_d128(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       __syncthreads();
 #pragma unroll
       for (int cidx = 0; cidx < WNB - 1; ++cidx) issue(cidx);
-      wait_vmcnt<2 * (WNB - 3)>();
+      wait_vmcnt<4 * (WNB - 3)>();
       __syncthreads();
       walk(std::true_type{});
       lsum = (part[0] + part[1]) + (part[2] + part[3]);
