@@ -891,11 +891,24 @@ tree_attn_d128(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     constexpr int kAhead = 4 * (WNB - 3);   // DMAs per thread of chunks j+2 .. j+WNB-2
     const int jm = min(max((mask_from - key_begin) / WC - 1, 0), n - 1);
     int j = 0;
-    for (; j < jm; ++j) {
+    // two iterations per pass: the tile-1 scores one iteration hands to the next then
+    // alternate between two register sets instead of being copied
+    for (; j + 1 < jm; j += 2) {
       wait_vmcnt<kAhead>();
       __syncthreads();
       issue(j + WNB - 1);
       iteration(j, std::false_type{}, std::false_type{});
+      wait_vmcnt<kAhead>();
+      __syncthreads();
+      issue(j + WNB);
+      iteration(j + 1, std::false_type{}, std::false_type{});
+    }
+    if (j < jm) {
+      wait_vmcnt<kAhead>();
+      __syncthreads();
+      issue(j + WNB - 1);
+      iteration(j, std::false_type{}, std::false_type{});
+      ++j;
     }
     for (; j < n - 1; ++j) {
       wait_vmcnt<kAhead>();
