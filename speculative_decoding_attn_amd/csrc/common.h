@@ -130,6 +130,22 @@ __device__ __forceinline__ void dma16_nt(const void* src, uint32_t lds_byte_addr
                : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_byte_addr))
                : "memory", "m0");
 }
+// The same non-temporal copy from a wave-uniform base address plus a per-lane byte
+// offset (the scalar-base form of the load): the base is kept in scalar registers,
+// so a stream that advances by whole blocks costs no vector instruction per load.
+__device__ __forceinline__ void dma16_nt_s(const void* base, uint32_t off, uint32_t lds_byte_addr) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  // readfirstlane returns a signed int: convert through uint32_t, so the low half is
+  // zero-extended (a sign extension would set the high half to all ones)
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  const uint64_t ua = (uint64_t)lo | ((uint64_t)hi << 32);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+               :
+               : "v"(off), "s"((const void*)(uintptr_t)ua),
+                 "s"(__builtin_amdgcn_readfirstlane(lds_byte_addr))
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {

@@ -655,10 +655,31 @@ tree_attn_d128(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   __syncthreads();
 
   const uint32_t xbase = lds_addr(xs);
-  // chunk cidx -> LDS stage cidx % WNB; wave wv moves rows 8wv .. 8wv+7 of K and V
-  auto issue = [&](int cidx) {
+  // byte offsets, within a chunk, of the 16 bytes of K and V this lane moves
+  uint32_t koff[2], voff[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int row = 8 * wv + 4 * t + (lane >> 4);
+    koff[t] = (uint32_t)(row * XROW + 16 * ((lane & 15) ^ (row & 15)));
+    voff[t] = (uint32_t)(row * XROW + 16 * ((lane & 15) ^ (4 * (row & 3))));
+  }
+  // chunk cidx -> LDS stage cidx % WNB; wave wv moves rows 8wv .. 8wv+7 of K and V.
+  // FAST: the chunk lies wholly at or below kmax, so a scalar base plus the fixed lane
+  // offsets address it (contiguous cache only); otherwise each row is clamped to kmax.
+  auto issue = [&](int cidx, auto FAST) {
     const int kb = key_begin + cidx * WC;
     const uint32_t st = xbase + (uint32_t)(cidx % WNB) * WSTAGE;
+    if constexpr (!PAGED && decltype(FAST)::value) {
+      const uint16_t* kc = kbase + (size_t)kb * D;
+      const uint16_t* vc = vbase + (size_t)kb * D;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const uint32_t dst = st + (uint32_t)(8 * wv + 4 * t) * XROW;
+        dma16_nt_s(kc, koff[t], dst);
+        dma16_nt_s(vc, voff[t], dst + WHALF);
+      }
+      return;
+    }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int row = 8 * wv + 4 * t + (lane >> 4);
@@ -669,9 +690,9 @@ tree_attn_d128(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     }
   };
   if (n > 0) {
-    issue(0);
-    issue(1);
-    issue(2);
+    issue(0, std::false_type{});
+    issue(1, std::false_type{});
+    issue(2, std::false_type{});
   }
 
   // ---- Q^T operand and ancestor mask of this wave's 32 rows
@@ -708,7 +729,7 @@ tree_attn_d128(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   __syncthreads();
   if (n > 0) {
 #pragma unroll
-    for (int c = 3; c < WNB - 1; ++c) issue(c);
+    for (int c = 3; c < WNB - 1; ++c) issue(c, std::false_type{});
   }
 
   f32x16 oacc[DBLK];   // O^T of the wave's rows, 32 dims per tile
@@ -890,32 +911,25 @@ tree_attn_d128(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     // c needs none when key_begin + (c+1)*WC <= mask_from.
     constexpr int kAhead = 4 * (WNB - 3);   // DMAs per thread of chunks j+2 .. j+WNB-2
     const int jm = min(max((mask_from - key_begin) / WC - 1, 0), n - 1);
+    auto step = [&](int j, auto MK, auto FAST) __attribute__((always_inline)) {
+      wait_vmcnt<kAhead>();
+      __syncthreads();
+      issue(j + WNB - 1, FAST);
+      iteration(j, MK, std::false_type{});
+    };
+    // iterations below jf run two per pass, so the tile-1 scores one iteration hands
+    // to the next alternate between two register sets instead of being copied.  In
+    // the contiguous cache the chunk each of them issues lies wholly at or below kmax
+    // (the paged issue clamps every row anyway, so there jf = jm).
+    const int nfull = (kmax + 1 - key_begin) / WC;
+    const int jf = PAGED ? jm : min(jm, max(0, nfull - (WNB - 1)));
     int j = 0;
-    // two iterations per pass: the tile-1 scores one iteration hands to the next then
-    // alternate between two register sets instead of being copied
-    for (; j + 1 < jm; j += 2) {
-      wait_vmcnt<kAhead>();
-      __syncthreads();
-      issue(j + WNB - 1);
-      iteration(j, std::false_type{}, std::false_type{});
-      wait_vmcnt<kAhead>();
-      __syncthreads();
-      issue(j + WNB);
-      iteration(j + 1, std::false_type{}, std::false_type{});
+    for (; j + 1 < jf; j += 2) {
+      step(j, std::false_type{}, std::true_type{});
+      step(j + 1, std::false_type{}, std::true_type{});
     }
-    if (j < jm) {
-      wait_vmcnt<kAhead>();
-      __syncthreads();
-      issue(j + WNB - 1);
-      iteration(j, std::false_type{}, std::false_type{});
-      ++j;
-    }
-    for (; j < n - 1; ++j) {
-      wait_vmcnt<kAhead>();
-      __syncthreads();
-      issue(j + WNB - 1);
-      iteration(j, std::true_type{}, std::false_type{});
-    }
+    for (; j < jm; ++j) step(j, std::false_type{}, std::false_type{});
+    for (; j < n - 1; ++j) step(j, std::true_type{}, std::false_type{});
     iteration(n - 1, std::true_type{}, std::true_type{});
     wait_vmcnt<0>();   // no DMA may still write this workgroup's LDS past this point
   };
@@ -931,9 +945,9 @@ tree_attn_d128(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       // exact row max over the split (scores only, one chunk in flight ahead), then
       // the walk again with it
       mref = -INFINITY;
-      issue(0);
+      issue(0, std::false_type{});
       for (int cidx = 0; cidx < n; ++cidx) {
-        issue(cidx + 1);
+        issue(cidx + 1, std::false_type{});
         wait_vmcnt<4>();
         __syncthreads();
         scores_of(cidx % WNB);
@@ -943,7 +957,7 @@ tree_attn_d128(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       wait_vmcnt<0>();
       __syncthreads();
 #pragma unroll
-      for (int cidx = 0; cidx < WNB - 1; ++cidx) issue(cidx);
+      for (int cidx = 0; cidx < WNB - 1; ++cidx) issue(cidx, std::false_type{});
       wait_vmcnt<4 * (WNB - 3)>();
       __syncthreads();
       walk(std::true_type{});
