@@ -113,6 +113,17 @@ __device__ __forceinline__ void wait_vmcnt() {
 // (m0 is a reserved register to the compiler, hence the warning about its clobber;
 // the kernels' assembly is checked to use m0 nowhere else.  The s_nop is the wait
 // state the ISA asks for between an SALU write of m0 and an LDS DMA that reads it.)
+// p read from the first lane: a wave-uniform pointer the compiler keeps in SGPRs.
+// readfirstlane returns a signed int, so each half goes through uint32_t: the low half
+// must be zero-extended (a sign extension would set the high half to all ones).
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  return (T*)(uintptr_t)((uint64_t)lo | ((uint64_t)hi << 32));
+}
+
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds_byte_addr) {
@@ -134,15 +145,9 @@ __device__ __forceinline__ void dma16_nt(const void* src, uint32_t lds_byte_addr
 // offset (the scalar-base form of the load): the base is kept in scalar registers,
 // so a stream that advances by whole blocks costs no vector instruction per load.
 __device__ __forceinline__ void dma16_nt_s(const void* base, uint32_t off, uint32_t lds_byte_addr) {
-  const uint64_t a = (uint64_t)(uintptr_t)base;
-  // readfirstlane returns a signed int: convert through uint32_t, so the low half is
-  // zero-extended (a sign extension would set the high half to all ones)
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
-  const uint64_t ua = (uint64_t)lo | ((uint64_t)hi << 32);
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                :
-               : "v"(off), "s"((const void*)(uintptr_t)ua),
+               : "v"(off), "s"(uniform_ptr(base)),
                  "s"(__builtin_amdgcn_readfirstlane(lds_byte_addr))
                : "memory", "m0");
 }

@@ -655,6 +655,12 @@ tree_attn_d128(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   __syncthreads();
 
   const uint32_t xbase = lds_addr(xs);
+  // a wave whose 32 rows all lie past R (the padding of the last row block) only moves
+  // its share of K and V and keeps the barriers: it computes nothing
+  const bool busy = rb * 256 + wv * 32 < R;
+  // the pair's K and V bases, in scalar registers
+  const uint16_t* const kbase_s = uniform_ptr(kbase);
+  const uint16_t* const vbase_s = uniform_ptr(vbase);
   // byte offsets, within a chunk, of the 16 bytes of K and V this lane moves
   uint32_t koff[2], voff[2];
 #pragma unroll
@@ -670,8 +676,8 @@ tree_attn_d128(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const int kb = key_begin + cidx * WC;
     const uint32_t st = xbase + (uint32_t)(cidx % WNB) * WSTAGE;
     if constexpr (!PAGED && decltype(FAST)::value) {
-      const uint16_t* kc = kbase + (size_t)kb * D;
-      const uint16_t* vc = vbase + (size_t)kb * D;
+      const uint16_t* kc = kbase_s + (size_t)kb * D;
+      const uint16_t* vc = vbase_s + (size_t)kb * D;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const uint32_t dst = st + (uint32_t)(8 * wv + 4 * t) * XROW;
@@ -881,9 +887,11 @@ tree_attn_d128(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   };
 
   // One walk over the split with the reference max fixed (EXACT: mref already holds
-  // the exact row max; else it is taken from chunk 0).  On entry chunks 0 .. WNB-2
-  // are issued and chunks 0, 1 visible to all waves; on exit no DMA is in flight.
-  auto walk = [&](auto EXACT) __attribute__((always_inline)) {
+  // the exact row max; else it is taken from chunk 0); ACTIVE false: the DMAs and
+  // barriers only.  On entry chunks 0 .. WNB-2 are issued and chunks 0, 1 visible to
+  // all waves; on exit no DMA is in flight.
+  auto walk = [&](auto EXACT, auto ACTIVE) __attribute__((always_inline)) {
+    constexpr bool ACT = decltype(ACTIVE)::value;
 #pragma unroll
     for (int db = 0; db < DBLK; ++db)
 #pragma unroll
@@ -891,10 +899,10 @@ tree_attn_d128(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
     for (int e = 0; e < 4; ++e) part[e] = 0.f;
     // prologue: scores of chunk 0, the reference max, the weights of its tile 0
-    scores_of(0);
-    if constexpr (!decltype(EXACT)::value) mref = chunk_max(0);
-    copy_hi();
-    {
+    if constexpr (ACT) {
+      scores_of(0);
+      if constexpr (!decltype(EXACT)::value) mref = chunk_max(0);
+      copy_hi();
       const uint64_t alw0 = mask_bits(0);
 #pragma unroll
       for (int p = 0; p < 8; ++p) {
@@ -915,7 +923,7 @@ tree_attn_d128(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       wait_vmcnt<kAhead>();
       __syncthreads();
       issue(j + WNB - 1, FAST);
-      iteration(j, MK, std::false_type{});
+      if constexpr (ACT) iteration(j, MK, std::false_type{});
     };
     // iterations below jf run two per pass, so the tile-1 scores one iteration hands
     // to the next alternate between two register sets instead of being copied.  In
@@ -930,13 +938,16 @@ tree_attn_d128(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     }
     for (; j < jm; ++j) step(j, std::false_type{}, std::false_type{});
     for (; j < n - 1; ++j) step(j, std::true_type{}, std::false_type{});
-    iteration(n - 1, std::true_type{}, std::true_type{});
+    if constexpr (ACT) iteration(n - 1, std::true_type{}, std::true_type{});
     wait_vmcnt<0>();   // no DMA may still write this workgroup's LDS past this point
   };
 
   float lsum = 0.f;
   if (n > 0) {
-    walk(std::false_type{});
+    if (busy)
+      walk(std::false_type{}, std::true_type{});
+    else
+      walk(std::false_type{}, std::false_type{});
     lsum = (part[0] + part[1]) + (part[2] + part[3]);
     const bool big = !((lsum + __shfl_xor(lsum, 32)) <= kRowSumLimit);
     if (__ballot(big) && lane == 0) atomicOr(&redo, 1);
@@ -950,8 +961,10 @@ tree_attn_d128(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         issue(cidx + 1, std::false_type{});
         wait_vmcnt<4>();
         __syncthreads();
-        scores_of(cidx % WNB);
-        mref = fmaxf(mref, chunk_max(cidx));
+        if (busy) {
+          scores_of(cidx % WNB);
+          mref = fmaxf(mref, chunk_max(cidx));
+        }
         __syncthreads();
       }
       wait_vmcnt<0>();
@@ -960,7 +973,10 @@ tree_attn_d128(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       for (int cidx = 0; cidx < WNB - 1; ++cidx) issue(cidx, std::false_type{});
       wait_vmcnt<4 * (WNB - 3)>();
       __syncthreads();
-      walk(std::true_type{});
+      if (busy)
+        walk(std::true_type{}, std::true_type{});
+      else
+        walk(std::true_type{}, std::false_type{});
       lsum = (part[0] + part[1]) + (part[2] + part[3]);
     }
   } else {
