@@ -87,6 +87,11 @@ lm_head_gemm(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W
                 "the waves load whole 8-row groups of both tiles");
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  // The 192-row tile keeps its accumulators in AGPRs: an AGPR operand anywhere in the
+  // kernel lets the compiler select the AGPR-result form of the MFMAs (396 against
+  // 404 us at 185 rows).  The 256-row tile stays in VGPRs: with the register file
+  // split in halves its other values no longer fit and it ran slower.
+  if constexpr (MT == 3) asm volatile("" ::"a"(0));
   uint8_t* const wst = smem;                 // [NW][VROWS][128 B] W blocks
   uint8_t* const hst = smem + NW * WSTAGE;   // [2][MROWS][128 B] hidden blocks
 
