@@ -735,8 +735,16 @@ tree_attn_d128(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   __syncthreads();
   if (n > 0) {
 #pragma unroll
-    for (int c = 3; c < WNB - 1; ++c) issue(c, std::false_type{});
+    for (int c = 3; c < WNB; ++c) issue(c, std::false_type{});
   }
+  // The workgroup barrier of iteration j sits after the wave's last LDS read of the
+  // iteration, before its last output MFMAs: it publishes chunk j+2 for iteration j+1
+  // (the wait leaves only chunk j+3 in flight), and once every wave is past it the
+  // iteration's stages are free, so the DMA of chunk j+WNB into stage j % WNB follows.
+  auto sync = [&]() __attribute__((always_inline)) {
+    wait_vmcnt<4 * (WNB - 3)>();
+    __syncthreads();
+  };
 
   f32x16 oacc[DBLK];   // O^T of the wave's rows, 32 dims per tile
   float mref;          // reference max (scale*log2e units), same in both lanes of a row
@@ -881,6 +889,7 @@ tree_attn_d128(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       oacc[db] = mfma32(ring[f % LA], pf[cc], oacc[db]);
       if constexpr (f + LA < 32) ring[f % LA] = frag(f + LA);
       if constexpr (!LAST) steps(S, 0, alw_n);
+      if constexpr (!LAST && f + LA == 32) sync();   // after this wave's last LDS read
       __builtin_amdgcn_sched_barrier(0);
     });
     if constexpr (!LAST) stepC(0, 7);
@@ -888,7 +897,7 @@ tree_attn_d128(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 
   // One walk over the split with the reference max fixed (EXACT: mref already holds
   // the exact row max; else it is taken from chunk 0); ACTIVE false: the DMAs and
-  // barriers only.  On entry chunks 0 .. WNB-2 are issued and chunks 0, 1 visible to
+  // barriers only.  On entry chunks 0 .. WNB-1 are issued and chunks 0, 1 visible to
   // all waves; on exit no DMA is in flight.
   auto walk = [&](auto EXACT, auto ACTIVE) __attribute__((always_inline)) {
     constexpr bool ACT = decltype(ACTIVE)::value;
@@ -913,25 +922,25 @@ tree_attn_d128(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         part[p & 3] += e0 + e1;
       }
     }
-    // iteration j: chunks up to j+WNB-2 are issued; chunk j+1 must have landed (all
-    // waves); the DMA of chunk j+WNB-1 goes to stage (j-1) % WNB, last read in
-    // iteration j-1, and is issued after the iteration's work, so the waves leave the
-    // barrier straight into their MFMAs (3% faster than issuing it first).  Iterations whose chunks j, j+1 need no mask come first: chunk
-    // c needs none when key_begin + (c+1)*WC <= mask_from.
-    constexpr int kAhead = 4 * (WNB - 3);   // DMAs per thread of chunks j+2 .. j+WNB-2
+    // iteration j: chunks up to j+WNB-1 are issued and chunks j, j+1 visible to all
+    // waves; the DMA of chunk j+WNB is issued after the iteration's work, so the
+    // waves go from one iteration's MFMAs straight into the next's.  Iterations whose
+    // chunks j, j+1 need no mask come first: chunk c needs none when key_begin +
+    // (c+1)*WC <= mask_from.
     const int jm = min(max((mask_from - key_begin) / WC - 1, 0), n - 1);
     auto step = [&](int j, auto MK, auto FAST) __attribute__((always_inline)) {
-      wait_vmcnt<kAhead>();
-      __syncthreads();
-      if constexpr (ACT) iteration(j, MK, std::false_type{});
-      issue(j + WNB - 1, FAST);
+      if constexpr (ACT)
+        iteration(j, MK, std::false_type{});
+      else
+        sync();
+      issue(j + WNB, FAST);
     };
     // iterations below jf run two per pass, so the tile-1 scores one iteration hands
     // to the next alternate between two register sets instead of being copied.  In
     // the contiguous cache the chunk each of them issues lies wholly at or below kmax
     // (the paged issue clamps every row anyway, so there jf = jm).
     const int nfull = (kmax + 1 - key_begin) / WC;
-    const int jf = PAGED ? jm : min(jm, max(0, nfull - (WNB - 1)));
+    const int jf = PAGED ? jm : min(jm, max(0, nfull - WNB));
     int j = 0;
     for (; j + 1 < jf; j += 2) {
       step(j, std::false_type{}, std::true_type{});
@@ -971,8 +980,8 @@ tree_attn_d128(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       wait_vmcnt<0>();
       __syncthreads();
 #pragma unroll
-      for (int cidx = 0; cidx < WNB - 1; ++cidx) issue(cidx, std::false_type{});
-      wait_vmcnt<4 * (WNB - 3)>();
+      for (int cidx = 0; cidx < WNB; ++cidx) issue(cidx, std::false_type{});
+      wait_vmcnt<4 * (WNB - 2)>();
       __syncthreads();
       if (busy)
         walk(std::true_type{}, std::true_type{});
