@@ -469,16 +469,43 @@ tree_attn_merge_hw(AttnPlan pl, const float* __restrict__ part_o, const float* _
   if (pl.tree_len && r >= min(max(pl.tree_len[b], 1), pl.N) * pl.G) return;   // past this tree
   const int ns = attn_nsplit(pl, b);
   float mx = -INFINITY;
-  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, part_lse[(size_t)attn_slot(pl, b, g, s) * pl.Rpad + r]);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const size_t prow = (size_t)attn_slot(pl, b, g, s) * pl.Rpad + r;
-    const float wgt = expf(part_lse[prow] - mx);
-    wsum += wgt;
-    const f32x4 o = *(const f32x4*)(part_o + prow * D + lane * 4);
+  constexpr int MS = 8;
+  if (ns <= MS) {
+    // every split's lse and partial loaded at once (one memory latency, not 2 ns)
+    float l[MS];
+    f32x4 o[MS];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] += wgt * o[e];
+    for (int s = 0; s < MS; ++s) {
+      if (s < ns) {
+        const size_t prow = (size_t)attn_slot(pl, b, g, s) * pl.Rpad + r;
+        l[s] = part_lse[prow];
+        o[s] = *(const f32x4*)(part_o + prow * D + lane * 4);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < MS; ++s)
+      if (s < ns) mx = fmaxf(mx, l[s]);
+#pragma unroll
+    for (int s = 0; s < MS; ++s) {
+      if (s < ns) {
+        const float wgt = expf(l[s] - mx);
+        wsum += wgt;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += wgt * o[s][e];
+      }
+    }
+  } else {
+    for (int s = 0; s < ns; ++s) mx = fmaxf(mx, part_lse[(size_t)attn_slot(pl, b, g, s) * pl.Rpad + r]);
+    for (int s = 0; s < ns; ++s) {
+      const size_t prow = (size_t)attn_slot(pl, b, g, s) * pl.Rpad + r;
+      const float wgt = expf(part_lse[prow] - mx);
+      wsum += wgt;
+      const f32x4 o = *(const f32x4*)(part_o + prow * D + lane * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += wgt * o[e];
+    }
   }
   const float inv = 1.f / wsum;
   const int il = r / pl.G;
