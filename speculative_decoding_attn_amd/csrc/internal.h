@@ -35,10 +35,11 @@ struct AttnPlan {
   // query subset (nq > 0): only nodes node0 .. node0+nq-1 of the N-node tree are
   // computed (the draft expansion's newest rows); masks and keys cover the whole tree
   int node0, nq;
-  // ragged batches with split keys (device memory in the workspace, filled by a plan
-  // kernel from prefix_len): [0] split length, [1] number of (sequence, split) items,
-  // [2, 2+B) first item of each sequence, [2+B, 2+2B) its number of splits,
-  // [2+2B, 2+2B+B*S) the sequence of each item.  Null otherwise.
+  // ragged batches with split keys (device memory in the workspace, written by the
+  // attention kernel's workgroup 0 from prefix_len for the merge): [0] split length,
+  // [1] number of (sequence, split) items, [2, 2+B) first item of each sequence,
+  // [2+B, 2+2B) its number of splits.  Non-null also tells the attention kernels to
+  // plan the splits themselves.  Null otherwise.
   int* dplan;
 };
 

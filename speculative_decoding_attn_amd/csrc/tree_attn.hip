@@ -56,11 +56,12 @@ __device__ __forceinline__ int vt_pos(int key) {
 }
 
 // The (sequence, KV head, row block, key split) a workgroup computes.  Uniform batches:
-// every (sequence, KV head) pair is cut into pl.S splits of pl.split_len keys.  Ragged
-// batches with a device plan: sequence b is cut into its own number of splits of one
-// common length, chosen on the device from the real prefix lengths (tree_attn_plan),
-// and blocks past the plan's items have nothing to do.  `slot` indexes the split
-// partials: uniform pair * S + split, planned item * Hkv + KV head.
+// every (sequence, KV head) pair is cut into pl.S splits of pl.split_len keys
+// (attn_item).  Ragged batches with a device plan: sequence b is cut into its own
+// number of splits of one common length, chosen on the device from the real prefix
+// lengths (planned_item, below), and blocks past the plan's items have nothing to
+// do.  `slot` indexes the split partials: uniform pair * S + split, planned item *
+// Hkv + KV head.
 struct AttnItem {
   bool valid;
   int b, g, rb, split, nsplit, len, slot;
@@ -69,26 +70,14 @@ struct AttnItem {
 __device__ __forceinline__ AttnItem attn_item(const AttnPlan& pl, int logical) {
   AttnItem it;
   it.rb = logical % pl.RB;
-  if (!pl.dplan) {
-    it.split = (logical / pl.RB) % pl.S;
-    const int pair = logical / (pl.RB * pl.S);
-    it.b = pair / pl.Hkv;
-    it.g = pair % pl.Hkv;
-    it.nsplit = pl.S;
-    it.len = pl.split_len;
-    it.slot = pair * pl.S + it.split;
-    it.valid = true;
-    return it;
-  }
-  it.g = (logical / pl.RB) % pl.Hkv;
-  const int t = logical / (pl.RB * pl.Hkv);
-  it.valid = t < pl.dplan[1];
-  const int tt = it.valid ? t : 0;
-  it.b = min(max(pl.dplan[2 + 2 * pl.B + tt], 0), pl.B - 1);
-  it.split = tt - pl.dplan[2 + it.b];
-  it.nsplit = pl.dplan[2 + pl.B + it.b];
-  it.len = pl.dplan[0];
-  it.slot = tt * pl.Hkv + it.g;
+  it.split = (logical / pl.RB) % pl.S;
+  const int pair = logical / (pl.RB * pl.S);
+  it.b = pair / pl.Hkv;
+  it.g = pair % pl.Hkv;
+  it.nsplit = pl.S;
+  it.len = pl.split_len;
+  it.slot = pair * pl.S + it.split;
+  it.valid = true;
   return it;
 }
 
@@ -100,22 +89,24 @@ __device__ __forceinline__ int attn_nsplit(const AttnPlan& pl, int b) {
   return pl.dplan ? pl.dplan[2 + pl.B + b] : pl.S;
 }
 
-// Ragged batches: choose the split length from the real prefix lengths so that the
-// (sequence, split) items, each sequence cut into ceil(prefix / length) splits (at
-// least one, its tree keys), number at most the B * S items of the uniform plan: the
-// smallest multiple of 32 keys (and at least kMinSplitKeys) that does so.  One
-// workgroup; thread 0 then lays out the item table.
-__global__ void __launch_bounds__(256) tree_attn_plan(AttnPlan pl, int* __restrict__ dplan) {
-  __shared__ int best;
+// Ragged batches: the split length and this workgroup's (sequence, split) item, from
+// the real prefix lengths.  The length is the smallest multiple of 32 keys, at least
+// kMinSplitKeys, for which the sequences' items (ceil(prefix / length) splits each,
+// at least one for the tree keys) number at most the B * S items of the uniform
+// plan; with every prefix at the maximum that is the uniform plan's split length
+// (the same splits).  Every workgroup computes it (a pure function of the prefix
+// lengths, so all agree) instead of a separate plan kernel; workgroup 0 also writes
+// the per-sequence table the merge reads.  All threads of the workgroup call it.
+__device__ AttnItem planned_item(const AttnPlan& pl, int logical) {
+  __shared__ int s_best;
+  __shared__ int s_item[4];   // valid, sequence, split, number of splits
   const int B = pl.B, cap = pl.B * pl.S;
-  // lengths in whole 32-key chunks, as in the uniform plan: with every prefix at the
-  // maximum the smallest feasible length is the uniform plan's split length (the same
-  // splits).  Each thread tries its own candidates in increasing order, all at once.
   const int lo = kMinSplitKeys / KC, hi = max(lo, (pl.P + KC - 1) / KC);   // hi: B items
-  if (threadIdx.x == 0) best = hi;
+  if (threadIdx.x == 0) s_best = hi;
   __syncthreads();
+  // each thread tries its own candidate lengths in increasing order, all at once
   int mine = hi;
-  for (int u = lo + (int)threadIdx.x; u < hi; u += 256) {
+  for (int u = lo + (int)threadIdx.x; u < hi; u += blockDim.x) {
     const int len = u * KC;
     int c = 0;
     for (int b = 0; b < B && c <= cap; ++b) {
@@ -128,23 +119,47 @@ __global__ void __launch_bounds__(256) tree_attn_plan(AttnPlan pl, int* __restri
     }
   }
   mine = wave_min_i(mine);
-  if ((threadIdx.x & 63) == 0) atomicMin(&best, mine);
+  if ((threadIdx.x & 63) == 0) atomicMin(&s_best, mine);
   __syncthreads();
-  const int lo_best = best;
+  const int len = s_best * KC;
+  const int t = logical / (pl.RB * pl.Hkv);
   if (threadIdx.x == 0) {
-    const int len = lo_best * KC;
-    int t = 0;
+    s_item[0] = 0;
+    s_item[1] = 0;
+    s_item[2] = 0;
+    s_item[3] = 1;
+    int first = 0;
     for (int b = 0; b < B; ++b) {
       const int P = min(max(pl.prefix_len[b], 0), pl.P);
-      const int nb = min(max(1, (P + len - 1) / len), cap - t - (B - 1 - b));
-      dplan[2 + b] = t;
-      dplan[2 + B + b] = nb;
-      for (int s = 0; s < nb; ++s) dplan[2 + 2 * B + t + s] = b;
-      t += nb;
+      const int nb = min(max(1, (P + len - 1) / len), cap - first - (B - 1 - b));
+      if (logical == 0) {
+        pl.dplan[2 + b] = first;
+        pl.dplan[2 + B + b] = nb;
+      }
+      if (t >= first && t < first + nb) {
+        s_item[0] = 1;
+        s_item[1] = b;
+        s_item[2] = t - first;
+        s_item[3] = nb;
+      }
+      first += nb;
     }
-    dplan[0] = len;
-    dplan[1] = t;
+    if (logical == 0) {
+      pl.dplan[0] = len;
+      pl.dplan[1] = first;
+    }
   }
+  __syncthreads();
+  AttnItem it;
+  it.rb = logical % pl.RB;
+  it.g = (logical / pl.RB) % pl.Hkv;
+  it.valid = s_item[0] != 0;
+  it.b = s_item[1];
+  it.split = s_item[2];
+  it.nsplit = s_item[3];
+  it.len = len;
+  it.slot = t * pl.Hkv + it.g;
+  return it;
 }
 
 template <int D, int WAVES, bool PAGED>
@@ -181,7 +196,7 @@ tree_attn_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int nwg = gridDim.x;
   const int w = blockIdx.x;
   const int logical = (nwg % 8 == 0) ? (w % 8) * (nwg / 8) + (w / 8) : w;
-  const AttnItem item = attn_item(pl, logical);
+  const AttnItem item = pl.dplan ? planned_item(pl, logical) : attn_item(pl, logical);
   if (!item.valid) return;   // a planned ragged batch with fewer items than blocks
   const int rb = item.rb;
   const int split = item.split;
@@ -636,7 +651,7 @@ tree_attn_d128(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int nwg = gridDim.x;
   const int w = blockIdx.x;
   const int logical = (nwg % 8 == 0) ? (w % 8) * (nwg / 8) + (w / 8) : w;
-  const AttnItem item = attn_item(pl, logical);
+  const AttnItem item = pl.dplan ? planned_item(pl, logical) : attn_item(pl, logical);
   if (!item.valid) return;   // a planned ragged batch with fewer items than blocks
   const int rb = item.rb;
   const int split = item.split;
@@ -1185,7 +1200,7 @@ static size_t plan_table_offset(const AttnPlan& pl) {
 
 size_t tree_attn_workspace_bytes(const AttnPlan& pl) {
   if (pl.S <= 1) return 0;
-  return plan_table_offset(pl) + (size_t)(2 + 2 * pl.B + pl.B * pl.S) * sizeof(int) + 256;
+  return plan_table_offset(pl) + (size_t)(2 + 2 * pl.B) * sizeof(int) + 256;
 }
 
 hipError_t launch_tree_attn(const AttnPlan& pl0, float scale, const void* q, const void* k,
@@ -1199,13 +1214,10 @@ hipError_t launch_tree_attn(const AttnPlan& pl0, float scale, const void* q, con
     const size_t rows = (size_t)pl.B * pl.Hkv * pl.S * pl.Rpad;
     part_o = (float*)workspace;
     part_lse = part_o + rows * pl.D;
-    // ragged prefixes: split lengths from the real prefix lengths (device plan)
-    if (pl.prefix_len && !pl.block_table && pl.nq == 0) {
+    // ragged prefixes: split lengths from the real prefix lengths, chosen by the
+    // attention workgroups themselves (planned_item); the table goes to the merge
+    if (pl.prefix_len && !pl.block_table && pl.nq == 0)
       pl.dplan = (int*)((char*)workspace + plan_table_offset(pl));
-      hipLaunchKernelGGL(tree_attn_plan, dim3(1), dim3(256), 0, stream, pl, pl.dplan);
-      const hipError_t e0 = hipGetLastError();
-      if (e0 != hipSuccess) return e0;
-    }
   }
   const hipError_t e =
       pl.D == 128 ? launch_fwd_d<128>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream)
