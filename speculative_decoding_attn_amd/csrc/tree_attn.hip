@@ -486,7 +486,7 @@ tree_attn_merge_hw(AttnPlan pl, const float* __restrict__ part_o, const float* _
   float mx = -INFINITY;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
-  constexpr int MS = 8;
+  constexpr int MS = 16;
   if (ns <= MS) {
     // every split's lse and partial loaded at once (one memory latency, not 2 ns)
     float l[MS];
@@ -686,8 +686,21 @@ tree_attn_d128(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     }
   };
 
-  // the tree's parent links and (paged) this split's slice of the block table to LDS
+  // the tree's parent links and (paged) this split's slice of the block table to LDS;
+  // this wave's Q^T operand to registers
   if (tid < pl.N) spar[tid] = parents[(size_t)b * pl.N + tid];
+  bf16x8 qf[KSTEPS];
+  const int r_row = rb * 256 + wv * 32 + l32;
+  if (r_row < R) {
+    const int il = r_row / G;
+    const int h = g * G + (r_row - il * G);
+    const uint16_t* qp = q + ((size_t)(b * pl.N + pl.node0 + il) * pl.Hq + h) * D + 8 * half;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) qf[s] = as_bf16x8(*(const u32x4*)(qp + 16 * s));
+  } else {
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) qf[s] = as_bf16x8(u32x4{0, 0, 0, 0});
+  }
   if constexpr (PAGED) {
     const int npages = min((kmax >> pl.page_shift) - first_page + 1, kMaxSplitPages);
     const int32_t* bt = pl.block_table + (size_t)b * pl.max_pages + first_page;
@@ -740,22 +753,15 @@ tree_attn_d128(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   if (n > 0) {
     issue(0, std::false_type{});
     issue(1, std::false_type{});
-    issue(2, std::false_type{});
   }
 
-  // ---- Q^T operand and ancestor mask of this wave's 32 rows
-  bf16x8 qf[KSTEPS];
+  // ---- ancestor mask of this wave's 32 rows (while chunks 0, 1 are in flight)
   uint64_t tmask;
-  const int r_row = rb * 256 + wv * 32 + l32;
   {
     uint64_t anc = 1;
     if (r_row < R) {
       const int il = r_row / G;
       const int i = pl.node0 + il;
-      const int h = g * G + (r_row - il * G);
-      const uint16_t* qp = q + ((size_t)(b * pl.N + i) * pl.Hq + h) * D + 8 * half;
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) qf[s] = as_bf16x8(*(const u32x4*)(qp + 16 * s));
       anc = 0;
       int nn = i;
       for (int step = 0; step < 64; ++step) {   // root path, bounded
@@ -765,19 +771,16 @@ tree_attn_d128(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         if (p >= nn) break;
         nn = p;
       }
-    } else {
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) qf[s] = as_bf16x8(u32x4{0, 0, 0, 0});
     }
     tmask = last ? (anc & (N >= 64 ? ~0ull : ((1ull << N) - 1ull))) : 0ull;
   }
-  // the Q loads and chunks 0-2 have landed (a wait the compiler sees, so it puts no
+  // the Q loads and chunks 0, 1 have landed (a wait the compiler sees, so it puts no
   // wait of its own for the Q loads inside the pipeline); the barrier publishes them
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
   if (n > 0) {
 #pragma unroll
-    for (int c = 3; c < WNB; ++c) issue(c, std::false_type{});
+    for (int c = 2; c < WNB; ++c) issue(c, std::false_type{});
   }
   // The workgroup barrier of iteration j sits after the wave's last LDS read of the
   // iteration, before its last output MFMAs: it publishes chunk j+2 for iteration j+1
