@@ -613,7 +613,10 @@ tree_attn_merge(AttnPlan pl, const float* __restrict__ part_o, const float* __re
 // A weight pair goes through three steps (scale and shift, exponentials, bf16 pack
 // and row sum) in consecutive slots, so each slot holds independent vector
 // instructions beside its MFMA; the other wave of the SIMD fills the gaps.  LDS
-// fragments are read four ahead of their MFMAs.
+// fragments are read four ahead of their MFMAs.  The iteration's workgroup barrier
+// comes after the wave's last LDS read, before its last four output MFMAs; past it
+// the DMA of chunk j+4 goes into the stage of chunk j, issued after the iteration's
+// work.  A wave whose rows are all padding keeps only the DMAs and the barriers.
 constexpr int XROW = 256;            // bytes per K or V row
 constexpr int WC = 64;               // keys per chunk (two 32-key score tiles)
 constexpr int WNB = 4;               // LDS stages
