@@ -89,9 +89,14 @@ __device__ __forceinline__ int attn_nsplit(const AttnPlan& pl, int b) {
   return pl.dplan ? pl.dplan[2 + pl.B + b] : pl.S;
 }
 
+// Shortest split: narrow workgroups (one or two waves) are cheap to start, so their
+// splits go down to 128 keys (C2: 22.0 -> 17.5 us); the eight-wave kernel's stay at
+// kMinSplitKeys.  The uniform and the ragged plans use the same bound.
+__host__ __device__ inline int min_split_keys(int waves) { return waves <= 2 ? 128 : kMinSplitKeys; }
+
 // Ragged batches: the split length and this workgroup's (sequence, split) item, from
 // the real prefix lengths.  The length is the smallest multiple of 32 keys, at least
-// kMinSplitKeys, for which the sequences' items (ceil(prefix / length) splits each,
+// min_split_keys, for which the sequences' items (ceil(prefix / length) splits each,
 // at least one for the tree keys) number at most the B * S items of the uniform
 // plan; with every prefix at the maximum that is the uniform plan's split length
 // (the same splits).  Every workgroup computes it (a pure function of the prefix
@@ -101,7 +106,7 @@ __device__ AttnItem planned_item(const AttnPlan& pl, int logical) {
   __shared__ int s_best;
   __shared__ int s_item[4];   // valid, sequence, split, number of splits
   const int B = pl.B, cap = pl.B * pl.S;
-  const int lo = kMinSplitKeys / KC, hi = max(lo, (pl.P + KC - 1) / KC);   // hi: B items
+  const int lo = min_split_keys(pl.waves) / KC, hi = max(lo, (pl.P + KC - 1) / KC);   // hi: B items
   if (threadIdx.x == 0) s_best = hi;
   __syncthreads();
   // each thread tries its own candidate lengths in increasing order, all at once
@@ -1164,9 +1169,7 @@ AttnPlan plan_tree_attn_rows(int B, int N, int node0, int nq, int Hq, int Hkv, i
   const long long units = (long long)B * Hkv * pl.RB;
   const int wg_per_cu = pl.waves == 1 ? 3 : (pl.waves == 2 ? 2 : 1);
   int s_target = (int)(((long long)kNumCUs * wg_per_cu + units - 1) / units);
-  // narrow workgroups (one wave's registers hold the whole pipeline) are cheap to start:
-  // their splits go down to 128 keys (C2: 22 -> 17.5 us), the wide ones' to kMinSplitKeys
-  int s_max = P / (pl.waves <= 2 ? 128 : kMinSplitKeys);
+  int s_max = P / min_split_keys(pl.waves);
   int S = s_target < s_max ? s_target : s_max;
   if (S < 1) S = 1;
   if (P <= 0) {

@@ -69,8 +69,12 @@ def test_ragged_attention(gpu_lib, shape):
         assert (got_lse[b, n:] == 12345.0).all()
 
 
-def test_ragged_attention_equals_uniform_when_sizes_agree(gpu_lib):
-    B, N, Hq, Hkv, D, P = 2, 20, 8, 2, 128, 700
+@pytest.mark.parametrize("shape", [
+    (2, 20, 8, 2, 128, 700),   # four-wave workgroups (256-key minimum split)
+    (2, 20, 2, 2, 128, 700),   # one-wave workgroups (128-key minimum split)
+])
+def test_ragged_attention_equals_uniform_when_sizes_agree(gpu_lib, shape):
+    B, N, Hq, Hkv, D, P = shape
     qb, kb, vb, parents, P_arr, N_arr = _ragged_attention_case(760, B, N, Hq, Hkv, D, [P, P], [N, N])
     args = (to_dev_bf16(qb), to_dev_bf16(kb), to_dev_bf16(vb), to_dev(parents), P, D ** -0.5)
     a, la = gpu_lib.eagle_tree_verify_attn(*args)
