@@ -50,6 +50,9 @@ CASES = [
     (1, 60, 16, 2, 128, 0, "rand"),
     (2, 20, 16, 2, 128, 0, "rand"),
     (1, 30, 8, 1, 128, 1, "chain"),
+    # one-wave D = 128 workgroups over 32 splits of 160 keys: the merge's path for more
+    # than 16 splits
+    (1, 10, 2, 1, 128, 5000, "rand"),
 ]
 
 
