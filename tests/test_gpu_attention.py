@@ -53,6 +53,12 @@ CASES = [
     # one-wave D = 128 workgroups over 32 splits of 160 keys: the merge's path for more
     # than 16 splits
     (1, 10, 2, 1, 128, 5000, "rand"),
+    # the eight-wave kernel on one split of 7-9 chunks: the two-iterations-per-pass loop
+    # with its scalar-base DMA for the first iterations (one and two passes), then the
+    # clamped, masked and last iterations
+    (1, 30, 8, 1, 128, 383, "rand"),
+    (1, 30, 8, 1, 128, 450, "rand"),
+    (1, 30, 8, 1, 128, 500, "chain"),
 ]
 
 
