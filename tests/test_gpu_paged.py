@@ -43,6 +43,8 @@ def _paged_case(cfg, B, N, Hq, Hkv, D, P, ps, spare=7, plant=()):
     (1, 26, 8, 8, 128, 1024, 32),
     (3, 17, 6, 3, 64, 700, 1),
     (2, 40, 8, 1, 128, 5000, 64),
+    # one split of 9 chunks: the eight-wave kernel's two-iterations-per-pass loop on pages
+    (1, 30, 8, 1, 128, 500, 16),
 ])
 def test_paged_attention(gpu_lib, shape):
     B, N, Hq, Hkv, D, P, ps = shape
