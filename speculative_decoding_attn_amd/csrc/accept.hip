@@ -104,7 +104,8 @@ accept_greedy_kernel(const int32_t* __restrict__ tokens, const int32_t* __restri
 // leave writes its outputs (an exit counter in the workspace).
 // ---------------------------------------------------------------------------
 constexpr int kSpecThreads = 256;
-constexpr int kSpecRegs = 16;   // entries per thread kept in registers (chunks up to 4096)
+constexpr int kSpecRegs = 16;   // entries per thread kept in registers
+constexpr int kSpecChunk = kSpecThreads * kSpecRegs;   // planned vocabulary entries per workgroup
 constexpr unsigned kSpinLimit = 1u << 24;
 
 struct SpecWs {
@@ -174,6 +175,28 @@ __device__ __forceinline__ double wg_max_d(double x, double* red) {
   return t;
 }
 
+// Waits until the exchange word *p carries `tag` in its high half and returns the word in
+// `out`.  Gives up (false) once the sequence's abort flag is set, or after kSpinLimit
+// polls, when it sets that flag itself.
+__device__ __forceinline__ bool poll_word(const unsigned long long* p, unsigned tag, int* abort_flag,
+                                          unsigned long long& out) {
+  unsigned spins = 0;
+  for (;;) {
+    const unsigned long long v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((unsigned)(v >> 32) == tag) {
+      out = v;
+      return true;
+    }
+    if ((++spins & 63u) == 0u && __hip_atomic_load(abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+      return false;
+    if (spins > kSpinLimit) {
+      __hip_atomic_store(abort_flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
 // Publish this workgroup's first nv partials (of 4) for generation `gen`, wait for
 // every chunk of the sequence, and return the chunk-ordered partials in
 // lds_all[chunks][4] (entries k < nv).  Returns false on timeout.
@@ -205,24 +228,11 @@ __device__ bool exchange(const SpecWs& w, int b, int chunks, int me, unsigned ge
   unsigned* words = (unsigned*)lds_all;
   for (int i = threadIdx.x; i < chunks * nw; i += blockDim.x) {
     const int c = i / nw, k = i - c * nw;
-    unsigned spins = 0;
     unsigned long long v;
-    for (;;) {
-      v = __hip_atomic_load(&slot[c * 8 + k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if ((unsigned)(v >> 32) == tag) break;
-      if ((++spins & 63u) == 0u &&
-          __hip_atomic_load(&w.abort_flags[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-        ok = false;
-        break;
-      }
-      if (spins > kSpinLimit) {
-        __hip_atomic_store(&w.abort_flags[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ok = false;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
+    if (!poll_word(&slot[c * 8 + k], tag, &w.abort_flags[b], v)) {
+      ok = false;
+      break;
     }
-    if (!ok) break;
     words[c * 8 + k] = (unsigned)v;
   }
   if (!ok) *lds_flag = 0;
@@ -230,6 +240,55 @@ __device__ bool exchange(const SpecWs& w, int b, int chunks, int me, unsigned ge
   return *lds_flag != 0;
 }
 
+// Sum of one double over the workgroups of a sequence: the workgroup's part (summed over
+// its waves in wave order) is published through exchange words as in exchange(), and
+// every workgroup adds the chunks' parts in chunk order, so all of them hold the same
+// sum.  Two workgroup barriers in all.  Returns false on timeout.
+__device__ bool exchange_sum(const SpecWs& w, int b, int chunks, int me, unsigned gen, double part,
+                             double* red, double* lds_all, int* lds_flag, double& out) {
+  part = wave_sum_d(part);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  if (lane == 0) red[wid] = part;
+  if (threadIdx.x == 0) *lds_flag = 1;
+  __syncthreads();   // red complete; every thread is done with the previous lds_all
+  unsigned long long* slot = w.slots + (((size_t)b * 2 + (gen & 1)) * chunks) * 8;
+  const unsigned tag = gen + 1;
+  if (threadIdx.x < 2) {
+    double s = red[0];
+#pragma unroll
+    for (int i = 1; i < kSpecThreads / 64; ++i) s += red[i];
+    const unsigned long long bits = (unsigned long long)__double_as_longlong(s);
+    const unsigned half = threadIdx.x ? (unsigned)(bits >> 32) : (unsigned)bits;
+    __hip_atomic_store(&slot[me * 8 + threadIdx.x], ((unsigned long long)tag << 32) | half,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  bool ok = true;
+  unsigned* words = (unsigned*)lds_all;
+  for (int i = threadIdx.x; i < chunks * 2; i += blockDim.x) {
+    const int c = i >> 1, k = i & 1;
+    unsigned long long v;
+    if (!poll_word(&slot[c * 8 + k], tag, &w.abort_flags[b], v)) {
+      ok = false;
+      break;
+    }
+    words[c * 8 + k] = (unsigned)v;
+  }
+  if (!ok) *lds_flag = 0;
+  __syncthreads();
+  if (*lds_flag == 0) return false;
+  double s = 0.0;
+#pragma unroll 8
+  for (int c = 0; c < chunks; ++c) s += lds_all[4 * c];
+  out = s;
+  return true;
+}
+
+// REGS: every chunk of the plan has at most kSpecRegs * kSpecThreads entries.  Each
+// thread then owns the contiguous entries [t0, t1) of its workgroup's chunk and keeps q
+// and p of the current node in registers from the logits load to the final draw; the
+// workspace copies of q and p are not used.  Otherwise q and p go through the workspace
+// (strided passes; the draw walks the same contiguous ranges).
+template <bool REGS>
 __global__ void __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)))
 accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict__ parents,
                    const int32_t* __restrict__ draft_row, const float* __restrict__ target_logits,
@@ -241,11 +300,16 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
   __shared__ int lds_flag;
   __shared__ int kids[64];
   __shared__ int nkids_s;
-  // per child (in sibling order): token, its target and draft logits, its uniform
   __shared__ double cterm[128];   // per-chunk softmax terms: q in [0, 64), p in [64, 128)
+  // per child (in sibling order): token, q and p of its token, its uniform
   __shared__ int kid_tok[64];
-  __shared__ float kid_tl[64], kid_dl[64], kid_u[64];
+  __shared__ double kid_q[64], kid_p[64];
+  __shared__ float kid_u[64];
+  __shared__ unsigned long long kid_same[64];   // bit i: child i < j carries child j's token
   __shared__ int path_s[65];
+  __shared__ double wtot_s[kSpecThreads / 64];   // draw: wave totals of the residual mass
+  __shared__ int wlast_s[kSpecThreads / 64];
+  __shared__ int found_s;
 
   const int chunks = pl.chunks;
   const int b = blockIdx.x / chunks;
@@ -254,12 +318,17 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
   const int chunk_len = (V + chunks - 1) / chunks;
   const int x0 = me * chunk_len;
   const int x1 = min(V, x0 + chunk_len);
+  // the thread's contiguous entries [t0, t1) (at most kSpecRegs of them when REGS)
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wid = tid >> 6;
+  const int per = (max(0, x1 - x0) + kSpecThreads - 1) / kSpecThreads;
+  const int t0 = x0 + tid * per;
+  const int t1 = min(x1, t0 + per);
   SpecWs w = spec_ws(ws, pl.B, chunks, V);
   double* qb = w.qbuf + (size_t)b * V;
   double* pb = w.pbuf + (size_t)b * V;
   const int32_t* tok = tokens + (size_t)b * N;
   const int32_t* par = parents + (size_t)b * N;
-  const int tid = threadIdx.x;
   // ragged batches: nodes past this sequence's tree do not exist
   const int Nb = pl.tree_len ? min(max(pl.tree_len[b], 1), N) : N;
   const bool pm = pl.mode != 0;   // deterministic siblings (point-mass draft per child)
@@ -273,10 +342,27 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
   double sample_c = 0.0;   // corrected target for the final draw: max(0, q - c p) / S
   double fallback_c = 0.0; // the previous c, should the residual at sample_c be empty
   int sample_node = 0;
-  const bool in_regs = x1 - x0 <= kSpecRegs * kSpecThreads;
-  double qr[kSpecRegs], pr[kSpecRegs];   // q, p of the thread's entries when in_regs
+  double qr[kSpecRegs], pr[kSpecRegs];   // REGS: q, p of entries t0 + i (0 past t1)
 
   for (;;) {
+    const size_t node = (size_t)b * N + v;
+    const int row = draft_row[node];
+    const bool row_ok = row >= 0 && row < pl.R;
+    const float* tl = target_logits + node * V;
+    const float* dl = draft_logits + ((size_t)b * pl.R + (row_ok ? row : 0)) * V;
+    // the node's logits are requested before its children are known, so that their
+    // latency overlaps the tree walk (the draft row only when the node has one)
+    float tr[kSpecRegs], dr[kSpecRegs];
+    if constexpr (REGS) {
+#pragma unroll
+      for (int i = 0; i < kSpecRegs; ++i) {
+        const int x = t0 + i;
+        tr[i] = x < t1 ? tl[x] : 0.f;
+        dr[i] = (x < t1 && row_ok && !pm) ? dl[x] : 0.f;
+      }
+    }
+    const float lse_t = pl.target_lse ? pl.target_lse[node] : 0.f;
+    const float lse_d = (pl.draft_lse && row_ok && !pm) ? pl.draft_lse[(size_t)b * pl.R + row] : 0.f;
     // children of v in ascending index (none at max_depth)
     if (tid < 64) {
       const bool is_kid = tid < Nb && tid > 0 && par[tid] == v && alpha < pl.max_depth;
@@ -286,45 +372,39 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
     }
     __syncthreads();
     const int nk = nkids_s;
-    int row = draft_row[(size_t)b * N + v];
-    const bool has_draft = nk > 0 && row >= 0 && row < pl.R;
-    const float* tl = target_logits + ((size_t)b * N + v) * V;
-    const float* dl = (has_draft && !pm) ? draft_logits + ((size_t)b * pl.R + row) * V : tl;
-    // the children's operands, loaded once here so that their latency overlaps the
+    const bool has_draft = nk > 0 && row_ok;
+    const bool need_p = has_draft && !pm;   // children tried against the draft distribution
+    // the children's tokens and logits, loaded here so that their latency overlaps the
     // softmax below instead of sitting in every rejection round
+    int ktok = -1;
+    float ktl = 0.f, kdl = 0.f;
     if (tid < nk) {
       const int kid = kids[tid];
       const int t = tok[kid];
-      const bool tv = t >= 0 && t < V;
-      kid_tok[tid] = tv ? t : -1;
-      kid_tl[tid] = tv ? tl[t] : 0.f;
-      kid_dl[tid] = tv ? dl[t] : 0.f;
+      if (t >= 0 && t < V) {
+        ktok = t;
+        ktl = tl[t];
+        kdl = need_p ? dl[t] : 0.f;
+      }
+      kid_tok[tid] = ktok;
       kid_u[tid] = u_accept[(size_t)b * N + kid];
     }
 
-    // ---- q and p of node v.  A thread's entries are x0 + tid + i * kSpecThreads; when
-    // the chunk fits, they are kept in registers (same order of operations either way).
-    // With the caller's normalisers (target_lse, and draft_lse when the children are
-    // tried against the draft distribution) every value is exp(logit - lse) at once;
-    // otherwise the chunk max and exp-sum are exchanged first and the normalisers
-    // formed from them.
-    const bool need_p = has_draft && !pm;
+    // ---- q and p of node v.  With the caller's normalisers (target_lse, and draft_lse
+    // when the children are tried against the draft distribution) every value is
+    // exp(logit - lse) at once; otherwise the chunk max and exp-sum are exchanged first
+    // and the normalisers formed from them.
     const bool given = pl.target_lse != nullptr && (!need_p || pl.draft_lse != nullptr);
     double lse_q = 0.0, lse_p = 0.0;
     if (given) {
-      lse_q = (double)pl.target_lse[(size_t)b * N + v];
-      if (need_p) lse_p = (double)pl.draft_lse[(size_t)b * pl.R + row];
-      if (in_regs) {
+      lse_q = (double)lse_t;
+      if (need_p) lse_p = (double)lse_d;
+      if constexpr (REGS) {
 #pragma unroll
         for (int i = 0; i < kSpecRegs; ++i) {
-          const int x = x0 + tid + i * kSpecThreads;
-          const bool in = x < x1;
-          qr[i] = in ? exp((double)tl[x] - lse_q) : 0.0;
-          pr[i] = (in && need_p) ? exp((double)dl[x] - lse_p) : 0.0;
-          if (in) {
-            qb[x] = qr[i];
-            if (!pm) pb[x] = pr[i];
-          }
+          const bool in = t0 + i < t1;
+          qr[i] = in ? exp((double)tr[i] - lse_q) : 0.0;
+          pr[i] = (in && need_p) ? exp((double)dr[i] - lse_p) : 0.0;
         }
       } else {
         for (int x = x0 + tid; x < x1; x += kSpecThreads) {
@@ -334,49 +414,41 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
       }
     } else {
       double mq = -INFINITY, mp = -INFINITY;
-      float tr[kSpecRegs], dr[kSpecRegs];
-      if (in_regs) {
+      if constexpr (REGS) {
 #pragma unroll
         for (int i = 0; i < kSpecRegs; ++i) {
-          const int x = x0 + tid + i * kSpecThreads;
-          tr[i] = x < x1 ? tl[x] : -INFINITY;
-          dr[i] = (x < x1 && !pm) ? dl[x] : -INFINITY;
-        }
-#pragma unroll
-        for (int i = 0; i < kSpecRegs; ++i) {
-          if (x0 + tid + i * kSpecThreads < x1) {
+          if (t0 + i < t1) {
             mq = fmax(mq, (double)tr[i]);
-            mp = fmax(mp, (double)dr[i]);
+            if (need_p) mp = fmax(mp, (double)dr[i]);
           }
         }
       } else {
         for (int x = x0 + tid; x < x1; x += kSpecThreads) {
           mq = fmax(mq, (double)tl[x]);
-          mp = fmax(mp, (double)dl[x]);
+          if (need_p) mp = fmax(mp, (double)dl[x]);
         }
       }
-      // (point-mass mode never uses the draft distribution: its half is skipped)
       mq = wg_max_d(mq, red);
-      if (!pm) mp = wg_max_d(mp, red);
+      if (need_p) mp = wg_max_d(mp, red);
       double zq = 0.0, zp = 0.0;
-      if (in_regs) {
+      if constexpr (REGS) {
         // exp(x - chunk max) stays in qr / pr; scaled to q / p once the totals are known
 #pragma unroll
         for (int i = 0; i < kSpecRegs; ++i) {
-          const bool in = x0 + tid + i * kSpecThreads < x1;
+          const bool in = t0 + i < t1;
           qr[i] = in ? exp((double)tr[i] - mq) : 0.0;
-          pr[i] = (in && !pm) ? exp((double)dr[i] - mp) : 0.0;
+          pr[i] = (in && need_p) ? exp((double)dr[i] - mp) : 0.0;
           zq += qr[i];
           zp += pr[i];
         }
       } else {
         for (int x = x0 + tid; x < x1; x += kSpecThreads) {
           zq += exp((double)tl[x] - mq);
-          if (!pm) zp += exp((double)dl[x] - mp);
+          if (need_p) zp += exp((double)dl[x] - mp);
         }
       }
       zq = wg_sum_d(zq, red);
-      if (!pm) zp = wg_sum_d(zp, red);
+      if (need_p) zp = wg_sum_d(zp, red);
       {
         const double mine[4] = {mq, zq, mp, zp};
         if (!exchange(w, b, chunks, me, gen++, 4, mine, lds_all, &lds_flag)) { aborted = true; break; }
@@ -390,36 +462,35 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
       // thread (an empty chunk adds +0.0, which leaves the sum unchanged)
       if (tid < chunks) {
         cterm[tid] = lds_all[4 * tid] > -INFINITY ? lds_all[4 * tid + 1] * exp(lds_all[4 * tid] - Mq) : 0.0;
-      } else if (tid >= 64 && tid < 64 + chunks && !pm) {
+      } else if (tid >= 64 && tid < 64 + chunks && need_p) {
         const int c = tid - 64;
         cterm[tid] = lds_all[4 * c + 2] > -INFINITY ? lds_all[4 * c + 3] * exp(lds_all[4 * c + 2] - Mp) : 0.0;
       }
       __syncthreads();
       double Zq = 0.0, Zp = 0.0;
       for (int c = 0; c < chunks; ++c) Zq += cterm[c];
-      if (!pm)
+      if (need_p)
         for (int c = 0; c < chunks; ++c) Zp += cterm[64 + c];
       lse_q = Mq + log(Zq);
-      lse_p = pm ? 0.0 : Mp + log(Zp);
-      if (in_regs) {
+      lse_p = need_p ? Mp + log(Zp) : 0.0;
+      if constexpr (REGS) {
         const double sq = exp(mq - lse_q);
-        const double sp = pm ? 0.0 : exp(mp - lse_p);
+        const double sp = need_p ? exp(mp - lse_p) : 0.0;
 #pragma unroll
         for (int i = 0; i < kSpecRegs; ++i) {
-          const int x = x0 + tid + i * kSpecThreads;
           qr[i] *= sq;
           pr[i] *= sp;
-          if (x < x1) {
-            qb[x] = qr[i];
-            if (!pm) pb[x] = pr[i];
-          }
         }
       } else {
         for (int x = x0 + tid; x < x1; x += kSpecThreads) {
           qb[x] = exp((double)tl[x] - lse_q);
-          if (!pm) pb[x] = exp((double)dl[x] - lse_p);
+          if (!pm) pb[x] = need_p ? exp((double)dl[x] - lse_p) : 0.0;
         }
       }
+    }
+    if (tid < nk) {
+      kid_q[tid] = ktok >= 0 ? exp((double)ktl - lse_q) : 0.0;
+      kid_p[tid] = (ktok >= 0 && need_p) ? exp((double)kdl - lse_p) : 0.0;
     }
     __syncthreads();
 
@@ -438,13 +509,19 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
       // at t, so q'(t) = q(t) / (1 - removed) for a token not rejected yet (0 for one
       // that was), and a rejection removes q(t).  Every workgroup takes the same
       // decisions from the same values: no exchange.
+      if (tid < nk) {
+        unsigned long long same = 0ull;
+        for (int i = 0; i < tid; ++i)
+          if (kid_tok[i] == ktok) same |= 1ull << i;
+        kid_same[tid] = same;
+      }
+      __syncthreads();
       double removed = 0.0;
       unsigned long long gone = 0ull;   // children whose token was removed from q'
       for (int j = 0; j < nk; ++j) {
         const int t = kid_tok[j];
-        bool dup = false;
-        for (int i = 0; i < j; ++i) dup |= ((gone >> i) & 1ull) && kid_tok[i] == t;
-        const double qt = t >= 0 ? exp((double)kid_tl[j] - lse_q) : 0.0;
+        const bool dup = (gone & kid_same[j]) != 0ull;
+        const double qt = kid_q[j];
         const double ratio = (t < 0 || dup) ? 0.0 : fmin(1.0, qt / (1.0 - removed));
         if ((double)kid_u[j] < ratio) {
           accepted = kids[j];
@@ -457,20 +534,27 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
       }
       if (accepted < 0) {
         // the draw from q without the removed tokens: zero them in this chunk of q
-        if (tid < nk && ((gone >> tid) & 1ull)) {
-          const int t = kid_tok[tid];
-          if (t >= x0 && t < x1) qb[t] = 0.0;
+        if constexpr (REGS) {
+          for (int j = 0; j < nk; ++j) {
+            const int t = kid_tok[j];
+            if (((gone >> j) & 1ull) && t >= t0 && t < t1) {
+#pragma unroll
+              for (int i = 0; i < kSpecRegs; ++i)
+                if (t0 + i == t) qr[i] = 0.0;
+            }
+          }
+        } else {
+          if (tid < nk && ((gone >> tid) & 1ull)) {
+            const int t = kid_tok[tid];
+            if (t >= x0 && t < x1) qb[t] = 0.0;
+          }
+          __syncthreads();
         }
-        __syncthreads();
       }
     }
     for (int j = 0; j < (pm ? 0 : nk); ++j) {
       const int kid = kids[j];
-      double qt = 0.0, pt = 0.0;
-      if (kid_tok[j] >= 0) {
-        qt = exp((double)kid_tl[j] - lse_q);
-        pt = exp((double)kid_dl[j] - lse_p);
-      }
+      const double qt = kid_q[j], pt = kid_p[j];
       const double resid = fmax(0.0, qt - cst * pt);
       const double ratio = pt > 0.0 ? fmin(1.0, resid / (S * pt)) : (resid > 0.0 ? 1.0 : 0.0);
       if ((double)kid_u[j] < ratio) {
@@ -485,18 +569,18 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
         break;
       }
       double part = 0.0;
-      if (in_regs) {
+      if constexpr (REGS) {
+        // entries past t1 hold q = p = 0 and add +0.0
 #pragma unroll
-        for (int i = 0; i < kSpecRegs; ++i)
-          if (x0 + tid + i * kSpecThreads < x1) part += fmax(0.0, qr[i] - c2 * pr[i]);
+        for (int i = 0; i < kSpecRegs; ++i) part += fmax(0.0, qr[i] - c2 * pr[i]);
       } else {
         for (int x = x0 + tid; x < x1; x += kSpecThreads) part += fmax(0.0, qb[x] - c2 * pb[x]);
       }
-      part = wg_sum_d(part, red);
-      const double mine[4] = {part, 0.0, 0.0, 0.0};
-      if (!exchange(w, b, chunks, me, gen++, 1, mine, lds_all, &lds_flag)) { aborted = true; break; }
-      double S2 = 0.0;
-      for (int c = 0; c < chunks; ++c) S2 += lds_all[4 * c];
+      double S2;
+      if (!exchange_sum(w, b, chunks, me, gen++, part, red, lds_all, &lds_flag, S2)) {
+        aborted = true;
+        break;
+      }
       if (S2 > 0.0) {
         cst = c2;
         S = S2;
@@ -521,34 +605,50 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
     // the last c vanished by rounding, the draw falls back to the previous c (the
     // decision every workgroup takes from the same totals)
     double c = sample_c;
+    const float us = u_sample[(size_t)b * N + sample_node];
     for (;;) {
-      // contiguous per-thread ranges so that the scan runs in index order
-      const int span = x1 - x0;
-      const int per = (span + kSpecThreads - 1) / kSpecThreads;
-      const int t0 = x0 + tid * per;
-      const int t1 = min(x1, t0 + per);
+      // the thread's mass over its contiguous entries, then an index-order scan of the
+      // threads' masses: within each wave by lanes, then over the waves
       double tsum = 0.0;
       int tlast = -1;
-      for (int x = t0; x < t1; ++x) {
-        const double m = pm ? qb[x] : fmax(0.0, qb[x] - c * pb[x]);
-        tsum += m;
-        if (m > 0.0) tlast = x;
+      if constexpr (REGS) {
+#pragma unroll
+        for (int i = 0; i < kSpecRegs; ++i) {
+          const double m = pm ? qr[i] : fmax(0.0, qr[i] - c * pr[i]);
+          tsum += m;
+          if (m > 0.0) tlast = t0 + i;
+        }
+      } else {
+        for (int x = t0; x < t1; ++x) {
+          const double m = pm ? qb[x] : fmax(0.0, qb[x] - c * pb[x]);
+          tsum += m;
+          if (m > 0.0) tlast = x;
+        }
       }
-      // exclusive scan of thread sums (index order) and the chunk total
-      __shared__ double scan_s[kSpecThreads];
-      __shared__ int last_s[kSpecThreads];
-      scan_s[tid] = tsum;
-      last_s[tid] = tlast;
+      double incl = tsum;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const double y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+      }
+      double excl = __shfl_up(incl, 1);
+      if (lane == 0) excl = 0.0;
+      const int wlast = wave_max_i(tlast);
+      if (lane == 63) {
+        wtot_s[wid] = incl;
+        wlast_s[wid] = wlast;
+      }
+      if (tid == 0) found_s = INT_MAX;
       __syncthreads();
       double chunk_total = 0.0;
       double before = 0.0;
       int chunk_last = -1;
-      for (int i = 0; i < kSpecThreads; ++i) {
-        if (i == tid) before = chunk_total;
-        chunk_total += scan_s[i];
-        chunk_last = max(chunk_last, last_s[i]);
+#pragma unroll
+      for (int i = 0; i < kSpecThreads / 64; ++i) {
+        if (i == wid) before = chunk_total + excl;
+        chunk_total += wtot_s[i];
+        chunk_last = max(chunk_last, wlast_s[i]);
       }
-      __syncthreads();
       const double mine[4] = {chunk_total, (double)chunk_last, 0.0, 0.0};
       if (!exchange(w, b, chunks, me, gen++, 2, mine, lds_all, &lds_flag)) {
         aborted = true;
@@ -568,29 +668,38 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
         c = fallback_c;
         continue;
       }
-      const double T = (double)u_sample[(size_t)b * N + sample_node] * total;
-      __shared__ int found_s;
-      if (tid == 0) found_s = -1;
-      __syncthreads();
+      const double T = (double)us * total;
       if (T < total && T >= offset && T < offset + chunk_total) {
         const double Tl = T - offset;
         if (Tl >= before && Tl < before + tsum) {
+          // the first entry whose running mass passes Tl; threads whose ranges touch at
+          // a rounding boundary both report, and the lower index is kept
           double run = before;
-          for (int x = t0; x < t1; ++x) {
-            run += pm ? qb[x] : fmax(0.0, qb[x] - c * pb[x]);
-            if (run > Tl) {
-              found_s = x;
-              break;
+          int f = -1;
+          if constexpr (REGS) {
+#pragma unroll
+            for (int i = 0; i < kSpecRegs; ++i) {
+              run += pm ? qr[i] : fmax(0.0, qr[i] - c * pr[i]);
+              if (f < 0 && run > Tl) f = t0 + i;
+            }
+          } else {
+            for (int x = t0; x < t1; ++x) {
+              run += pm ? qb[x] : fmax(0.0, qb[x] - c * pb[x]);
+              if (run > Tl) {
+                f = x;
+                break;
+              }
             }
           }
+          if (f >= 0) atomicMin(&found_s, f);
         }
         __syncthreads();
-        if (tid == 0 && found_s < 0) found_s = chunk_last;   // rounding inside the chunk
+        if (tid == 0 && found_s == INT_MAX) found_s = chunk_last;   // rounding inside the chunk
       } else if (!(T < total) && me == glast_owner) {
-        if (tid == 0) found_s = glast;                         // rounding past the total
+        if (tid == 0) found_s = glast;                               // rounding past the total
       }
       __syncthreads();
-      if (tid == 0 && found_s >= 0) out_tokens[(size_t)b * cap + alpha] = found_s;
+      if (tid == 0 && found_s != INT_MAX && found_s >= 0) out_tokens[(size_t)b * cap + alpha] = found_s;
       break;
     }
   }
@@ -643,7 +752,7 @@ SpecPlan plan_accept_spec(int B, int N, int V) {
   pl.V = V;
   // about 4K vocabulary entries per workgroup, at most 64 per sequence, and at most
   // 256 workgroups in all so that every workgroup of a sequence is resident at once
-  int c = (V + 4095) / 4096;
+  int c = (V + kSpecChunk - 1) / kSpecChunk;
   if (c > 64) c = 64;
   int cap = 256 / (B > 0 ? B : 1);
   if (cap < 1) cap = 1;
@@ -673,9 +782,15 @@ hipError_t launch_accept_spec(const SpecPlan& pl, const int32_t* tokens, const i
                      pl.chunks, pl.V);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(accept_spec_kernel, dim3(pl.B * pl.chunks), dim3(kSpecThreads), 0, stream,
-                     tokens, parents, draft_row, target_logits, draft_logits, u_accept, u_sample, pl,
-                     accept_len, accept_path, out_tokens, workspace);
+  const int chunk_len = (pl.V + pl.chunks - 1) / pl.chunks;
+  if (chunk_len <= kSpecChunk)
+    hipLaunchKernelGGL(accept_spec_kernel<true>, dim3(pl.B * pl.chunks), dim3(kSpecThreads), 0,
+                       stream, tokens, parents, draft_row, target_logits, draft_logits, u_accept,
+                       u_sample, pl, accept_len, accept_path, out_tokens, workspace);
+  else
+    hipLaunchKernelGGL(accept_spec_kernel<false>, dim3(pl.B * pl.chunks), dim3(kSpecThreads), 0,
+                       stream, tokens, parents, draft_row, target_logits, draft_logits, u_accept,
+                       u_sample, pl, accept_len, accept_path, out_tokens, workspace);
   return hipGetLastError();
 }
 
