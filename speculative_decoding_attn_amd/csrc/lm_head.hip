@@ -199,6 +199,19 @@ lm_head_gemm(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W
   // loads go out over the second half of the block only, which keeps fewer of them in
   // flight and measured faster there; the smaller tiles spread them over the block
   constexpr int WSTART = WVM > 1 ? NGI / 2 : 0;
+  // Hidden-stage rows of the 8-row groups wholly past M are never loaded, but the
+  // MFMAs still read them: zero them once (both stages) so that those products run on
+  // zeros instead of whatever an earlier kernel left in LDS.  The chip is power-
+  // limited and zero operands draw less (240 rows: 527 -> 517 us after an attention
+  // call); their outputs are never written either way.
+  {
+    const int r0 = min(MROWS, (max(0, M - m0) + 7) & ~7);
+    const int n16 = (MROWS - r0) * (RB / 16);
+    for (int i = tid; i < 2 * n16; i += THREADS) {
+      const int st = i / n16, k = i - st * n16;
+      *(uint4*)(hst + st * HSTAGE + r0 * RB + k * 16) = uint4{0u, 0u, 0u, 0u};
+    }
+  }
 #pragma unroll
   for (int t = 0; t < W_DMA; ++t) issue_w(0, 0, t);
 #pragma unroll
