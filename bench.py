@@ -247,6 +247,23 @@ def copy_calibration(torch, dev, nbytes=1 << 30, reps=5):
                       "copy_gbs_read_plus_write": round(2 * nbytes / sec / 1e9, 1)}))
 
 
+def _warm(torch, fn, seconds=0.25, min_calls=3):
+    """Untimed calls of fn until the GPU has run this workload for about `seconds`.  The
+    chip's power management runs a fresh load fast for its first milliseconds, then
+    throttles hard and settles over the next few tens of milliseconds (a C5 step: 0.91 ms
+    over its first 50 steps, then 0.79-0.81 ms, flat over 10 s), so every timed window
+    starts in the settled state."""
+    n = 0
+    t0 = time.perf_counter()
+    while n < min_calls or time.perf_counter() - t0 < seconds:
+        fn()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
 def measured_ceilings(torch, sda, dev, read_bytes=4 << 30, reps=10, mfma_iters=20000):
     """What this GPU reaches, next to the nominal peaks: a streaming HBM read of a 4 GiB
     buffer (the library's read probe, 16-byte non-temporal loads), a 1 GiB device copy
@@ -255,8 +272,7 @@ def measured_ceilings(torch, sda, dev, read_bytes=4 << 30, reps=10, mfma_iters=2
     s = torch.cuda.current_stream()
 
     def timed(fn, n):
-        fn()
-        torch.cuda.synchronize()
+        _warm(torch, fn, seconds=0.15, min_calls=1)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(s)
         for _ in range(n):
@@ -292,9 +308,7 @@ def lm_head_back_to_back(torch, sda, dev, x, iters=20):
     cfg = synth.CONFIGS["C5"]
     M, H, V = cfg.B * cfg.N, cfg.H, cfg.V
     ws = torch.empty(sda.load().eagle_lm_head_workspace(M, H, V), dtype=torch.uint8, device=dev)
-    for _ in range(3):
-        sda.eagle_lm_head_argmax(x["hidden"], x["W"], want_logits=False, workspace=ws)
-    torch.cuda.synchronize()
+    _warm(torch, lambda: sda.eagle_lm_head_argmax(x["hidden"], x["W"], want_logits=False, workspace=ws))
     s = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(s)
@@ -306,7 +320,7 @@ def lm_head_back_to_back(torch, sda, dev, x, iters=20):
     return dict(roof(us, lm_bytes(M, H, V), 2.0 * M * H * V), calls=iters)
 
 
-def config_step(torch, sda, dev, name, steps=20, warmup=3):
+def config_step(torch, sda, dev, name, steps=50):
     """One verification step at another of the five workloads, each call timed with HIP
     events on the launch stream:
       C2  static EAGLE-1 tree: attention -> LM head -> greedy acceptance
@@ -375,9 +389,9 @@ def config_step(torch, sda, dev, name, steps=20, warmup=3):
             ev[k].record(stream)
         return tree, acc
 
-    for _ in range(warmup):
-        tree, acc = step()
-    torch.cuda.synchronize()
+    last = {}
+    _warm(torch, lambda: last.update(r=step()))
+    tree, acc = last["r"]
     parents_np = tree["parents"].cpu().numpy()
     alen = acc[0].cpu().numpy()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
@@ -427,9 +441,7 @@ def spec_latency(torch, sda, dev, iters=100, mode="sampled", with_lse=True):
         sda.eagle_accept_spec(tree["tokens"], tree["parents"], tree["draft_row"], tl, dl, ua, us,
                               cfg.max_depth, workspace=ws, mode=mode, **lse)
 
-    for _ in range(3):
-        call()
-    torch.cuda.synchronize()
+    _warm(torch, call)
     s = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(s)
@@ -467,9 +479,7 @@ def kv_commit_latency(torch, sda, dev, parents, iters=50, layers=80):
     v = torch.empty(shape, dtype=torch.bfloat16, device=dev).normal_()
     a = torch.from_numpy(alen).to(dev)
     p = torch.from_numpy(path).to(dev)
-    for _ in range(5):
-        sda.eagle_kv_commit(k, v, a, p, P)
-    torch.cuda.synchronize()
+    _warm(torch, lambda: sda.eagle_kv_commit(k, v, a, p, P))
     s = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(s)
@@ -504,9 +514,7 @@ def paged_attention(torch, sda, dev, x, parents, page_size=16, iters=20):
     kp, vp = pool_of(x["k"]), pool_of(x["v"])
     ws = torch.empty(max(1, sda.load().eagle_tree_verify_attn_paged_workspace(
         B, N, cfg.Hq, Hkv, D, P, page_size)), dtype=torch.uint8, device=dev)
-    for _ in range(3):
-        sda.eagle_tree_verify_attn_paged(x["q"], kp, vp, table, parents, P, workspace=ws)
-    torch.cuda.synchronize()
+    _warm(torch, lambda: sda.eagle_tree_verify_attn_paged(x["q"], kp, vp, table, parents, P, workspace=ws))
     s = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(s)
@@ -518,6 +526,10 @@ def paged_attention(torch, sda, dev, x, parents, page_size=16, iters=20):
     del kp, vp
     return {"page_size": page_size, "us": round(us, 2)}
 
+
+# untimed expansions after the first (about 0.2 s of work at C5: past the power
+# transient, see _warm)
+DRAFT_WARMUP = 40
 
 DRAFT_SHAPES = {
     # name: (B, H, Hq, Hkv, D, I, V, P)  draft head = one decoder layer of the target family
@@ -553,6 +565,11 @@ def draft_expansion(torch, sda, dev, name="C5", top_k=10, depth=6, n_nodes=60, i
                                                              depth)), dtype=torch.uint8, device=dev)
     out = sda.eagle_draft_expand(head, f0, root, kc, vc, P, Hq, top_k, depth, n_nodes, D ** -0.5, 1e-5,
                                  workspace=ws)
+    for i in range(DRAFT_WARMUP):
+        sda.eagle_draft_expand(head, f0, root, kc, vc, P, Hq, top_k, depth, n_nodes, D ** -0.5, 1e-5,
+                               workspace=ws, out=out)
+        if i % 4 == 3:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     s = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -578,7 +595,7 @@ RAGGED_PREFIX = [32768, 8192, 24576, 2048]
 RAGGED_TREE = [60, 40, 60, 25]
 
 
-def ragged_step(torch, sda, dev, x, steps=20):
+def ragged_step(torch, sda, dev, x, steps=50):
     """The verification step (attention, LM head, greedy acceptance) on a ragged C5
     batch: the four sequences keep C5's shapes but have prefixes of RAGGED_PREFIX
     tokens and trees of RAGGED_TREE nodes (rows of the C5 tensors past them are
@@ -619,9 +636,7 @@ def ragged_step(torch, sda, dev, x, steps=20):
         if ev:
             ev[3].record(stream)
 
-    for _ in range(3):
-        one()
-    torch.cuda.synchronize()
+    _warm(torch, one)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     for i in range(steps):
         one(evs[i])
@@ -638,7 +653,7 @@ def ragged_step(torch, sda, dev, x, steps=20):
 # (the same directory is then passed to --summarize-profiles)
 PROFILE_RUNS = {
     "prof": "rocprofv3 --kernel-trace --stats -T -d {out}/prof -o run --output-format csv "
-            "-- python -u bench.py --steps 50 --warmup 5 --no-cpu-baseline --no-spec",
+            "-- python -u bench.py --steps 200 --warmup 250 --no-cpu-baseline --no-spec",
     "prof_draft": "rocprofv3 --kernel-trace --stats -T -d {out}/prof_draft -o run --output-format csv "
                   "-- python -u bench.py --only-draft",
     "pmc_fetch": "rocprofv3 --pmc FETCH_SIZE -T -d {out}/pmc_fetch -o run --output-format csv "
@@ -673,43 +688,73 @@ def _read_csv(path):
         return list(csv.DictReader(f))
 
 
+def step_kernel_stats(trace_csv, n_warm, n_timed):
+    """(name, calls, avg us, min us, max us, total us) per kernel of a rocprofv3 kernel
+    trace, from its dispatches in launch order.  A kernel dispatched once per step (n_warm
+    + n_timed dispatches) keeps only the timed steps' dispatches, the window bench.py's
+    events cover; any other kernel keeps all of its dispatches."""
+    runs = {}
+    for r in sorted(_read_csv(trace_csv), key=lambda r: int(r["Start_Timestamp"])):
+        runs.setdefault(r["Kernel_Name"], []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    stats = []
+    for name, d in runs.items():
+        if len(d) == n_warm + n_timed:
+            d = d[n_warm:]
+        stats.append((name, len(d), sum(d) / len(d), min(d), max(d), sum(d)))
+    return stats
+
+
 def summarize_profiles(root):
     """Turn the five rocprofv3 runs of PROFILE_RUNS (under `root`) into the committed
     text summaries under profiles/ and the per-kernel traffic records bench.py reads."""
     cfg = synth.CONFIGS["C5"]
     B, N, Hq, Hkv, D, P, H, V = cfg.B, cfg.N, cfg.Hq, cfg.Hkv, cfg.D, cfg.P, cfg.H, cfg.V
-    stats = _read_csv(os.path.join(root, "prof", "run_kernel_stats.csv"))
-    total = sum(float(r["TotalDurationNs"]) for r in stats)
+    cmd = _run_cmd("prof", root)
+    flags = cmd.split()
+    n_warm = int(flags[flags.index("--warmup") + 1])
+    n_timed = int(flags[flags.index("--steps") + 1])
+    stats = step_kernel_stats(os.path.join(root, "prof", "run_kernel_trace.csv"), n_warm, n_timed)
+    total = sum(st[5] for st in stats)
     lines = ["# rocprofv3 kernel trace: C5 verification step", "",
-             "Command (repository root, one MI355X):", "", "    " + _run_cmd("prof", root), "",
+             "Command (repository root, one MI355X):", "", "    " + cmd, "",
              f"Workload: C5 (B={B}, N={N}, Hq={Hq}, Hkv={Hkv}, D={D}, P={P}, H={H}, V={V}); "
-             "55 steps (5 warmup + 50 timed, as bench.py times them), nothing else.", "",
+             f"{n_warm + n_timed} steps ({n_warm} warmup + {n_timed} timed, as bench.py times them), "
+             "nothing else.  Per-step kernels: the timed steps' dispatches only (from the kernel "
+             "trace), the window bench.py's events cover.", "",
              "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
-    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
-        lines.append(f"| {r['Name']} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
-                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
-                     f"{100.0 * float(r['TotalDurationNs']) / total:.1f} |")
+    for name, n, avg, lo, hi, tot in sorted(stats, key=lambda st: -st[5]):
+        lines.append(f"| {name} | {n} | {avg:.2f} | {lo:.2f} | {hi:.2f} | {100.0 * tot / total:.1f} |")
     with open(os.path.join(PROFILE_DIR, TRACE_MD), "w") as f:
         f.write("\n".join(lines) + "\n")
     dpath = os.path.join(root, "prof_draft", "run_kernel_stats.csv")
     if os.path.exists(dpath):
         # the library's kernels only (torch's weight initialisation is left out)
         ours = ("lm_head_", "gemm_splitk", "tree_attn_", "draft_", "rerank_")
-        dstats = [r for r in _read_csv(dpath) if r["Name"].startswith(ours)]
-        dtotal = sum(float(r["TotalDurationNs"]) for r in dstats)
+        calls = 1 + DRAFT_WARMUP + 3   # first call, warm-up calls, timed calls
+        druns = {}
+        for r in sorted(_read_csv(os.path.join(root, "prof_draft", "run_kernel_trace.csv")),
+                        key=lambda r: int(r["Start_Timestamp"])):
+            if r["Kernel_Name"].startswith(ours):
+                druns.setdefault(r["Kernel_Name"], []).append(
+                    (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        dstats = []
+        for name, d in druns.items():
+            if len(d) % calls == 0:
+                d = d[len(d) - 3 * (len(d) // calls):]   # the three timed expansions
+            dstats.append((name, len(d), sum(d) / len(d), sum(d)))
+        dtotal = sum(st[3] for st in dstats)
         B_, H_, Hq_, Hkv_, D_, I_, V_, P_ = DRAFT_SHAPES["C5"]
         dl = ["# rocprofv3 kernel trace: per-depth draft expansion, C5 shapes", "",
               "Command (repository root, one MI355X):", "", "    " + _run_cmd("prof_draft", root), "",
               f"Workload: eagle_draft_expand with a one-layer draft head (B={B_}, H={H_}, Hq={Hq_}, "
               f"Hkv={Hkv_}, D={D_}, MLP {I_}, V={V_}, draft prefix {P_}), top-k 10, depth 6, 60 nodes; "
-              "4 expansions (1 warmup + 3 timed).  lm_head_gemm runs every projection and the LM head "
-              "(6 GEMMs per depth); the library's kernels only (torch's weight initialisation is left "
-              "out).", "",
+              f"{calls} expansions ({calls - 3} warmup + 3 timed), the 3 timed ones summarised.  "
+              "lm_head_gemm runs every projection and the LM head (6 GEMMs per depth); the library's "
+              "kernels only (torch's weight initialisation is left out).", "",
               "| kernel | calls | avg us | total ms | share % |", "|---|---|---|---|---|"]
-        for r in sorted(dstats, key=lambda r: -float(r["TotalDurationNs"])):
-            dl.append(f"| {r['Name']} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
-                      f"{float(r['TotalDurationNs']) / 1e6:.3f} | "
-                      f"{100.0 * float(r['TotalDurationNs']) / dtotal:.1f} |")
+        for name, n, avg, tot in sorted(dstats, key=lambda st: -st[3]):
+            dl.append(f"| {name} | {n} | {avg:.2f} | {tot / 1e3:.3f} | {100.0 * tot / dtotal:.1f} |")
         with open(os.path.join(PROFILE_DIR, DRAFT_TRACE_MD), "w") as f:
             f.write("\n".join(dl) + "\n")
         lines += ["", *dl]
@@ -818,8 +863,11 @@ def summarize_mfma(path, root=None):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    # about 0.2 s of steps: the chip's power management throttles a fresh load hard
+    # over its first few tens of milliseconds and then settles (see _warm); the timed
+    # steps measure the settled rate, and the warmup steps' own rate is reported too
+    ap.add_argument("--warmup", type=int, default=250)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-spec", action="store_true",
                     help="only the C5 step: skip the other workloads' steps, the measured "
@@ -898,9 +946,15 @@ def main(argv=None):
             ev[4].record(stream)
         return tree, acc
 
-    for _ in range(args.warmup):
+    ew = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ew[0].record(stream)
+    for i in range(args.warmup):
         tree, _ = step()
+        if i % 8 == 7:
+            torch.cuda.synchronize()
+    ew[1].record(stream)
     torch.cuda.synchronize()
+    warmup_ms = ew[0].elapsed_time(ew[1]) / args.warmup if args.warmup > 0 else None
     parents_np = tree["parents"].cpu().numpy()
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
@@ -939,6 +993,7 @@ def main(argv=None):
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "warmup_ms_per_step": None if warmup_ms is None else round(warmup_ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "C5 Llama-3-70B-shaped tree verification: 4 sequences x 60-node "

@@ -84,3 +84,22 @@ def test_host_info_names_the_cpu():
     assert set(info) == {"cpu_model", "usable_cores", "machine_cores"}
     assert 1 <= info["usable_cores"] <= info["machine_cores"]
     assert isinstance(info["cpu_model"], str) and info["cpu_model"]
+
+
+def test_trace_summary_keeps_the_timed_steps(tmp_path):
+    """A per-step kernel's warmup dispatches (slow here) are left out of the trace
+    summary; a kernel with another dispatch count keeps all of its dispatches."""
+    path = tmp_path / "run_kernel_trace.csv"
+    rows = ["Kernel_Name,Start_Timestamp,End_Timestamp"]
+    t = 0
+    for i in range(5):   # 2 warmup + 3 timed steps
+        dur = 900_000 if i < 2 else 500_000
+        rows.append(f"step_kernel,{t},{t + dur}")
+        t += dur + 1000
+        if i == 0:
+            rows.append(f"once_kernel,{t},{t + 7000}")
+            t += 8000
+    path.write_text("\n".join(rows) + "\n")
+    stats = {st[0]: st for st in bench.step_kernel_stats(str(path), 2, 3)}
+    assert stats["step_kernel"][1:5] == (3, 500.0, 500.0, 500.0)
+    assert stats["once_kernel"][1:3] == (1, 7.0)
