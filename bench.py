@@ -247,6 +247,20 @@ def copy_calibration(torch, dev, nbytes=1 << 30, reps=5):
                       "copy_gbs_read_plus_write": round(2 * nbytes / sec / 1e9, 1)}))
 
 
+def _window_ms(torch, fn, n):
+    """Mean event time (ms) of n back-to-back calls of fn, with one event before the
+    first and one after the last (nothing recorded in between)."""
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(s)
+    for _ in range(n):
+        fn()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
 def _warm(torch, fn, seconds=0.25, min_calls=3):
     """Untimed calls of fn until the GPU has run this workload for about `seconds`.  The
     chip's power management runs a fresh load fast for its first milliseconds, then
@@ -394,11 +408,13 @@ def config_step(torch, sda, dev, name, steps=50):
     tree, acc = last["r"]
     parents_np = tree["parents"].cpu().numpy()
     alen = acc[0].cpu().numpy()
+    # step time from a window with no events inside; the per-call times from a second
+    # window with an event between the calls
+    ms = _window_ms(torch, step, steps)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
     for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()
-    ms = evs[0][0].elapsed_time(evs[-1][-1]) / steps
     per = {n: 1000.0 * sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps
            for j, n in enumerate(names)}
     kern = {"tree_attn": roof(per["tree_attn"], attn_bytes(cfg), attn_flops(parents_np, cfg)),
@@ -637,11 +653,11 @@ def ragged_step(torch, sda, dev, x, steps=50):
             ev[3].record(stream)
 
     _warm(torch, one)
+    ms = _window_ms(torch, one, steps)   # no events inside the window
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     for i in range(steps):
         one(evs[i])
     torch.cuda.synchronize()
-    ms = evs[0][0].elapsed_time(evs[-1][3]) / steps
     per = {n: 1000.0 * sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps
            for j, n in enumerate(["tree_attn", "lm_head", "accept_greedy"])}
     return {"prefix_len": RAGGED_PREFIX, "tree_len": RAGGED_TREE,
@@ -690,16 +706,17 @@ def _read_csv(path):
 
 def step_kernel_stats(trace_csv, n_warm, n_timed):
     """(name, calls, avg us, min us, max us, total us) per kernel of a rocprofv3 kernel
-    trace, from its dispatches in launch order.  A kernel dispatched once per step (n_warm
-    + n_timed dispatches) keeps only the timed steps' dispatches, the window bench.py's
-    events cover; any other kernel keeps all of its dispatches."""
+    trace, from its dispatches in launch order.  A kernel dispatched once per step keeps
+    only the dispatches of the timed steps: bench.py runs n_warm warm-up steps, then
+    n_timed steps timed as a whole, then n_timed more with an event between the calls
+    (n_warm + 2 n_timed dispatches).  Any other kernel keeps all of its dispatches."""
     runs = {}
     for r in sorted(_read_csv(trace_csv), key=lambda r: int(r["Start_Timestamp"])):
         runs.setdefault(r["Kernel_Name"], []).append(
             (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     stats = []
     for name, d in runs.items():
-        if len(d) == n_warm + n_timed:
+        if len(d) == n_warm + 2 * n_timed:
             d = d[n_warm:]
         stats.append((name, len(d), sum(d) / len(d), min(d), max(d), sum(d)))
     return stats
@@ -719,9 +736,9 @@ def summarize_profiles(root):
     lines = ["# rocprofv3 kernel trace: C5 verification step", "",
              "Command (repository root, one MI355X):", "", "    " + cmd, "",
              f"Workload: C5 (B={B}, N={N}, Hq={Hq}, Hkv={Hkv}, D={D}, P={P}, H={H}, V={V}); "
-             f"{n_warm + n_timed} steps ({n_warm} warmup + {n_timed} timed, as bench.py times them), "
-             "nothing else.  Per-step kernels: the timed steps' dispatches only (from the kernel "
-             "trace), the window bench.py's events cover.", "",
+             f"{n_warm + 2 * n_timed} steps ({n_warm} warmup, {n_timed} timed as a whole, {n_timed} "
+             "timed call by call, as bench.py runs them), nothing else.  Per-step kernels: the "
+             f"{2 * n_timed} timed steps' dispatches only (from the kernel trace).", "",
              "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
     for name, n, avg, lo, hi, tot in sorted(stats, key=lambda st: -st[5]):
         lines.append(f"| {name} | {n} | {avg:.2f} | {lo:.2f} | {hi:.2f} | {100.0 * tot / total:.1f} |")
@@ -957,16 +974,26 @@ def main(argv=None):
     warmup_ms = ew[0].elapsed_time(ew[1]) / args.warmup if args.warmup > 0 else None
     parents_np = tree["parents"].cpu().numpy()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # the timed steps: one event before and one after, nothing recorded in between (an
+    # event between the calls of a step costs the step about 11 us)
+    ew = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     torch.cuda.synchronize()
+    ew[0].record(stream)
+    for i in range(args.steps):
+        step()
+    ew[1].record(stream)
+    torch.cuda.synchronize()
+    total_ms = ew[0].elapsed_time(ew[1])
+    ms_per_step = total_ms / args.steps
+    # the per-call breakdown: as many steps again, with an event between the calls
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
-    total_ms = evs[0][0].elapsed_time(evs[-1][4])
     names = ["rerank", "tree_attn", "lm_head", "accept_greedy"]
     per = {n: 1000.0 * sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps
            for j, n in enumerate(names)}
-    ms_per_step = total_ms / args.steps
+    breakdown_ms = evs[0][0].elapsed_time(evs[-1][4]) / args.steps
     value = B * N / (ms_per_step / 1000.0)
 
     # rooflines
@@ -994,6 +1021,7 @@ def main(argv=None):
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "warmup_ms_per_step": None if warmup_ms is None else round(warmup_ms, 4),
+        "breakdown_ms_per_step": round(breakdown_ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "C5 Llama-3-70B-shaped tree verification: 4 sequences x 60-node "

@@ -92,7 +92,7 @@ def test_trace_summary_keeps_the_timed_steps(tmp_path):
     path = tmp_path / "run_kernel_trace.csv"
     rows = ["Kernel_Name,Start_Timestamp,End_Timestamp"]
     t = 0
-    for i in range(5):   # 2 warmup + 3 timed steps
+    for i in range(8):   # 2 warmup steps, 3 timed as a whole, 3 timed call by call
         dur = 900_000 if i < 2 else 500_000
         rows.append(f"step_kernel,{t},{t + dur}")
         t += dur + 1000
@@ -101,5 +101,5 @@ def test_trace_summary_keeps_the_timed_steps(tmp_path):
             t += 8000
     path.write_text("\n".join(rows) + "\n")
     stats = {st[0]: st for st in bench.step_kernel_stats(str(path), 2, 3)}
-    assert stats["step_kernel"][1:5] == (3, 500.0, 500.0, 500.0)
+    assert stats["step_kernel"][1:5] == (6, 500.0, 500.0, 500.0)
     assert stats["once_kernel"][1:3] == (1, 7.0)
