@@ -159,6 +159,16 @@ lm_head_gemm(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W
             base + NW * WSTAGE + st * HSTAGE + 8 * (wv * H_DMA + t) * RB);
   };
 
+  // The last row tile of the second row half holds at most 16 real rows when M sits
+  // just past a multiple of 32 below the tile's end (240 rows in the 256-row tile:
+  // rows 224-239).  Its waves then multiply that tile on the 16x16x32 MFMA (16 hidden
+  // rows x 16 vocabulary rows, half the matrix-core time of a 32-row tile) and the
+  // other tiles as usual: HALF below.  The switch is wave-uniform; both paths run the
+  // same barriers.
+  const bool half_tail = WVM > 1 && wvm == WVM - 1 && M - (m0 + MROWS - 32) <= 16;
+  f32x4* red = (f32x4*)smem;   // [WVV][MROWS] partials of this workgroup (reuses the staging LDS)
+  auto body = [&](auto HALFC) __attribute__((always_inline)) {
+  constexpr bool HALF = decltype(HALFC)::value;
   f32x16 acc[VT][MT];
 #pragma unroll
   for (int j = 0; j < VT; ++j)
@@ -166,6 +176,9 @@ lm_head_gemm(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W
     for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[j][i][r] = 0.f;
+  f32x4 acc16[2 * VT];   // HALF: vocabulary rows 16q .. 16q+15 of the last row tile
+#pragma unroll
+  for (int q = 0; q < 2 * VT; ++q) acc16[q] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // LDS fragment reads.  A block is NG = 4*MT groups g = (k-step s, row tile i); group
   // g multiplies the VT W fragments of step s with hidden fragment (s, i).
@@ -174,10 +187,28 @@ lm_head_gemm(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W
     const int r = wvv * VT * 32 + 32 * j + l32;
     return *(const bf16x8*)(wst + stage * WSTAGE + r * RB + 16 * swz(r, 2 * s + half));
   };
-  auto h_frag = [&](int stage, int g) {
+  auto h_frag32 = [&](int stage, int g) {
     const int s = g / MT, i = g % MT;
     const int r = wvm * MT * 32 + 32 * i + l32;
     return *(const bf16x8*)(hst + stage * HSTAGE + r * RB + 16 * swz(r, 2 * s + half));
+  };
+  // 16x16x32 operands of the last row tile (HALF): lane l holds row l % 16 of its 16
+  // rows and columns 32kk + 8(l/16) .. +7 of the block (k-steps 2kk, 2kk+1)
+  const int l16 = lane & 15, q16 = lane >> 4;
+  auto h_frag16 = [&](int stage, int kk) {
+    const int r = wvm * MT * 32 + 32 * (MT - 1) + l16;
+    return *(const bf16x8*)(hst + stage * HSTAGE + r * RB + 16 * swz(r, 4 * kk + q16));
+  };
+  auto w_frag16 = [&](int stage, int kk, int q) {
+    const int r = wvv * VT * 32 + 16 * q + l16;
+    return *(const bf16x8*)(wst + stage * WSTAGE + r * RB + 16 * swz(r, 4 * kk + q16));
+  };
+  // hidden operand of group g: with HALF the last tile's groups of odd k-steps carry the
+  // 16x16x32 operand of k-steps s-1, s, those of even k-steps none
+  auto h_frag = [&](int stage, int g) {
+    if (HALF && g % MT == MT - 1)
+      return (g / MT) % 2 == 1 ? h_frag16(stage, (g / MT) / 2) : bf16x8{};
+    return h_frag32(stage, g);
   };
 
   // Pipeline.  Block b's W is in stage b%3, its hidden rows in stage b%2.  Hidden
@@ -230,6 +261,7 @@ lm_head_gemm(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W
   }
 
   bf16x8 wf[2][VT];
+  bf16x8 w16[2 * VT];   // HALF: the last tile's W operands of the current odd k-step
   bf16x8 hf[LA + 1];
 #pragma unroll
   for (int j = 0; j < VT; ++j) wf[0][j] = w_frag(0, 0, j);
@@ -264,17 +296,77 @@ lm_head_gemm(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W
       for (int t = 0; t < H_DMA; ++t)
         if (NGI + (t * LA) / H_DMA == g && more) issue_h(b + 2, sh, t);
       if (g >= NGI) hf[(g + LA) % (LA + 1)] = h_frag(sh1, g + LA - NG);
+      if constexpr (HALF) {
+        if (i == 0 && s % 2 == 1) {
 #pragma unroll
-      for (int j = 0; j < VT; ++j) acc[j][i] = mfma32(wf[s & 1][j], hf[g % (LA + 1)], acc[j][i]);
+          for (int q = 0; q < 2 * VT; ++q) w16[q] = w_frag16(sw, s / 2, q);
+        }
+      }
+      if (HALF && i == MT - 1) {
+        if (s % 2 == 1) {
+#pragma unroll
+          for (int q = 0; q < 2 * VT; ++q)
+            acc16[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w16[q], hf[g % (LA + 1)], acc16[q], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < VT; ++j) acc[j][i] = mfma32(wf[s & 1][j], hf[g % (LA + 1)], acc[j][i]);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
   __syncthreads();   // every wave is done with the stages; the epilogue reuses them
 
   // ---- epilogue: per-lane top-2 / exp-sum over its 16*VT vocabulary entries
-  f32x4* red = (f32x4*)smem;   // [WVV][MROWS] partials of this workgroup (reuses the staging LDS)
+  if constexpr (HALF) {
+    // the 16x16x32 tile: lane l holds hidden row l % 16 and, per q, vocabulary rows
+    // 16q + 4(l/16) .. +3; the four lanes of a row are l % 16 + 16 {0, 1, 2, 3}
+    const int mloc = wvm * MT * 32 + 32 * (MT - 1) + l16;
+    const int m = m0 + mloc;
+    Top2 t{-INFINITY, -INFINITY, 0.f, 0x7fffffff};
 #pragma unroll
-  for (int i = 0; i < MT; ++i) {
+    for (int q = 0; q < 2 * VT; ++q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int vocab = v0 + 16 * q + 4 * q16 + r;
+        const float x = vocab < V ? acc16[q][r] : -INFINITY;
+        if (x > t.mx) {
+          t.sec = t.mx;
+          t.mx = x;
+          t.idx = vocab;
+        } else if (x > t.sec) {
+          t.sec = x;
+        }
+      }
+    float z = 0.f;
+#pragma unroll
+    for (int q = 0; q < 2 * VT; ++q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int vocab = v0 + 16 * q + 4 * q16 + r;
+        if (vocab < V) z += __builtin_amdgcn_exp2f((acc16[q][r] - t.mx) * kLog2e);
+      }
+    t.z = z;
+    if (logits != nullptr && m < M) {
+#pragma unroll
+      for (int q = 0; q < 2 * VT; ++q) {
+        const int vocab = v0 + 16 * q + 4 * q16;
+        float* dst = logits + ((size_t)ks * M + m) * V + vocab;   // split-K: slice ks
+        if (vocab + 3 < V && (V & 3) == 0) {
+          *(f32x4*)dst = acc16[q];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (vocab + e < V) dst[e] = acc16[q][e];
+        }
+      }
+    }
+    t = merge_top2(t, shfl_xor_top2(t, 16));
+    t = merge_top2(t, shfl_xor_top2(t, 32));
+    if (q16 == 0) red[wvv * MROWS + mloc] = f32x4{t.mx, t.sec, t.z, __int_as_float(t.idx)};
+  }
+#pragma unroll
+  for (int i = 0; i < (HALF ? MT - 1 : MT); ++i) {
     const int mloc = wvm * MT * 32 + 32 * i + l32;
     const int m = m0 + mloc;
     Top2 t{-INFINITY, -INFINITY, 0.f, 0x7fffffff};
@@ -321,6 +413,11 @@ lm_head_gemm(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W
     t = merge_top2(t, shfl_xor_top2(t, 32));
     if (half == 0) red[wvv * MROWS + mloc] = f32x4{t.mx, t.sec, t.z, __int_as_float(t.idx)};
   }
+  };
+  if (half_tail)
+    body(std::true_type{});
+  else
+    body(std::false_type{});
   __syncthreads();
   if (pl.ksplit > 1) return;   // partial sums: no row statistics
   for (int mloc = tid; mloc < MROWS; mloc += THREADS) {

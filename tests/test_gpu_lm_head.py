@@ -25,7 +25,11 @@ CASES = [
     (129, 512, 777),
     (185, 1024, 2560),
     (192, 256, 1000),
+    (170, 512, 1500),    # 192-row tile, 10 real rows in its last 32-row tile (16x16 path)
+    (225, 384, 700),     # 256-row tile, 1 real row in its last 32-row tile
+    (231, 512, 1000),
     (240, 1024, 2560),
+    (250, 256, 999),     # 26 real rows in the last tile: the 32x32 path
     (300, 512, 1337),
 ]
 
