@@ -1163,11 +1163,13 @@ AttnPlan plan_tree_attn_rows(int B, int N, int node0, int nq, int Hq, int Hkv, i
   while (pl.waves < max_waves && pl.waves * wave_rows < pl.R) pl.waves *= 2;
   pl.RB = (pl.R + pl.waves * wave_rows - 1) / (pl.waves * wave_rows);
   pl.Rpad = pl.RB * pl.waves * wave_rows;
-  // About one workgroup per CU; narrow workgroups (one or two waves, one wave per SIMD
-  // at most) get three or two per CU so that every SIMD streams keys (the LDS of
-  // three fits in a CU)
+  // About one workgroup per CU for the eight-wave kernel; the narrower ones get three
+  // (one wave) or two (two or four waves) per CU, so that every SIMD streams keys
+  // with a second wave beside it (the LDS of three fits in a CU).  Four-wave
+  // workgroups are the draft expansion's 80-row queries over its 32K prefix: two per
+  // CU take 144.5 -> 115 us there; more splits than that cost more in the merge.
   const long long units = (long long)B * Hkv * pl.RB;
-  const int wg_per_cu = pl.waves == 1 ? 3 : (pl.waves == 2 ? 2 : 1);
+  const int wg_per_cu = pl.waves == 1 ? 3 : (pl.waves == 2 || pl.waves == 4 ? 2 : 1);
   int s_target = (int)(((long long)kNumCUs * wg_per_cu + units - 1) / units);
   int s_max = P / min_split_keys(pl.waves);
   int S = s_target < s_max ? s_target : s_max;
