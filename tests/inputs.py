@@ -97,6 +97,9 @@ DRAFT_CASES = [
     (26, 3, 192, 2, 1, 64, 320, 96, 37, 5, 3, 16, True),
     (7, 4, 256, 4, 2, 64, 512, 200, 100, 4, 4, 12, False),
     (4, 2, 256, 4, 2, 64, 512, 1000, 100, 4, 4, 12, False),
+    # 225 rows per depth (45 x 5): the GEMMs' 256-row tile with one real row in its
+    # last 32-row tile (the 16x16x32 path), split over K in W_down (I = 2048)
+    (31, 45, 128, 4, 2, 64, 2048, 300, 40, 5, 3, 12, False),
 ]
 # Float tolerance (max-abs, logits and bf16 features) of the draft expansion: at least
 # 1.5 x the largest deviation from the fp64 oracle that a CPU model of the kernels'
