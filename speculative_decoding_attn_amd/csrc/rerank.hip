@@ -309,36 +309,64 @@ rerank_merge(RerankPlan pl, void* ws, float* __restrict__ draft_lse) {
   if (rr >= pl.B * pl.nrows) return;
   const int row = (rr / pl.nrows) * pl.R + pl.row0 + rr % pl.nrows;
   const int k = pl.k, chunks = pl.chunks;
-  float mx = -INFINITY;
-  for (int c = lane; c < chunks; c += 64) mx = fmaxf(mx, w.chunk_mz[(size_t)row * chunks + c].x);
+  const float* cv = w.chunk_v + (size_t)row * chunks * k;
+  const int* ci = w.chunk_i + (size_t)row * chunks * k;
+  const int n_all = chunks * k;
+  // every load the wave needs is requested here, before any of it is used: the chunk
+  // (max, exp-sum) pairs, the chunk maxima for the threshold, and the first
+  // kMergePre * 64 list entries (one memory round trip for the usual sizes)
+  constexpr int kMergePre = 4;
+  float2 mz[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int c = lane + 64 * u;
+    mz[u] = c < chunks ? w.chunk_mz[(size_t)row * chunks + c] : make_float2(-INFINITY, 0.f);
+  }
+  const bool use_thr = chunks <= 64 && k <= chunks;
+  const float cm = (use_thr && lane < chunks) ? cv[(size_t)lane * k] : -INFINITY;
+  float pv[kMergePre];
+  int pi[kMergePre];
+#pragma unroll
+  for (int u = 0; u < kMergePre; ++u) {
+    const int e = 64 * u + lane;
+    pv[u] = e < n_all ? cv[e] : -INFINITY;
+    pi[u] = e < n_all ? ci[e] : 0;
+  }
+  float mx = fmaxf(mz[0].x, mz[1].x);
+  for (int c = lane + 128; c < chunks; c += 64) mx = fmaxf(mx, w.chunk_mz[(size_t)row * chunks + c].x);
   mx = wave_reduce<true>(mx);
   float z = 0.f;
-  for (int c = lane; c < chunks; c += 64) {
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    if (mz[u].x > -INFINITY) z += mz[u].y * __builtin_amdgcn_exp2f((mz[u].x - mx) * kLog2e);
+  for (int c = lane + 128; c < chunks; c += 64) {
     const float2 e = w.chunk_mz[(size_t)row * chunks + c];
     if (e.x > -INFINITY) z += e.y * __builtin_amdgcn_exp2f((e.x - mx) * kLog2e);
   }
   z = wave_reduce<false>(z);
   if (lane == 0) draft_lse[row] = mx + logf(z);
 
-  const float* cv = w.chunk_v + (size_t)row * chunks * k;
-  const int* ci = w.chunk_i + (size_t)row * chunks * k;
   // threshold: k-th largest chunk maximum (entry 0 of each chunk list); chunks <= 64
   // whenever chunks * k <= 1024 and k >= 16, otherwise keep everything
-  float thr = -INFINITY;
-  if (chunks <= 64 && k <= chunks) {
-    const float cm = lane < chunks ? cv[(size_t)lane * k] : -INFINITY;
-    thr = wave_kth_largest(cm, k);
-  }
+  const float thr = use_thr ? wave_kth_largest(cm, k) : -INFINITY;
   // keep entries >= thr (lane-major over the chunks * k entries)
   uint64_t* kk = keys[wid];
-  const int n_all = chunks * k;
   int kept = 0;
   for (int base = 0; base < n_all; base += 64) {
     const int e = base + lane;
-    const float v = e < n_all ? cv[e] : -INFINITY;
+    const int u = base / 64;
+    float v;
+    int vi;
+    if (u < kMergePre) {
+      v = u == 0 ? pv[0] : (u == 1 ? pv[1] : (u == 2 ? pv[2] : pv[3]));
+      vi = u == 0 ? pi[0] : (u == 1 ? pi[1] : (u == 2 ? pi[2] : pi[3]));
+    } else {
+      v = e < n_all ? cv[e] : -INFINITY;
+      vi = e < n_all ? ci[e] : 0;
+    }
     const bool keep = e < n_all && v >= thr;
     const uint64_t m = __ballot(keep);
-    if (keep) kk[kept + __popcll(m & ((1ull << lane) - 1ull))] = vi_key(v, ci[e]);
+    if (keep) kk[kept + __popcll(m & ((1ull << lane) - 1ull))] = vi_key(v, vi);
     kept += __popcll(m);
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the wave's own LDS writes are done
