@@ -517,14 +517,37 @@ tree_attn_merge_hw(AttnPlan pl, const float* __restrict__ part_o, const float* _
       }
     }
   } else {
-    for (int s = 0; s < ns; ++s) mx = fmaxf(mx, part_lse[(size_t)attn_slot(pl, b, g, s) * pl.Rpad + r]);
-    for (int s = 0; s < ns; ++s) {
-      const size_t prow = (size_t)attn_slot(pl, b, g, s) * pl.Rpad + r;
-      const float wgt = expf(part_lse[prow] - mx);
-      wsum += wgt;
-      const f32x4 o = *(const f32x4*)(part_o + prow * D + lane * 4);
+    // more splits: the same arithmetic in two passes over batches of MS splits, each
+    // batch's loads issued at once (the max first, then the weighted sum in split order)
+    for (int s0 = 0; s0 < ns; s0 += MS) {
+      float l[MS];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] += wgt * o[e];
+      for (int s = 0; s < MS; ++s)
+        if (s0 + s < ns) l[s] = part_lse[(size_t)attn_slot(pl, b, g, s0 + s) * pl.Rpad + r];
+#pragma unroll
+      for (int s = 0; s < MS; ++s)
+        if (s0 + s < ns) mx = fmaxf(mx, l[s]);
+    }
+    for (int s0 = 0; s0 < ns; s0 += MS) {
+      float l[MS];
+      f32x4 o[MS];
+#pragma unroll
+      for (int s = 0; s < MS; ++s) {
+        if (s0 + s < ns) {
+          const size_t prow = (size_t)attn_slot(pl, b, g, s0 + s) * pl.Rpad + r;
+          l[s] = part_lse[prow];
+          o[s] = *(const f32x4*)(part_o + prow * D + lane * 4);
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < MS; ++s) {
+        if (s0 + s < ns) {
+          const float wgt = expf(l[s] - mx);
+          wsum += wgt;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[e] += wgt * o[s][e];
+        }
+      }
     }
   }
   const float inv = 1.f / wsum;
