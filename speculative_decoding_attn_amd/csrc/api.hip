@@ -543,6 +543,13 @@ hipError_t draft_gemm(int M, int K, int N, const void* X, const void* W, float* 
   return eagle::launch_gemm_f32(M, K, N, X, W, out, ws + L.off_lm, stream);
 }
 
+// the same GEMM with its split-K slices handed to the consumer kernel, which sums
+// them while reading (no separate summing pass)
+hipError_t draft_gemm_slices(int M, int K, int N, const void* X, const void* W, float* out, char* ws,
+                             const DraftLayout& L, eagle::F32Slices* r, hipStream_t stream) {
+  return eagle::launch_gemm_f32_slices(M, K, N, X, W, out, ws + L.off_lm, r, stream);
+}
+
 }  // namespace
 
 size_t eagle_draft_expand_workspace(int32_t B, int32_t H, int32_t Hq, int32_t Hkv, int32_t D,
@@ -611,20 +618,21 @@ eagle_status_t eagle_draft_expand(const eagle_draft_head* head, const void* f0,
                 "draft frontier");
     DRAFT_TRY(eagle::launch_draft_gather_input(dd, row0, nr, f0, root_token, head->embed, features,
                                                row_token, parent_row, X, stream), "draft gather");
-    DRAFT_TRY(draft_gemm(M, 2 * H, H, X, head->w_fc, G, ws, L, stream), "draft fc");
-    DRAFT_TRY(eagle::launch_draft_rms(M, H, eps, G, H, nullptr, head->g1, xres, nb, stream), "draft norm 1");
-    DRAFT_TRY(draft_gemm(M, H, qkvn, nb, head->w_qkv, G, ws, L, stream), "draft qkv");
-    DRAFT_TRY(eagle::launch_draft_qkv_scatter(dd, row0, nr, G, qbuf, k_cache, v_cache, stream), "draft scatter");
+    eagle::F32Slices gs;
+    DRAFT_TRY(draft_gemm_slices(M, 2 * H, H, X, head->w_fc, G, ws, L, &gs, stream), "draft fc");
+    DRAFT_TRY(eagle::launch_draft_rms(M, H, eps, gs, nullptr, head->g1, xres, nb, stream), "draft norm 1");
+    DRAFT_TRY(draft_gemm_slices(M, H, qkvn, nb, head->w_qkv, G, ws, L, &gs, stream), "draft qkv");
+    DRAFT_TRY(eagle::launch_draft_qkv_scatter(dd, row0, nr, gs, qbuf, k_cache, v_cache, stream), "draft scatter");
     const eagle::AttnPlan apl = eagle::plan_tree_attn_rows(B, R, row0, nr, Hq, Hkv, D, P, kv_cap);
     DRAFT_TRY(eagle::launch_tree_attn(apl, scale, qbuf, k_cache, v_cache, parent_row, att, nullptr,
                                       ws + L.off_attws, stream), "draft attention");
     DRAFT_TRY(eagle::launch_draft_gather_rows(dd, row0, nr, Hq * D, att, nb, stream), "draft gather rows");
-    DRAFT_TRY(draft_gemm(M, Hq * D, H, nb, head->w_o, G, ws, L, stream), "draft o");
-    DRAFT_TRY(eagle::launch_draft_rms(M, H, eps, G, H, xres, head->g2, hres, nb, stream), "draft norm 2");
+    DRAFT_TRY(draft_gemm_slices(M, Hq * D, H, nb, head->w_o, G, ws, L, &gs, stream), "draft o");
+    DRAFT_TRY(eagle::launch_draft_rms(M, H, eps, gs, xres, head->g2, hres, nb, stream), "draft norm 2");
     DRAFT_TRY(draft_gemm(M, H, 2 * I, nb, head->w_gate_up, G, ws, L, stream), "draft gate/up");
     DRAFT_TRY(eagle::launch_draft_silu_mul(M, I, G, nb, stream), "draft silu");
-    DRAFT_TRY(draft_gemm(M, I, H, nb, head->w_down, G, ws, L, stream), "draft down");
-    DRAFT_TRY(eagle::launch_draft_output(dd, row0, nr, G, hres, yb, features, stream), "draft output");
+    DRAFT_TRY(draft_gemm_slices(M, I, H, nb, head->w_down, G, ws, L, &gs, stream), "draft down");
+    DRAFT_TRY(eagle::launch_draft_output(dd, row0, nr, gs, hres, yb, features, stream), "draft output");
     DRAFT_TRY(draft_gemm(M, H, V, yb, head->w_lm, G, ws, L, stream), "draft lm head");
     DRAFT_TRY(eagle::launch_draft_place_logits(dd, row0, nr, G, draft_logits, stream), "draft place");
     eagle::RerankPlan rp = L.rpl;

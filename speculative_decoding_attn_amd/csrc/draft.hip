@@ -58,6 +58,14 @@ draft_gather_input(DraftDims dd, int row0, int nr, const uint16_t* __restrict__ 
   *(u32x4*)(X + (size_t)m * 2 * H + e) = *(const u32x4*)src;
 }
 
+// 16 bytes of a GEMM output given as split-K slices, summed in slice order (the
+// order of the GEMM's own summing pass)
+__device__ __forceinline__ f32x4 load4(const F32Slices& a, size_t i) {
+  f32x4 v = *(const f32x4*)(a.p + i);
+  for (int s = 1; s < a.S; ++s) v += *(const f32x4*)(a.p + (size_t)s * a.stride + i);
+  return v;
+}
+
 constexpr int kRmsThreads = 1024;
 constexpr int kRmsRegs = 4;   // float4 pieces per thread kept in registers: H <= 16384
 
@@ -65,13 +73,13 @@ constexpr int kRmsRegs = 4;   // float4 pieces per thread kept in registers: H <
 // One 1024-thread workgroup per row; for H <= 16384 every thread keeps its pieces of
 // s in registers, beyond that s is re-read from res_out.
 __global__ void __launch_bounds__(kRmsThreads)
-draft_rms(int H, float eps, const float* __restrict__ a, int lda, const float* __restrict__ res,
+draft_rms(int H, float eps, F32Slices a, const float* __restrict__ res,
           const float* __restrict__ gain, float* __restrict__ res_out, uint16_t* __restrict__ norm_out) {
   __shared__ float red[kRmsThreads / 64];
   const int m = blockIdx.x;
   const int tid = threadIdx.x;
   const int nq = H / 4;
-  const f32x4* ar = (const f32x4*)(a + (size_t)m * lda);
+  const size_t a0 = (size_t)m * H;   // this row's first entry in each slice of a
   const f32x4* rr = res ? (const f32x4*)(res + (size_t)m * H) : nullptr;
   f32x4* so = (f32x4*)(res_out + (size_t)m * H);
   f32x4 sv[kRmsRegs];
@@ -80,7 +88,7 @@ draft_rms(int H, float eps, const float* __restrict__ a, int lda, const float* _
   for (int j = 0; j < kRmsRegs; ++j) {
     const int q = tid + j * kRmsThreads;
     if (q < nq) {
-      f32x4 v = ar[q];
+      f32x4 v = load4(a, a0 + 4 * (size_t)q);
       if (rr) v += rr[q];
       sv[j] = v;
       so[q] = v;
@@ -88,7 +96,7 @@ draft_rms(int H, float eps, const float* __restrict__ a, int lda, const float* _
     }
   }
   for (int q = tid + kRmsRegs * kRmsThreads; q < nq; q += kRmsThreads) {
-    f32x4 v = ar[q];
+    f32x4 v = load4(a, a0 + 4 * (size_t)q);
     if (rr) v += rr[q];
     so[q] = v;
     ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
@@ -117,7 +125,7 @@ draft_rms(int H, float eps, const float* __restrict__ a, int lda, const float* _
 // qkv fp32 [M][(Hq + 2 Hkv) D] -> q bf16 at [b][r][Hq][D]; k, v bf16 at cache row P + r.
 // A thread's 8 columns stay inside one head (D and the q / k / v widths are multiples of 8).
 __global__ void __launch_bounds__(kGlueThreads)
-draft_qkv_scatter(DraftDims dd, int row0, int nr, const float* __restrict__ qkv,
+draft_qkv_scatter(DraftDims dd, int row0, int nr, F32Slices qkv,
                   uint16_t* __restrict__ qbuf, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc) {
   const int m = blockIdx.y;
   const int D = dd.D, qn = dd.Hq * D, kn = dd.Hkv * D;
@@ -126,8 +134,8 @@ draft_qkv_scatter(DraftDims dd, int row0, int nr, const float* __restrict__ qkv,
   int b;
   const int grow = seq_row(m, nr, row0, dd.R, &b);
   const int r = grow - b * dd.R;
-  const f32x4* src = (const f32x4*)(qkv + (size_t)m * (qn + 2 * kn) + e);
-  const f32x4 v0 = src[0], v1 = src[1];
+  const size_t i = (size_t)m * (qn + 2 * kn) + e;
+  const f32x4 v0 = load4(qkv, i), v1 = load4(qkv, i + 4);
   const u32x4 pk = {pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]), pack_bf16x2(v1[0], v1[1]),
                     pack_bf16x2(v1[2], v1[3])};
   if (e < qn) {
@@ -169,7 +177,7 @@ draft_silu_mul(int I, const float* __restrict__ gu, uint16_t* __restrict__ z) {
 
 // y = bf16(h + d): dense [M][H] (the LM head input) and the row's feature [b][r][H]
 __global__ void __launch_bounds__(kGlueThreads)
-draft_output(DraftDims dd, int row0, int nr, const float* __restrict__ d, const float* __restrict__ h,
+draft_output(DraftDims dd, int row0, int nr, F32Slices d, const float* __restrict__ h,
              uint16_t* __restrict__ y, uint16_t* __restrict__ feats) {
   const int m = blockIdx.y;
   const int H = dd.H;
@@ -179,7 +187,7 @@ draft_output(DraftDims dd, int row0, int nr, const float* __restrict__ d, const 
   const int grow = seq_row(m, nr, row0, dd.R, &b);
   const size_t i = (size_t)m * H + e;
   const f32x4 h0 = *(const f32x4*)(h + i), h1 = *(const f32x4*)(h + i + 4);
-  const f32x4 d0 = *(const f32x4*)(d + i), d1 = *(const f32x4*)(d + i + 4);
+  const f32x4 d0 = load4(d, i), d1 = load4(d, i + 4);
   const u32x4 pk = {pack_bf16x2(h0[0] + d0[0], h0[1] + d0[1]), pack_bf16x2(h0[2] + d0[2], h0[3] + d0[3]),
                     pack_bf16x2(h1[0] + d1[0], h1[1] + d1[1]), pack_bf16x2(h1[2] + d1[2], h1[3] + d1[3])};
   *(u32x4*)(y + i) = pk;
@@ -232,14 +240,14 @@ hipError_t launch_draft_gather_input(const DraftDims& dd, int row0, int nr, cons
   return hipGetLastError();
 }
 
-hipError_t launch_draft_rms(int M, int H, float eps, const float* a, int lda, const float* res,
+hipError_t launch_draft_rms(int M, int H, float eps, F32Slices a, const float* res,
                             const float* gain, float* res_out, void* norm_out, hipStream_t s) {
-  hipLaunchKernelGGL(draft_rms, dim3(M), dim3(kRmsThreads), 0, s, H, eps, a, lda, res, gain, res_out,
+  hipLaunchKernelGGL(draft_rms, dim3(M), dim3(kRmsThreads), 0, s, H, eps, a, res, gain, res_out,
                      (uint16_t*)norm_out);
   return hipGetLastError();
 }
 
-hipError_t launch_draft_qkv_scatter(const DraftDims& dd, int row0, int nr, const float* qkv, void* qbuf,
+hipError_t launch_draft_qkv_scatter(const DraftDims& dd, int row0, int nr, F32Slices qkv, void* qbuf,
                                     void* k_cache, void* v_cache, hipStream_t s) {
   const int width = (dd.Hq + 2 * dd.Hkv) * dd.D;
   hipLaunchKernelGGL(draft_qkv_scatter, dim3((width + kSlice - 1) / kSlice, dd.B * nr), dim3(kGlueThreads),
@@ -262,7 +270,7 @@ hipError_t launch_draft_silu_mul(int M, int I, const float* gu, void* z, hipStre
   return hipGetLastError();
 }
 
-hipError_t launch_draft_output(const DraftDims& dd, int row0, int nr, const float* d, const float* h,
+hipError_t launch_draft_output(const DraftDims& dd, int row0, int nr, F32Slices d, const float* h,
                                void* y, void* feats, hipStream_t s) {
   hipLaunchKernelGGL(draft_output, dim3((dd.H + kSlice - 1) / kSlice, dd.B * nr), dim3(kGlueThreads), 0, s,
                      dd, row0, nr, d, h,

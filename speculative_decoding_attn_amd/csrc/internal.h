@@ -70,7 +70,19 @@ LmPlan plan_lm_head(int M, int H, int V);
 size_t lm_head_workspace_bytes(const LmPlan& pl);
 // Plain GEMM out[M][N] = X[M][K] W[N][K]^T in fp32 on the LM-head kernel, with split-K
 // (fp32 partials summed by a second kernel) when the N tiles alone leave most CUs idle.
+// A GEMM output left as its split-K slices: element i is p[i] + p[stride + i] + ... +
+// p[(S-1) stride + i], summed in slice order (S = 1: the plain output p).
+struct F32Slices {
+  const float* p;
+  int S;
+  size_t stride;
+};
+
 size_t gemm_f32_workspace_bytes(int M, int K, int N);
+// launch_gemm_f32 without its slice-summing pass: the result as slices (in the
+// workspace when the GEMM splits K, else in `out`), for a consumer that sums them
+hipError_t launch_gemm_f32_slices(int M, int K, int N, const void* X, const void* W, float* out,
+                                  void* workspace, F32Slices* result, hipStream_t stream);
 hipError_t launch_gemm_f32(int M, int K, int N, const void* X, const void* W, float* out,
                            void* workspace, hipStream_t stream);
 hipError_t launch_lm_head(const LmPlan& pl, const void* hidden, const void* W, float* out_max,
@@ -150,14 +162,14 @@ hipError_t launch_draft_gather_input(const DraftDims& dd, int row0, int nr, cons
                                      const int32_t* root_token, const void* embed, const void* feats,
                                      const int32_t* row_token, const int32_t* parent_row, void* X,
                                      hipStream_t s);
-hipError_t launch_draft_rms(int M, int H, float eps, const float* a, int lda, const float* res,
+hipError_t launch_draft_rms(int M, int H, float eps, F32Slices a, const float* res,
                             const float* gain, float* res_out, void* norm_out, hipStream_t s);
-hipError_t launch_draft_qkv_scatter(const DraftDims& dd, int row0, int nr, const float* qkv, void* qbuf,
+hipError_t launch_draft_qkv_scatter(const DraftDims& dd, int row0, int nr, F32Slices qkv, void* qbuf,
                                     void* k_cache, void* v_cache, hipStream_t s);
 hipError_t launch_draft_gather_rows(const DraftDims& dd, int row0, int nr, int width, const void* src,
                                     void* dst, hipStream_t s);
 hipError_t launch_draft_silu_mul(int M, int I, const float* gu, void* z, hipStream_t s);
-hipError_t launch_draft_output(const DraftDims& dd, int row0, int nr, const float* d, const float* h,
+hipError_t launch_draft_output(const DraftDims& dd, int row0, int nr, F32Slices d, const float* h,
                                void* y, void* feats, hipStream_t s);
 hipError_t launch_draft_place_logits(const DraftDims& dd, int row0, int nr, const float* src,
                                      float* draft_logits, hipStream_t s);

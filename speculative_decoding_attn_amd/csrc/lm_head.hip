@@ -575,8 +575,8 @@ size_t gemm_f32_workspace_bytes(int M, int K, int N) {
   return b;
 }
 
-hipError_t launch_gemm_f32(int M, int K, int N, const void* X, const void* W, float* out,
-                           void* workspace, hipStream_t stream) {
+hipError_t launch_gemm_f32_slices(int M, int K, int N, const void* X, const void* W, float* out,
+                                  void* workspace, F32Slices* result, hipStream_t stream) {
   const LmPlan pl = plan_gemm_f32(M, K, N);
   f32x4* part = (f32x4*)workspace;
   float* dst = out;
@@ -591,10 +591,17 @@ hipError_t launch_gemm_f32(int M, int K, int N, const void* X, const void* W, fl
     case 5: e = launch_gemm<2, 1, 4, 1, 1>(pl, X, W, part, dst, stream); break;
     default: e = launch_gemm<1, 1, 4, 1, 1>(pl, X, W, part, dst, stream); break;
   }
-  if (e != hipSuccess || pl.ksplit == 1) return e;
-  const size_t n = (size_t)M * N;
-  hipLaunchKernelGGL(gemm_splitk_sum, dim3((unsigned)((n + 1023) / 1024)), dim3(256), 0, stream, n,
-                     pl.ksplit, dst, out);
+  *result = F32Slices{dst, pl.ksplit, (size_t)M * N};
+  return e;
+}
+
+hipError_t launch_gemm_f32(int M, int K, int N, const void* X, const void* W, float* out,
+                           void* workspace, hipStream_t stream) {
+  F32Slices r;
+  const hipError_t e = launch_gemm_f32_slices(M, K, N, X, W, out, workspace, &r, stream);
+  if (e != hipSuccess || r.S == 1) return e;
+  hipLaunchKernelGGL(gemm_splitk_sum, dim3((unsigned)((r.stride + 1023) / 1024)), dim3(256), 0, stream,
+                     r.stride, r.S, r.p, out);
   return hipGetLastError();
 }
 
