@@ -30,6 +30,8 @@ CASES = [
     (231, 512, 1000),
     (240, 1024, 2560),
     (250, 256, 999),     # 26 real rows in the last tile: the 32x32 path
+    (240, 256, 1001),    # the 16x16 path with V % 4 != 0 (element-wise logits stores)
+    (226, 128, 37),      # the 16x16 path with most vocabulary rows of the tile past V
     (300, 512, 1337),
 ]
 
