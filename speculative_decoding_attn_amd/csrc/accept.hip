@@ -310,6 +310,7 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
   __shared__ double wtot_s[kSpecThreads / 64];   // draw: wave totals of the residual mass
   __shared__ int wlast_s[kSpecThreads / 64];
   __shared__ int found_s;
+  __shared__ int tok_s[64];   // every node's token (the children's are read from here)
 
   const int chunks = pl.chunks;
   const int b = blockIdx.x / chunks;
@@ -343,6 +344,8 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
   double fallback_c = 0.0; // the previous c, should the residual at sample_c be empty
   int sample_node = 0;
   double qr[kSpecRegs], pr[kSpecRegs];   // REGS: q, p of entries t0 + i (0 past t1)
+  // the tree's tokens, read once (published by the first barrier of the node loop)
+  if (tid < 64) tok_s[tid] = tid < Nb ? tok[tid] : -1;
 
   for (;;) {
     const size_t node = (size_t)b * N + v;
@@ -380,7 +383,7 @@ accept_spec_kernel(const int32_t* __restrict__ tokens, const int32_t* __restrict
     float ktl = 0.f, kdl = 0.f;
     if (tid < nk) {
       const int kid = kids[tid];
-      const int t = tok[kid];
+      const int t = tok_s[kid];
       if (t >= 0 && t < V) {
         ktok = t;
         ktl = tl[t];
