@@ -1184,6 +1184,11 @@ AttnPlan plan_tree_attn_rows(int B, int N, int node0, int nq, int Hq, int Hkv, i
   const int max_waves = D == 64 ? 4 : 8;
   pl.waves = 1;
   while (pl.waves < max_waves && pl.waves * wave_rows < pl.R) pl.waves *= 2;
+  // D = 128, 65-128 rows (the draft expansion's 80-row queries): the eight-wave kernel,
+  // whose waves past the rows only move K and V, streams with its deeper LDS pipeline
+  // (114 -> 108 us per call there) where the four-wave kernel's two-chunk register ring
+  // runs dry
+  if (D == 128 && pl.waves == 4) pl.waves = 8;
   pl.RB = (pl.R + pl.waves * wave_rows - 1) / (pl.waves * wave_rows);
   pl.Rpad = pl.RB * pl.waves * wave_rows;
   // About one workgroup per CU for the eight-wave kernel; the narrower ones get three

@@ -59,6 +59,10 @@ CASES = [
     (1, 30, 8, 1, 128, 383, "rand"),
     (1, 30, 8, 1, 128, 450, "rand"),
     (1, 30, 8, 1, 128, 500, "chain"),
+    # D = 128 with 65-128 rows per pair: the eight-wave kernel with waves past the rows
+    # (80 rows as in the draft expansion's depths, over several splits; 128 rows)
+    (2, 10, 8, 1, 128, 4096, "rand"),
+    (1, 16, 8, 1, 128, 100, "chain"),
 ]
 
 
