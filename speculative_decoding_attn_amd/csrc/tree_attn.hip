@@ -90,7 +90,7 @@ __device__ __forceinline__ int attn_nsplit(const AttnPlan& pl, int b) {
 }
 
 // Shortest split: narrow workgroups (one or two waves) are cheap to start, so their
-// splits go down to 128 keys (C2: 22.0 -> 17.5 us); the eight-wave kernel's stay at
+// splits go down to 128 keys (head dim 64); the eight-wave kernel's stay at
 // kMinSplitKeys.  The uniform and the ragged plans use the same bound.
 __host__ __device__ inline int min_split_keys(int waves) { return waves <= 2 ? 128 : kMinSplitKeys; }
 
@@ -1184,18 +1184,18 @@ AttnPlan plan_tree_attn_rows(int B, int N, int node0, int nq, int Hq, int Hkv, i
   const int max_waves = D == 64 ? 4 : 8;
   pl.waves = 1;
   while (pl.waves < max_waves && pl.waves * wave_rows < pl.R) pl.waves *= 2;
-  // D = 128, 65-128 rows (the draft expansion's 80-row queries): the eight-wave kernel,
-  // whose waves past the rows only move K and V, streams with its deeper LDS pipeline
-  // (114 -> 108 us per call there) where the four-wave kernel's two-chunk register ring
-  // runs dry
-  if (D == 128 && pl.waves == 4) pl.waves = 8;
+  // D = 128 always takes the eight-wave kernel, also for 128 rows or fewer: its waves
+  // past the rows only move K and V, and its four 64-key LDS stages keep more of the
+  // stream in flight than the narrow kernels' two-chunk register ring (the draft
+  // expansion's 80-row queries 114 -> 108 us, its 8-row ones 102 -> 93 us, C2's 26
+  // rows 16.7 -> 14.9 us); the narrow kernels serve D = 64
+  if (D == 128) pl.waves = 8;
   pl.RB = (pl.R + pl.waves * wave_rows - 1) / (pl.waves * wave_rows);
   pl.Rpad = pl.RB * pl.waves * wave_rows;
-  // About one workgroup per CU for the eight-wave kernel; the narrower ones get three
-  // (one wave) or two (two or four waves) per CU, so that every SIMD streams keys
-  // with a second wave beside it (the LDS of three fits in a CU).  Four-wave
-  // workgroups are the draft expansion's 80-row queries over its 32K prefix: two per
-  // CU take 144.5 -> 115 us there; more splits than that cost more in the merge.
+  // About one workgroup per CU for the eight-wave kernel; the narrower ones (head dim
+  // 64) get three (one wave) or two (two or four waves) per CU, so that every SIMD
+  // streams keys with a second wave beside it (the LDS of three fits in a CU); more
+  // splits than that cost more in the merge.
   const long long units = (long long)B * Hkv * pl.RB;
   const int wg_per_cu = pl.waves == 1 ? 3 : (pl.waves == 2 || pl.waves == 4 ? 2 : 1);
   int s_target = (int)(((long long)kNumCUs * wg_per_cu + units - 1) / units);
