@@ -45,7 +45,7 @@ CASES = [
     (2, 60, 8, 1, 128, 777, "rand"),
     (1, 40, 16, 2, 128, 2048, "rand"),
     (1, 5, 12, 4, 64, 5000, "rand"),
-    # the D = 128 eight-wave kernel (more than 128 rows per pair) on a tree with no
+    # the D = 128 eight-wave kernel with more than 128 rows per pair on a tree with no
     # prefix (two chunks, both masked) and on a one-chunk split
     (1, 60, 16, 2, 128, 0, "rand"),
     (2, 20, 16, 2, 128, 0, "rand"),
