@@ -1144,16 +1144,16 @@ template <int D>
 hipError_t launch_fwd_d(const AttnPlan& pl, const void* q, const void* k, const void* v,
                         const int32_t* parents, void* out, float* lse, float* part_o,
                         float* part_lse, hipStream_t stream) {
-  if constexpr (D == 128) {   // D=64 uses at most 4 waves (chunk staging must divide evenly)
-    if (pl.waves == 8) {
-      if (pl.block_table)
-        return launch_d128<true>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
-      return launch_d128<false>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
-    }
+  if constexpr (D == 128) {   // every D = 128 plan has eight waves (plan_tree_attn_rows)
+    if (pl.waves != 8) return hipErrorInvalidValue;
+    if (pl.block_table)
+      return launch_d128<true>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
+    return launch_d128<false>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
+  } else {   // D = 64: at most four waves (chunk staging must divide evenly)
+    if (pl.waves == 4) return launch_fwd<D, 4>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
+    if (pl.waves == 2) return launch_fwd<D, 2>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
+    return launch_fwd<D, 1>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
   }
-  if (pl.waves == 4) return launch_fwd<D, 4>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
-  if (pl.waves == 2) return launch_fwd<D, 2>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
-  return launch_fwd<D, 1>(pl, q, k, v, parents, out, lse, part_o, part_lse, stream);
 }
 
 }  // namespace
